@@ -1,0 +1,243 @@
+"""Blockwise-scaled FP8 oracle (CPU): plain reference for the quantize + scaled-GEMM path.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this package. The product path (the HIP library and its Python
+binding) never imports it, and it imports nothing from the product path.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE binary32 for the quantizer steps, fp64 for the
+GEMM); this module only builds/loads it with gcc and marshals numpy arrays. The SQNR helpers below
+follow the GEMM-correctness table of "Enable blockwise FP8 dense training kernels on ROCm"
+(FP8 GEMM compared with a BF16 matmul by SQNR in dB).
+
+Array conventions:
+  bf16 tensors are ``np.uint16`` bit patterns; fp8 tensors are ``np.uint8`` e4m3fn codes.
+  ``a_s`` of the LHS quantizer is column-major [M, Kb]; it is returned as a C-contiguous numpy
+  array of shape (Kb, M), which has the same bytes (element (m, kb) at kb * M + m).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+BLOCK = 128
+
+_CFLAGS = [
+    "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
+    "-fopenmp", "-fPIC", "-shared", "-Wall",
+]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (seconds)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", *_CFLAGS, os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(LIB_PATH)
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode_array.argtypes = [_f32p, _u8p, _i64]
+        L.oracle_e4m3_encode_array.restype = None
+        L.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, _u8p, _i64]
+        L.oracle_e4m3_encode_bits.restype = None
+        L.oracle_quantize_lhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
+        L.oracle_quantize_rhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
+        L.oracle_quantize_weight_128x128.argtypes = [
+            _u16p, _i64, _i64, _i64, _u8p, _i64, _u8p, _i64, _f32p]
+        L.oracle_gemm_1x128_128x128.argtypes = [
+            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64, _i64, _i64p, _i64, _f64p]
+        L.oracle_gemm_1x128_128x1.argtypes = [
+            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64p, _i64, _f64p]
+        for f in ("oracle_quantize_lhs", "oracle_quantize_rhs", "oracle_quantize_weight_128x128",
+                  "oracle_gemm_1x128_128x128", "oracle_gemm_1x128_128x1", "oracle_num_threads"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(arr, t):
+    return arr.ctypes.data_as(t)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what}: oracle returned {rc}")
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def cdiv(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+# ------------------------------------------------------------------ codec
+
+def e4m3_encode(v) -> np.ndarray:
+    """Round-to-nearest-even, saturating e4m3fn encode of fp32 values (finite inputs)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_array(_p(v, _f32p), _p(out, _u8p), v.size)
+    return out
+
+
+def e4m3_encode_bits(first: int, n: int) -> np.ndarray:
+    """Codes of the fp32 bit patterns first .. first+n-1 (NaN patterns give 0xFF)."""
+    out = np.empty(n, dtype=np.uint8)
+    lib().oracle_e4m3_encode_bits(ctypes.c_uint32(first), _p(out, _u8p), n)
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    table = np.array([lib().oracle_e4m3_decode(i) for i in range(256)], dtype=np.float64)
+    return table[codes]
+
+
+# ------------------------------------------------------------------ quantizers
+
+def quantize_lhs(x: np.ndarray):
+    """1x128 row-wise groups of x [M, K] (bf16 bits). Returns (q [M, K], a_s as (Kb, M))."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, K = x.shape
+    Kb = cdiv(K, BLOCK)
+    q = np.zeros((M, K), dtype=np.uint8)
+    a_s = np.zeros((Kb, M), dtype=np.float32)
+    _check(lib().oracle_quantize_lhs(_p(x, _u16p), M, K, K, _p(q, _u8p), K, _p(a_s, _f32p)),
+           "quantize_lhs")
+    return q, a_s
+
+
+def quantize_rhs(x: np.ndarray):
+    """128x1 column-wise groups of x [K, N] (bf16 bits). Returns (qT [N, K], s [Kb, N])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    K, N = x.shape
+    Kb = cdiv(K, BLOCK)
+    qT = np.zeros((N, K), dtype=np.uint8)
+    s = np.zeros((Kb, N), dtype=np.float32)
+    _check(lib().oracle_quantize_rhs(_p(x, _u16p), K, N, N, _p(qT, _u8p), K, _p(s, _f32p)),
+           "quantize_rhs")
+    return qT, s
+
+
+def quantize_weight_128x128(w: np.ndarray, want_qT: bool = True):
+    """128x128 blocks of w [N, K] (bf16 bits). Returns (q [N, K], qT [K, N] or None, s [Nb, Kb])."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    N, K = w.shape
+    q = np.zeros((N, K), dtype=np.uint8)
+    qT = np.zeros((K, N), dtype=np.uint8) if want_qT else None
+    s = np.zeros((cdiv(N, BLOCK), cdiv(K, BLOCK)), dtype=np.float32)
+    qTp = _p(qT, _u8p) if want_qT else None
+    _check(lib().oracle_quantize_weight_128x128(_p(w, _u16p), N, K, K, _p(q, _u8p), K, qTp, N,
+                                                _p(s, _f32p)), "quantize_weight_128x128")
+    return q, qT, s
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def _rows_arg(rows, M):
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    return np.ascontiguousarray(rows, dtype=np.int64)
+
+
+def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb, bs_stride_kb, rows=None) -> np.ndarray:
+    """fp64 C rows for A [M, K] codes, a_s (Kb, M), B [N, K] codes, 128x128 b_s via strides."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.float32)
+    b_s = np.ascontiguousarray(b_s, dtype=np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    rows = _rows_arg(rows, M)
+    out = np.zeros((rows.size, N), dtype=np.float64)
+    _check(lib().oracle_gemm_1x128_128x128(
+        _p(a, _u8p), K, _p(a_s, _f32p), _p(b, _u8p), K, _p(b_s, _f32p),
+        bs_stride_nb, bs_stride_kb, M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p)),
+        "gemm_1x128_128x128")
+    return out
+
+
+def gemm_1x128_128x1(a, a_s, b, b_s, rows=None) -> np.ndarray:
+    """fp64 C rows for A [M, K] codes, a_s (Kb, M), B [N, K] codes, per-column b_s [Kb, N]."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.float32)
+    b_s = np.ascontiguousarray(b_s, dtype=np.float32)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K
+    rows = _rows_arg(rows, M)
+    out = np.zeros((rows.size, N), dtype=np.float64)
+    _check(lib().oracle_gemm_1x128_128x1(
+        _p(a, _u8p), K, _p(a_s, _f32p), _p(b, _u8p), K, _p(b_s, _f32p),
+        M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p)), "gemm_1x128_128x1")
+    return out
+
+
+# ------------------------------------------------------------------ accuracy metrics
+
+def bf16_bits_to_f64(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.uint16)
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def matmul_bf16_f64(a_bits, b_bits_nk, rows=None) -> np.ndarray:
+    """fp64 reference C = A @ B^T of the original bf16 operands (B given as [N, K])."""
+    a = bf16_bits_to_f64(a_bits if rows is None else np.asarray(a_bits)[rows])
+    b = bf16_bits_to_f64(b_bits_nk)
+    return a @ b.T
+
+
+def sqnr_db(ref, test) -> float:
+    """20 log10(||ref||_F / ||ref - test||_F)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    test = np.asarray(test, dtype=np.float64)
+    err = np.linalg.norm(ref - test)
+    if err == 0.0:
+        return float("inf")
+    return float(20.0 * np.log10(np.linalg.norm(ref) / err))
+
+
+def gemm_tolerance_report(c, c_oracle) -> dict:
+    """Elementwise bound |C - C_o| <= 2e-2 (|C_o| + 1) and relative Frobenius error."""
+    c = np.asarray(c, dtype=np.float64)
+    c_oracle = np.asarray(c_oracle, dtype=np.float64)
+    diff = np.abs(c - c_oracle)
+    bound = 2e-2 * (np.abs(c_oracle) + 1.0)
+    nf = np.linalg.norm(c_oracle)
+    rel_f = float(np.linalg.norm(c - c_oracle) / nf) if nf > 0 else float(np.linalg.norm(c))
+    return {
+        "max_excess": float(np.max(diff - bound)) if diff.size else 0.0,
+        "n_bad": int(np.count_nonzero(diff > bound)),
+        "rel_frobenius": rel_f,
+        "ok": bool(np.all(diff <= bound) and rel_f <= 4e-3),
+    }

@@ -1,0 +1,160 @@
+"""Pins for the oracle's two scaled GEMMs and the SQNR metric (CPU only).
+
+Pinned by: brute force over the dequantized operands (a different, algebraically identical
+evaluation), a library matmul for the single-K-block unit-scale case, a closed form, the pages'
+printed SQNR levels (tests/golden/pages_sqnr_table.txt) and the pages' scale-store bug as a planted
+negative control.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from blockwise_scaled_fp8_act_amd import inputs
+from tests import _golden
+
+FINITE_CODES = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def _rand_codes(g, shape):
+    return g.choice(FINITE_CODES, size=shape)
+
+
+def _rand_scales(g, shape):
+    return (np.exp2(g.uniform(-12, 4, size=shape))).astype(np.float32)
+
+
+def _dequant_brute(a, a_s_kbm, b, b_scale_of):
+    """Direct sum over k of (A[m,k] a_s[m,k//128]) (B[n,k] b_scale(k//128, n)), one element at a
+    time with plain Python floats (fp64), no blocking."""
+    M, K = a.shape
+    N = b.shape[0]
+    da = oracle.e4m3_decode(a)
+    db = oracle.e4m3_decode(b)
+    out = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                kb = k // 128
+                acc += (da[m, k] * float(a_s_kbm[kb, m])) * (db[n, k] * float(b_scale_of(kb, n)))
+            out[m, n] = acc
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 300), (2, 130, 128), (4, 257, 129), (1, 1, 1)])
+def test_gemm_128x128_bruteforce(M, N, K):
+    g = np.random.Generator(np.random.PCG64(M * 1000 + N + K))
+    Kb, Nb = (K + 127) // 128, (N + 127) // 128
+    a, b = _rand_codes(g, (M, K)), _rand_codes(g, (N, K))
+    a_s, b_s = _rand_scales(g, (Kb, M)), _rand_scales(g, (Nb, Kb))
+    got = oracle.gemm_1x128_128x128(a, a_s, b, b_s, Kb, 1)
+    ref = _dequant_brute(a, a_s, b, lambda kb, n: b_s[n // 128, kb])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+    # the same b_s given transposed ([Kb, Nb]) through strides
+    got_t = oracle.gemm_1x128_128x128(a, a_s, b, np.ascontiguousarray(b_s.T), 1, Nb)
+    assert np.array_equal(got, got_t)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 300), (2, 130, 256), (5, 7, 129)])
+def test_gemm_128x1_bruteforce(M, N, K):
+    g = np.random.Generator(np.random.PCG64(M * 1000 + N + K + 1))
+    Kb = (K + 127) // 128
+    a, b = _rand_codes(g, (M, K)), _rand_codes(g, (N, K))
+    a_s, b_s = _rand_scales(g, (Kb, M)), _rand_scales(g, (Kb, N))
+    got = oracle.gemm_1x128_128x1(a, a_s, b, b_s)
+    ref = _dequant_brute(a, a_s, b, lambda kb, n: b_s[kb, n])
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_gemm_128x1_with_constant_columns_equals_128x128():
+    """Per-column scales that are constant over each 128-column block give the block-scale result."""
+    g = np.random.Generator(np.random.PCG64(5))
+    M, N, K = 6, 300, 384
+    Kb, Nb = 3, 3
+    a, b = _rand_codes(g, (M, K)), _rand_codes(g, (N, K))
+    a_s, b_blk = _rand_scales(g, (Kb, M)), _rand_scales(g, (Nb, Kb))
+    b_col = np.ascontiguousarray(np.repeat(b_blk.T, 128, axis=1)[:, :N])
+    assert np.array_equal(oracle.gemm_1x128_128x1(a, a_s, b, b_col),
+                          oracle.gemm_1x128_128x128(a, a_s, b, b_blk, Kb, 1))
+
+
+def test_single_block_unit_scales_is_plain_matmul():
+    g = np.random.Generator(np.random.PCG64(6))
+    a, b = _rand_codes(g, (17, 128)), _rand_codes(g, (33, 128))
+    ones_a, ones_b = np.ones((1, 17), np.float32), np.ones((1, 1), np.float32)
+    got = oracle.gemm_1x128_128x128(a, ones_a, b, ones_b, 1, 1)
+    ta = torch.from_numpy(a.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    tb = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    assert np.array_equal(got, (ta @ tb.T).numpy())
+
+
+@pytest.mark.parametrize("K", [128, 200, 1280])
+def test_closed_form_constant_codes(K):
+    """All codes 0x38 (= 1.0), a_s = alpha, b_s = beta: C = alpha * beta * K."""
+    M, N = 3, 260
+    Kb, Nb = (K + 127) // 128, (N + 127) // 128
+    a = np.full((M, K), 0x38, np.uint8)
+    b = np.full((N, K), 0x38, np.uint8)
+    alpha, beta = np.float32(0.375), np.float32(3.0e-3)
+    got = oracle.gemm_1x128_128x128(a, np.full((Kb, M), alpha, np.float32), b,
+                                    np.full((Nb, Kb), beta, np.float32), Kb, 1)
+    assert np.all(got == float(alpha) * float(beta) * K)
+
+
+def test_row_subset_and_empty_k():
+    g = np.random.Generator(np.random.PCG64(8))
+    a, b = _rand_codes(g, (9, 256)), _rand_codes(g, (20, 256))
+    a_s, b_s = _rand_scales(g, (2, 9)), _rand_scales(g, (1, 2))
+    full = oracle.gemm_1x128_128x128(a, a_s, b, b_s, 2, 1)
+    part = oracle.gemm_1x128_128x128(a, a_s, b, b_s, 2, 1, rows=[8, 0, 4])
+    assert np.array_equal(part, full[[8, 0, 4]])
+    z = oracle.gemm_1x128_128x128(np.zeros((3, 0), np.uint8), np.zeros((0, 3), np.float32),
+                                  np.zeros((4, 0), np.uint8), np.zeros((1, 0), np.float32), 0, 1)
+    assert z.shape == (3, 4) and np.all(z == 0)
+
+
+def _oracle_path_sqnr(M, N, K, seed=0, rows=None):
+    g = inputs.rng(seed)
+    a = inputs.normal_bf16(g, (M, K))
+    w = inputs.normal_bf16(g, (N, K), 0.02)
+    qa, sa = oracle.quantize_lhs(a)
+    qw, _, sw = oracle.quantize_weight_128x128(w, want_qT=False)
+    c = oracle.gemm_1x128_128x128(qa, sa, qw, sw, sw.shape[1], 1, rows=rows)
+    ref = oracle.matmul_bf16_f64(a, w, rows=rows)
+    return oracle.sqnr_db(ref, c)
+
+
+@pytest.mark.parametrize("row", _golden.table("pages_sqnr_table.txt"),
+                         ids=lambda r: "x".join(str(int(v)) for v in r[:3]))
+def test_sqnr_matches_pages_table(row):
+    """The pages print 28.6-28.8 dB for the FP8 path against a BF16 matmul. Tiny outputs (M=2, 4) have
+    a seed-to-seed spread of about 0.35 dB, so they get a wider band; at M >= 128 the SQNR of 64
+    sampled rows must sit within 0.3 dB of the printed value."""
+    M, N, K, db = int(row[0]), int(row[1]), int(row[2]), row[3]
+    rows = None if M <= 128 else np.linspace(0, M - 1, 64).astype(np.int64)
+    s = _oracle_path_sqnr(M, N, K, rows=rows)
+    band = 1.2 if M * N < 100000 else 0.3
+    assert abs(s - db) <= band, s
+
+
+def test_sqnr_negative_control_scale_store_bug():
+    """Planted in the oracle's output on the CPU: the pages' quantizer bug wrote scales of rows >= M
+    into the column-major a_s, landing on the next K-block's rows. The SQNR metric must fall to the
+    2-10 dB the pages report for it."""
+    g = inputs.rng(1)
+    M, N, K = 2, 512, 256
+    a = inputs.normal_bf16(g, (M, K))
+    w = inputs.normal_bf16(g, (N, K), 0.02)
+    qa, sa = oracle.quantize_lhs(a)
+    qw, _, sw = oracle.quantize_weight_128x128(w, want_qT=False)
+    ref = oracle.matmul_bf16_f64(a, w)
+    good = oracle.gemm_1x128_128x128(qa, sa, qw, sw, sw.shape[1], 1)
+    # an unmasked 16-row store for K-block 0: rows 2..15 of an all-zero (masked-load) tile carry the
+    # eps scale and alias onto flat positions 2..15, i.e. column 1 (K-block 1) rows 0..1 ...
+    flat = sa.reshape(-1).copy()
+    eps_scale = np.float32(np.float32(1e-12) / np.float32(448))
+    flat[M:16] = eps_scale
+    bad = oracle.gemm_1x128_128x128(qa, flat[: M * 2].reshape(2, M), qw, sw, sw.shape[1], 1)
+    assert oracle.sqnr_db(ref, good) > 27.0
+    assert 2.0 <= oracle.sqnr_db(ref, bad) <= 10.0
