@@ -1,0 +1,322 @@
+"""Benchmark of the blockwise FP8 linear-layer hot path on one MI355X.
+
+Step (the timed unit): the 4096^3 forward pass of a blockwise-FP8 linear layer,
+    quantize_lhs(A [4096,4096]) + quantize_weight_128x128(W [4096,4096]) + gemm_1x128_128x128,
+on seeded synthetic bf16 inputs (A ~ N(0,1), W ~ N(0, 0.02^2)) already resident in HBM. Steps
+rotate over several input/output buffer sets (> 1 GB in total) so the 256 MB last-level cache
+does not serve the inputs of the next step.
+
+Printed: one JSON line with the whole-step throughput (2MNK per step time, TFLOP/s), the GEMM's
+roofline (TFLOP/s against the dense FP8 MFMA peak), the quantizers' GB/s against HBM, per-kernel
+figures for every kernel of the path on the training-step and outlier shapes, and the CPU oracle
+timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+BLOCK = 128
+
+
+def lhs_bytes(M, K):
+    """Algorithmic bytes of a 1x128 / 128x1 activation quantizer: read 2 B, write 1 B per element,
+    plus one fp32 scale per 128 elements."""
+    return 2 * M * K + M * K + 4 * M * ((K + BLOCK - 1) // BLOCK)
+
+
+def weight_bytes(N, K, with_qT):
+    return 2 * N * K + N * K * (2 if with_qT else 1) + 4 * ((N + 127) // 128) * ((K + 127) // 128)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--sets", type=int, default=8, help="rotated buffer sets (cold cache)")
+    p.add_argument("--no-rows", action="store_true", help="omit the per-kernel shape table")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="omit the CPU oracle leg")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="GEMM rows in the CPU oracle sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   f"(got {args.gpus}); multi-GPU sharding is design only"}))
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import blockwise_scaled_fp8_act_amd as bf
+    from blockwise_scaled_fp8_act_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def dev_bf16(h):
+        return torch.from_numpy(np.ascontiguousarray(h).view(np.int16)).to(dev)
+
+    # ---------------------------------------------------------------- step workload
+    d = inputs.make_workload(2)
+    A_h, W_h = d["A"], d["W"]
+    M, K = A_h.shape
+    N = W_h.shape[0]
+    Kb, Nb = K // BLOCK, N // BLOCK
+    sets = []
+    for i in range(args.sets):
+        A = dev_bf16(A_h)
+        W = dev_bf16(W_h)
+        sets.append(dict(
+            A=A, W=W,
+            qa=torch.empty((M, K), dtype=torch.uint8, device=dev),
+            sa=torch.empty((Kb, M), dtype=torch.float32, device=dev),
+            qw=torch.empty((N, K), dtype=torch.uint8, device=dev),
+            sw=torch.empty((Nb, Kb), dtype=torch.float32, device=dev),
+            c=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        ))
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bf.quantize_lhs(s["A"], s["qa"], s["sa"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bf.quantize_weight_128x128(s["W"], s["qw"], None, s["sw"], want_qT=False, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bf.gemm_1x128_128x128(s["qa"], s["sa"], s["qw"], s["sw"], c=s["c"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    k_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    k_avg = k_ms.mean(axis=0)
+    k_med = np.median(k_ms, axis=0)
+
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (k_avg[2] * 1e-3) / 1e12
+    qlhs_gbs = lhs_bytes(M, K) / (k_avg[0] * 1e-3) / 1e9
+    qw_gbs = weight_bytes(N, K, False) / (k_avg[1] * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- per-kernel shape table
+    rows = []
+    if not args.no_rows:
+        rows = kernel_rows(bf, inputs, dev_bf16, dev, stream, torch)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A_h, W_h, args.cpu_rows)
+
+    out = {
+        "metric": "blockwise-FP8 GEMM TFLOPS @4096^3 (% FP8 MFMA peak) + quantizer GB/s (% HBM)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn x fp8_e4m3fn -> fp32 accumulate, bf16 in/out",
+        "data": "synthetic (seeded numpy PCG64, bf16 RNE)",
+        "config": {
+            "workload": "forward 4096^3: quantize_lhs A[4096,4096] + quantize_weight_128x128 "
+                        "W[4096,4096] + gemm_1x128_128x128 (A~N(0,1), W~N(0,0.02^2))",
+            "M": M, "N": N, "K": K, "rotated_sets": len(sets),
+            "rotated_bytes": set_bytes * len(sets),
+        },
+        "roofline": {
+            "kernel": "gemm_1x128_128x128",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+        },
+        "step_kernels": {
+            "quantize_lhs": {"avg_us": round(k_avg[0] * 1e3, 2), "median_us": round(k_med[0] * 1e3, 2),
+                             "GB/s": round(qlhs_gbs, 1), "frac_hbm": round(qlhs_gbs / PEAK_HBM_GBS, 4)},
+            "quantize_weight_128x128": {"avg_us": round(k_avg[1] * 1e3, 2),
+                                        "median_us": round(k_med[1] * 1e3, 2),
+                                        "GB/s": round(qw_gbs, 1),
+                                        "frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4)},
+            "gemm_1x128_128x128": {"avg_us": round(k_avg[2] * 1e3, 2),
+                                   "median_us": round(k_med[2] * 1e3, 2),
+                                   "TFLOP/s": round(gemm_tflops, 1),
+                                   "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
+        },
+        "rows": rows,
+        "cpu_baseline": cpu,
+        "context": {"pages_mi300x_triton_fp8_tflops_4096": 299.3,
+                    "pages_mi300x_hipblas_bf16_tflops_4096": 565.8},
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def _time_kernel(fn, reps, stream, torch):
+    """Average and median duration (ms) of fn(i) over reps launches, HIP events on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(t.mean()), float(np.median(t))
+
+
+def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
+    """Per-kernel timings on the training-step (8192 tokens, 4096x4096 weight) and outlier
+    (16384 x 5120 x 5120) shapes, each rotating over buffer sets larger than the cache."""
+    out = []
+
+    def add(name, shape, avg, med, work, unit):
+        rate = work / (avg * 1e-3)
+        if unit == "GB/s":
+            r, peak = rate / 1e9, PEAK_HBM_GBS
+        else:
+            r, peak = rate / 1e12, PEAK_FP8_TFLOPS
+        out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2),
+                    "median_us": round(med * 1e3, 2), unit: round(r, 1),
+                    "frac": round(r / peak, 4)})
+
+    d3 = inputs.make_workload(3)
+    T, D = d3["X"].shape
+    X = [dev_bf16(d3["X"]) for _ in range(nsets)]
+    dY = [dev_bf16(d3["dY"]) for _ in range(nsets)]
+    W = [dev_bf16(d3["W"]) for _ in range(nsets)]
+    Kb = D // BLOCK
+    qx = [torch.empty((T, D), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sx = [torch.empty((Kb, T), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    qxT = [torch.empty((D, T), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sxT = [torch.empty((T // BLOCK, D), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    qdy = [torch.empty((T, D), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sdy = [torch.empty((Kb, T), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    qdyT = [torch.empty((D, T), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sdyT = [torch.empty((T // BLOCK, D), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    qw = [torch.empty((D, D), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    qwT = [torch.empty((D, D), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    sw = [torch.empty((Kb, Kb), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    out_c = [torch.empty((T, D), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    dw = [torch.empty((D, D), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+
+    j = lambda i: i % nsets  # noqa: E731
+    a, m = _time_kernel(lambda i: bf.quantize_lhs(X[j(i)], qx[j(i)], sx[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs", [T, D], a, m, lhs_bytes(T, D), "GB/s")
+    a, m = _time_kernel(lambda i: bf.quantize_lhs(dY[j(i)], qdy[j(i)], sdy[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs(dY)", [T, D], a, m, lhs_bytes(T, D), "GB/s")
+    a, m = _time_kernel(lambda i: bf.quantize_rhs(X[j(i)], qxT[j(i)], sxT[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_rhs", [T, D], a, m, lhs_bytes(T, D), "GB/s")
+    a, m = _time_kernel(lambda i: bf.quantize_rhs(dY[j(i)], qdyT[j(i)], sdyT[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_rhs(dY)", [T, D], a, m, lhs_bytes(T, D), "GB/s")
+    a, m = _time_kernel(lambda i: bf.quantize_weight_128x128(W[j(i)], qw[j(i)], qwT[j(i)], sw[j(i)], stream=stream),
+                        reps, stream, torch)
+    add("quantize_weight_128x128(+qT)", [D, D], a, m, weight_bytes(D, D, True), "GB/s")
+    fl = 2.0 * T * D * D
+    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qx[j(i)], sx[j(i)], qw[j(i)], sw[j(i)], c=out_c[j(i)],
+                                                        stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x128 fwd", [T, D, D], a, m, fl, "TFLOP/s")
+    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qdy[j(i)], sdy[j(i)], qwT[j(i)], sw[j(i)], 1, Kb,
+                                                        c=out_c[j(i)], stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x128 dgrad", [T, D, D], a, m, fl, "TFLOP/s")
+    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)], sdyT[j(i)], qxT[j(i)], sxT[j(i)], c=dw[j(i)],
+                                                      stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x1 wgrad", [D, D, T], a, m, fl, "TFLOP/s")
+    del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw
+    torch.cuda.empty_cache()
+
+    d4 = inputs.make_workload(4)
+    M4, K4 = d4["A"].shape
+    N4 = d4["W"].shape[0]
+    ns4 = 3
+    A4 = [dev_bf16(d4["A"]) for _ in range(ns4)]
+    W4 = [dev_bf16(d4["W"]) for _ in range(ns4)]
+    qa4 = [torch.empty((M4, K4), dtype=torch.uint8, device=dev) for _ in range(ns4)]
+    sa4 = [torch.empty((K4 // BLOCK, M4), dtype=torch.float32, device=dev) for _ in range(ns4)]
+    qw4 = [torch.empty((N4, K4), dtype=torch.uint8, device=dev) for _ in range(ns4)]
+    sw4 = [torch.empty((N4 // BLOCK, K4 // BLOCK), dtype=torch.float32, device=dev) for _ in range(ns4)]
+    c4 = [torch.empty((M4, N4), dtype=torch.bfloat16, device=dev) for _ in range(ns4)]
+    k = lambda i: i % ns4  # noqa: E731
+    a, m = _time_kernel(lambda i: bf.quantize_lhs(A4[k(i)], qa4[k(i)], sa4[k(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs outlier", [M4, K4], a, m, lhs_bytes(M4, K4), "GB/s")
+    a, m = _time_kernel(lambda i: bf.quantize_weight_128x128(W4[k(i)], qw4[k(i)], None, sw4[k(i)], want_qT=False,
+                                                             stream=stream), reps, stream, torch)
+    add("quantize_weight_128x128 outlier", [N4, K4], a, m, weight_bytes(N4, K4, False), "GB/s")
+    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa4[k(i)], sa4[k(i)], qw4[k(i)], sw4[k(i)], c=c4[k(i)],
+                                                        stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x128 outlier", [M4, N4, K4], a, m, 2.0 * M4 * N4 * K4, "TFLOP/s")
+    del A4, W4, qa4, sa4, qw4, sw4, c4
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(A_h, W_h, gemm_rows):
+    """The CPU oracle (as it stands) on a bounded sample of the step: both quantizers on the full
+    tensors, the GEMM on `gemm_rows` evenly spaced rows; scaled to the whole step."""
+    import oracle
+    M, K = A_h.shape
+    N = W_h.shape[0]
+    t0 = time.perf_counter()
+    qa, sa = oracle.quantize_lhs(A_h)
+    qw, _, sw = oracle.quantize_weight_128x128(W_h, want_qT=False)
+    t1 = time.perf_counter()
+    rows = np.linspace(0, M - 1, gemm_rows).astype(np.int64)
+    oracle.gemm_1x128_128x128(qa, sa, qw, sw, sw.shape[1], 1, rows=rows)
+    t2 = time.perf_counter()
+    step_s = (t1 - t0) + (t2 - t1) * (M / gemm_rows)
+    return {
+        "value": round(2.0 * M * N * K / step_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"quantize_lhs + quantize_weight_128x128 on the full 4096x4096 tensors, GEMM on "
+                  f"{gemm_rows} of {M} rows; GEMM time scaled by {M / gemm_rows:g}",
+        "measured_s": round(t2 - t0, 2),
+        "quant_s": round(t1 - t0, 3),
+        "gemm_sample_s": round(t2 - t1, 3),
+    }
+
+
+if __name__ == "__main__":
+    main()

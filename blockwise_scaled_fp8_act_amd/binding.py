@@ -1,0 +1,162 @@
+"""Thin ctypes binding of libbsfp8.so (the gfx950 HIP library); declarations in include/blockwise_fp8.h.
+
+Argument marshalling only: every step runs in the HIP kernels. torch provides device memory and the
+current stream. There is no CPU fallback: if the library is missing, loading raises.
+
+Tensor conventions (torch, on the GPU):
+  bf16 inputs       torch.bfloat16 (or int16/uint16 holding bf16 bits)
+  fp8 codes         torch.uint8 (``.view(torch.float8_e4m3fn)`` gives the same bytes as fp8)
+  LHS scales a_s    torch.float32 of shape (Kb, M), C-contiguous == column-major [M, Kb], ld M
+  RHS scales s      torch.float32 (Kb, N) row-major
+  weight scales s   torch.float32 (Nb, Kb) row-major
+  GEMM output       torch.bfloat16 [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsfp8.so")
+BLOCK = 128
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+_lib = None
+
+
+class Bsfp8Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().bsfp8_status_string(status).decode()
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def lib():
+    """Load libbsfp8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m blockwise_scaled_fp8_act_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.bsfp8_status_string.argtypes = [ctypes.c_int]
+        L.bsfp8_status_string.restype = ctypes.c_char_p
+        L.quantize_lhs.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]
+        L.quantize_rhs.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]
+        L.quantize_weight_128x128.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
+        L.gemm_1x128_128x128.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
+                                         _i64, _i64, _i64, _vp]
+        L.gemm_1x128_128x1.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       _vp]
+        L.encode_e4m3_f32.argtypes = [_vp, _vp, _i64, _vp]
+        for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
+                  "gemm_1x128_128x1", "encode_e4m3_f32"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _vp(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def _ld(t):
+    """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _call(fn, *args):
+    rc = getattr(lib(), fn)(*args)
+    if rc != 0:
+        raise Bsfp8Error(fn, rc)
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def quantize_lhs(x, q=None, a_s=None, stream=None):
+    """1x128 row-wise quantization of x [M, K]. Returns (q [M, K] uint8, a_s (Kb, M) fp32)."""
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if a_s is None:
+        a_s = torch.empty((cdiv(K, BLOCK), M), dtype=torch.float32, device=x.device)
+    _call("quantize_lhs", _ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(a_s), _stream(stream))
+    return q, a_s
+
+
+def quantize_rhs(x, qT=None, s=None, stream=None):
+    """128x1 column-wise quantization of x [K, N]. Returns (qT [N, K] uint8, s (Kb, N) fp32)."""
+    K, N = x.shape
+    if qT is None:
+        qT = torch.empty((N, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((cdiv(K, BLOCK), N), dtype=torch.float32, device=x.device)
+    _call("quantize_rhs", _ptr(x), K, N, _ld(x), _ptr(qT), _ld(qT), _ptr(s), _stream(stream))
+    return qT, s
+
+
+def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=None):
+    """128x128 block quantization of w [N, K]. Returns (q [N, K], qT [K, N] or None, s (Nb, Kb))."""
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if qT is None and want_qT:
+        qT = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty((cdiv(N, BLOCK), cdiv(K, BLOCK)), dtype=torch.float32, device=w.device)
+    ldqT = _ld(qT) if qT is not None else 0
+    _call("quantize_weight_128x128", _ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(qT), ldqT,
+          _ptr(s), _stream(stream))
+    return q, qT, s
+
+
+def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb=None, bs_stride_kb=None, c=None, K=None,
+                       stream=None):
+    """C = A B^T, A [M, K] codes with a_s (Kb, M); B [N, K] codes with 128x128 scales.
+    ``b_s`` is addressed as b_s[nb * bs_stride_nb + kb * bs_stride_kb]; the default strides treat it
+    as the weight quantizer's (Nb, Kb) tensor."""
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] if K is None else K
+    if bs_stride_nb is None:
+        bs_stride_nb, bs_stride_kb = b_s.stride(0), b_s.stride(1)
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _call("gemm_1x128_128x128", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
+          bs_stride_nb, bs_stride_kb, _ptr(c), _ld(c), M, N, K, _stream(stream))
+    return c
+
+
+def gemm_1x128_128x1(a, a_s, b, b_s, c=None, K=None, stream=None):
+    """C = A B^T, A [M, K] codes with a_s (Kb, M); B [N, K] codes with per-column b_s (Kb, N)."""
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] if K is None else K
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _call("gemm_1x128_128x1", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s), _ptr(c),
+          _ld(c), M, N, K, _stream(stream))
+    return c
+
+
+def encode_e4m3_f32(x, q=None, stream=None):
+    """Element conversion of fp32 values to e4m3fn codes (clamped to +-448, RNE)."""
+    n = x.numel()
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _call("encode_e4m3_f32", _ptr(x), _ptr(q), n, _stream(stream))
+    return q

@@ -1,0 +1,146 @@
+// C ABI of the blockwise FP8 library: argument validation (before any HIP call), a per-device
+// gfx950 check, and launches on the caller's stream. Declarations and contracts: blockwise_fp8.h.
+#include "blockwise_fp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kGroupEdge = 128;
+constexpr int64_t kMaxGridY = 65535;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 0 = unknown, 1 = gfx950, 2 = other. Indexed by HIP device ordinal.
+std::atomic<int> g_arch_state[64];
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BSFP8_EHIP;
+    if (dev < 0 || dev >= 64) return BSFP8_EDEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BSFP8_EHIP;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? BSFP8_OK : BSFP8_EDEVICE;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                  const float* b_s, const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return BSFP8_EINVAL;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (c == nullptr || ldc < N) return BSFP8_EINVAL;
+    if (cdiv(M, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (K == 0) return BSFP8_OK;
+    if (a == nullptr || b == nullptr || a_s == nullptr || b_s == nullptr) return BSFP8_EINVAL;
+    if (lda < K || ldb < K) return BSFP8_EINVAL;
+    if (!aligned16(a) || !aligned16(b) || (lda % 16) != 0 || (ldb % 16) != 0) return BSFP8_EALIGN;
+    return BSFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsfp8_status_string(int status) {
+    switch (status) {
+        case BSFP8_OK: return "ok";
+        case BSFP8_EINVAL: return "invalid argument";
+        case BSFP8_EALIGN: return "operand rows not 16-byte aligned";
+        case BSFP8_EDEVICE: return "current device is not gfx950";
+        case BSFP8_EHIP: return "HIP call or kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int quantize_lhs(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
+                 float* a_s, void* stream) {
+    if (M < 0 || K < 0) return BSFP8_EINVAL;
+    if (M == 0 || K == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr || a_s == nullptr) return BSFP8_EINVAL;
+    if (ldx < K || ldq < K) return BSFP8_EINVAL;
+    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_lhs(static_cast<const uint16_t*>(x), M, K, ldx,
+                                             static_cast<uint8_t*>(q), ldq, a_s,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int quantize_rhs(const void* x, int64_t K, int64_t N, int64_t ldx, void* qT, int64_t ldqT,
+                 float* s, void* stream) {
+    if (K < 0 || N < 0) return BSFP8_EINVAL;
+    if (K == 0 || N == 0) return BSFP8_OK;
+    if (x == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldx < N || ldqT < K) return BSFP8_EINVAL;
+    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_rhs(static_cast<const uint16_t*>(x), K, N, ldx,
+                                             static_cast<uint8_t*>(qT), ldqT, s,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int quantize_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, void* q,
+                            int64_t ldq, void* qT, int64_t ldqT, float* s, void* stream) {
+    if (N < 0 || K < 0) return BSFP8_EINVAL;
+    if (N == 0 || K == 0) return BSFP8_OK;
+    if (w == nullptr || q == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldw < K || ldq < K || (qT != nullptr && ldqT < N)) return BSFP8_EINVAL;
+    if (cdiv(N, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_weight(static_cast<const uint16_t*>(w), N, K, ldw,
+                                                static_cast<uint8_t*>(q), ldq,
+                                                static_cast<uint8_t*>(qT), ldqT, s,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                       const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
+                       int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (bs_stride_nb < 0 || bs_stride_kb < 0) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
+    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
+                                     static_cast<const uint8_t*>(b), ldb, bs,
+                                     static_cast<uint16_t*>(c), ldc, M, N, K,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                     const float* b_s, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                     void* stream) {
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (int rc = check_device()) return rc;
+    bsfp8::BScale bs{b_s, 0, 0, 1};
+    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
+                                     static_cast<const uint8_t*>(b), ldb, bs,
+                                     static_cast<uint16_t*>(c), ldc, M, N, K,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream) {
+    if (n < 0) return BSFP8_EINVAL;
+    if (n == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr) return BSFP8_EINVAL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 3) != 0) return BSFP8_EALIGN;
+    if ((n + 1023) / 1024 > 0x7FFFFFFFLL) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_encode(x, static_cast<uint8_t*>(q), n,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Device helpers shared by the gfx950 quantizer and GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfp8 {
+
+constexpr int kGroup = 128;         // 1x128 / 128x1 / 128x128 group edge
+constexpr float kFp8Max = 448.0f;   // finfo(float8_e4m3fn).max
+constexpr float kAmaxEps = 1e-12f;  // floor on a group's amax (all-zero groups)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Low and high bf16 of a packed dword.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Quantization of one value already multiplied by the group multiplier: clamp to +-448 (keeps the
+// sign of zero), then the hardware RNE fp32 -> e4m3fn conversion. Four values -> one dword, byte i
+// holding value i.
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -kFp8Max), kFp8Max);
+    b = fminf(fmaxf(b, -kFp8Max), kFp8Max);
+    c = fminf(fmaxf(c, -kFp8Max), kFp8Max);
+    d = fminf(fmaxf(d, -kFp8Max), kFp8Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0,1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);        // bytes 2,3
+    return static_cast<uint32_t>(w);
+}
+
+// Group scale pair from the group's max magnitude: the stored (dequantizing) scale s = amax/448
+// and the multiplier m = 448/amax, both IEEE-correct fp32 divisions (the compiler's default fp32
+// division is correctly rounded; fp32 denormals are preserved).
+struct GroupScale {
+    float s;
+    float m;
+};
+
+__device__ __forceinline__ GroupScale group_scale(float amax) {
+    float a = fmaxf(amax, kAmaxEps);
+    GroupScale g;
+    g.s = a / kFp8Max;
+    g.m = kFp8Max / a;
+    return g;
+}
+
+// Max over the 16 lanes of a DPP row (lanes 16r .. 16r+15) of a non-negative float, via the
+// unsigned order of the bit patterns (valid for non-negative, non-NaN values). Every lane of the
+// row receives the result.
+__device__ __forceinline__ uint32_t umax_row16(uint32_t v) {
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+// Max over all 64 lanes of a wave (non-negative floats as bit patterns).
+__device__ __forceinline__ uint32_t umax_wave(uint32_t v) {
+    v = umax_row16(v);
+    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 16)));
+    v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), 32)));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+
+}  // namespace bsfp8

@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the C ABI validates first).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfp8 {
+
+hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                               int64_t ldq, float* a_s, hipStream_t stream);
+hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
+                               int64_t ldqT, float* s, hipStream_t stream);
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                                  hipStream_t stream);
+hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
+
+// b-scale addressing of the GEMM: kind 0 = one scale per (K-block, 128-column block) at
+// b_s[nb * stride_nb + kb * stride_kb]; kind 1 = one scale per (K-block, column) at b_s[kb * N + n].
+struct BScale {
+    const float* ptr;
+    int64_t stride_nb;
+    int64_t stride_kb;
+    int per_column;
+};
+
+hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
+                       int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
+                       int64_t K, hipStream_t stream);
+
+}  // namespace bsfp8

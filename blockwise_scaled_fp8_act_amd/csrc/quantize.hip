@@ -1,0 +1,353 @@
+// gfx950 group quantizers: bf16 -> float8_e4m3fn codes + fp32 scales.
+//
+//   quantize_lhs             1x128 groups along K (act_quant_lhs), scales column-major [M, Kb]
+//   quantize_rhs             128x1 groups down each column (act_quant_rhs), codes written transposed
+//   quantize_weight_128x128  128x128 blocks (weight_quant_rhs), optional transposed copy
+//
+// Operations as listed in the quantization-correctness table of "Enable blockwise FP8 dense
+// training kernels on ROCm" (block_size 128); the column-major scale layout and the rule that a
+// scale store of a row >= M must be dropped come from that page's root-cause comment.
+//
+// All three are HBM-bound: every input byte is read once with 16-byte loads, every output byte is
+// written once, 16-lane (1x128) or LDS (128x1, 128x128) max reductions run on data already in
+// registers, and the transposing variants turn the tile around in LDS so global stores stay
+// contiguous along the output rows.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace bsfp8 {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive bf16 of one row starting at column c; columns >= ncols read as +0.
+template <bool VEC>
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ row, int64_t c, int64_t ncols,
+                                      float f[8]) {
+    if (VEC && c + 8 <= ncols) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
+        f[0] = bf16_lo(v[0]); f[1] = bf16_hi(v[0]);
+        f[2] = bf16_lo(v[1]); f[3] = bf16_hi(v[1]);
+        f[4] = bf16_lo(v[2]); f[5] = bf16_hi(v[2]);
+        f[6] = bf16_lo(v[3]); f[7] = bf16_hi(v[3]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            f[j] = (c + j < ncols) ? bf16_to_f32(row[c + j]) : 0.0f;
+    }
+}
+
+// Store 8 code bytes (w0 = bytes 0..3, w1 = bytes 4..7) at row[c ..]; bytes at columns >= ncols
+// are not written.
+template <bool VEC>
+__device__ __forceinline__ void store8(uint8_t* __restrict__ row, int64_t c, int64_t ncols,
+                                       uint32_t w0, uint32_t w1) {
+    if (VEC && c + 8 <= ncols) {
+        *reinterpret_cast<uint2*>(row + c) = make_uint2(w0, w1);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (c + j < ncols)
+                row[c + j] = static_cast<uint8_t>(((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFF);
+    }
+}
+
+// Store 16 code bytes at row[c ..], masked at ncols.
+template <bool VEC>
+__device__ __forceinline__ void store16(uint8_t* __restrict__ row, int64_t c, int64_t ncols,
+                                        uint4 v) {
+    if (VEC && c + 16 <= ncols) {
+        *reinterpret_cast<uint4*>(row + c) = v;
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (c + j < ncols)
+                row[c + j] = static_cast<uint8_t>((w[j >> 2] >> (8 * (j & 3))) & 0xFF);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 1x128: a 16-lane team owns one (row, K-block) group, 8 elements per lane; a workgroup covers
+// kLhsRows consecutive rows of one K-block, so its scale stores form one contiguous run of the
+// column-major scale column kb.
+constexpr int kLhsRowsPerTeam = 4;
+constexpr int kLhsRows = 16 * kLhsRowsPerTeam;
+
+template <bool VEC_X, bool VEC_Q>
+__global__ __launch_bounds__(256) void quantize_lhs_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s) {
+    const int lane16 = threadIdx.x & 15;
+    const int team = threadIdx.x >> 4;
+    const int64_t kb = blockIdx.y;
+    const int64_t c = kb * kGroup + lane16 * 8;
+    const int64_t mbase = static_cast<int64_t>(blockIdx.x) * kLhsRows;
+
+    float f[kLhsRowsPerTeam][8];
+#pragma unroll
+    for (int r = 0; r < kLhsRowsPerTeam; ++r) {
+        const int64_t m = mbase + r * 16 + team;
+        if (m < M) {
+            load8<VEC_X>(x + m * ldx, c, K, f[r]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[r][j] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kLhsRowsPerTeam; ++r) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[r][j]));
+        am = umax_row16(am);
+        const GroupScale g = group_scale(__uint_as_float(am));
+        const uint32_t w0 = encode4(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
+        const uint32_t w1 = encode4(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
+        const int64_t m = mbase + r * 16 + team;
+        if (m < M) {  // rows >= M store neither codes nor scales
+            store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
+            if (lane16 == 0) a_s[kb * M + m] = g.s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 128x1 with transposed output: a workgroup owns one K-block (128 rows) x 64 columns.
+// Thread t loads 4 consecutive rows (4*(t/8) ..) x 8 columns (8*(t%8) ..); column maxima go
+// through LDS; the 4 codes of a column form one dword of the transposed tile, which is then
+// written out as 128 contiguous bytes per output row.
+constexpr int kRhsCols = 64;
+
+template <bool VEC_X, bool VEC_Q>
+__global__ __launch_bounds__(256) void quantize_rhs_kernel(
+    const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t ldx,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ s) {
+    __shared__ uint32_t red[32][kRhsCols + 1];
+    __shared__ float mult[kRhsCols];
+    __shared__ uint4 tileT[kRhsCols * 8];  // [column][8 x 16-byte chunks], chunk index swizzled
+
+    const int t = threadIdx.x;
+    const int cg = t & 7;
+    const int rq = t >> 3;
+    const int64_t kb = blockIdx.y;
+    const int64_t k0 = kb * kGroup;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRhsCols;
+    const int64_t col = n0 + cg * 8;
+
+    float f[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t k = k0 + rq * 4 + i;
+        if (k < K) {
+            load8<VEC_X>(x + k * ldx, col, N, f[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t am = max(max(abs_bits(f[0][j]), abs_bits(f[1][j])),
+                          max(abs_bits(f[2][j]), abs_bits(f[3][j])));
+        red[rq][cg * 8 + j] = am;
+    }
+    __syncthreads();
+    if (t < kRhsCols) {
+        uint32_t am = 0;
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) am = max(am, red[r][t]);
+        const GroupScale g = group_scale(__uint_as_float(am));
+        mult[t] = g.m;
+        if (n0 + t < N) s[kb * N + n0 + t] = g.s;
+    }
+    __syncthreads();
+    uint32_t* tw = reinterpret_cast<uint32_t*>(tileT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float mj = mult[cg * 8 + j];
+        const uint32_t w = encode4(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
+        const int cl = cg * 8 + j;
+        const int chunk = (rq >> 2) ^ (cl >> 3);
+        tw[cl * 32 + chunk * 4 + (rq & 3)] = w;
+    }
+    __syncthreads();
+    const int cl = t >> 2;
+    const int64_t n = n0 + cl;
+    if (n < N) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int chunk = 2 * (t & 3) + h;
+            const uint4 v = tileT[cl * 8 + (chunk ^ (cl >> 3))];
+            store16<VEC_Q>(qT + n * ldqT, k0 + chunk * 16, K, v);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// 128x128 blocks: one workgroup per block; thread t holds rows 8*(t/16) .. +8 x columns
+// 8*(t%16) .. +8 (64 values in registers, read once). The block max is a wave reduction plus a
+// 4-entry LDS combine. The optional transposed copy goes through a swizzled LDS tile.
+template <bool VEC_W, bool VEC_Q, bool VEC_QT>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
+    float* __restrict__ s, int64_t Kb) {
+    __shared__ uint32_t wmax[4];
+    __shared__ uint4 tileT[kGroup * 8];  // [column][8 x 16-byte chunks of rows], swizzled
+
+    const int t = threadIdx.x;
+    const int cg = t & 15;
+    const int rg = t >> 4;
+    const int64_t kb = blockIdx.x;
+    const int64_t nb = blockIdx.y;
+    const int64_t n0 = nb * kGroup;
+    const int64_t k0 = kb * kGroup;
+    const int64_t c = k0 + cg * 8;
+
+    float f[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t n = n0 + rg * 8 + i;
+        if (n < N) {
+            load8<VEC_W>(w + n * ldw, c, K, f[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
+        }
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[i][j]));
+    am = umax_wave(am);
+    if ((t & 63) == 0) wmax[t >> 6] = am;
+    __syncthreads();
+    am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const GroupScale g = group_scale(__uint_as_float(am));
+    if (t == 0) s[nb * Kb + kb] = g.s;
+
+    uint32_t code[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        code[i][0] = encode4(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
+        code[i][1] = encode4(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
+        const int64_t n = n0 + rg * 8 + i;
+        if (n < N) store8<VEC_Q>(q + n * ldq, c, K, code[i][0], code[i][1]);
+    }
+    if (qT == nullptr) return;  // uniform over the grid
+
+    // 8x8 byte transpose: column j of my 8 columns collects byte j of rows 0..7.
+    uint32_t* tw = reinterpret_cast<uint32_t*>(tileT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int wsel = j >> 2;
+        const int sh = 8 * (j & 3);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= ((code[i][wsel] >> sh) & 0xFFu) << (8 * i);
+            hi |= ((code[i + 4][wsel] >> sh) & 0xFFu) << (8 * i);
+        }
+        const int cl = cg * 8 + j;
+        const int chunk = (rg >> 1) ^ (cg & 7);
+        const int idx = cl * 32 + chunk * 4 + (rg & 1) * 2;
+        *reinterpret_cast<uint2*>(tw + idx) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+    const int cl = t >> 1;
+    const int64_t k = k0 + cl;
+    if (k < K) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int chunk = (t & 1) * 4 + h;
+            const uint4 v = tileT[cl * 8 + (chunk ^ ((cl >> 3) & 7))];
+            store16<VEC_QT>(qT + k * ldqT, n0 + chunk * 16, N, v);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x,
+                                                     uint8_t* __restrict__ q, int64_t n) {
+    const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i0 + 4 <= n) {
+        const float4 v = *reinterpret_cast<const float4*>(x + i0);
+        const uint32_t w = encode4(v.x, v.y, v.z, v.w);
+        *reinterpret_cast<uint32_t*>(q + i0) = w;
+    } else {
+        for (int64_t i = i0; i < n; ++i) q[i] = static_cast<uint8_t>(encode4(x[i], 0.f, 0.f, 0.f) & 0xFF);
+    }
+}
+
+bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                               int64_t ldq, float* a_s, hipStream_t stream) {
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const dim3 grid(static_cast<unsigned>((M + kLhsRows - 1) / kLhsRows), static_cast<unsigned>(Kb));
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
+    if (vx && vq)
+        quantize_lhs_kernel<true, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
+    else if (vx)
+        quantize_lhs_kernel<true, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
+    else if (vq)
+        quantize_lhs_kernel<false, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
+    else
+        quantize_lhs_kernel<false, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
+                               int64_t ldqT, float* s, hipStream_t stream) {
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const dim3 grid(static_cast<unsigned>((N + kRhsCols - 1) / kRhsCols), static_cast<unsigned>(Kb));
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
+    const bool vq = aligned(qT, 16) && (ldqT % 16 == 0);
+    if (vx && vq)
+        quantize_rhs_kernel<true, true><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
+    else if (vx)
+        quantize_rhs_kernel<true, false><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
+    else if (vq)
+        quantize_rhs_kernel<false, true><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
+    else
+        quantize_rhs_kernel<false, false><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                                  hipStream_t stream) {
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const int64_t Nb = (N + kGroup - 1) / kGroup;
+    const dim3 grid(static_cast<unsigned>(Kb), static_cast<unsigned>(Nb));
+    const bool vw = aligned(w, 16) && (ldw % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
+    const bool vt = qT != nullptr && aligned(qT, 16) && (ldqT % 16 == 0);
+#define BSFP8_QW(A, B, C) \
+    quantize_weight_kernel<A, B, C><<<grid, 256, 0, stream>>>(w, N, K, ldw, q, ldq, qT, ldqT, s, Kb)
+    if (vw && vq && vt) BSFP8_QW(true, true, true);
+    else if (vw && vq) BSFP8_QW(true, true, false);
+    else if (vw && vt) BSFP8_QW(true, false, true);
+    else if (vw) BSFP8_QW(true, false, false);
+    else if (vq && vt) BSFP8_QW(false, true, true);
+    else if (vq) BSFP8_QW(false, true, false);
+    else if (vt) BSFP8_QW(false, false, true);
+    else BSFP8_QW(false, false, false);
+#undef BSFP8_QW
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream) {
+    if (!aligned(x, 16) || !aligned(q, 4)) return hipErrorInvalidValue;
+    const int64_t threads = (n + 3) / 4;
+    const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+    encode_kernel<<<grid, 256, 0, stream>>>(x, q, n);
+    return hipGetLastError();
+}
+
+}  // namespace bsfp8

@@ -1,0 +1,143 @@
+/*
+ * blockwise_fp8.h: C ABI of the MI355X (gfx950) blockwise-scaled FP8 linear-layer kernels.
+ *
+ * The operations are those of pytorch/ao's blockwise FP8 training path as its pull-request pages
+ * describe it:
+ *   - "Enable blockwise FP8 dense training kernels on ROCm": description (FP8_MAX is the float8
+ *     format's finfo max), quantization-correctness table (act_quant_lhs, act_quant_rhs,
+ *     weight_quant_rhs, block_size 128), GEMM SQNR table, and the root-cause comment (the LHS
+ *     quantizer stores reciprocal scales column-major; stores of rows >= M must be masked);
+ *   - "Mask a_s/b_s scale loads in blockwise FP8 training GEMM kernels": Summary and Fix (the
+ *     1x128_128x128 and 1x128_128x1 GEMMs; scale loads of rows >= M / columns >= N are masked).
+ *
+ * Element formats
+ *   bf16   : 16-bit bfloat16 bit patterns (uint16).
+ *   fp8    : OCP float8_e4m3fn codes (uint8): bias 7, largest finite 448, no infinities.
+ *   scales : IEEE fp32.
+ *
+ * Quantization of one group g (1x128, 128x1 or 128x128 elements; a group at a tensor edge has only
+ * its in-range elements):
+ *   amax = max |x| over g;  amax_c = max(amax, 1e-12f);
+ *   s    = amax_c / 448      (IEEE fp32 division; the stored, dequantizing scale: x ~= dec(q) * s)
+ *   m    = 448 / amax_c      (IEEE fp32 division)
+ *   q    = e4m3( clamp(fl32(x * m), -448, 448) )   round to nearest, ties to even; sign kept.
+ *
+ * Scaled GEMM (C = A B^T with both operands K-contiguous):
+ *   C[m,n] = sum_kb  a_s[m,kb] * b_s(kb,n) * sum_{k in block kb, k < K} dec(A[m,k]) dec(B[n,k])
+ *   Each K-block's inner sum is one 128-deep fp8 matrix-core dot product with fp32 output (measured
+ *   on gfx950: not an exactly rounded fp32 sum; its error stays below about 2^-11 of the largest
+ *   product in the block); it is multiplied by its two scales and added to an fp32 total before
+ *   the next block; C is rounded to bf16 (RNE).
+ *
+ * Memory and ownership
+ *   Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates,
+ *   frees or retains memory and keeps no state besides a per-device architecture check.
+ *   Row-major tensors take a row stride "ld" in elements (bytes for fp8).
+ *   Outputs must not overlap inputs. Every in-range output element is written; nothing outside the
+ *   in-range elements (padding between rows, rows >= M, ...) is written.
+ *
+ * Calls are asynchronous: arguments are validated, kernels are enqueued on `stream` (a hipStream_t
+ * passed as void*, NULL = the default stream) and the call returns. Results are ready once the
+ * caller synchronizes the stream. Calls are thread-safe.
+ *
+ * Return codes
+ *   BSFP8_OK (0); BSFP8_EINVAL (1) bad argument: a null pointer with a non-empty extent, a negative
+ *   size, ld smaller than the row length, a stride out of range; BSFP8_EALIGN (2) a GEMM operand
+ *   row is not 16-byte aligned (see the GEMMs); BSFP8_EDEVICE (3) the current device is not gfx950;
+ *   BSFP8_EHIP (4) a HIP call or launch failed. Argument checks happen before any HIP call, so
+ *   codes 1 and 2 need no GPU. Empty problems (a zero extent) return BSFP8_OK without launching,
+ *   except that a GEMM with K == 0 and M, N > 0 writes C = 0.
+ */
+#ifndef BLOCKWISE_FP8_H
+#define BLOCKWISE_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BSFP8_OK = 0,
+    BSFP8_EINVAL = 1,
+    BSFP8_EALIGN = 2,
+    BSFP8_EDEVICE = 3,
+    BSFP8_EHIP = 4
+};
+
+/* Text for a return code (static storage). */
+const char* bsfp8_status_string(int status);
+
+/*
+ * quantize_lhs: 1x128 row-wise activation quantizer (act_quant_lhs).
+ *   x   [M, K] bf16, row stride ldx >= K.
+ *   q   [M, K] fp8, row stride ldq >= K.
+ *   a_s column-major [M, ceil(K/128)] fp32 with leading dimension exactly M: the scale of row m,
+ *       K-block kb is a_s[kb * M + m] (the layout of the ROCm page's root-cause comment; nothing
+ *       past M * ceil(K/128) floats is written).
+ * Any alignment is accepted; 16-byte-aligned rows take the vector path.
+ */
+int quantize_lhs(const void* x, int64_t M, int64_t K, int64_t ldx,
+                 void* q, int64_t ldq, float* a_s, void* stream);
+
+/*
+ * quantize_rhs: 128x1 column-wise activation quantizer (act_quant_rhs), with transposed output.
+ *   x   [K, N] bf16 row-major, row stride ldx >= N; groups are 128 consecutive rows of a column.
+ *   qT  [N, K] fp8 row-major (K-contiguous), row stride ldqT >= K: qT[n, k] is the code of x[k, n].
+ *   s   [ceil(K/128), N] fp32 row-major: s[kb * N + n]. These bytes equal a column-major
+ *       [N, ceil(K/128)] a_s with ld N, so qT/s can be the A operand of either GEMM.
+ */
+int quantize_rhs(const void* x, int64_t K, int64_t N, int64_t ldx,
+                 void* qT, int64_t ldqT, float* s, void* stream);
+
+/*
+ * quantize_weight_128x128: 128x128 block weight quantizer (weight_quant_rhs).
+ *   w   [N, K] bf16 (nn.Linear layout [out, in]), row stride ldw >= K.
+ *   q   [N, K] fp8, row stride ldq >= K.
+ *   qT  [K, N] fp8 or NULL: the same codes transposed (the dgrad operand), row stride ldqT >= N.
+ *   s   [ceil(N/128), ceil(K/128)] fp32 row-major: s[nb * ceil(K/128) + kb].
+ */
+int quantize_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
+                            void* q, int64_t ldq, void* qT, int64_t ldqT,
+                            float* s, void* stream);
+
+/*
+ * gemm_1x128_128x128: C = A B^T with 1x128 scales on A and 128x128 block scales on B
+ * (forward Y = X W^T, and dgrad dX = dY W using the transposed weight codes).
+ *   a   [M, K] fp8, row stride lda; a_s column-major [M, ceil(K/128)], ld M.
+ *   b   [N, K] fp8, row stride ldb.
+ *   b_s scale of (K-block kb, N-block nb) at b_s[nb * bs_stride_nb + kb * bs_stride_kb]
+ *       (forward with the weight scales [Nb, Kb]: strides (Kb, 1); dgrad with the same weight
+ *       scales read transposed: strides (1, Nb_of_weight)). Strides must be >= 0.
+ *   c   [M, N] bf16, row stride ldc >= N.
+ * Alignment (else BSFP8_EALIGN): a and b 16-byte aligned, lda and ldb multiples of 16.
+ * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
+ */
+int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
+                       const void* b, int64_t ldb, const float* b_s,
+                       int64_t bs_stride_nb, int64_t bs_stride_kb,
+                       void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_1x128_128x1: C = A B^T with 1x128 scales on A and per-column 128x1 scales on B
+ * (wgrad dW = dY^T X, contracting over tokens: A and B are quantize_rhs outputs).
+ *   a, lda, a_s as above;  b [N, K] fp8, row stride ldb;
+ *   b_s [ceil(K/128), N] fp32 row-major: the scale of (kb, n) is b_s[kb * N + n].
+ *   c   [M, N] bf16, row stride ldc >= N.  Alignment as for gemm_1x128_128x128.
+ */
+int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s,
+                     const void* b, int64_t ldb, const float* b_s,
+                     void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * encode_e4m3_f32: the quantizers' element conversion applied to n arbitrary fp32 values:
+ *   q[i] = e4m3(clamp(x[i], -448, 448)), round to nearest even, sign kept. NaN inputs are outside
+ *   the contract. Exposed so the device conversion can be checked over every fp32 pattern.
+ *   Alignment (else BSFP8_EALIGN): x 16-byte aligned, q 4-byte aligned.
+ */
+int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

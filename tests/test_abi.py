@@ -1,0 +1,82 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared entry point, and rejects
+bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from blockwise_scaled_fp8_act_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blockwise_fp8.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from blockwise_scaled_fp8_act_amd import build
+        build.build()
+    return binding.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert set(names) >= {"quantize_lhs", "quantize_rhs", "quantize_weight_128x128",
+                          "gemm_1x128_128x128", "gemm_1x128_128x1", "bsfp8_status_string",
+                          "encode_e4m3_f32"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.bsfp8_status_string(code)
+    assert L.bsfp8_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(16 * 1024)  # a fake, 16-byte aligned address: never dereferenced on these paths
+
+
+def test_quantizers_reject_bad_arguments(L):
+    assert L.quantize_lhs(None, 4, 128, 128, P, 128, P, None) == 1
+    assert L.quantize_lhs(P, -1, 128, 128, P, 128, P, None) == 1
+    assert L.quantize_lhs(P, 4, 128, 127, P, 128, P, None) == 1      # ldx < K
+    assert L.quantize_lhs(P, 4, 128, 128, P, 100, P, None) == 1      # ldq < K
+    assert L.quantize_lhs(P, 4, 128, 128, P, 128, None, None) == 1
+    assert L.quantize_rhs(P, 128, 64, 63, P, 128, P, None) == 1      # ldx < N
+    assert L.quantize_rhs(P, 128, 64, 64, P, 100, P, None) == 1      # ldqT < K
+    assert L.quantize_weight_128x128(P, 64, 64, 64, P, 64, P, 10, P, None) == 1  # ldqT < N
+    assert L.quantize_weight_128x128(P, 64, 64, 64, None, 64, None, 0, P, None) == 1
+
+
+def test_empty_problems_are_noops(L):
+    assert L.quantize_lhs(None, 0, 128, 128, None, 128, None, None) == 0
+    assert L.quantize_lhs(None, 4, 0, 0, None, 0, None, None) == 0
+    assert L.quantize_rhs(None, 0, 5, 5, None, 0, None, None) == 0
+    assert L.quantize_weight_128x128(None, 0, 0, 0, None, 0, None, 0, None, None) == 0
+    assert L.gemm_1x128_128x128(None, 0, None, None, 0, None, 1, 1, None, 0, 0, 5, 7, None) == 0
+    assert L.gemm_1x128_128x1(None, 0, None, None, 0, None, None, 0, 3, 0, 7, None) == 0
+    assert L.encode_e4m3_f32(None, None, 0, None) == 0
+
+
+def test_gemms_reject_bad_arguments(L):
+    g = L.gemm_1x128_128x128
+    assert g(P, 128, P, P, 128, P, 1, 1, P, 63, 4, 64, 128, None) == 1       # ldc < N
+    assert g(P, 100, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1       # lda < K
+    assert g(P, 144, P, P, 136, P, 1, 1, P, 64, 4, 64, 130, None) == 2       # ldb % 16
+    odd = ctypes.c_void_p(16 * 1024 + 8)
+    assert g(odd, 128, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 2     # a misaligned
+    assert g(P, 128, None, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1    # a_s null
+    assert g(P, 128, P, P, 128, P, -1, 1, P, 64, 4, 64, 128, None) == 1      # negative stride
+    assert g(P, 128, P, P, 128, P, 1, 1, P, 64, -4, 64, 128, None) == 1
+    h = L.gemm_1x128_128x1
+    assert h(P, 128, P, P, 128, None, P, 64, 4, 64, 128, None) == 1          # b_s null
+    assert h(P, 128, P, P, 120, P, P, 64, 4, 64, 128, None) == 1             # ldb < K
+    assert L.encode_e4m3_f32(odd, P, 16, None) == 2

@@ -1,0 +1,263 @@
+"""GPU parity of the two scaled GEMMs against the CPU oracle.
+
+The GEMMs run on the GPU's own codes and scales, which must first equal the oracle's bit for bit;
+the oracle then evaluates the blockwise sum in fp64 on the same codes. Acceptance:
+  max |C - C_o| <= 2e-2 (|C_o| + 1) elementwise and ||C - C_o||_F / ||C_o||_F <= 4e-3;
+and for the end-to-end path SQNR against the fp64 matmul of the bf16 inputs >= 28 dB, within
+0.05 dB of the oracle path's own SQNR.
+Small problems are compared in full; full-size problems on a seeded sample of rows (always the
+first and the last row, and any tail rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_act_amd as bf
+import oracle
+from blockwise_scaled_fp8_act_amd import inputs
+from tests._gpu import DEV, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def _sample_rows(M, n=64, seed=0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = set(g.choice(M, size=min(n, M), replace=False).tolist())
+    rows |= {0, M - 1}
+    rows |= set(range(M - M % 128, M))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _assert_close(c_gpu, c_or, what):
+    rep = oracle.gemm_tolerance_report(c_gpu, c_or)
+    assert rep["ok"], f"{what}: {rep}"
+    return rep
+
+
+def _codes(shape, seed, ld=None):
+    """Random finite e4m3 codes [rows, cols] on the device, in a buffer with row stride ld."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    h = g.choice(finite, size=shape)
+    ld = ld or shape[1]
+    buf = torch.zeros((shape[0], ld), dtype=torch.uint8, device=DEV)
+    buf[:, :shape[1]] = torch.from_numpy(h).to(DEV)
+    return h, buf[:, :shape[1]]
+
+
+def _scales(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return np.exp2(g.uniform(-10, 2, size=shape)).astype(np.float32)
+
+
+GEMM_SHAPES = [
+    # M, N, K, lda/ldb (multiple of 16), ldc
+    (2, 512, 128, 128, 512), (130, 512, 1280, 1280, 512), (1, 1, 1, 16, 1), (3, 5, 300, 304, 5),
+    (128, 128, 128, 128, 128), (129, 130, 129, 144, 131), (257, 384, 520, 528, 384),
+    (64, 200, 4096, 4096, 200), (300, 260, 256, 256, 262),
+]
+
+
+def _run_guarded(fn, M, N, ldc):
+    cbuf = torch.full((M + 2, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
+    fn(cbuf[1:M + 1, :N])
+    torch.cuda.synchronize()
+    got = cbuf.float().cpu().numpy()
+    assert np.all(np.isnan(got[0])) and np.all(np.isnan(got[M + 1])), "write outside rows"
+    assert np.all(np.isnan(got[1:M + 1, N:])), "write into row padding"
+    return got[1:M + 1, :N]
+
+
+def _quantized_operands(M, N, K, ld, seed, per_column):
+    """A [M, K] and B [N, K] from seeded Gaussian bf16 data through the GPU quantizers (checked
+    bit-exact against the oracle), padded to row stride ld. A ~ N(0,1) rows (1x128 scales);
+    B ~ N(0, 0.02^2) as a weight (128x128 scales) or as 128x1 column groups of a [K, N] tensor."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    ah = inputs.bf16_bits_from_f64(g.standard_normal((M, K)))
+    qa = torch.zeros((M, ld), dtype=torch.uint8, device=DEV)[:, :K]
+    qa, sa = bf.quantize_lhs(to_dev(ah), q=qa)
+    oqa, osa = oracle.quantize_lhs(ah)
+    assert np.array_equal(qa.cpu().numpy(), oqa) and np.array_equal(sa.cpu().numpy(), osa)
+    if per_column:
+        xh = inputs.bf16_bits_from_f64(g.standard_normal((K, N)) * 0.02)   # [K, N], groups down K
+        qb = torch.zeros((N, ld), dtype=torch.uint8, device=DEV)[:, :K]
+        qb, sb = bf.quantize_rhs(to_dev(xh), qT=qb)
+        oqb, osb = oracle.quantize_rhs(xh)
+    else:
+        wh = inputs.bf16_bits_from_f64(g.standard_normal((N, K)) * 0.02)
+        qb = torch.zeros((N, ld), dtype=torch.uint8, device=DEV)[:, :K]
+        qb, _, sb = bf.quantize_weight_128x128(to_dev(wh), q=qb, want_qT=False)
+        oqb, _, osb = oracle.quantize_weight_128x128(wh, want_qT=False)
+    assert np.array_equal(qb.cpu().numpy(), oqb) and np.array_equal(sb.cpu().numpy(), osb)
+    return qa, sa, qb, sb, oqa, osa, oqb, osb
+
+
+@pytest.mark.parametrize("M,N,K,ld,ldc", GEMM_SHAPES, ids=lambda v: str(v))
+def test_gemm_128x128_ragged(M, N, K, ld, ldc):
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + N + K, False)
+    got = _run_guarded(lambda c: bf.gemm_1x128_128x128(qa, sa, qb, sb, c=c), M, N, ldc)
+    co = oracle.gemm_1x128_128x128(oqa, osa, oqb, osb, osb.shape[1], 1)
+    _assert_close(got, co, "gemm_1x128_128x128")
+
+
+@pytest.mark.parametrize("M,N,K,ld,ldc", GEMM_SHAPES, ids=lambda v: str(v))
+def test_gemm_128x1_ragged(M, N, K, ld, ldc):
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + N + K + 1, True)
+    got = _run_guarded(lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c), M, N, ldc)
+    co = oracle.gemm_1x128_128x1(oqa, osa, oqb, osb)
+    _assert_close(got, co, "gemm_1x128_128x1")
+
+
+def _abs_codes(h):
+    return h & 0x7F
+
+
+def _assert_dot_bound(got, co, c_abs, what):
+    """Full-range random codes: the matrix core's 128-term fp8 dot product is not an exactly
+    rounded fp32 sum (its error reaches about 2^-12 of the sum of |products|), so under heavy
+    cancellation the error is bounded by the absolute-value sum, not by |C|. Bound used:
+    |C - C_o| <= 2^-10 * sum_kb |f_kb| sum_k |a_k b_k|  +  2^-8 |C_o|  (bf16 output rounding)."""
+    bound = 2.0 ** -10 * c_abs + 2.0 ** -8 * np.abs(co)
+    excess = np.abs(got - co) - bound
+    assert np.all(excess <= 0), f"{what}: {int(np.count_nonzero(excess > 0))} elements over bound"
+    nf = np.linalg.norm(co)
+    assert np.linalg.norm(got - co) <= 4e-3 * nf, f"{what}: relative Frobenius"
+
+
+@pytest.mark.parametrize("M,N,K,ld,ldc", GEMM_SHAPES, ids=lambda v: str(v))
+def test_gemm_128x128_full_range_codes(M, N, K, ld, ldc):
+    Kb, Nb = _cdiv(K, 128), _cdiv(N, 128)
+    ah, a = _codes((M, K), 1, ld)
+    bh, b = _codes((N, K), 2, ld)
+    a_s, b_s = _scales((Kb, M), 3), _scales((Nb, Kb), 4)
+    got = _run_guarded(lambda c: bf.gemm_1x128_128x128(a, to_dev(a_s), b, to_dev(b_s), Kb, 1, c=c),
+                       M, N, ldc)
+    co = oracle.gemm_1x128_128x128(ah, a_s, bh, b_s, Kb, 1)
+    c_abs = oracle.gemm_1x128_128x128(_abs_codes(ah), a_s, _abs_codes(bh), b_s, Kb, 1)
+    _assert_dot_bound(got, co, c_abs, "gemm_1x128_128x128")
+
+
+@pytest.mark.parametrize("M,N,K,ld,ldc", GEMM_SHAPES, ids=lambda v: str(v))
+def test_gemm_128x1_full_range_codes(M, N, K, ld, ldc):
+    Kb = _cdiv(K, 128)
+    ah, a = _codes((M, K), 5, ld)
+    bh, b = _codes((N, K), 6, ld)
+    a_s, b_s = _scales((Kb, M), 7), _scales((Kb, N), 8)
+    got = _run_guarded(lambda c: bf.gemm_1x128_128x1(a, to_dev(a_s), b, to_dev(b_s), c=c), M, N, ldc)
+    co = oracle.gemm_1x128_128x1(ah, a_s, bh, b_s)
+    c_abs = oracle.gemm_1x128_128x1(_abs_codes(ah), a_s, _abs_codes(bh), b_s)
+    _assert_dot_bound(got, co, c_abs, "gemm_1x128_128x1")
+
+
+def test_gemm_transposed_scale_strides():
+    """dgrad reads the weight's [Nb_w, Kb_w] scales transposed through the strides."""
+    M, N, K = 256, 384, 512
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, K, 11, False)
+    sbt = np.ascontiguousarray(osb.T)          # stored [Kb, Nb]: element (kb, nb) at kb * Nb + nb
+    Nb = sbt.shape[1]
+    c = bf.gemm_1x128_128x128(qa, sa, qb, to_dev(sbt), 1, Nb)
+    co = oracle.gemm_1x128_128x128(oqa, osa, oqb, sbt, 1, Nb)
+    _assert_close(c.float().cpu().numpy(), co, "strided b_s")
+
+
+def test_gemm_k_zero_writes_zeros():
+    M, N = 5, 40
+    c = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    a = torch.zeros((M, 16), dtype=torch.uint8, device=DEV)[:, :0]
+    b = torch.zeros((N, 16), dtype=torch.uint8, device=DEV)[:, :0]
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    bf.gemm_1x128_128x128(a, one, b, one, 1, 1, c=c, K=0)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0)
+
+
+# ------------------------------------------------------------------ end-to-end on the workloads
+
+def _forward_check(a_h, w_h, rows, sqnr_min=28.0):
+    a, w = to_dev(a_h), to_dev(w_h)
+    qa, sa = bf.quantize_lhs(a)
+    qw, _, sw = bf.quantize_weight_128x128(w, want_qT=False)
+    c = bf.gemm_1x128_128x128(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    oqa, osa = oracle.quantize_lhs(a_h)
+    oqw, _, osw = oracle.quantize_weight_128x128(w_h, want_qT=False)
+    qa_h, sa_h = qa.cpu().numpy(), sa.cpu().numpy()
+    assert np.array_equal(qa_h, oqa) and np.array_equal(sa_h, osa)
+    assert np.array_equal(qw.cpu().numpy(), oqw) and np.array_equal(sw.cpu().numpy(), osw)
+    co = oracle.gemm_1x128_128x128(oqa, osa, oqw, osw, osw.shape[1], 1, rows=rows)
+    cg = c.float().cpu().numpy()[rows]
+    _assert_close(cg, co, "forward")
+    ref = oracle.matmul_bf16_f64(a_h, w_h, rows=rows)
+    s_gpu, s_or = oracle.sqnr_db(ref, cg), oracle.sqnr_db(ref, co)
+    assert s_gpu >= sqnr_min, (s_gpu, s_or)
+    assert abs(s_gpu - s_or) <= 0.05, (s_gpu, s_or)
+    return s_gpu, s_or
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_forward_small_workloads_full(idx):
+    d = inputs.make_workload(idx)
+    M = d["A"].shape[0]
+    # the 2x512x128 case has a seed-dependent SQNR near 28 dB even for an exact path; the
+    # 0.05 dB agreement with the oracle is the check there
+    _forward_check(d["A"], d["W"], np.arange(M), sqnr_min=27.5 if idx == 0 else 28.0)
+
+
+def test_forward_4096_sampled():
+    d = inputs.make_workload(2)
+    _forward_check(d["A"], d["W"], _sample_rows(4096))
+
+
+def test_forward_outlier_sampled():
+    d = inputs.make_workload(4)
+    _forward_check(d["A"], d["W"], _sample_rows(16384))
+
+
+def test_training_step_full_size_sampled():
+    """Forward Y = X W^T, dgrad dX = dY W (transposed weight codes, transposed scale strides) and
+    wgrad dW = dY^T X (128x1 scales, contracting over the 8192 tokens)."""
+    d = inputs.make_workload(3)
+    Xh, Wh, dYh = d["X"], d["W"], d["dY"]
+    X, W, dY = to_dev(Xh), to_dev(Wh), to_dev(dYh)
+    qx, sx = bf.quantize_lhs(X)
+    qdy, sdy = bf.quantize_lhs(dY)
+    qxT, sxT = bf.quantize_rhs(X)
+    qdyT, sdyT = bf.quantize_rhs(dY)
+    qw, qwT, sw = bf.quantize_weight_128x128(W)
+    Kbw = sw.shape[1]
+    y = bf.gemm_1x128_128x128(qx, sx, qw, sw)                      # [8192, 4096]
+    dx = bf.gemm_1x128_128x128(qdy, sdy, qwT, sw, 1, Kbw)          # [8192, 4096]
+    dw = bf.gemm_1x128_128x1(qdyT, sdyT, qxT, sxT)                 # [4096, 4096]
+    torch.cuda.synchronize()
+
+    o = {}
+    o["qx"], o["sx"] = oracle.quantize_lhs(Xh)
+    o["qdy"], o["sdy"] = oracle.quantize_lhs(dYh)
+    o["qxT"], o["sxT"] = oracle.quantize_rhs(Xh)
+    o["qdyT"], o["sdyT"] = oracle.quantize_rhs(dYh)
+    o["qw"], o["qwT"], o["sw"] = oracle.quantize_weight_128x128(Wh)
+    for name, t in [("qx", qx), ("sx", sx), ("qdy", qdy), ("sdy", sdy), ("qxT", qxT),
+                    ("sxT", sxT), ("qdyT", qdyT), ("sdyT", sdyT), ("qw", qw), ("qwT", qwT),
+                    ("sw", sw)]:
+        assert np.array_equal(t.cpu().numpy(), o[name]), name
+
+    rows = _sample_rows(8192, 48)
+    co = oracle.gemm_1x128_128x128(o["qx"], o["sx"], o["qw"], o["sw"], Kbw, 1, rows=rows)
+    _assert_close(y.float().cpu().numpy()[rows], co, "forward")
+    co = oracle.gemm_1x128_128x128(o["qdy"], o["sdy"], o["qwT"], o["sw"], 1, Kbw, rows=rows)
+    _assert_close(dx.float().cpu().numpy()[rows], co, "dgrad")
+    rows_w = _sample_rows(4096, 48)
+    co = oracle.gemm_1x128_128x1(o["qdyT"], o["sdyT"], o["qxT"], o["sxT"], rows=rows_w)
+    _assert_close(dw.float().cpu().numpy()[rows_w], co, "wgrad")
+    # SQNR of each product against the fp64 matmul of the bf16 operands
+    xf = oracle.bf16_bits_to_f64(Xh)
+    dyf = oracle.bf16_bits_to_f64(dYh)
+    wf = oracle.bf16_bits_to_f64(Wh)
+    ref_dx = dyf[rows] @ wf
+    ref_dw = dyf.T[rows_w] @ xf
+    assert oracle.sqnr_db(ref_dx, dx.float().cpu().numpy()[rows]) >= 28.0
+    assert oracle.sqnr_db(ref_dw, dw.float().cpu().numpy()[rows_w]) >= 28.0
