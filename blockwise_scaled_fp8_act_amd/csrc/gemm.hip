@@ -4,18 +4,21 @@
 // GEMM kernels", Summary; the scale loads there are masked to rows < M and columns < N, as every
 // scale load here is).
 //
-// Tile engine
+// Shared by both kernels below:
 //   * one K-block (128) is exactly one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output subtile, so a
 //     K-block's partial sum comes out of the matrix core in one instruction with zero C-in;
 //   * the partial is multiplied by a_s[m,kb] * b_s(kb,n) and added into fp32 totals (one FMA per
 //     element per K-block) before the next K-block, as the method prescribes;
-//   * the MFMA is issued with B as its first operand, so a lane's four outputs are four consecutive
-//     columns n of one row m: the 128x128 rescale factor is one scalar per (lane, M-subtile) and
-//     the bf16 epilogue writes 8 contiguous bytes per lane;
-//   * A and B tiles are staged in LDS with a 16-byte-chunk XOR swizzle (chunk ^ row%8) so the
-//     fragment reads (16 rows x 32 bytes per 16 lanes) are bank-conflict free;
-//   * rows >= M / columns >= N are never loaded (zero in LDS) nor stored; a ragged last K-block is
-//     zero-filled beyond K.
+//   * the MFMA takes B as its first operand, so a lane's four outputs are four consecutive columns n
+//     of one row m: the 128x128 rescale factor is one scalar per (lane, 16-row subtile) and the bf16
+//     epilogue writes 8 contiguous bytes per lane;
+//   * tiles are staged in LDS with a 16-byte-chunk XOR swizzle (chunk ^ row % 8), so the fragment
+//     reads (16 rows x 32 bytes per 16 lanes) are bank-conflict free;
+//   * operands are read through buffer resources that end at the matrix edge: rows >= M / >= N read
+//     as zero, and their outputs are never stored; every scale read is limited to rows < M,
+//     columns < N.
+// The fast kernel (namespace fast) serves K % 128 == 0; the general kernel also handles a ragged
+// last K-block (bytes past K are zeroed).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -27,9 +30,15 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kThreads = 256;
+constexpr int kBM = 256;      // workgroup rows (M)
+constexpr int kBN = 128;      // workgroup columns (N)
+constexpr int kWM = 64;       // rows per wave
+constexpr int kWN = 64;       // columns per wave
+constexpr int kWavesM = kBM / kWM;  // 4
+constexpr int kWavesN = kBN / kWN;  // 2
+constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512: two waves per SIMD
+constexpr int kMSub = kWM / 16;   // 16-row subtiles per wave
+constexpr int kNSub = kWN / 16;   // 16-column subtiles per wave
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -43,124 +52,309 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2v));
 }
 
-// 16 bytes of an fp8 row starting at column kc; columns >= K are zero. Rows are 16-byte aligned.
-__device__ __forceinline__ uint4 load16_k(const uint8_t* __restrict__ row, int64_t kc, int64_t K) {
-    if (kc + 16 <= K) return *reinterpret_cast<const uint4*>(row + kc);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    for (int j = 0; j < 16; ++j)
-        if (kc + j < K) w[j >> 2] |= static_cast<uint32_t>(row[kc + j]) << (8 * (j & 3));
-    return make_uint4(w[0], w[1], w[2], w[3]);
+template <int V>
+struct IntTag {
+    static constexpr int value = V;
+};
+
+// Workgroup -> output tile. Workgroups are dispatched round-robin over the 8 XCDs; consecutive
+// logical tiles are given to the same XCD, and logical tiles are ordered in groups of kGroupRows
+// tile-rows so the workgroups one XCD runs at the same time share A rows and B columns in its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupRows = 4;
+
+__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& tm, int& tn) {
+    const int total = mt * nt;
+    int logical = bid;
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    const int per_group = kGroupRows * nt;
+    const int group = logical / per_group;
+    const int first_m = group * kGroupRows;
+    const int gsize = min(mt - first_m, kGroupRows);
+    const int in_group = logical - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes),
+                                             0x00020000);
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer this kernel builds
+
+// Zero the bytes of a 16-byte chunk that lie at or past `valid` (valid counted from the chunk start).
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int64_t valid) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int64_t keep = valid - 4 * d;  // bytes of dword d to keep
+        const uint32_t msk = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+        v[d] &= msk;
+    }
+    return v;
+}
+
+__device__ __forceinline__ v8i to_v8i(u32x4 lo, u32x4 hi) {
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Per-workgroup addressing state. Tensors are read through buffer resources whose extent stops at
+// the last row of the matrix, so rows >= M (A) or >= N (B) read as zero; per-lane offsets are
+// 32-bit and block/subtile steps are uniform (scalar) offsets.
+struct Operands {
+    __amdgpu_buffer_rsrc_t a, b, as, bs;
+    uint32_t a_lane;          // (wave rows + l16) * lda + 32 lg  within the A tile
+    uint32_t b_lane;          // (tid / 8) * ldb + 16 (tid % 8)   within the B tile
+    uint32_t b_dma_lane;      // direct-to-LDS B load: row 16 wave + lane / 8, chunk (lane % 8) ^ (lane / 8)
+    uint32_t as_off[kMSub];   // 4 * m, or kOob for m >= M
+    uint32_t bs_off[kNSub];   // 4 * n for the per-column scales (n = first of the lane's 4), or kOob
+    uint32_t bs_partial;      // bit j: the lane's 4 columns of subtile j straddle column N
+    uint32_t a_sub;           // 16 * lda: A offset between consecutive 16-row subtiles
+    uint32_t b_half;          // 64 * ldb: B offset between the 2 row halves a thread loads
+    uint32_t b_eighth;        // 8 * ldb
+};
+
+// A operand of K-block kb for this lane: subtile i covers rows 16 i + l16 of the wave's 64 rows and
+// bytes [32 lg, 32 lg + 32) of the block, exactly the MFMA's per-lane operand layout.
+template <bool FULL>
+__device__ __forceinline__ void load_a(v8i (&af)[kMSub], const Operands& op, int64_t kb, int64_t K, int lg) {
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i) {
+        const uint32_t so = static_cast<uint32_t>(i) * op.a_sub + static_cast<uint32_t>(kb * kGroup);
+        u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(op.a, op.a_lane, so, 0);
+        u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(op.a, op.a_lane + 16, so, 0);
+        if (!FULL) {
+            const int64_t valid = K - (kb * kGroup + 32 * lg);
+            lo = mask_tail(lo, valid);
+            hi = mask_tail(hi, valid - 16);
+        }
+        af[i] = to_v8i(lo, hi);
+    }
+}
+
+// B tile of K-block kb (128 rows x 128 bytes) into registers: thread t holds rows t/8 + 64 p,
+// 16-byte chunk t % 8.
+template <bool FULL>
+__device__ __forceinline__ void load_b(u32x4 (&bst)[2], const Operands& op, int64_t kb, int64_t K, int tid) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint32_t so = static_cast<uint32_t>(p) * op.b_half + static_cast<uint32_t>(kb * kGroup);
+        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(op.b, op.b_lane, so, 0);
+        if (!FULL) v = mask_tail(v, K - (kb * kGroup + 16 * (tid & 7)));
+        bst[p] = v;
+    }
+}
+
+// LDS image of a B tile: row r, 16-byte chunk c stored at chunk position c ^ (r % 8), so the
+// fragment reads (rows 16 j .. 16 j + 15 at one logical chunk) spread over all banks.
+__device__ __forceinline__ void store_b(u32x4* __restrict__ sb, const u32x4 (&bst)[2], int tid) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int r = (tid >> 3) + 64 * p;
+        const int ch = tid & 7;
+        sb[r * 8 + (ch ^ (r & 7))] = bst[p];
+    }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// B tile of a full K-block straight from global memory into its LDS image (no registers): wave w
+// fills tile rows [16 w, 16 w + 16) with two 1 KB loads; lane i of load q lands at 16-byte position
+// (16 w + 8 q) * 8 + i, i.e. row 16 w + 8 q + i / 8, chunk position i % 8, which holds logical chunk
+// (i % 8) ^ (i / 8) of that row -- the same swizzled image store_b writes.
+__device__ __forceinline__ void dma_b(u32x4* __restrict__ sb, const Operands& op, int64_t kb, int wave) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        lds_void_t* dst = (lds_void_t*)(sb + (16 * wave + 8 * q) * 8);
+        const uint32_t so = static_cast<uint32_t>(q) * op.b_eighth + static_cast<uint32_t>(kb * kGroup);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, dst, 16, op.b_dma_lane, so, 0, 0);
+    }
 }
 
 template <bool PER_COL>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+__device__ __forceinline__ void load_scales(float (&as)[kMSub], u32x4 (&bsv)[kNSub], float& bscal,
+                                            const Operands& op, const float* __restrict__ b_s,
+                                            int64_t bs_nb, int64_t bs_kb, int64_t kb, int64_t M,
+                                            int64_t N, int tn) {
+    const uint32_t col = static_cast<uint32_t>(kb * M * 4);
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i)
+        as[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(op.as, op.as_off[i], col, 0));
+    if (PER_COL) {
+        const uint32_t row = static_cast<uint32_t>(kb * N * 4);
+#pragma unroll
+        for (int j = 0; j < kNSub; ++j) {
+            if (op.bs_partial & (1u << j)) {  // the quad straddles column N: per-element loads
+                const int64_t n = op.bs_off[j] / 4;
+                u32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = (n + e < N) ? __builtin_amdgcn_raw_buffer_load_b32(op.bs, op.bs_off[j] + 4 * e, row, 0) : 0u;
+                bsv[j] = v;
+            } else {
+                bsv[j] = __builtin_amdgcn_raw_buffer_load_b128(op.bs, op.bs_off[j], row, 0);
+            }
+        }
+    } else {
+        bscal = b_s[static_cast<int64_t>(tn) * bs_nb + kb * bs_kb];
+    }
+}
+
+template <bool PER_COL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s,
     int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc,
-    int64_t M, int64_t N, int64_t K, int c_vec) {
-    __shared__ uint4 sA[kBM * 8];
-    __shared__ uint4 sB[kBN * 8];
+    int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
+    __shared__ u32x4 sB[2][kBN * 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
     const int l16 = lane & 15;
     const int lg = lane >> 4;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kBN;
+    int tm, tn;
+    tile_of(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int64_t mw = m0 + kWM * wm;
+    const int64_t nw = n0 + kWN * wn;
     const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const int64_t Kfull = K / kGroup;  // K-blocks with all 128 columns in range
 
-    v4f acc[4][4];
+    Operands op;
+    {
+        const int64_t arows = (M - m0) < kBM ? (M - m0) : kBM;
+        const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
+        op.a = make_rsrc(A + m0 * lda, static_cast<uint32_t>(arows * lda));
+        op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
+        op.as = make_rsrc(a_s, static_cast<uint32_t>(M * Kb * 4));
+        op.bs = make_rsrc(b_s, PER_COL ? static_cast<uint32_t>(N * Kb * 4) : 0u);
+        op.a_lane = static_cast<uint32_t>((kWM * wm + l16) * lda + 32 * lg);
+        op.b_lane = static_cast<uint32_t>((tid >> 3) * ldb + 16 * (tid & 7));
+        op.a_sub = static_cast<uint32_t>(16 * lda);
+        op.b_half = static_cast<uint32_t>(64 * ldb);
+        op.b_eighth = static_cast<uint32_t>(8 * ldb);
+        op.b_dma_lane = static_cast<uint32_t>((16 * wave + (lane >> 3)) * ldb + 16 * ((lane & 7) ^ (lane >> 3)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    for (int64_t kb = 0; kb < Kb; ++kb) {
-        const int64_t k0 = kb * kGroup;
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = (tid >> 3) + 32 * p;
-            const int ch = tid & 7;
-            const int64_t kc = k0 + ch * 16;
-            uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = make_uint4(0u, 0u, 0u, 0u);
-            if (m0 + r < M) va = load16_k(A + (m0 + r) * lda, kc, K);
-            if (n0 + r < N) vb = load16_k(B + (n0 + r) * ldb, kc, K);
-            sA[r * 8 + (ch ^ (r & 7))] = va;
-            sB[r * 8 + (ch ^ (r & 7))] = vb;
+        for (int i = 0; i < kMSub; ++i) {
+            const int64_t m = mw + 16 * i + l16;
+            op.as_off[i] = m < M ? static_cast<uint32_t>(4 * m) : kOob;
         }
-        __syncthreads();
-
-        v8i af[4], bfr[4];
+        op.bs_partial = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + i * 16 + l16;
-            const uint4 lo = sA[r * 8 + ((2 * lg) ^ (r & 7))];
-            const uint4 hi = sA[r * 8 + ((2 * lg + 1) ^ (r & 7))];
-            af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wn * 64 + j * 16 + l16;
-            const uint4 lo = sB[r * 8 + ((2 * lg) ^ (r & 7))];
-            const uint4 hi = sB[r * 8 + ((2 * lg + 1) ^ (r & 7))];
-            bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-
-        // scales: the lane's row m of each M-subtile; masked to m < M
-        float as[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t m = m0 + wm * 64 + i * 16 + l16;
-            as[i] = (m < M) ? a_s[kb * M + m] : 0.0f;
-        }
-        if (!PER_COL) {
-            const float bsc = b_s[static_cast<int64_t>(blockIdx.x) * bs_nb + kb * bs_kb];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float f = as[i] * bsc;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4f p = mfma_fp8_16x16x128(bfr[j], af[i]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r], f, acc[i][j][r]);
-                }
-            }
-        } else {
-            float bsv[4][4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t n = n0 + wn * 64 + j * 16 + 4 * lg;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bsv[j][r] = (n + r < N) ? b_s[kb * N + n + r] : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4f p = mfma_fp8_16x16x128(bfr[j], af[i]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[i][j][r] = fmaf(p[r], as[i] * bsv[j][r], acc[i][j][r]);
-                }
-            }
+        for (int j = 0; j < kNSub; ++j) {
+            const int64_t n = nw + 16 * j + 4 * lg;
+            op.bs_off[j] = n < N ? static_cast<uint32_t>(4 * n) : kOob;
+            if (n < N && n + 4 > N) op.bs_partial |= 1u << j;
         }
     }
 
-    // epilogue: lane holds C[m][n .. n+3]
+    v4f acc[kMSub][kNSub];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 64 + i * 16 + l16;
+    for (int i = 0; i < kMSub; ++i)
+#pragma unroll
+        for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (Kb > 0) {
+        v8i af[2][kMSub];
+        float as[2][kMSub];
+        u32x4 bsv[2][kNSub];
+        float bscal[2];
+
+        // prologue: B(0) -> LDS[0]; A(0) and scales(0) -> registers
+        if (Kfull > 0) {
+            dma_b(sB[0], op, 0, wave);
+            load_a<true>(af[0], op, 0, K, lg);
+        } else {
+            u32x4 bst[2];
+            load_b<false>(bst, op, 0, K, tid);
+            store_b(sB[0], bst, tid);
+            load_a<false>(af[0], op, 0, K, lg);
+        }
+        load_scales<PER_COL>(as[0], bsv[0], bscal[0], op, b_s, bs_nb, bs_kb, 0, M, N, tn);
+        __syncthreads();
+
+        // One K-block; the buffer index is a compile-time constant so every register array stays
+        // in registers. B(kb+1) streams into the other LDS buffer and A(kb+1) into the other
+        // register set while this block computes; the barrier at the end publishes B(kb+1).
+        auto step = [&](auto cur_tag, int64_t kb) {
+            constexpr int cur = decltype(cur_tag)::value;
+            constexpr int nxt = cur ^ 1;
+            const bool more = kb + 1 < Kb;
+            const bool next_full = kb + 1 < Kfull;
+            if (more) {
+                if (next_full) {
+                    dma_b(sB[nxt], op, kb + 1, wave);
+                    load_a<true>(af[nxt], op, kb + 1, K, lg);
+                } else {
+                    load_a<false>(af[nxt], op, kb + 1, K, lg);
+                }
+                load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, M, N, tn);
+            }
+            // this K-block: partial products of every 16x16 subtile, rescaled into the totals.
+            // Software pipeline over the 8 column subtiles: the B fragment of subtile j+1 is read
+            // from LDS while subtile j's four MFMAs run, and subtile j-1's partials are rescaled
+            // into the totals between them (one MFMA, then four FMAs).
+            const u32x4* sb = sB[cur];
+            float f[kMSub];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? as[cur][i] : as[cur][i] * bscal[cur];
+            auto read_bf = [&](int j) {
+                const int r = kWN * wn + 16 * j + l16;
+                return to_v8i(sb[r * 8 + ((2 * lg) ^ (r & 7))], sb[r * 8 + ((2 * lg + 1) ^ (r & 7))]);
+            };
+            auto rescale = [&](int j, const v4f (&pj)[kMSub]) {
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) {
+                    if (PER_COL) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][e] = fmaf(pj[i][e], f[i] * __uint_as_float(bsv[cur][j][e]), acc[i][j][e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i], acc[i][j][e]);
+                    }
+                }
+            };
+            v8i bf[2];
+            v4f pp[2][kMSub];
+            bf[0] = read_bf(0);
+#pragma unroll
+            for (int j = 0; j < kNSub; ++j) {
+                if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[cur][i]);
+                if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
+            }
+            rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
+            if (more && !next_full) {  // ragged last K-block: masked register path
+                u32x4 bst[2];
+                load_b<false>(bst, op, kb + 1, K, tid);
+                store_b(sB[nxt], bst, tid);
+            }
+            __syncthreads();
+        };
+        for (int64_t kb = 0; kb < Kb; kb += 2) {
+            step(IntTag<0>{}, kb);
+            if (kb + 1 < Kb) step(IntTag<1>{}, kb + 1);
+        }
+    }
+
+    // epilogue: lane holds C[m][n .. n+3] of every subtile
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i) {
+        const int64_t m = mw + 16 * i + l16;
         if (m >= M) continue;
         uint16_t* crow = C + m * ldc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 16 + 4 * lg;
+        for (int j = 0; j < kNSub; ++j) {
+            const int64_t n = nw + 16 * j + 4 * lg;
             const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
             if (c_vec && n + 4 <= N) {
@@ -169,26 +363,273 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                 const uint16_t h[4] = {static_cast<uint16_t>(w0 & 0xFFFF), static_cast<uint16_t>(w0 >> 16),
                                        static_cast<uint16_t>(w1 & 0xFFFF), static_cast<uint16_t>(w1 >> 16)};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (n + r < N) crow[n + r] = h[r];
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) crow[n + e] = h[e];
             }
         }
     }
 }
+
+// ==============================================================================================
+// Fast path for K % 128 == 0 (and, with per-column scales, N % 4 == 0): a 256 x 128 workgroup tile
+// of 4 waves, one per SIMD, each wave owning 64 full-width rows (64 x 128 outputs, 128 fp32 totals
+// in VGPRs).
+//   * Every K-block's A tile (256 x 128 bytes), B tile (128 x 128 bytes) and scale slices go
+//     global -> LDS by direct buffer loads (no registers) into one of three LDS stages, two
+//     K-blocks ahead of the block being multiplied: about 100 KB per CU in flight, enough to cover
+//     the L2 / last-level-cache latency at the MFMA rate.
+//   * Each wave waits for its own loads of the block it is about to use (an exact vector-memory
+//     count), then the workgroup barrier makes every wave's part visible; fragments and scales are
+//     then read from LDS with ordinary loads.
+// Per K-block and CU: 49 KB written to LDS, about 100 KB read from it, 32 MFMAs (1024 cycles) per
+// SIMD.
+namespace fast {
+
+constexpr int kBM = 256;
+constexpr int kBN = 128;
+constexpr int kWM = 64;
+constexpr int kWaves = kBM / kWM;      // 4: one wave per SIMD
+constexpr int kThreads = 64 * kWaves;  // 256
+constexpr int kMSub = kWM / 16;        // 4
+constexpr int kNSub = kBN / 16;        // 8
+constexpr int kStages = 3;
+
+// LDS image of one stage (16-byte units): A tile rows 0..255, B tile rows 0..127 (both with the
+// chunk ^ (row % 8) swizzle), then the A scales of the tile rows and the per-column B scales.
+constexpr int kStageA = 0;
+constexpr int kStageB = kStageA + kBM * 8;
+constexpr int kStageSA = kStageB + kBN * 8;
+constexpr int kStageSB = kStageSA + kBM / 4;
+constexpr int kStageSize = kStageSB + kBN / 4;  // 3136 x 16 B = 49 KB
+
+// vector-memory instructions each wave issues per stage
+constexpr int kLoadsPerStage(bool per_col) { return 8 + 4 + 1 + (per_col ? 1 : 0); }
+
+// Direct global -> LDS load of 16 bytes per active lane to LDS address lds + 16 * lane (lds must be
+// wave-uniform). M0 carries the LDS address; its previous value is restored afterwards.
+__device__ __forceinline__ void ld_lds(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(soff)
+        : "memory");
+}
+
+struct Ops {
+    __amdgpu_buffer_rsrc_t a, b, as, bs;
+    uint32_t a_lane;   // tile row 64 wave + lane / 8, chunk (lane % 8) ^ (lane / 8): rows of load q add 8 q
+    uint32_t b_lane;   // tile row 32 wave + lane / 8, same chunk rule
+    uint32_t as_lane;  // 4 (m0 + 64 wave + 4 lane): 4 A scales per lane (lanes 0..15)
+    uint32_t bs_lane;  // 4 (n0 + 32 wave + 4 lane): 4 B scales per lane (lanes 0..7)
+    uint32_t a_eighth; // 8 lda
+    uint32_t b_eighth; // 8 ldb
+    uint32_t lds_wave; // LDS byte address of stage 0
+};
+
+template <bool PER_COL>
+__device__ __forceinline__ void issue_stage(const Ops& op, int stage, int64_t kb, int64_t M, int64_t N,
+                                            int wave, int lane) {
+    const uint32_t base = op.lds_wave + static_cast<uint32_t>(stage * kStageSize * 16);
+    const uint32_t k = static_cast<uint32_t>(kb * kGroup);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)  // A rows 64 wave .. + 64
+        ld_lds(base + (kStageA + (64 * wave + 8 * q) * 8) * 16, op.a, op.a_lane, q * op.a_eighth + k);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)  // B rows 32 wave .. + 32
+        ld_lds(base + (kStageB + (32 * wave + 8 * q) * 8) * 16, op.b, op.b_lane, q * op.b_eighth + k);
+    // A scales of rows 64 wave .. + 64 (column kb of the column-major scales): 16 lanes x 4 floats.
+    // A direct load writes LDS for every active lane (out-of-range lanes write zeros), so the lanes
+    // beyond the slice are switched off rather than pointed out of range. Lane 0 is always active,
+    // so each wave issues the same number of loads per stage.
+    if (lane < 16) ld_lds(base + (kStageSA + 16 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
+    if (PER_COL) {  // B scales of columns 32 wave .. + 32 (row kb): 8 lanes x 4 floats
+        if (lane < 8) ld_lds(base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
+    }
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding and all its LDS
+// reads have returned, then synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_and_sync() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool PER_COL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
+    const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s,
+    int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc,
+    int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
+    __shared__ u32x4 smem[kStages * kStageSize];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    int tm, tn;
+    tile_of(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * kBN;
+    const int64_t mw = m0 + kWM * wave;
+    const int64_t Kb = K / kGroup;
+    constexpr int kLoads = kLoadsPerStage(PER_COL);
+
+    Ops op;
+    {
+        const int64_t arows = (M - m0) < kBM ? (M - m0) : kBM;
+        const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
+        op.a = make_rsrc(A + m0 * lda, static_cast<uint32_t>(arows * lda));
+        op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
+        op.as = make_rsrc(a_s, static_cast<uint32_t>(M * Kb * 4));
+        op.bs = make_rsrc(b_s, PER_COL ? static_cast<uint32_t>(N * Kb * 4) : 0u);
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        op.a_lane = static_cast<uint32_t>((64 * wave + (lane >> 3)) * lda + 16 * chunk);
+        op.b_lane = static_cast<uint32_t>((32 * wave + (lane >> 3)) * ldb + 16 * chunk);
+        op.as_lane = static_cast<uint32_t>(4 * (m0 + 64 * wave + 4 * lane));
+        op.bs_lane = static_cast<uint32_t>(4 * (n0 + 32 * wave + 4 * lane));
+        op.a_eighth = static_cast<uint32_t>(8 * lda);
+        op.b_eighth = static_cast<uint32_t>(8 * ldb);
+        op.lds_wave = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
+    }
+
+    v4f acc[kMSub][kNSub];
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i)
+#pragma unroll
+        for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (Kb > 0) {
+        float bscal[kStages];
+        issue_stage<PER_COL>(op, 0, 0, M, N, wave, lane);
+        if (!PER_COL) bscal[0] = b_s[static_cast<int64_t>(tn) * bs_nb];
+        if (Kb > 1) {
+            issue_stage<PER_COL>(op, 1, 1, M, N, wave, lane);
+            if (!PER_COL) bscal[1] = b_s[static_cast<int64_t>(tn) * bs_nb + bs_kb];
+        }
+
+        auto step = [&](auto cur_tag, int64_t kb) {
+            constexpr int cur = decltype(cur_tag)::value;
+            constexpr int nx2 = (cur + 2) % kStages;
+            if (kb + 1 < Kb) wait_and_sync<kLoads>();  // only block kb+1's loads may be in flight
+            else wait_and_sync<0>();
+            if (kb + 2 < Kb) {
+                issue_stage<PER_COL>(op, nx2, kb + 2, M, N, wave, lane);
+                if (!PER_COL) bscal[nx2] = b_s[static_cast<int64_t>(tn) * bs_nb + (kb + 2) * bs_kb];
+            }
+            const u32x4* st = smem + cur * kStageSize;
+            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wave;
+            const float* sbs = reinterpret_cast<const float*>(st + kStageSB);
+            float f[kMSub];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bscal[cur];
+            v8i af[kMSub];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) {
+                const int r = 64 * wave + 16 * i + l16;
+                af[i] = to_v8i(st[kStageA + r * 8 + ((2 * lg) ^ (r & 7))],
+                               st[kStageA + r * 8 + ((2 * lg + 1) ^ (r & 7))]);
+            }
+            auto read_bf = [&](int j) {
+                const int r = 16 * j + l16;
+                return to_v8i(st[kStageB + r * 8 + ((2 * lg) ^ (r & 7))],
+                              st[kStageB + r * 8 + ((2 * lg + 1) ^ (r & 7))]);
+            };
+            auto rescale = [&](int j, const v4f (&pj)[kMSub]) {
+                v4f bsj = {1.0f, 1.0f, 1.0f, 1.0f};
+                if (PER_COL) bsj = *reinterpret_cast<const v4f*>(sbs + 16 * j + 4 * lg);
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) {
+                    if (PER_COL) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i] * bsj[e], acc[i][j][e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i], acc[i][j][e]);
+                    }
+                }
+            };
+            v8i bf[2];
+            v4f pp[2][kMSub];
+            bf[0] = read_bf(0);
+#pragma unroll
+            for (int j = 0; j < kNSub; ++j) {
+                if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
+                if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
+            }
+            rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
+        };
+        for (int64_t kb = 0; kb < Kb; kb += kStages) {
+            step(IntTag<0>{}, kb);
+            if (kb + 1 < Kb) step(IntTag<1>{}, kb + 1);
+            if (kb + 2 < Kb) step(IntTag<2>{}, kb + 2);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i) {
+        const int64_t m = mw + 16 * i + l16;
+        if (m >= M) continue;
+        uint16_t* crow = C + m * ldc;
+#pragma unroll
+        for (int j = 0; j < kNSub; ++j) {
+            const int64_t n = n0 + 16 * j + 4 * lg;
+            const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            if (c_vec && n + 4 <= N) {
+                *reinterpret_cast<uint2*>(crow + n) = make_uint2(w0, w1);
+            } else {
+                const uint16_t h[4] = {static_cast<uint16_t>(w0 & 0xFFFF), static_cast<uint16_t>(w0 >> 16),
+                                       static_cast<uint16_t>(w1 & 0xFFFF), static_cast<uint16_t>(w1 >> 16)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) crow[n + e] = h[e];
+            }
+        }
+    }
+}
+
+}  // namespace fast
 
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((N + kBN - 1) / kBN), static_cast<unsigned>((M + kBM - 1) / kBM));
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    if (K % kGroup == 0 && (!bs.per_column || N % 4 == 0)) {
+        const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
+        const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
+        if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+        const dim3 grid(static_cast<unsigned>(mt * nt));
+        if (bs.per_column)
+            fast::gemm_kernel<true><<<grid, fast::kThreads, 0, stream>>>(
+                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
+        else
+            fast::gemm_kernel<false><<<grid, fast::kThreads, 0, stream>>>(
+                a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt,
+                (int)nt, c_vec);
+        return hipGetLastError();
+    }
+    const int64_t mt = (M + kBM - 1) / kBM;
+    const int64_t nt = (N + kBN - 1) / kBN;
+    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(mt * nt));
     if (bs.per_column)
         gemm_kernel<true><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc,
-                                                         M, N, K, c_vec);
+                                                         M, N, K, (int)mt, (int)nt, c_vec);
     else
         gemm_kernel<false><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb,
-                                                          bs.stride_kb, c, ldc, M, N, K, c_vec);
+                                                          bs.stride_kb, c, ldc, M, N, K, (int)mt,
+                                                          (int)nt, c_vec);
     return hipGetLastError();
 }
 
