@@ -39,6 +39,24 @@ def weight_bytes(N, K, with_qT):
     return 2 * N * K + N * K * (2 if with_qT else 1) + 4 * ((N + 127) // 128) * ((K + 127) // 128)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE record in profiles/, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    csrc = os.path.join(ROOT, "blockwise_scaled_fp8_act_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "device_common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec.get("traffic_bytes")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -48,11 +66,28 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="omit the per-kernel shape table")
     p.add_argument("--no-cpu-baseline", action="store_true", help="omit the CPU oracle leg")
     p.add_argument("--cpu-rows", type=int, default=4096, help="GEMM rows in the CPU oracle sample")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
+                        "kernel for scaling HBM traffic counters) and exit")
     return p.parse_args()
+
+
+def copy_probe(nbytes):
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reads": nbytes, "writes": nbytes}))
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    f"(got {args.gpus}); multi-GPU sharding is design only"}))
@@ -167,7 +202,8 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("gemm_1x128_128x128"),
+            "traffic_unit": "bytes per launch (HBM/MALL, rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
         },
         "step_kernels": {
             "quantize_lhs": {"avg_us": round(k_avg[0] * 1e3, 2), "median_us": round(k_med[0] * 1e3, 2),
