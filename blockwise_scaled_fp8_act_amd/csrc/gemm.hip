@@ -401,23 +401,11 @@ constexpr int kStageB = kStageA + kBM * 8;
 constexpr int kStageSA = kStageB + kBN * 8;
 constexpr int kStageSB = kStageSA + kBM / 4;
 constexpr int kStageSize = kStageSB + kBN / 4;  // 3136 x 16 B = 49 KB
+constexpr int kMaxKbFast = 512;                 // 128x128 B scales of the tile's column, kept in LDS
 
 // vector-memory instructions each wave issues per stage
 constexpr int kLoadsPerStage(bool per_col) { return 8 + 4 + 1 + (per_col ? 1 : 0); }
 
-// Direct global -> LDS load of 16 bytes per active lane to LDS address lds + 16 * lane (lds must be
-// wave-uniform). M0 carries the LDS address; its previous value is restored afterwards.
-__device__ __forceinline__ void ld_lds(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(soff)
-        : "memory");
-}
 
 struct Ops {
     __amdgpu_buffer_rsrc_t a, b, as, bs;
@@ -430,32 +418,89 @@ struct Ops {
     uint32_t lds_wave; // LDS byte address of stage 0
 };
 
+// One direct load (16 B per lane, LDS address lds + 16 * lane) with M0 saved and restored.
+__device__ __forceinline__ void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+}
+// Direct load of 16 B per lane for lanes 0 .. 15 (lo = 0xFFFF) or 0 .. 7 (lo = 0xFF) only. A
+// direct load writes LDS for every active lane (lanes whose offset is out of range write zeros),
+// so the lanes beyond a scale slice are switched off. EXEC is changed and restored inside the one
+// asm block rather than through a branch: a branch would split the K-block's straight-line code.
+template <uint32_t LO>
+__device__ __forceinline__ void dma16_lanes(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    uint32_t saved_m0;
+    uint64_t saved_exec;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\t"
+        "s_mov_b32 exec_lo, %6\n\t"
+        "s_mov_b32 exec_hi, 0\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_mov_b64 exec, %1"
+        : "=&s"(saved_m0), "=&s"(saved_exec)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
+          "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(LO)
+        : "memory");
+}
+
+// Same with 4 B per lane (LDS address lds + 4 * lane).
+__device__ __forceinline__ void dma4(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+}
+
+// Load number q of a stage, q = 0 .. kLoadsPerStage - 1: 0..7 the wave's A rows 64 wave + 8 q ..,
+// 8..11 B rows 32 wave + 8 (q - 8) .., 12 the A scales of the wave's rows, 13 (per-column) the B
+// scales of columns 32 wave .. + 32. The loads of one stage can be spread over a K-block.
 template <bool PER_COL>
-__device__ __forceinline__ void issue_stage(const Ops& op, int stage, int64_t kb, int64_t M, int64_t N,
-                                            int wave, int lane) {
-    const uint32_t base = op.lds_wave + static_cast<uint32_t>(stage * kStageSize * 16);
+__device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb,
+                                           int64_t M, int64_t N, int wave, int lane) {
     const uint32_t k = static_cast<uint32_t>(kb * kGroup);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)  // A rows 64 wave .. + 64
-        ld_lds(base + (kStageA + (64 * wave + 8 * q) * 8) * 16, op.a, op.a_lane, q * op.a_eighth + k);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)  // B rows 32 wave .. + 32
-        ld_lds(base + (kStageB + (32 * wave + 8 * q) * 8) * 16, op.b, op.b_lane, q * op.b_eighth + k);
-    // A scales of rows 64 wave .. + 64 (column kb of the column-major scales): 16 lanes x 4 floats.
-    // A direct load writes LDS for every active lane (out-of-range lanes write zeros), so the lanes
-    // beyond the slice are switched off rather than pointed out of range. Lane 0 is always active,
-    // so each wave issues the same number of loads per stage.
-    if (lane < 16) ld_lds(base + (kStageSA + 16 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
-    if (PER_COL) {  // B scales of columns 32 wave .. + 32 (row kb): 8 lanes x 4 floats
-        if (lane < 8) ld_lds(base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
+    if (q < 8) {
+        dma16(stage_base + (kStageA + (64 * wave + 8 * q) * 8) * 16, op.a, op.a_lane, q * op.a_eighth + k);
+    } else if (q < 12) {
+        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 8)) * 8) * 16, op.b, op.b_lane, (q - 8) * op.b_eighth + k);
+    } else if (q == 12) {
+        dma16_lanes<0xFFFFu>(stage_base + (kStageSA + 16 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
+    } else if (PER_COL && q == 13) {
+        dma16_lanes<0xFFu>(stage_base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
     }
 }
 
-// Wait until at most N vector-memory instructions of this wave are outstanding and all its LDS
-// reads have returned, then synchronise the workgroup.
+template <bool PER_COL>
+__device__ __forceinline__ void issue_stage(const Ops& op, uint32_t stage_base, int64_t kb, int64_t M,
+                                            int64_t N, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < kLoadsPerStage(PER_COL); ++q) issue_load<PER_COL>(q, op, stage_base, kb, M, N, wave, lane);
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding (its own direct
+// loads of an older stage have landed in LDS).
 template <int N>
-__device__ __forceinline__ void wait_and_sync() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
+__device__ __forceinline__ void wait_own_loads() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// All LDS reads of this wave have returned, then the workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -467,6 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc,
     int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
     __shared__ u32x4 smem[kStages * kStageSize];
+    __shared__ float bscale_lds[kMaxKbFast];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -506,36 +552,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (Kb > 0) {
-        float bscal[kStages];
-        issue_stage<PER_COL>(op, 0, 0, M, N, wave, lane);
-        if (!PER_COL) bscal[0] = b_s[static_cast<int64_t>(tn) * bs_nb];
-        if (Kb > 1) {
-            issue_stage<PER_COL>(op, 1, 1, M, N, wave, lane);
-            if (!PER_COL) bscal[1] = b_s[static_cast<int64_t>(tn) * bs_nb + bs_kb];
-        }
-
-        auto step = [&](auto cur_tag, int64_t kb) {
-            constexpr int cur = decltype(cur_tag)::value;
-            constexpr int nx2 = (cur + 2) % kStages;
-            if (kb + 1 < Kb) wait_and_sync<kLoads>();  // only block kb+1's loads may be in flight
-            else wait_and_sync<0>();
-            if (kb + 2 < Kb) {
-                issue_stage<PER_COL>(op, nx2, kb + 2, M, N, wave, lane);
-                if (!PER_COL) bscal[nx2] = b_s[static_cast<int64_t>(tn) * bs_nb + (kb + 2) * bs_kb];
-            }
-            const u32x4* st = smem + cur * kStageSize;
+        // The wave's own A rows and A scales of a stage can be read as soon as its own direct loads
+        // of that stage have landed; the B tile (and per-column B scales) is shared, so reading it
+        // also needs the barrier that follows every wave's wait.
+        v8i af[kMSub];
+        float f[kMSub];
+        auto stage_base = [&](int stage) {
+            return op.lds_wave + static_cast<uint32_t>(stage * kStageSize * 16);
+        };
+        auto read_own = [&](int stage, int64_t kb) {
+            const u32x4* st = smem + stage * kStageSize;
             const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wave;
-            const float* sbs = reinterpret_cast<const float*>(st + kStageSB);
-            float f[kMSub];
-#pragma unroll
-            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bscal[cur];
-            v8i af[kMSub];
+            const float bsc = PER_COL ? 1.0f : bscale_lds[kb];
 #pragma unroll
             for (int i = 0; i < kMSub; ++i) {
                 const int r = 64 * wave + 16 * i + l16;
                 af[i] = to_v8i(st[kStageA + r * 8 + ((2 * lg) ^ (r & 7))],
                                st[kStageA + r * 8 + ((2 * lg + 1) ^ (r & 7))]);
+                f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
             }
+        };
+
+        // 128x128 B scales of this tile's column (kb = 0 .. Kb-1) into LDS, 4 bytes per lane,
+        // before the first stage (so they are covered by the first stage's wait and barrier).
+        if (!PER_COL) {
+            const uint32_t lds_bs = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bscale_lds));
+            const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_s, 0x7FFFFFFFu);
+            for (int64_t c = 0; c < Kb; c += 64) {
+                if (wave == 0 && c + lane < Kb)
+                    dma4(lds_bs + static_cast<uint32_t>(4 * c), rbs,
+                         static_cast<uint32_t>(4 * (tn * bs_nb + (c + lane) * bs_kb)), 0u);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+
+        // Stages past the last K-block are still issued (their rows are in range, only the data is
+        // unused) so every step waits for the same number of loads and stays straight-line code.
+        issue_stage<PER_COL>(op, stage_base(0), 0, M, N, wave, lane);
+        issue_stage<PER_COL>(op, stage_base(1), 1, M, N, wave, lane);
+        wait_own_loads<kLoads>();
+        read_own(0, 0);
+
+        auto step = [&](auto cur_tag, int64_t kb) {
+            constexpr int cur = decltype(cur_tag)::value;
+            constexpr int nx1 = (cur + 1) % kStages;
+            constexpr int nx2 = (cur + 2) % kStages;
+            // every wave has its block-kb loads in LDS and is done reading block kb-1
+            lds_barrier();
+            const uint32_t base2 = stage_base(nx2);
+
+            const u32x4* st = smem + cur * kStageSize;
+            const float* sbs = reinterpret_cast<const float*>(st + kStageSB);
             auto read_bf = [&](int j) {
                 const int r = 16 * j + l16;
                 return to_v8i(st[kStageB + r * 8 + ((2 * lg) ^ (r & 7))],
@@ -558,20 +627,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             v8i bf[2];
             v4f pp[2][kMSub];
             bf[0] = read_bf(0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNSub; ++j) {
+                // the loads of block kb+2, spread over the subtiles
+                issue_load<PER_COL>(2 * j, op, base2, kb + 2, M, N, wave, lane);
+                issue_load<PER_COL>(2 * j + 1, op, base2, kb + 2, M, N, wave, lane);
                 if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
                 if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
+                // issue order inside the subtile: the next fragment's LDS reads, then each MFMA
+                // followed by the four rescale FMAs of the previous subtile's partials
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, PER_COL ? 8 : 4, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
             rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
+            // this wave's loads of block kb+1 (issued two blocks ago) -> next A fragments and scales
+            wait_own_loads<kLoads>();
+            read_own(nx1, kb + 1 < Kb ? kb + 1 : kb);
         };
         for (int64_t kb = 0; kb < Kb; kb += kStages) {
             step(IntTag<0>{}, kb);
             if (kb + 1 < Kb) step(IntTag<1>{}, kb + 1);
             if (kb + 2 < Kb) step(IntTag<2>{}, kb + 2);
         }
+        wait_own_loads<0>();  // no direct load may outlive the workgroup's LDS
     }
 
 #pragma unroll
@@ -605,7 +691,15 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
-    if (K % kGroup == 0 && (!bs.per_column || N % 4 == 0)) {
+    // Fast path: whole K-blocks; per-column scales read 4 columns at a time; 128x128 scales of a
+    // tile's column staged in LDS (at most kMaxKbFast K-blocks, byte offsets below 2^31).
+    const int64_t kb_all = K / kGroup;
+    const int64_t nb_all = (N + kGroup - 1) / kGroup;
+    const bool fast_scales =
+        bs.per_column ? (N % 4 == 0)
+                      : (kb_all <= fast::kMaxKbFast &&
+                         4 * ((nb_all - 1) * bs.stride_nb + (kb_all - 1) * bs.stride_kb) < 0x7FFFFFFFLL);
+    if (K % kGroup == 0 && fast_scales) {
         const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
         if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
