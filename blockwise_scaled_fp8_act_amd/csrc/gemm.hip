@@ -371,54 +371,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 }
 
 // ==============================================================================================
-// Fast path for K % 128 == 0 (and, with per-column scales, N % 4 == 0): a 256 x 128 workgroup tile
-// of 4 waves, one per SIMD, each wave owning 64 full-width rows (64 x 128 outputs, 128 fp32 totals
-// in VGPRs).
-//   * Every K-block's A tile (256 x 128 bytes), B tile (128 x 128 bytes) and scale slices go
-//     global -> LDS by direct buffer loads (no registers) into one of three LDS stages, two
-//     K-blocks ahead of the block being multiplied: about 100 KB per CU in flight, enough to cover
-//     the L2 / last-level-cache latency at the MFMA rate.
-//   * Each wave waits for its own loads of the block it is about to use (an exact vector-memory
-//     count), then the workgroup barrier makes every wave's part visible; fragments and scales are
-//     then read from LDS with ordinary loads.
-// Per K-block and CU: 49 KB written to LDS, about 100 KB read from it, 32 MFMAs (1024 cycles) per
-// SIMD.
+// Fast path for K % 128 == 0 (and, with per-column scales, N % 4 == 0): a 256 x 256 workgroup tile
+// of 8 waves, two per SIMD, each wave owning a 64 x 128 block of the tile (128 fp32 totals in
+// VGPRs).
+//   * Every K-block's A tile (256 x 128 bytes), B tile (256 x 128 bytes) and scale slices go
+//     global -> LDS by direct buffer loads (no registers) into one of two LDS stages, one K-block
+//     ahead of the block being multiplied. Each wave loads 1/8 of every tile; the workgroup barrier
+//     that follows each wave's wait for its own loads makes the stage visible to all.
+//   * Two waves per SIMD: while one waits at the barrier or for LDS data, the other keeps the
+//     matrix core busy. Per K-block and CU: 64 KB written to LDS and 192 KB read from it against
+//     2048 MFMA cycles per SIMD.
+//   * LDS rows hold their 16-byte chunks XOR-swizzled by (row / 2) % 8, so the 16 rows one fragment
+//     read touches (per lane group) fall in 16 distinct groups of 4 banks.
 namespace fast {
 
 constexpr int kBM = 256;
-constexpr int kBN = 128;
+constexpr int kBN = 256;
 constexpr int kWM = 64;
-constexpr int kWaves = kBM / kWM;      // 4: one wave per SIMD
-constexpr int kThreads = 64 * kWaves;  // 256
+constexpr int kWN = 128;
+constexpr int kWaves = 8;              // 4 (M) x 2 (N): two per SIMD
+constexpr int kThreads = 64 * kWaves;  // 512
 constexpr int kMSub = kWM / 16;        // 4
-constexpr int kNSub = kBN / 16;        // 8
-constexpr int kStages = 3;
+constexpr int kNSub = kWN / 16;        // 8
+constexpr int kStages = 2;
+constexpr int kMaxKbFast = 512;        // 128x128 B scales of the tile's columns, kept in LDS
 
-// LDS image of one stage (16-byte units): A tile rows 0..255, B tile rows 0..127 (both with the
-// chunk ^ (row % 8) swizzle), then the A scales of the tile rows and the per-column B scales.
+// LDS image of one stage (16-byte units): A tile rows 0..255, B tile rows 0..255, then the A scales
+// of the tile rows and the per-column B scales of the tile columns.
 constexpr int kStageA = 0;
 constexpr int kStageB = kStageA + kBM * 8;
 constexpr int kStageSA = kStageB + kBN * 8;
 constexpr int kStageSB = kStageSA + kBM / 4;
-constexpr int kStageSize = kStageSB + kBN / 4;  // 3136 x 16 B = 49 KB
-constexpr int kMaxKbFast = 512;                 // 128x128 B scales of the tile's column, kept in LDS
+constexpr int kStageSize = kStageSB + kBN / 4;  // 4224 x 16 B = 66 KB
 
-// vector-memory instructions each wave issues per stage
-constexpr int kLoadsPerStage(bool per_col) { return 8 + 4 + 1 + (per_col ? 1 : 0); }
+// vector-memory instructions each wave issues per stage: 4 A loads, 4 B loads (8 rows of 128 bytes
+// each), the A scales and (per-column) the B scales of 32 rows / columns
+constexpr int kLoadsPerStage(bool per_col) { return 4 + 4 + 1 + (per_col ? 1 : 0); }
 
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 struct Ops {
     __amdgpu_buffer_rsrc_t a, b, as, bs;
-    uint32_t a_lane;   // tile row 64 wave + lane / 8, chunk (lane % 8) ^ (lane / 8): rows of load q add 8 q
-    uint32_t b_lane;   // tile row 32 wave + lane / 8, same chunk rule
-    uint32_t as_lane;  // 4 (m0 + 64 wave + 4 lane): 4 A scales per lane (lanes 0..15)
-    uint32_t bs_lane;  // 4 (n0 + 32 wave + 4 lane): 4 B scales per lane (lanes 0..7)
-    uint32_t a_eighth; // 8 lda
-    uint32_t b_eighth; // 8 ldb
-    uint32_t lds_wave; // LDS byte address of stage 0
+    uint32_t a_lane[2];  // tile row 32 wave + lane / 8, chunk (lane % 8) ^ swz(row) for loads q even / odd
+    uint32_t b_lane[2];  // same for B
+    uint32_t as_lane;    // 4 (m0 + 32 wave + 4 lane): 4 A scales per lane (lanes 0..7)
+    uint32_t bs_lane;    // 4 (n0 + 32 wave + 4 lane): 4 B scales per lane (lanes 0..7)
+    uint32_t a_eighth;   // 8 lda
+    uint32_t b_eighth;   // 8 ldb
+    uint32_t lds;        // LDS byte address of stage 0
 };
 
-// One direct load (16 B per lane, LDS address lds + 16 * lane) with M0 saved and restored.
+// One direct load, 16 bytes per lane to LDS address lds + 16 * lane; M0 is saved and restored.
 __device__ __forceinline__ void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     uint32_t saved;
     asm volatile(
@@ -430,17 +433,17 @@ __device__ __forceinline__ void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t r, ui
         : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
         : "memory");
 }
-// Direct load of 16 B per lane for lanes 0 .. 15 (lo = 0xFFFF) or 0 .. 7 (lo = 0xFF) only. A
-// direct load writes LDS for every active lane (lanes whose offset is out of range write zeros),
-// so the lanes beyond a scale slice are switched off. EXEC is changed and restored inside the one
-// asm block rather than through a branch: a branch would split the K-block's straight-line code.
-template <uint32_t LO>
-__device__ __forceinline__ void dma16_lanes(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+
+// The same for lanes 0 .. 7 only. A direct load writes LDS for every active lane (lanes whose offset
+// is out of range write zeros), so the lanes beyond a scale slice are switched off; EXEC is changed
+// and restored inside the asm block rather than through a branch, which would split the K-block's
+// straight-line code.
+__device__ __forceinline__ void dma16_8lanes(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     uint32_t saved_m0;
     uint64_t saved_exec;
     asm volatile(
         "s_mov_b64 %1, exec\n\t"
-        "s_mov_b32 exec_lo, %6\n\t"
+        "s_mov_b32 exec_lo, 0xff\n\t"
         "s_mov_b32 exec_hi, 0\n\t"
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
@@ -449,50 +452,29 @@ __device__ __forceinline__ void dma16_lanes(uint32_t lds, __amdgpu_buffer_rsrc_t
         "s_mov_b64 exec, %1"
         : "=&s"(saved_m0), "=&s"(saved_exec)
         : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
-          "s"(__builtin_amdgcn_readfirstlane(soff)), "i"(LO)
+          "s"(__builtin_amdgcn_readfirstlane(soff))
         : "memory");
 }
 
-// Same with 4 B per lane (LDS address lds + 4 * lane).
-__device__ __forceinline__ void dma4(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dword %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
-        : "memory");
-}
-
-// Load number q of a stage, q = 0 .. kLoadsPerStage - 1: 0..7 the wave's A rows 64 wave + 8 q ..,
-// 8..11 B rows 32 wave + 8 (q - 8) .., 12 the A scales of the wave's rows, 13 (per-column) the B
-// scales of columns 32 wave .. + 32. The loads of one stage can be spread over a K-block.
+// Load number q of a stage, q = 0 .. kLoadsPerStage - 1: 0..3 A rows 32 wave + 8 q .., 4..7 B rows
+// 32 wave + 8 (q - 4) .., 8 the A scales of rows 32 wave .. + 32, 9 (per-column) the B scales of
+// columns 32 wave .. + 32. The loads of one stage can be spread over a K-block.
 template <bool PER_COL>
 __device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb,
-                                           int64_t M, int64_t N, int wave, int lane) {
+                                           int64_t M, int64_t N, int wave) {
     const uint32_t k = static_cast<uint32_t>(kb * kGroup);
-    if (q < 8) {
-        dma16(stage_base + (kStageA + (64 * wave + 8 * q) * 8) * 16, op.a, op.a_lane, q * op.a_eighth + k);
-    } else if (q < 12) {
-        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 8)) * 8) * 16, op.b, op.b_lane, (q - 8) * op.b_eighth + k);
-    } else if (q == 12) {
-        dma16_lanes<0xFFFFu>(stage_base + (kStageSA + 16 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
-    } else if (PER_COL && q == 13) {
-        dma16_lanes<0xFFu>(stage_base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
+    if (q < 4) {
+        dma16(stage_base + (kStageA + (32 * wave + 8 * q) * 8) * 16, op.a, op.a_lane[q & 1], q * op.a_eighth + k);
+    } else if (q < 8) {
+        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 4)) * 8) * 16, op.b, op.b_lane[q & 1], (q - 4) * op.b_eighth + k);
+    } else if (q == 8) {
+        dma16_8lanes(stage_base + (kStageSA + 8 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
+    } else if (PER_COL && q == 9) {
+        dma16_8lanes(stage_base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
     }
 }
 
-template <bool PER_COL>
-__device__ __forceinline__ void issue_stage(const Ops& op, uint32_t stage_base, int64_t kb, int64_t M,
-                                            int64_t N, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < kLoadsPerStage(PER_COL); ++q) issue_load<PER_COL>(q, op, stage_base, kb, M, N, wave, lane);
-}
-
-// Wait until at most N vector-memory instructions of this wave are outstanding (its own direct
-// loads of an older stage have landed in LDS).
+// Wait until at most N vector-memory instructions of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_own_loads() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -508,22 +490,23 @@ __device__ __forceinline__ void lds_barrier() {
 template <bool PER_COL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
-    const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s,
-    int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc,
-    int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
+    const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb,
+    int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt,
+    int nt, int c_vec) {
     __shared__ u32x4 smem[kStages * kStageSize];
-    __shared__ float bscale_lds[kMaxKbFast];
+    __shared__ float bscale_lds[2][kMaxKbFast];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3;   // rows 64 wm .. of the tile
+    const int wn = wave >> 2;  // columns 128 wn .. of the tile
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     int tm, tn;
     tile_of(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * kBM;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
-    const int64_t mw = m0 + kWM * wave;
     const int64_t Kb = K / kGroup;
     constexpr int kLoads = kLoadsPerStage(PER_COL);
 
@@ -535,14 +518,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
         op.as = make_rsrc(a_s, static_cast<uint32_t>(M * Kb * 4));
         op.bs = make_rsrc(b_s, PER_COL ? static_cast<uint32_t>(N * Kb * 4) : 0u);
-        const int chunk = (lane & 7) ^ (lane >> 3);
-        op.a_lane = static_cast<uint32_t>((64 * wave + (lane >> 3)) * lda + 16 * chunk);
-        op.b_lane = static_cast<uint32_t>((32 * wave + (lane >> 3)) * ldb + 16 * chunk);
-        op.as_lane = static_cast<uint32_t>(4 * (m0 + 64 * wave + 4 * lane));
+        // row 32 wave + 8 q + lane / 8 has swz = (4 q + lane / 16) % 8, which depends on q % 2
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int chunk = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+            op.a_lane[par] = static_cast<uint32_t>((32 * wave + (lane >> 3)) * lda + 16 * chunk);
+            op.b_lane[par] = static_cast<uint32_t>((32 * wave + (lane >> 3)) * ldb + 16 * chunk);
+        }
+        op.as_lane = static_cast<uint32_t>(4 * (m0 + 32 * wave + 4 * lane));
         op.bs_lane = static_cast<uint32_t>(4 * (n0 + 32 * wave + 4 * lane));
         op.a_eighth = static_cast<uint32_t>(8 * lda);
         op.b_eighth = static_cast<uint32_t>(8 * ldb);
-        op.lds_wave = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
+        op.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
     }
 
     v4f acc[kMSub][kNSub];
@@ -552,63 +539,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (Kb > 0) {
-        // The wave's own A rows and A scales of a stage can be read as soon as its own direct loads
-        // of that stage have landed; the B tile (and per-column B scales) is shared, so reading it
-        // also needs the barrier that follows every wave's wait.
-        v8i af[kMSub];
-        float f[kMSub];
-        auto stage_base = [&](int stage) {
-            return op.lds_wave + static_cast<uint32_t>(stage * kStageSize * 16);
-        };
-        auto read_own = [&](int stage, int64_t kb) {
-            const u32x4* st = smem + stage * kStageSize;
-            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wave;
-            const float bsc = PER_COL ? 1.0f : bscale_lds[kb];
-#pragma unroll
-            for (int i = 0; i < kMSub; ++i) {
-                const int r = 64 * wave + 16 * i + l16;
-                af[i] = to_v8i(st[kStageA + r * 8 + ((2 * lg) ^ (r & 7))],
-                               st[kStageA + r * 8 + ((2 * lg + 1) ^ (r & 7))]);
-                f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
-            }
-        };
-
-        // 128x128 B scales of this tile's column (kb = 0 .. Kb-1) into LDS, 4 bytes per lane,
-        // before the first stage (so they are covered by the first stage's wait and barrier).
+        // 128x128 B scales of the tile's two 128-column blocks for every K-block
         if (!PER_COL) {
-            const uint32_t lds_bs = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bscale_lds));
-            const __amdgpu_buffer_rsrc_t rbs = make_rsrc(b_s, 0x7FFFFFFFu);
-            for (int64_t c = 0; c < Kb; c += 64) {
-                if (wave == 0 && c + lane < Kb)
-                    dma4(lds_bs + static_cast<uint32_t>(4 * c), rbs,
-                         static_cast<uint32_t>(4 * (tn * bs_nb + (c + lane) * bs_kb)), 0u);
+            for (int64_t c = tid; c < 2 * Kb; c += kThreads) {
+                const int half = c >= Kb;
+                const int64_t kb = c - half * Kb;
+                const int64_t nb = 2 * static_cast<int64_t>(tn) + half;
+                // a column block past N is never stored; read block 0's scale instead
+                bscale_lds[half][kb] = b_s[(nb * kGroup < N ? nb : 0) * bs_nb + kb * bs_kb];
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
         }
 
-        // Stages past the last K-block are still issued (their rows are in range, only the data is
-        // unused) so every step waits for the same number of loads and stays straight-line code.
-        issue_stage<PER_COL>(op, stage_base(0), 0, M, N, wave, lane);
-        issue_stage<PER_COL>(op, stage_base(1), 1, M, N, wave, lane);
-        wait_own_loads<kLoads>();
-        read_own(0, 0);
+        auto stage_base = [&](int stage) { return op.lds + static_cast<uint32_t>(stage * kStageSize * 16); };
+        const int sw = swz(l16);  // the same for every fragment row 16 x + l16
+        const int pos_lo = (2 * lg) ^ sw;
+        const int pos_hi = (2 * lg + 1) ^ sw;
 
-        auto step = [&](auto cur_tag, int64_t kb) {
-            constexpr int cur = decltype(cur_tag)::value;
-            constexpr int nx1 = (cur + 1) % kStages;
-            constexpr int nx2 = (cur + 2) % kStages;
-            // every wave has its block-kb loads in LDS and is done reading block kb-1
+        // prologue: block 0 into stage 0
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, M, N, wave);
+        wait_own_loads<0>();
+
+        // One loop body for both stages (stage = kb % 2 at run time): a body unrolled per stage
+        // makes the register allocator spill.
+        auto step = [&](int64_t kb) {
+            const int cur = static_cast<int>(kb & 1);
+            const int nxt = cur ^ 1;
+            // every wave's block-kb loads are in LDS, and every wave is done with block kb-1
             lds_barrier();
-            const uint32_t base2 = stage_base(nx2);
+            const uint32_t base_n = stage_base(nxt);
+            const int64_t kb_next = kb + 1 < Kb ? kb + 1 : kb;  // past the end: reload (unused)
 
             const u32x4* st = smem + cur * kStageSize;
-            const float* sbs = reinterpret_cast<const float*>(st + kStageSB);
+            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wm;
+            const float* sbs = reinterpret_cast<const float*>(st + kStageSB) + 128 * wn;
+            const float bsc = PER_COL ? 1.0f : bscale_lds[wn][kb];
+            v8i af[kMSub];
+            float f[kMSub];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) {
+                const int r = 64 * wm + 16 * i + l16;
+                af[i] = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
+                f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
+            }
             auto read_bf = [&](int j) {
-                const int r = 16 * j + l16;
-                return to_v8i(st[kStageB + r * 8 + ((2 * lg) ^ (r & 7))],
-                              st[kStageB + r * 8 + ((2 * lg + 1) ^ (r & 7))]);
+                const int r = 128 * wn + 16 * j + l16;
+                return to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
             };
             auto rescale = [&](int j, const v4f (&pj)[kMSub]) {
                 v4f bsj = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -630,15 +606,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNSub; ++j) {
-                // the loads of block kb+2, spread over the subtiles
-                issue_load<PER_COL>(2 * j, op, base2, kb + 2, M, N, wave, lane);
-                issue_load<PER_COL>(2 * j + 1, op, base2, kb + 2, M, N, wave, lane);
+                // the next block's loads, spread over the first subtiles
+                if (2 * j < kLoads) issue_load<PER_COL>(2 * j, op, base_n, kb_next, M, N, wave);
+                if (2 * j + 1 < kLoads) issue_load<PER_COL>(2 * j + 1, op, base_n, kb_next, M, N, wave);
                 if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
                 if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
                 // issue order inside the subtile: the next fragment's LDS reads, then each MFMA
-                // followed by the four rescale FMAs of the previous subtile's partials
+                // followed by the rescale FMAs of the previous subtile's partials
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) {
@@ -648,26 +624,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
             rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
-            // this wave's loads of block kb+1 (issued two blocks ago) -> next A fragments and scales
-            wait_own_loads<kLoads>();
-            read_own(nx1, kb + 1 < Kb ? kb + 1 : kb);
+            wait_own_loads<0>();  // this wave's loads of block kb+1 have landed
         };
-        for (int64_t kb = 0; kb < Kb; kb += kStages) {
-            step(IntTag<0>{}, kb);
-            if (kb + 1 < Kb) step(IntTag<1>{}, kb + 1);
-            if (kb + 2 < Kb) step(IntTag<2>{}, kb + 2);
-        }
-        wait_own_loads<0>();  // no direct load may outlive the workgroup's LDS
+
+        for (int64_t kb = 0; kb < Kb; ++kb) step(kb);
     }
 
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
-        const int64_t m = mw + 16 * i + l16;
+        const int64_t m = m0 + 64 * wm + 16 * i + l16;
         if (m >= M) continue;
         uint16_t* crow = C + m * ldc;
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
-            const int64_t n = n0 + 16 * j + 4 * lg;
+            const int64_t n = n0 + 128 * wn + 16 * j + 4 * lg;
             const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
             if (c_vec && n + 4 <= N) {
@@ -692,13 +662,8 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        int64_t K, hipStream_t stream) {
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
     // Fast path: whole K-blocks; per-column scales read 4 columns at a time; 128x128 scales of a
-    // tile's column staged in LDS (at most kMaxKbFast K-blocks, byte offsets below 2^31).
-    const int64_t kb_all = K / kGroup;
-    const int64_t nb_all = (N + kGroup - 1) / kGroup;
-    const bool fast_scales =
-        bs.per_column ? (N % 4 == 0)
-                      : (kb_all <= fast::kMaxKbFast &&
-                         4 * ((nb_all - 1) * bs.stride_nb + (kb_all - 1) * bs.stride_kb) < 0x7FFFFFFFLL);
+    // tile's column staged in LDS (at most kMaxKbFast K-blocks).
+    const bool fast_scales = bs.per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
     if (K % kGroup == 0 && fast_scales) {
         const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
