@@ -573,57 +573,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             const u32x4* st = smem + cur * kStageSize;
             const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wm;
             const float* sbs = reinterpret_cast<const float*>(st + kStageSB) + 128 * wn;
-            const float bsc = PER_COL ? 1.0f : bscale_lds[wn][kb];
-            v8i af[kMSub];
-            float f[kMSub];
-#pragma unroll
-            for (int i = 0; i < kMSub; ++i) {
-                const int r = 64 * wm + 16 * i + l16;
-                af[i] = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
-                f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
-            }
             auto read_bf = [&](int j) {
                 const int r = 128 * wn + 16 * j + l16;
                 return to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
             };
-            auto rescale = [&](int j, const v4f (&pj)[kMSub]) {
-                v4f bsj = {1.0f, 1.0f, 1.0f, 1.0f};
-                if (PER_COL) bsj = *reinterpret_cast<const v4f*>(sbs + 16 * j + 4 * lg);
-#pragma unroll
-                for (int i = 0; i < kMSub; ++i) {
-                    if (PER_COL) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i] * bsj[e], acc[i][j][e]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i], acc[i][j][e]);
-                    }
-                }
-            };
-            v8i bf[2];
-            v4f pp[2][kMSub];
+            // B fragments are read two subtiles ahead of their MFMAs (three in registers); the
+            // first MFMA needs only bf[0] and af[0], so those are read first
+            v8i bf[3];
+            v8i af[kMSub];
             bf[0] = read_bf(0);
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) {
+                const int r = 64 * wm + 16 * i + l16;
+                af[i] = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
+            }
+            bf[1] = read_bf(1);
+            const float bsc = PER_COL ? 1.0f : bscale_lds[wn][kb];
+            float f[kMSub];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
+
+            // partial of subtile (i, j) times its scales, into the totals
+            auto rescale = [&](int i, int j, const v4f& p, const v4f& bsj) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[i][j][e] = fmaf(p[e], PER_COL ? f[i] * bsj[e] : f[i], acc[i][j][e]);
+            };
+            auto read_bsj = [&](int j) {
+                return PER_COL ? *reinterpret_cast<const v4f*>(sbs + 16 * j + 4 * lg) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+            };
+            v4f pp[kMSub];  // partials of the previous subtile until rescaled, then of the current one
+            v4f bsj_prev = {1.0f, 1.0f, 1.0f, 1.0f};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNSub; ++j) {
                 // the next block's loads, spread over the first subtiles
                 if (2 * j < kLoads) issue_load<PER_COL>(2 * j, op, base_n, kb_next, M, N, wave);
                 if (2 * j + 1 < kLoads) issue_load<PER_COL>(2 * j + 1, op, base_n, kb_next, M, N, wave);
-                if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
-#pragma unroll
-                for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
-                if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
-                // issue order inside the subtile: the next fragment's LDS reads, then each MFMA
-                // followed by the rescale FMAs of the previous subtile's partials
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (j + 2 < kNSub) bf[(j + 2) % 3] = read_bf(j + 2);
+                const v4f bsj = read_bsj(j);
+                // the previous subtile's partial of row block i is rescaled just before the MFMA
+                // that overwrites it (4 MFMAs after the one that produced it)
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) {
+                    if (j > 0) rescale(i, j - 1, pp[i], bsj_prev);
+                    pp[i] = mfma_fp8_16x16x128(bf[j % 3], af[i]);
+                }
+                bsj_prev = bsj;
+                if (j + 2 < kNSub) __builtin_amdgcn_sched_group_barrier(0x100, PER_COL ? 3 : 2, 0);
+#pragma unroll
+                for (int i = 0; i < kMSub; ++i) {
+                    if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, PER_COL ? 8 : 4, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, PER_COL ? 8 : 4, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) rescale(i, kNSub - 1, pp[i], bsj_prev);
             wait_own_loads<0>();  // this wave's loads of block kb+1 have landed
         };
 
