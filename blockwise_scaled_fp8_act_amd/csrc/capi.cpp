@@ -37,6 +37,9 @@ int finish(hipError_t e) { return e == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+constexpr int64_t kMaxOffset = 0xFFFFFFFFLL;
+constexpr int64_t kMaxOperandLd = kMaxOffset / 256;
+
 int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                   const float* b_s, const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return BSFP8_EINVAL;
@@ -46,6 +49,10 @@ int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, i
     if (K == 0) return BSFP8_OK;
     if (a == nullptr || b == nullptr || a_s == nullptr || b_s == nullptr) return BSFP8_EINVAL;
     if (lda < K || ldb < K) return BSFP8_EINVAL;
+    // the kernels address a 256-row band of each operand and the scale arrays with 32-bit byte
+    // offsets
+    if (lda > kMaxOperandLd || ldb > kMaxOperandLd) return BSFP8_EINVAL;
+    if (4 * M * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
     if (!aligned16(a) || !aligned16(b) || (lda % 16) != 0 || (ldb % 16) != 0) return BSFP8_EALIGN;
     return BSFP8_OK;
 }
@@ -124,6 +131,7 @@ int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s, const void* b
                      void* stream) {
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (M == 0 || N == 0) return BSFP8_OK;
+    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, 0, 0, 1};
     return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,

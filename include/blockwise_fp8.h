@@ -42,7 +42,8 @@
  *
  * Return codes
  *   BSFP8_OK (0); BSFP8_EINVAL (1) bad argument: a null pointer with a non-empty extent, a negative
- *   size, ld smaller than the row length, a stride out of range; BSFP8_EALIGN (2) a GEMM operand
+ *   size, ld smaller than the row length, a stride out of range, a GEMM beyond its size limits;
+ *   BSFP8_EALIGN (2) a GEMM operand
  *   row is not 16-byte aligned (see the GEMMs); BSFP8_EDEVICE (3) the current device is not gfx950;
  *   BSFP8_EHIP (4) a HIP call or launch failed. Argument checks happen before any HIP call, so
  *   codes 1 and 2 need no GPU. Empty problems (a zero extent) return BSFP8_OK without launching,
@@ -111,6 +112,8 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
  *       scales read transposed: strides (1, Nb_of_weight)). Strides must be >= 0.
  *   c   [M, N] bf16, row stride ldc >= N.
  * Alignment (else BSFP8_EALIGN): a and b 16-byte aligned, lda and ldb multiples of 16.
+ * Size limits (else BSFP8_EINVAL; operands are addressed with 32-bit byte offsets):
+ *   256 * lda and 256 * ldb below 2^32, and 4 * M * ceil(K/128) below 2^32.
  * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
  */
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
@@ -123,7 +126,8 @@ int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
  * (wgrad dW = dY^T X, contracting over tokens: A and B are quantize_rhs outputs).
  *   a, lda, a_s as above;  b [N, K] fp8, row stride ldb;
  *   b_s [ceil(K/128), N] fp32 row-major: the scale of (kb, n) is b_s[kb * N + n].
- *   c   [M, N] bf16, row stride ldc >= N.  Alignment as for gemm_1x128_128x128.
+ *   c   [M, N] bf16, row stride ldc >= N.  Alignment and size limits as for gemm_1x128_128x128,
+ *   and also 4 * N * ceil(K/128) below 2^32.
  */
 int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s,
                      const void* b, int64_t ldb, const float* b_s,

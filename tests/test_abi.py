@@ -80,3 +80,12 @@ def test_gemms_reject_bad_arguments(L):
     assert h(P, 128, P, P, 128, None, P, 64, 4, 64, 128, None) == 1          # b_s null
     assert h(P, 128, P, P, 120, P, P, 64, 4, 64, 128, None) == 1             # ldb < K
     assert L.encode_e4m3_f32(odd, P, 16, None) == 2
+
+
+def test_gemms_reject_sizes_past_32bit_offsets(L):
+    g, h = L.gemm_1x128_128x128, L.gemm_1x128_128x1
+    big_ld = (2**32) // 256 + 16                       # 256 rows of the operand exceed 2^32 bytes
+    assert g(P, big_ld, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1
+    assert g(P, 128, P, P, big_ld, P, 1, 1, P, 64, 4, 64, 128, None) == 1
+    assert g(P, 128, P, P, 128, P, 1, 1, P, 64, 2**30, 64, 128, None) == 1   # 4 M Kb >= 2^32
+    assert h(P, 128, P, P, 128, P, P, 2**30, 4, 2**30, 128, None) == 1     # 4 N Kb >= 2^32
