@@ -39,6 +39,42 @@ def weight_bytes(N, K, with_qT):
     return 2 * N * K + N * K * (2 if with_qT else 1) + 4 * ((N + 127) // 128) * ((K + 127) // 128)
 
 
+class TimingEvent:
+    """A HIP event created with hipEventDisableSystemFence: recording it writes a timestamp
+    without the system-scope cache writeback/invalidate a default event performs, so the kernels
+    around it run as they would without the event (HIP documents the flag for timing)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._ctypes = ctypes
+        self.h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.h, self._ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._ctypes.c_float()
+        TimingEvent._hip.hipEventSynchronize(end.h)
+        rc = TimingEvent._hip.hipEventElapsedTime(self._ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE record in profiles/, or None
     when the kernel source has changed since the counters were taken."""
@@ -127,11 +163,13 @@ def main():
         ))
     set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
 
-    def step(s, ev=None):
-        if ev is not None:
+    def step(s, ev=None, per_kernel=False):
+        # ev: events recorded on the launch stream; in the timed loop only the GEMM is bracketed
+        # (its duration feeds the roofline), to keep event packets between kernels to a minimum
+        if per_kernel:
             ev[0].record(stream)
         bf.quantize_lhs(s["A"], s["qa"], s["sa"], stream=stream)
-        if ev is not None:
+        if per_kernel:
             ev[1].record(stream)
         bf.quantize_weight_128x128(s["W"], s["qw"], None, s["sw"], want_qT=False, stream=stream)
         if ev is not None:
@@ -144,9 +182,9 @@ def main():
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
+    t_start = TimingEvent()
+    t_end = TimingEvent()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -157,7 +195,15 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+    gemm_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # per-kernel durations of the quantizers: a separate pass of the same steps with every
+    # kernel bracketed (not part of the timed region)
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i], per_kernel=True)
+    torch.cuda.synchronize()
     k_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    k_ms[:, 2] = gemm_ms  # the GEMM column is the timed region's
     k_avg = k_ms.mean(axis=0)
     k_med = np.median(k_ms, axis=0)
 
@@ -227,19 +273,18 @@ def main():
 
 
 def _time_kernel(fn, reps, stream, torch):
-    """Average and median duration (ms) of fn(i) over reps launches, HIP events on `stream`."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
+    """Average duration (ms) of fn(i) over reps back-to-back launches: one HIP event pair on
+    `stream` around the whole batch, so host-side launch cost never shows as GPU time."""
     for i in range(3):
         fn(i)
     torch.cuda.synchronize()
+    e0, e1 = TimingEvent(), TimingEvent()
+    e0.record(stream)
     for i in range(reps):
-        ev[i][0].record(stream)
         fn(i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    t = np.array([a.elapsed_time(b) for a, b in ev])
-    return float(t.mean()), float(np.median(t))
+    return e0.elapsed_time(e1) / reps
 
 
 def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
@@ -247,14 +292,13 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     (16384 x 5120 x 5120) shapes, each rotating over buffer sets larger than the cache."""
     out = []
 
-    def add(name, shape, avg, med, work, unit):
+    def add(name, shape, avg, work, unit):
         rate = work / (avg * 1e-3)
         if unit == "GB/s":
             r, peak = rate / 1e9, PEAK_HBM_GBS
         else:
             r, peak = rate / 1e12, PEAK_FP8_TFLOPS
-        out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2),
-                    "median_us": round(med * 1e3, 2), unit: round(r, 1),
+        out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2), unit: round(r, 1),
                     "frac": round(r / peak, 4)})
 
     d3 = inputs.make_workload(3)
@@ -278,27 +322,27 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     dw = [torch.empty((D, D), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
 
     j = lambda i: i % nsets  # noqa: E731
-    a, m = _time_kernel(lambda i: bf.quantize_lhs(X[j(i)], qx[j(i)], sx[j(i)], stream=stream), reps, stream, torch)
-    add("quantize_lhs", [T, D], a, m, lhs_bytes(T, D), "GB/s")
-    a, m = _time_kernel(lambda i: bf.quantize_lhs(dY[j(i)], qdy[j(i)], sdy[j(i)], stream=stream), reps, stream, torch)
-    add("quantize_lhs(dY)", [T, D], a, m, lhs_bytes(T, D), "GB/s")
-    a, m = _time_kernel(lambda i: bf.quantize_rhs(X[j(i)], qxT[j(i)], sxT[j(i)], stream=stream), reps, stream, torch)
-    add("quantize_rhs", [T, D], a, m, lhs_bytes(T, D), "GB/s")
-    a, m = _time_kernel(lambda i: bf.quantize_rhs(dY[j(i)], qdyT[j(i)], sdyT[j(i)], stream=stream), reps, stream, torch)
-    add("quantize_rhs(dY)", [T, D], a, m, lhs_bytes(T, D), "GB/s")
-    a, m = _time_kernel(lambda i: bf.quantize_weight_128x128(W[j(i)], qw[j(i)], qwT[j(i)], sw[j(i)], stream=stream),
+    a = _time_kernel(lambda i: bf.quantize_lhs(X[j(i)], qx[j(i)], sx[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs", [T, D], a, lhs_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_lhs(dY[j(i)], qdy[j(i)], sdy[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs(dY)", [T, D], a, lhs_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_rhs(X[j(i)], qxT[j(i)], sxT[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_rhs", [T, D], a, lhs_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_rhs(dY[j(i)], qdyT[j(i)], sdyT[j(i)], stream=stream), reps, stream, torch)
+    add("quantize_rhs(dY)", [T, D], a, lhs_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_weight_128x128(W[j(i)], qw[j(i)], qwT[j(i)], sw[j(i)], stream=stream),
                         reps, stream, torch)
-    add("quantize_weight_128x128(+qT)", [D, D], a, m, weight_bytes(D, D, True), "GB/s")
+    add("quantize_weight_128x128(+qT)", [D, D], a, weight_bytes(D, D, True), "GB/s")
     fl = 2.0 * T * D * D
-    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qx[j(i)], sx[j(i)], qw[j(i)], sw[j(i)], c=out_c[j(i)],
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qx[j(i)], sx[j(i)], qw[j(i)], sw[j(i)], c=out_c[j(i)],
                                                         stream=stream), reps, stream, torch)
-    add("gemm_1x128_128x128 fwd", [T, D, D], a, m, fl, "TFLOP/s")
-    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qdy[j(i)], sdy[j(i)], qwT[j(i)], sw[j(i)], 1, Kb,
+    add("gemm_1x128_128x128 fwd", [T, D, D], a, fl, "TFLOP/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qdy[j(i)], sdy[j(i)], qwT[j(i)], sw[j(i)], 1, Kb,
                                                         c=out_c[j(i)], stream=stream), reps, stream, torch)
-    add("gemm_1x128_128x128 dgrad", [T, D, D], a, m, fl, "TFLOP/s")
-    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)], sdyT[j(i)], qxT[j(i)], sxT[j(i)], c=dw[j(i)],
+    add("gemm_1x128_128x128 dgrad", [T, D, D], a, fl, "TFLOP/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)], sdyT[j(i)], qxT[j(i)], sxT[j(i)], c=dw[j(i)],
                                                       stream=stream), reps, stream, torch)
-    add("gemm_1x128_128x1 wgrad", [D, D, T], a, m, fl, "TFLOP/s")
+    add("gemm_1x128_128x1 wgrad", [D, D, T], a, fl, "TFLOP/s")
     del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw
     torch.cuda.empty_cache()
 
@@ -314,14 +358,14 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     sw4 = [torch.empty((N4 // BLOCK, K4 // BLOCK), dtype=torch.float32, device=dev) for _ in range(ns4)]
     c4 = [torch.empty((M4, N4), dtype=torch.bfloat16, device=dev) for _ in range(ns4)]
     k = lambda i: i % ns4  # noqa: E731
-    a, m = _time_kernel(lambda i: bf.quantize_lhs(A4[k(i)], qa4[k(i)], sa4[k(i)], stream=stream), reps, stream, torch)
-    add("quantize_lhs outlier", [M4, K4], a, m, lhs_bytes(M4, K4), "GB/s")
-    a, m = _time_kernel(lambda i: bf.quantize_weight_128x128(W4[k(i)], qw4[k(i)], None, sw4[k(i)], want_qT=False,
+    a = _time_kernel(lambda i: bf.quantize_lhs(A4[k(i)], qa4[k(i)], sa4[k(i)], stream=stream), reps, stream, torch)
+    add("quantize_lhs outlier", [M4, K4], a, lhs_bytes(M4, K4), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_weight_128x128(W4[k(i)], qw4[k(i)], None, sw4[k(i)], want_qT=False,
                                                              stream=stream), reps, stream, torch)
-    add("quantize_weight_128x128 outlier", [N4, K4], a, m, weight_bytes(N4, K4, False), "GB/s")
-    a, m = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa4[k(i)], sa4[k(i)], qw4[k(i)], sw4[k(i)], c=c4[k(i)],
+    add("quantize_weight_128x128 outlier", [N4, K4], a, weight_bytes(N4, K4, False), "GB/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa4[k(i)], sa4[k(i)], qw4[k(i)], sw4[k(i)], c=c4[k(i)],
                                                         stream=stream), reps, stream, torch)
-    add("gemm_1x128_128x128 outlier", [M4, N4, K4], a, m, 2.0 * M4 * N4 * K4, "TFLOP/s")
+    add("gemm_1x128_128x128 outlier", [M4, N4, K4], a, 2.0 * M4 * N4 * K4, "TFLOP/s")
     del A4, W4, qa4, sa4, qw4, sw4, c4
     torch.cuda.empty_cache()
     return out

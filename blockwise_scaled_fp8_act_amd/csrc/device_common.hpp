@@ -31,6 +31,17 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
     return static_cast<uint32_t>(w);
 }
 
+// encode4 for values x * m of a group whose multiplier is m = fl(448 / amax_c) with |x| <= amax_c:
+// then |fl(x * m)| <= 448 (1 + 2^-24)^2 rounded, at most two fp32 ulps above 448, and the
+// conversion rounds every magnitude up to 464 (the tie between 448 and the next binade step,
+// resolved to even) to 448 -- the clamp of encode4 can never change such a value, so it is left
+// out.
+__device__ __forceinline__ uint32_t encode4_in_range(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return static_cast<uint32_t>(w);
+}
+
 // Group scale pair from the group's max magnitude: the stored (dequantizing) scale s = amax/448
 // and the multiplier m = 448/amax, both IEEE-correct fp32 divisions (the compiler's default fp32
 // division is correctly rounded; fp32 denormals are preserved).

@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
         for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[r][j]));
         am = umax_row16(am);
         const GroupScale g = group_scale(__uint_as_float(am));
-        const uint32_t w0 = encode4(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
-        const uint32_t w1 = encode4(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
+        const uint32_t w0 = encode4_in_range(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
+        const uint32_t w1 = encode4_in_range(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
         const int64_t m = mbase + r * 16 + team;
         if (m < M) {  // rows >= M store neither codes nor scales
             store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float mj = mult[cg * 8 + j];
-        const uint32_t w = encode4(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
+        const uint32_t w = encode4_in_range(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
         const int cl = cg * 8 + j;
         const int chunk = (rq >> 2) ^ (cl >> 3);
         tw[cl * 32 + chunk * 4 + (rq & 3)] = w;
@@ -231,8 +231,8 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
     uint32_t code[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        code[i][0] = encode4(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
-        code[i][1] = encode4(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
+        code[i][0] = encode4_in_range(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
+        code[i][1] = encode4_in_range(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
         const int64_t n = n0 + rg * 8 + i;
         if (n < N) store8<VEC_Q>(q + n * ldq, c, K, code[i][0], code[i][1]);
     }
