@@ -35,6 +35,12 @@ def lhs_bytes(M, K):
     return 2 * M * K + M * K + 4 * M * ((K + BLOCK - 1) // BLOCK)
 
 
+def dual_bytes(R, C):
+    """Algorithmic bytes of the one-pass 1x128 + 128x1 quantizer: read 2 B, write 2 B per element,
+    plus the two scale tensors."""
+    return 2 * R * C + 2 * R * C + 4 * R * ((C + BLOCK - 1) // BLOCK) + 4 * C * ((R + BLOCK - 1) // BLOCK)
+
+
 def weight_bytes(N, K, with_qT):
     return 2 * N * K + N * K * (2 if with_qT else 1) + 4 * ((N + 127) // 128) * ((K + 127) // 128)
 
@@ -330,6 +336,12 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     add("quantize_rhs", [T, D], a, lhs_bytes(T, D), "GB/s")
     a = _time_kernel(lambda i: bf.quantize_rhs(dY[j(i)], qdyT[j(i)], sdyT[j(i)], stream=stream), reps, stream, torch)
     add("quantize_rhs(dY)", [T, D], a, lhs_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_lhs_and_rhs(X[j(i)], qx[j(i)], sx[j(i)], qxT[j(i)], sxT[j(i)],
+                                                      stream=stream), reps, stream, torch)
+    add("quantize_lhs_and_rhs", [T, D], a, dual_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_lhs_and_rhs(dY[j(i)], qdy[j(i)], sdy[j(i)], qdyT[j(i)], sdyT[j(i)],
+                                                      stream=stream), reps, stream, torch)
+    add("quantize_lhs_and_rhs(dY)", [T, D], a, dual_bytes(T, D), "GB/s")
     a = _time_kernel(lambda i: bf.quantize_weight_128x128(W[j(i)], qw[j(i)], qwT[j(i)], sw[j(i)], stream=stream),
                         reps, stream, torch)
     add("quantize_weight_128x128(+qT)", [D, D], a, weight_bytes(D, D, True), "GB/s")

@@ -1,6 +1,7 @@
 """Blockwise-scaled FP8 linear-layer kernels for MI355X (gfx950).
 
-Group quantizers (1x128, 128x1, 128x128) from bf16 to float8_e4m3fn with fp32 scales, and the
+Group quantizers (1x128, 128x1, 128x128, and 1x128 + 128x1 of one tensor in a single pass) from
+bf16 to float8_e4m3fn with fp32 scales, and the
 1x128 x 128x128 / 1x128 x 128x1 scaled FP8 GEMMs with bf16 output, as hand-written HIP kernels
 behind the C ABI of include/blockwise_fp8.h. This package is the thin Python binding over that
 library (``binding``), its in-tree build (``build``) and the seeded input generators (``inputs``).
@@ -11,6 +12,7 @@ from .binding import (  # noqa: F401
     gemm_1x128_128x1,
     gemm_1x128_128x128,
     quantize_lhs,
+    quantize_lhs_and_rhs,
     quantize_rhs,
     quantize_weight_128x128,
 )

@@ -53,8 +53,9 @@ def lib():
         L.gemm_1x128_128x1.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
                                        _vp]
         L.encode_e4m3_f32.argtypes = [_vp, _vp, _i64, _vp]
+        L.quantize_lhs_and_rhs.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp]
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
-                  "gemm_1x128_128x1", "encode_e4m3_f32"):
+                  "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -107,6 +108,23 @@ def quantize_rhs(x, qT=None, s=None, stream=None):
         s = torch.empty((cdiv(K, BLOCK), N), dtype=torch.float32, device=x.device)
     _call("quantize_rhs", _ptr(x), K, N, _ld(x), _ptr(qT), _ld(qT), _ptr(s), _stream(stream))
     return qT, s
+
+
+def quantize_lhs_and_rhs(x, q=None, a_s=None, qT=None, s=None, stream=None):
+    """Both activation quantizations of x [R, C] in one pass. Returns (q [R, C], a_s (Kb_C, R),
+    qT [C, R], s (Kb_R, C)): the outputs of quantize_lhs(x) and of quantize_rhs(x)."""
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if a_s is None:
+        a_s = torch.empty((cdiv(C, BLOCK), R), dtype=torch.float32, device=x.device)
+    if qT is None:
+        qT = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((cdiv(R, BLOCK), C), dtype=torch.float32, device=x.device)
+    _call("quantize_lhs_and_rhs", _ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(a_s), _ptr(qT),
+          _ld(qT), _ptr(s), _stream(stream))
+    return q, a_s, qT, s
 
 
 def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=None):

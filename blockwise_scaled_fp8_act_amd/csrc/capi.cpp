@@ -140,6 +140,20 @@ int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s, const void* b
                                      static_cast<hipStream_t>(stream)));
 }
 
+int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx, void* q, int64_t ldq,
+                         float* a_s, void* qT, int64_t ldqT, float* s, void* stream) {
+    if (R < 0 || C < 0) return BSFP8_EINVAL;
+    if (R == 0 || C == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr || a_s == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldx < C || ldq < C || ldqT < R) return BSFP8_EINVAL;
+    if (cdiv(R, kGroupEdge) > kMaxGridY || cdiv(C, kGroupEdge) > 0x7FFFFFFFLL) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_dual(static_cast<const uint16_t*>(x), R, C, ldx,
+                                              static_cast<uint8_t*>(q), ldq, a_s,
+                                              static_cast<uint8_t*>(qT), ldqT, s,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream) {
     if (n < 0) return BSFP8_EINVAL;
     if (n == 0) return BSFP8_OK;

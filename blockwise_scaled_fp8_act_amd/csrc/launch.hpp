@@ -8,6 +8,9 @@ namespace bsfp8 {
 
 hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                                int64_t ldq, float* a_s, hipStream_t stream);
+hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
+                                hipStream_t stream);
 hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
                                int64_t ldqT, float* s, hipStream_t stream);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,

@@ -172,12 +172,13 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
         tw[cl * 32 + chunk * 4 + (rq & 3)] = w;
     }
     __syncthreads();
-    const int cl = t >> 2;
-    const int64_t n = n0 + cl;
-    if (n < N) {
+    // 8 consecutive lanes write one output row's 128 bytes: each store covers 8 whole lines
+    const int chunk = t & 7;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int chunk = 2 * (t & 3) + h;
+    for (int p = 0; p < 2; ++p) {
+        const int cl = p * 32 + (t >> 3);
+        const int64_t n = n0 + cl;
+        if (n < N) {
             const uint4 v = tileT[cl * 8 + (chunk ^ (cl >> 3))];
             store16<VEC_Q>(qT + n * ldqT, k0 + chunk * 16, K, v);
         }
@@ -256,14 +257,147 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
         *reinterpret_cast<uint2*>(tw + idx) = make_uint2(lo, hi);
     }
     __syncthreads();
-    const int cl = t >> 1;
-    const int64_t k = k0 + cl;
-    if (k < K) {
+    // 8 consecutive lanes write one qT row's 128 bytes: each store covers 8 whole lines
+    const int chunk = t & 7;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int chunk = (t & 1) * 4 + h;
+    for (int p = 0; p < 4; ++p) {
+        const int cl = p * 32 + (t >> 3);
+        const int64_t k = k0 + cl;
+        if (k < K) {
             const uint4 v = tileT[cl * 8 + (chunk ^ ((cl >> 3) & 7))];
             store16<VEC_QT>(qT + k * ldqT, n0 + chunk * 16, N, v);
+        }
+    }
+}
+
+// Value of lane l (0..7) of this lane's 16-lane DPP row (DPP row broadcast, control 0x150 + l);
+// l is a constant once the caller's loop is unrolled.
+__device__ __forceinline__ float bcast_row16(float v, int l) {
+#define BSFP8_BC(L) \
+    case L: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + L, 0xF, 0xF, false))
+    switch (l) {
+        BSFP8_BC(0); BSFP8_BC(1); BSFP8_BC(2); BSFP8_BC(3);
+        BSFP8_BC(4); BSFP8_BC(5); BSFP8_BC(6); default: BSFP8_BC(7);
+    }
+#undef BSFP8_BC
+}
+
+// ------------------------------------------------------------------------------------------
+// 1x128 and 128x1 of the same tensor in one pass: x [R, C] is read once and both the row-wise
+// output of quantize_lhs (q [R, C], a_s column-major [R, ceil(C/128)]) and the transposed
+// column-wise output of quantize_rhs (qT [C, R], s [ceil(R/128), C]) are written. A workgroup owns
+// a 128 x 128 tile, which holds exactly one 1x128 group per row and one 128x1 group per column.
+// Thread t holds rows 8 (t / 16) .. + 8 x columns 8 (t % 16) .. + 8; the 16 lanes of a DPP row
+// share the rows, so a row maximum is one 16-lane DPP reduction; column maxima combine the 16 row
+// groups through LDS. The transposed codes go through a swizzled LDS tile as in the weight kernel.
+template <bool VEC_X, bool VEC_Q, bool VEC_QT>
+__global__ __launch_bounds__(256) void quantize_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s,
+    uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ s) {
+    // the column-max scratch and the transposed code tile are never live together: one buffer
+    // (16 KB + the 128 multipliers), so enough workgroups fit per CU for one wave of the grid
+    __shared__ uint4 tileT[kGroup * 8];  // [column][8 x 16-byte chunks of rows], swizzled
+    __shared__ float colm[kGroup];
+    uint32_t (*red)[kGroup + 1] = reinterpret_cast<uint32_t (*)[kGroup + 1]>(tileT);
+    static_assert(16 * (kGroup + 1) * 4 <= kGroup * 8 * 16, "column maxima fit in the tile buffer");
+
+    const int t = threadIdx.x;
+    const int cg = t & 15;
+    const int rg = t >> 4;
+    const int64_t cb = blockIdx.x;  // column block (K-block of the row-wise groups)
+    const int64_t rb = blockIdx.y;  // row block (K-block of the column-wise groups)
+    const int64_t r0 = rb * kGroup;
+    const int64_t c0 = cb * kGroup;
+    const int64_t c = c0 + cg * 8;
+
+    float f[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + rg * 8 + i;
+        if (r < R) {
+            load8<VEC_X>(x + r * ldx, c, C, f[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
+        }
+    }
+    uint32_t ab[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ab[i][j] = abs_bits(f[i][j]);
+
+    // column-wise partial maxima of this thread's 8 rows, combined over the 16 row groups in LDS
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = max(am, ab[i][j]);
+        red[rg][cg * 8 + j] = am;
+    }
+
+    // row-wise groups: max over the row's 128 columns (8 per lane x 16 lanes). Each of the 16 lanes
+    // holds all 8 row maxima; lane cg computes the scale pair of row cg % 8 only, and every lane
+    // then takes row i's pair from lane i of its DPP row (row broadcast).
+    uint32_t rmax[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = max(am, ab[i][j]);
+        rmax[i] = umax_row16(am);
+    }
+    uint32_t mine = rmax[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mine = (cg & 7) == i ? rmax[i] : mine;
+    const GroupScale gm = group_scale(__uint_as_float(mine));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float m = bcast_row16(gm.m, i);
+        const float sc = bcast_row16(gm.s, i);
+        const uint32_t w0 = encode4_in_range(f[i][0] * m, f[i][1] * m, f[i][2] * m, f[i][3] * m);
+        const uint32_t w1 = encode4_in_range(f[i][4] * m, f[i][5] * m, f[i][6] * m, f[i][7] * m);
+        const int64_t r = r0 + rg * 8 + i;
+        if (r < R) {  // rows >= R store neither codes nor scales
+            store8<VEC_Q>(q + r * ldq, c, C, w0, w1);
+            if (cg == 0) a_s[cb * R + r] = sc;
+        }
+    }
+
+    __syncthreads();
+    if (t < kGroup) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am = max(am, red[r][t]);
+        const GroupScale g = group_scale(__uint_as_float(am));
+        colm[t] = g.m;
+        if (c0 + t < C) s[rb * C + c0 + t] = g.s;
+    }
+    __syncthreads();
+
+    // column-wise codes, transposed through LDS: column j of my 8 collects byte j of rows 0..7
+    uint32_t* tw = reinterpret_cast<uint32_t*>(tileT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float mj = colm[cg * 8 + j];
+        const uint32_t lo = encode4_in_range(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
+        const uint32_t hi = encode4_in_range(f[4][j] * mj, f[5][j] * mj, f[6][j] * mj, f[7][j] * mj);
+        const int cl = cg * 8 + j;
+        const int chunk = (rg >> 1) ^ (cg & 7);
+        *reinterpret_cast<uint2*>(tw + cl * 32 + chunk * 4 + (rg & 1) * 2) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+    // 8 consecutive lanes write one column's 128 bytes, so each store instruction covers 8 whole
+    // 128-byte lines of qT
+    const int chunk = t & 7;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int cl = p * 32 + (t >> 3);
+        const int64_t col = c0 + cl;
+        if (col < C) {
+            const uint4 v = tileT[cl * 8 + (chunk ^ ((cl >> 3) & 7))];
+            store16<VEC_QT>(qT + col * ldqT, r0 + chunk * 16, R, v);
         }
     }
 }
@@ -339,6 +473,27 @@ hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64
     else if (vt) BSFP8_QW(false, false, true);
     else BSFP8_QW(false, false, false);
 #undef BSFP8_QW
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
+                                hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((C + kGroup - 1) / kGroup), static_cast<unsigned>((R + kGroup - 1) / kGroup));
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
+    const bool vt = aligned(qT, 16) && (ldqT % 16 == 0);
+#define BSFP8_QD(A, B, D) \
+    quantize_dual_kernel<A, B, D><<<grid, 256, 0, stream>>>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s)
+    if (vx && vq && vt) BSFP8_QD(true, true, true);
+    else if (vx && vq) BSFP8_QD(true, true, false);
+    else if (vx && vt) BSFP8_QD(true, false, true);
+    else if (vx) BSFP8_QD(true, false, false);
+    else if (vq && vt) BSFP8_QD(false, true, true);
+    else if (vq) BSFP8_QD(false, true, false);
+    else if (vt) BSFP8_QD(false, false, true);
+    else BSFP8_QD(false, false, false);
+#undef BSFP8_QD
     return hipGetLastError();
 }
 

@@ -103,6 +103,23 @@ int quantize_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw,
                             float* s, void* stream);
 
 /*
+ * quantize_lhs_and_rhs: both activation quantizations of one tensor in a single pass (the input is
+ * read once), for a tensor that is the A operand of one GEMM and, transposed, an operand of the
+ * weight-gradient GEMM (activations X and output gradients dY of a linear layer in training).
+ *   x   [R, C] bf16, row stride ldx >= C.
+ *   q, a_s  exactly what quantize_lhs(x, M = R, K = C) writes: q [R, C] fp8 (ldq >= C), a_s
+ *           column-major [R, ceil(C/128)] with ld R.
+ *   qT, s   exactly what quantize_rhs(x, K = R, N = C) writes: qT [C, R] fp8 (ldqT >= R), s
+ *           [ceil(R/128), C] row-major.
+ * The codes and scales are bit-identical to those two calls (act_quant_lhs and act_quant_rhs of the
+ * ROCm page's quantization-correctness table); only the traffic differs: 2 B read and 2 B written
+ * per element instead of 4 B and 2 B.
+ */
+int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
+                         void* q, int64_t ldq, float* a_s,
+                         void* qT, int64_t ldqT, float* s, void* stream);
+
+/*
  * gemm_1x128_128x128: C = A B^T with 1x128 scales on A and 128x128 block scales on B
  * (forward Y = X W^T, and dgrad dX = dY W using the transposed weight codes).
  *   a   [M, K] fp8, row stride lda; a_s column-major [M, ceil(K/128)], ld M.

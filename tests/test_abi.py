@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared_functions()
     assert set(names) >= {"quantize_lhs", "quantize_rhs", "quantize_weight_128x128",
                           "gemm_1x128_128x128", "gemm_1x128_128x1", "bsfp8_status_string",
-                          "encode_e4m3_f32"}
+                          "encode_e4m3_f32", "quantize_lhs_and_rhs"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -54,6 +54,17 @@ def test_quantizers_reject_bad_arguments(L):
     assert L.quantize_rhs(P, 128, 64, 64, P, 100, P, None) == 1      # ldqT < K
     assert L.quantize_weight_128x128(P, 64, 64, 64, P, 64, P, 10, P, None) == 1  # ldqT < N
     assert L.quantize_weight_128x128(P, 64, 64, 64, None, 64, None, 0, P, None) == 1
+
+
+def test_fused_quantizer_rejects_bad_arguments(L):
+    f = L.quantize_lhs_and_rhs
+    assert f(P, -1, 4, 4, P, 4, P, P, 0, P, None) == 1            # negative size
+    assert f(P, 3, 64, 63, P, 64, P, P, 3, P, None) == 1          # ldx < C
+    assert f(P, 3, 64, 64, P, 60, P, P, 3, P, None) == 1          # ldq < C
+    assert f(P, 3, 64, 64, P, 64, P, P, 2, P, None) == 1          # ldqT < R
+    assert f(P, 3, 64, 64, P, 64, None, P, 3, P, None) == 1       # a_s null
+    assert f(P, 3, 64, 64, P, 64, P, None, 3, P, None) == 1       # qT null
+    assert f(None, 0, 64, 64, None, 64, None, None, 0, None, None) == 0   # empty
 
 
 def test_empty_problems_are_noops(L):

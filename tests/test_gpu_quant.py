@@ -146,6 +146,70 @@ def test_quantize_rhs_training_step_full_size():
         assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), name
 
 
+# ------------------------------------------------------------------ quantize_lhs_and_rhs
+
+DUAL_SHAPES = [
+    (128, 128, 128, 128, 128), (130, 1280, 1288, 1296, 144), (1, 1, 1, 1, 1),
+    (257, 300, 304, 312, 272), (300, 129, 136, 144, 304), (129, 257, 264, 264, 129),
+    (5, 200, 203, 211, 5), (2048, 2048, 2048, 2048, 2048), (384, 640, 640, 640, 390),
+]
+
+
+@pytest.mark.parametrize("R,C,ldx,ldq,ldqT", DUAL_SHAPES, ids=lambda v: str(v))
+def test_quantize_lhs_and_rhs_parity(R, C, ldx, ldq, ldqT):
+    """One pass writes exactly the oracle's 1x128 row-wise and 128x1 transposed outputs; nothing
+    outside them (sentinel rows/padding, NaN guard bands around both scale tensors)."""
+    xh = _rand_bf16((R, C), seed=R * 7 + C)
+    x = bf16_view(R, C, ldx, xh)
+    q = GuardedU8(R, C, ldq)
+    a_s = GuardedF32((_cdiv(C, 128), R))
+    qT = GuardedU8(C, R, ldqT)
+    s = GuardedF32((_cdiv(R, 128), C))
+    bf.quantize_lhs_and_rhs(x, q.view, a_s.view, qT.view, s.view)
+    torch.cuda.synchronize()
+    oq, oas = oracle.quantize_lhs(xh)
+    oqT, os_ = oracle.quantize_rhs(xh)
+    for g in (q, a_s, qT, s):
+        g.check_untouched()
+    assert np.array_equal(q.host(), oq)
+    assert np.array_equal(a_s.host().view(np.uint32), oas.view(np.uint32))
+    assert np.array_equal(qT.host(), oqT)
+    assert np.array_equal(s.host().view(np.uint32), os_.view(np.uint32))
+
+
+def test_quantize_lhs_and_rhs_training_step_full_size():
+    """X and dY of the training step [8192, 4096]: oracle parity, and equal bytes to the two
+    single-purpose kernels."""
+    d = inputs.make_workload(3)
+    for name in ("X", "dY"):
+        xh = d[name]
+        x = to_dev(xh)
+        q, a_s, qT, s = bf.quantize_lhs_and_rhs(x)
+        oq, oas = oracle.quantize_lhs(xh)
+        assert np.array_equal(q.cpu().numpy(), oq), name
+        assert np.array_equal(a_s.cpu().numpy().view(np.uint32), oas.view(np.uint32)), name
+        oqT, os_ = oracle.quantize_rhs(xh)
+        assert np.array_equal(qT.cpu().numpy(), oqT), name
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), name
+        q1, s1 = bf.quantize_lhs(x)
+        q2, s2 = bf.quantize_rhs(x)
+        assert torch.equal(q1, q) and torch.equal(s1.view(torch.int32), a_s.view(torch.int32)), name
+        assert torch.equal(q2, qT) and torch.equal(s2.view(torch.int32), s.view(torch.int32)), name
+
+
+def test_quantize_lhs_and_rhs_outliers_and_zero_groups():
+    """Outlier columns and all-zero 1x128 groups (the eps clamp) through the fused kernel."""
+    d = inputs.make_workload(4, scale_down=8)
+    xh = d["A"]
+    q, a_s, qT, s = bf.quantize_lhs_and_rhs(to_dev(xh))
+    oq, oas = oracle.quantize_lhs(xh)
+    oqT, os_ = oracle.quantize_rhs(xh)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(a_s.cpu().numpy().view(np.uint32), oas.view(np.uint32))
+    assert np.array_equal(qT.cpu().numpy(), oqT)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
 # ------------------------------------------------------------------ quantize_weight_128x128
 
 W_SHAPES = [
