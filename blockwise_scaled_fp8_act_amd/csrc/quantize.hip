@@ -37,6 +37,24 @@ __device__ __forceinline__ void load8(const uint16_t* __restrict__ row, int64_t 
     }
 }
 
+// The same 8 bf16 as 4 packed dwords (element 2d in the low half of dword d); columns >= ncols are
+// +0.
+template <bool VEC>
+__device__ __forceinline__ void load8_packed(const uint16_t* __restrict__ row, int64_t c, int64_t ncols,
+                                             uint32_t w[4]) {
+    if (VEC && c + 8 <= ncols) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t lo = (c + 2 * d < ncols) ? row[c + 2 * d] : 0u;
+            const uint32_t hi = (c + 2 * d + 1 < ncols) ? row[c + 2 * d + 1] : 0u;
+            w[d] = lo | (hi << 16);
+        }
+    }
+}
+
 // Store 8 code bytes (w0 = bytes 0..3, w1 = bytes 4..7) at row[c ..]; bytes at columns >= ncols
 // are not written.
 template <bool VEC>
@@ -291,7 +309,7 @@ __device__ __forceinline__ float bcast_row16(float v, int l) {
 // share the rows, so a row maximum is one 16-lane DPP reduction; column maxima combine the 16 row
 // groups through LDS. The transposed codes go through a swizzled LDS tile as in the weight kernel.
 template <bool VEC_X, bool VEC_Q, bool VEC_QT>
-__global__ __launch_bounds__(256) void quantize_dual_kernel(
+__global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ s) {
@@ -311,29 +329,30 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
     const int64_t c0 = cb * kGroup;
     const int64_t c = c0 + cg * 8;
 
-    float f[8][8];
+    // the tile stays packed as bf16 pairs (32 registers rather than 64 floats), so more waves fit
+    uint32_t w[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t r = r0 + rg * 8 + i;
         if (r < R) {
-            load8<VEC_X>(x + r * ldx, c, C, f[i]);
+            load8_packed<VEC_X>(x + r * ldx, c, C, w[i]);
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
+            for (int d = 0; d < 4; ++d) w[i][d] = 0u;
         }
     }
-    uint32_t ab[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ab[i][j] = abs_bits(f[i][j]);
+    // element j (0..7) of row i as fp32, and its magnitude's bit pattern
+    auto val = [&](int i, int j) { return (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]); };
+    auto mag = [&](int i, int j) {
+        return (j & 1) ? (w[i][j >> 1] & 0x7FFF0000u) : ((w[i][j >> 1] << 16) & 0x7FFFFFFFu);
+    };
 
     // column-wise partial maxima of this thread's 8 rows, combined over the 16 row groups in LDS
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         uint32_t am = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am = max(am, ab[i][j]);
+        for (int i = 0; i < 8; ++i) am = max(am, mag(i, j));
         red[rg][cg * 8 + j] = am;
     }
 
@@ -345,7 +364,7 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
     for (int i = 0; i < 8; ++i) {
         uint32_t am = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) am = max(am, ab[i][j]);
+        for (int j = 0; j < 8; ++j) am = max(am, mag(i, j));
         rmax[i] = umax_row16(am);
     }
     uint32_t mine = rmax[0];
@@ -356,8 +375,8 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
     for (int i = 0; i < 8; ++i) {
         const float m = bcast_row16(gm.m, i);
         const float sc = bcast_row16(gm.s, i);
-        const uint32_t w0 = encode4_in_range(f[i][0] * m, f[i][1] * m, f[i][2] * m, f[i][3] * m);
-        const uint32_t w1 = encode4_in_range(f[i][4] * m, f[i][5] * m, f[i][6] * m, f[i][7] * m);
+        const uint32_t w0 = encode4_in_range(val(i, 0) * m, val(i, 1) * m, val(i, 2) * m, val(i, 3) * m);
+        const uint32_t w1 = encode4_in_range(val(i, 4) * m, val(i, 5) * m, val(i, 6) * m, val(i, 7) * m);
         const int64_t r = r0 + rg * 8 + i;
         if (r < R) {  // rows >= R store neither codes nor scales
             store8<VEC_Q>(q + r * ldq, c, C, w0, w1);
@@ -365,6 +384,11 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
         }
     }
 
+    // only the packed tile stays live across the barriers: the fp32 values are unpacked again below
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) asm volatile("" : "+v"(w[i][d]));
     __syncthreads();
     if (t < kGroup) {
         uint32_t am = 0;
@@ -381,8 +405,8 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float mj = colm[cg * 8 + j];
-        const uint32_t lo = encode4_in_range(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
-        const uint32_t hi = encode4_in_range(f[4][j] * mj, f[5][j] * mj, f[6][j] * mj, f[7][j] * mj);
+        const uint32_t lo = encode4_in_range(val(0, j) * mj, val(1, j) * mj, val(2, j) * mj, val(3, j) * mj);
+        const uint32_t hi = encode4_in_range(val(4, j) * mj, val(5, j) * mj, val(6, j) * mj, val(7, j) * mj);
         const int cl = cg * 8 + j;
         const int chunk = (rg >> 1) ^ (cg & 7);
         *reinterpret_cast<uint2*>(tw + cl * 32 + chunk * 4 + (rg & 1) * 2) = make_uint2(lo, hi);
