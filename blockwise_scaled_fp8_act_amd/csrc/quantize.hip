@@ -87,10 +87,11 @@ __device__ __forceinline__ void store16(uint8_t* __restrict__ row, int64_t c, in
 
 // ------------------------------------------------------------------------------------------
 // 1x128: a 16-lane team owns one (row, K-block) group, 8 elements per lane; a workgroup covers
-// kLhsRows consecutive rows of one K-block, so its scale stores form one contiguous run of the
-// column-major scale column kb.
+// kLhsRows consecutive rows of kLhsBlocks consecutive K-blocks (one after the other), so its scale
+// stores form contiguous runs of the column-major scale columns.
 constexpr int kLhsRowsPerTeam = 4;
 constexpr int kLhsRows = 16 * kLhsRowsPerTeam;
+constexpr int kLhsBlocks = 2;
 
 template <bool VEC_X, bool VEC_Q>
 __global__ __launch_bounds__(256) void quantize_lhs_kernel(
@@ -98,9 +99,11 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s) {
     const int lane16 = threadIdx.x & 15;
     const int team = threadIdx.x >> 4;
-    const int64_t kb = blockIdx.y;
-    const int64_t c = kb * kGroup + lane16 * 8;
     const int64_t mbase = static_cast<int64_t>(blockIdx.x) * kLhsRows;
+    for (int kk = 0; kk < kLhsBlocks; ++kk) {
+    const int64_t kb = static_cast<int64_t>(blockIdx.y) * kLhsBlocks + kk;
+    if (kb * kGroup >= K) break;  // uniform over the workgroup
+    const int64_t c = kb * kGroup + lane16 * 8;
 
     float f[kLhsRowsPerTeam][8];
 #pragma unroll
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
             store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
             if (lane16 == 0) a_s[kb * M + m] = g.s;
         }
+    }
     }
 }
 
@@ -446,7 +450,8 @@ bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a)
 hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                                int64_t ldq, float* a_s, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
-    const dim3 grid(static_cast<unsigned>((M + kLhsRows - 1) / kLhsRows), static_cast<unsigned>(Kb));
+    const dim3 grid(static_cast<unsigned>((M + kLhsRows - 1) / kLhsRows),
+                    static_cast<unsigned>((Kb + kLhsBlocks - 1) / kLhsBlocks));
     const bool vx = aligned(x, 16) && (ldx % 8 == 0);
     const bool vq = aligned(q, 8) && (ldq % 8 == 0);
     if (vx && vq)
