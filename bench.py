@@ -355,7 +355,21 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     a = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)], sdyT[j(i)], qxT[j(i)], sxT[j(i)], c=dw[j(i)],
                                                       stream=stream), reps, stream, torch)
     add("gemm_1x128_128x1 wgrad", [D, D, T], a, fl, "TFLOP/s")
-    del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw
+    # the whole training step of one linear layer through torch.autograd (quantize X, W, dY; the
+    # forward, dgrad and wgrad GEMMs), 3 GEMMs of 2*T*D*D flop each
+    Xg = [x.view(torch.bfloat16).clone().requires_grad_(True) for x in X[:2]]
+    Wg = [w.view(torch.bfloat16).clone().requires_grad_(True) for w in W[:2]]
+    dYg = [y.view(torch.bfloat16) for y in dY[:2]]
+
+    def train_step(i):
+        k = i % 2
+        Xg[k].grad = None
+        Wg[k].grad = None
+        bf.blockwise_fp8_linear(Xg[k], Wg[k]).backward(dYg[k])
+
+    a = _time_kernel(train_step, reps, stream, torch)
+    add("linear fwd+dgrad+wgrad (autograd, all quantizers)", [T, D, D], a, 3 * fl, "TFLOP/s")
+    del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw, Xg, Wg, dYg
     torch.cuda.empty_cache()
 
     d4 = inputs.make_workload(4)

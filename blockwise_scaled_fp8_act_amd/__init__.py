@@ -4,7 +4,8 @@ Group quantizers (1x128, 128x1, 128x128, and 1x128 + 128x1 of one tensor in a si
 bf16 to float8_e4m3fn with fp32 scales, and the
 1x128 x 128x128 / 1x128 x 128x1 scaled FP8 GEMMs with bf16 output, as hand-written HIP kernels
 behind the C ABI of include/blockwise_fp8.h. This package is the thin Python binding over that
-library (``binding``), its in-tree build (``build``) and the seeded input generators (``inputs``).
+library (``binding``), the blockwise-FP8 linear layer composed from those kernels for training
+(``linear``), its in-tree build (``build``) and the seeded input generators (``inputs``).
 """
 from .binding import (  # noqa: F401
     Bsfp8Error,
@@ -16,3 +17,4 @@ from .binding import (  # noqa: F401
     quantize_rhs,
     quantize_weight_128x128,
 )
+from .linear import BlockwiseFp8Linear, blockwise_fp8_linear  # noqa: F401

@@ -1,0 +1,111 @@
+"""GPU parity of the blockwise-FP8 linear layer (forward, dgrad and wgrad through torch.autograd)
+against the oracle composition of the same recipe.
+
+The oracle side quantizes X, W and dY with the oracle quantizers and evaluates the three GEMMs in
+fp64 on those codes; the layer's outputs must meet the GEMM tolerance (elementwise
+2e-2 (|C_o| + 1), relative Frobenius 4e-3), and each product must keep the method's accuracy
+against the fp64 product of the bf16 operands (SQNR >= 28 dB, the ROCm page's GEMM SQNR table).
+Full-size problems are compared on a seeded sample of rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import blockwise_scaled_fp8_act_amd as bf
+import oracle
+from blockwise_scaled_fp8_act_amd import inputs
+from tests._gpu import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(M, n, seed=0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = set(g.choice(M, size=min(n, M), replace=False).tolist()) | {0, M - 1}
+    rows |= set(range(M - M % 128, M))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check(c_gpu, c_oracle, what):
+    rep = oracle.gemm_tolerance_report(c_gpu, c_oracle)
+    assert rep["ok"], f"{what}: {rep}"
+
+
+def _run_layer(xh, wh, dyh):
+    x = to_dev(xh).view(torch.bfloat16).requires_grad_(True)
+    w = to_dev(wh).view(torch.bfloat16).requires_grad_(True)
+    y = bf.blockwise_fp8_linear(x, w)
+    y.backward(to_dev(dyh).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    return (y.detach().float().cpu().numpy(), x.grad.float().cpu().numpy(),
+            w.grad.float().cpu().numpy())
+
+
+def _oracle_layer(xh, wh, dyh, rows_t=None, rows_w=None):
+    qx, sx = oracle.quantize_lhs(xh)
+    qw, qwT, sw = oracle.quantize_weight_128x128(wh)
+    qdy, sdy = oracle.quantize_lhs(dyh)
+    qxT, sxT = oracle.quantize_rhs(xh)
+    qdyT, sdyT = oracle.quantize_rhs(dyh)
+    kbw = sw.shape[1]
+    y = oracle.gemm_1x128_128x128(qx, sx, qw, sw, kbw, 1, rows=rows_t)
+    dx = oracle.gemm_1x128_128x128(qdy, sdy, qwT, sw, 1, kbw, rows=rows_t)
+    dw = oracle.gemm_1x128_128x1(qdyT, sdyT, qxT, sxT, rows=rows_w)
+    return y, dx, dw
+
+
+def _dy(shape, seed):
+    return inputs.normal_bf16(np.random.Generator(np.random.PCG64(seed)), shape, 0.01)
+
+
+@pytest.mark.parametrize("case", ["small", "tail", "ragged"])
+def test_linear_layer_small_shapes(case):
+    """Forward + backward on the small forward case (x [2,128], W [512,128]), the tail case
+    (x [130,1280], W [5120,1280]) and a token count off the 128 grid (wgrad K = 300)."""
+    if case == "small":
+        d = inputs.make_workload(0)
+        xh, wh = d["A"], d["W"]
+    elif case == "tail":
+        d = inputs.make_workload(1)
+        xh, wh = d["A"], d["W"]
+    else:
+        g = np.random.Generator(np.random.PCG64(11))
+        xh = inputs.normal_bf16(g, (300, 256))
+        wh = inputs.normal_bf16(g, (384, 256), 0.02)
+    dyh = _dy((xh.shape[0], wh.shape[0]), seed=xh.shape[0])
+    y, dx, dw = _run_layer(xh, wh, dyh)
+    oy, odx, odw = _oracle_layer(xh, wh, dyh)
+    _check(y, oy, "forward")
+    _check(dx, odx, "dgrad")
+    _check(dw, odw, "wgrad")
+
+
+def test_linear_layer_training_step_sampled():
+    """The training-step shapes (X, dY [8192, 4096], W [4096, 4096]) through autograd, against the
+    oracle on sampled rows, plus the SQNR of each product against the bf16 operands in fp64."""
+    d = inputs.make_workload(3)
+    xh, wh, dyh = d["X"], d["W"], d["dY"]
+    y, dx, dw = _run_layer(xh, wh, dyh)
+    rows_t = _sample_rows(xh.shape[0], 40)
+    rows_w = _sample_rows(wh.shape[0], 40)
+    oy, odx, odw = _oracle_layer(xh, wh, dyh, rows_t, rows_w)
+    _check(y[rows_t], oy, "forward")
+    _check(dx[rows_t], odx, "dgrad")
+    _check(dw[rows_w], odw, "wgrad")
+    xf, wf, dyf = (oracle.bf16_bits_to_f64(a) for a in (xh, wh, dyh))
+    assert oracle.sqnr_db(xf[rows_t] @ wf.T, y[rows_t]) >= 28.0
+    assert oracle.sqnr_db(dyf[rows_t] @ wf, dx[rows_t]) >= 28.0
+    assert oracle.sqnr_db(dyf.T[rows_w] @ xf, dw[rows_w]) >= 28.0
+
+
+def test_linear_module_matches_function():
+    """The nn.Module wrapper (leading batch dims, bf16 bias) gives the function's result."""
+    torch.manual_seed(0)
+    m = bf.BlockwiseFp8Linear(256, 384, bias=True, device="cuda")
+    with torch.no_grad():
+        m.bias.copy_(torch.linspace(-1, 1, 384, dtype=torch.bfloat16))
+    x = torch.randn(3, 100, 256, device="cuda").to(torch.bfloat16)
+    y = m(x)
+    ref = bf.blockwise_fp8_linear(x.reshape(-1, 256), m.weight.detach()) + m.bias.detach()
+    assert y.shape == (3, 100, 384)
+    assert torch.equal(y.reshape(-1, 384), ref)
