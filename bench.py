@@ -372,6 +372,34 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw, Xg, Wg, dYg
     torch.cuda.empty_cache()
 
+    # expert-grouped (MoE) GEMMs: 8 experts, 16384 routed tokens split unevenly in multiples of
+    # 128, 4096 -> 2048 features per expert; forward (rows grouped) and weight gradient (tokens
+    # grouped), 2*T*2048*4096 flop each
+    E, Tm, Di, Do = 8, 16384, 4096, 2048
+    gm = np.random.Generator(np.random.PCG64(5))
+    counts = gm.multinomial(Tm // BLOCK, np.full(E, 1.0 / E)) * BLOCK
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int64, device=dev)
+    nsm = 2
+    Am = [dev_bf16(inputs.normal_bf16(gm, (Tm, Di))) for _ in range(nsm)]
+    Wm = dev_bf16(inputs.normal_bf16(gm, (E * Do, Di), 0.02))
+    dYm = dev_bf16(inputs.normal_bf16(gm, (Tm, Do), 0.01))
+    qam = [bf.quantize_lhs(x) for x in Am]
+    qwm, _, swm = bf.quantize_weight_128x128(Wm, want_qT=False)
+    qxTm, sxTm = bf.quantize_rhs(Am[0])
+    qdyTm, sdyTm = bf.quantize_rhs(dYm)
+    cm = [torch.empty((Tm, Do), dtype=torch.bfloat16, device=dev) for _ in range(nsm)]
+    dwm = torch.empty((E, Do, Di), dtype=torch.bfloat16, device=dev)
+    Kbm, Nbm = Di // BLOCK, Do // BLOCK
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128_grouped(
+        qam[i % nsm][0], qam[i % nsm][1], qwm, swm, offs, E, b_stride=Do * Di, bs_stride=Nbm * Kbm,
+        bs_stride_nb=Kbm, bs_stride_kb=1, c=cm[i % nsm], N=Do, stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x128_grouped fwd (8 experts)", [Tm, Do, Di], a, 2.0 * Tm * Do * Di, "TFLOP/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x1_grouped(qdyTm, sdyTm, qxTm, sxTm, offs, E, c=dwm,
+                                                           stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x1_grouped wgrad (8 experts)", [Do, Di, Tm], a, 2.0 * Tm * Do * Di, "TFLOP/s")
+    del Am, Wm, dYm, qam, qwm, swm, qxTm, sxTm, qdyTm, sdyTm, cm, dwm
+    torch.cuda.empty_cache()
+
     d4 = inputs.make_workload(4)
     M4, K4 = d4["A"].shape
     N4 = d4["W"].shape[0]

@@ -11,7 +11,9 @@ from .binding import (  # noqa: F401
     Bsfp8Error,
     encode_e4m3_f32,
     gemm_1x128_128x1,
+    gemm_1x128_128x1_grouped,
     gemm_1x128_128x128,
+    gemm_1x128_128x128_grouped,
     quantize_lhs,
     quantize_lhs_and_rhs,
     quantize_rhs,

@@ -54,8 +54,13 @@ def lib():
                                        _vp]
         L.encode_e4m3_f32.argtypes = [_vp, _vp, _i64, _vp]
         L.quantize_lhs_and_rhs.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp]
+        L.gemm_1x128_128x128_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64,
+                                                 _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]
+        L.gemm_1x128_128x1_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
+                                               _i64, _i64, _i64, _i64, _vp]
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
-                  "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs"):
+                  "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs",
+                  "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -178,3 +183,39 @@ def encode_e4m3_f32(x, q=None, stream=None):
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _call("encode_e4m3_f32", _ptr(x), _ptr(q), n, _stream(stream))
     return q
+
+
+def gemm_1x128_128x128_grouped(a, a_s, b, b_s, offsets, E, b_stride, bs_stride, bs_stride_nb,
+                               bs_stride_kb, ldb=None, c=None, N=None, stream=None):
+    """Expert-grouped C = A B_e^T over the row ranges [offsets[e], offsets[e+1]) of A and C.
+    a [M, K] codes with a_s (Kb, M); B_e starts b_stride bytes after B_(e-1) in ``b`` (a uint8
+    tensor, rows of stride ldb, default its row stride); scales of expert e start bs_stride floats
+    after those of e-1 in ``b_s`` and are addressed with (bs_stride_nb, bs_stride_kb); ``offsets``
+    is an int64 device tensor of E + 1 boundaries. N defaults to b's row count when b holds the
+    experts' rows stacked ([E*N, K])."""
+    M, K = a.shape
+    if ldb is None:
+        ldb = _ld(b)
+    if N is None:
+        N = b.shape[0] // E
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _call("gemm_1x128_128x128_grouped", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), ldb, b_stride,
+          _ptr(b_s), bs_stride, bs_stride_nb, bs_stride_kb, _ptr(offsets), E, _ptr(c), _ld(c), M, N,
+          K, _stream(stream))
+    return c
+
+
+def gemm_1x128_128x1_grouped(a, a_s, b, b_s, offsets, E, c=None, stream=None):
+    """Per-expert C_e = A_e B_e^T over the token (column) ranges [offsets[e], offsets[e+1]) of
+    A [M, K] and B [N, K] (quantize_rhs codes over all tokens, scales (Kb, M) and (Kb, N)); returns
+    c [E, M, N] bf16."""
+    M, K = a.shape
+    N = b.shape[0]
+    if c is None:
+        c = torch.empty((E, M, N), dtype=torch.bfloat16, device=a.device)
+    if c.dim() != 3 or c.stride(2) != 1:
+        raise ValueError("expected c [E, M, N] with contiguous rows")
+    _call("gemm_1x128_128x1_grouped", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
+          _ptr(offsets), E, _ptr(c), c.stride(1), c.stride(0), M, N, K, _stream(stream))
+    return c

@@ -154,6 +154,43 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx, void*
                                               static_cast<hipStream_t>(stream)));
 }
 
+int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s, const void* b,
+                               int64_t ldb, int64_t b_stride, const float* b_s, int64_t bs_stride,
+                               int64_t bs_stride_nb, int64_t bs_stride_kb, const int64_t* offsets,
+                               int64_t E, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               void* stream) {
+    if (E < 0 || K < 0) return BSFP8_EINVAL;
+    if (E == 0 || M == 0 || N == 0) return M < 0 || N < 0 ? BSFP8_EINVAL : BSFP8_OK;
+    if (K == 0 || K % kGroupEdge != 0 || K / kGroupEdge > 512) return BSFP8_EINVAL;
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (offsets == nullptr || b_stride < 0 || bs_stride < 0 || bs_stride_nb < 0 || bs_stride_kb < 0)
+        return BSFP8_EINVAL;
+    if (b_stride % 16 != 0) return BSFP8_EALIGN;
+    if (int rc = check_device()) return rc;
+    bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
+    return finish(bsfp8::launch_gemm_grouped_rows(
+        static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b), ldb, b_stride, bs,
+        bs_stride, offsets, E, static_cast<uint16_t*>(c), ldc, M, N, K,
+        static_cast<hipStream_t>(stream)));
+}
+
+int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const void* b,
+                             int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
+                             void* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
+                             int64_t K, void* stream) {
+    if (E < 0 || K < 0) return BSFP8_EINVAL;
+    if (E == 0 || M == 0 || N == 0) return M < 0 || N < 0 ? BSFP8_EINVAL : BSFP8_OK;
+    if (K == 0 || K % kGroupEdge != 0 || N % 4 != 0 || E > 65535) return BSFP8_EINVAL;
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
+    if (offsets == nullptr) return BSFP8_EINVAL;
+    if (E > 1 && c_stride < (M - 1) * ldc + N) return BSFP8_EINVAL;  // expert outputs must not overlap
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_gemm_grouped_k(
+        static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b), ldb, b_s, offsets,
+        E, static_cast<uint16_t*>(c), ldc, c_stride, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream) {
     if (n < 0) return BSFP8_EINVAL;
     if (n == 0) return BSFP8_OK;

@@ -410,6 +410,20 @@ constexpr int kLoadsPerStage(bool per_col) { return 4 + 4 + 1 + (per_col ? 1 : 0
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// Expert grouping of one launch (MoE): kGroupRows -- experts own row ranges of A and C and bring
+// their own B (forward, dgrad); kGroupK -- experts own token (K) ranges and write their own C
+// (weight gradient).
+constexpr int kGroupNone = 0;
+constexpr int kGroupRows = 1;
+constexpr int kGroupK = 2;
+struct Grouping {
+    const int64_t* offsets;  // E + 1 boundaries (device memory)
+    int64_t E;
+    int64_t b_stride;   // bytes between consecutive experts' B            (kGroupRows)
+    int64_t bs_stride;  // floats between consecutive experts' B scales    (kGroupRows)
+    int64_t c_stride;   // elements between consecutive experts' C         (kGroupK)
+};
+
 struct Ops {
     __amdgpu_buffer_rsrc_t a, b, as, bs;
     uint32_t a_lane[2];  // tile row 32 wave + lane / 8, chunk (lane % 8) ^ swz(row) for loads q even / odd
@@ -487,12 +501,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool PER_COL>
+template <bool PER_COL, int GROUP>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb,
     int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt,
-    int nt, int c_vec) {
+    int nt, int c_vec, Grouping grp) {
     __shared__ u32x4 smem[kStages * kStageSize];
     __shared__ float bscale_lds[2][kMaxKbFast];
 
@@ -505,14 +519,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int lg = lane >> 4;
     int tm, tn;
     tile_of(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    int64_t m0 = static_cast<int64_t>(tm) * kBM;  // this tile's rows are [m0, min(m0 + kBM, m_end))
+    int64_t m_end = M;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
-    const int64_t Kb = K / kGroup;
+    int64_t Kb = K / kGroup;
+    if (GROUP == kGroupRows) {
+        // tm indexes the concatenated row tiles of the experts; expert e owns rows
+        // [offsets[e], offsets[e + 1]) of A and C (clamped to [0, M] and made non-decreasing) and
+        // multiplies them by its own B and B scales
+        int64_t first = 0, lo = 0, hi = 0;
+        int64_t e = -1;
+        int64_t prev = 0;
+        for (int64_t j = 0; j < grp.E; ++j) {
+            const int64_t a = min(max(grp.offsets[j], prev), M);
+            const int64_t b = min(max(grp.offsets[j + 1], a), M);
+            prev = b;
+            const int64_t tiles = (b - a + kBM - 1) / kBM;
+            if (tm < first + tiles) {
+                e = j;
+                lo = a;
+                hi = b;
+                break;
+            }
+            first += tiles;
+        }
+        if (e < 0) return;  // a spare workgroup of the grid's upper bound: the whole group leaves
+        m0 = lo + (tm - first) * kBM;
+        m_end = hi;
+        B += e * grp.b_stride;
+        b_s += e * grp.bs_stride;
+    } else if (GROUP == kGroupK) {
+        // expert e = blockIdx.y owns the K-blocks [offsets[e] / 128, offsets[e + 1] / 128) of A and B
+        // (token ranges of the weight gradient) and writes its own C
+        const int64_t e = blockIdx.y;
+        const int64_t lo = min(max(grp.offsets[e], int64_t{0}), K);
+        const int64_t hi = min(max(grp.offsets[e + 1], lo), K);
+        const int64_t kb0 = lo / kGroup;
+        Kb = hi / kGroup - kb0;
+        A += kb0 * kGroup;
+        B += kb0 * kGroup;
+        a_s += kb0 * M;
+        b_s += PER_COL ? kb0 * N : kb0 * bs_kb;
+        C += e * grp.c_stride;
+    }
     constexpr int kLoads = kLoadsPerStage(PER_COL);
 
     Ops op;
     {
-        const int64_t arows = (M - m0) < kBM ? (M - m0) : kBM;
+        const int64_t arows = (m_end - m0) < kBM ? (m_end - m0) : kBM;
         const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
         op.a = make_rsrc(A + m0 * lda, static_cast<uint32_t>(arows * lda));
         op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
@@ -639,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
         const int64_t m = m0 + 64 * wm + 16 * i + l16;
-        if (m >= M) continue;
+        if (m >= m_end) continue;
         uint16_t* crow = C + m * ldc;
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
@@ -675,13 +729,14 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
         if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(mt * nt));
+        const fast::Grouping none{nullptr, 0, 0, 0, 0};
         if (bs.per_column)
-            fast::gemm_kernel<true><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
+            fast::gemm_kernel<true, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
+                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec, none);
         else
-            fast::gemm_kernel<false><<<grid, fast::kThreads, 0, stream>>>(
+            fast::gemm_kernel<false, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
                 a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt,
-                (int)nt, c_vec);
+                (int)nt, c_vec, none);
         return hipGetLastError();
     }
     const int64_t mt = (M + kBM - 1) / kBM;
@@ -695,6 +750,44 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
         gemm_kernel<false><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb,
                                                           bs.stride_kb, c, ldc, M, N, K, (int)mt,
                                                           (int)nt, c_vec);
+    return hipGetLastError();
+}
+
+bool gemm_grouped_supported(bool per_column, int64_t N, int64_t K) {
+    if (K % kGroup != 0) return false;
+    return per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
+}
+
+hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* a_s,
+                                    const uint8_t* b, int64_t ldb, int64_t b_stride, BScale bs,
+                                    int64_t bs_stride, const int64_t* offsets, int64_t E,
+                                    uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                    hipStream_t stream) {
+    if (!gemm_grouped_supported(false, N, K)) return hipErrorInvalidValue;
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    // every expert's last row tile may be partial: at most ceil(M / 256) + E row tiles
+    const int64_t mt = (M + fast::kBM - 1) / fast::kBM + E;
+    const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
+    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const fast::Grouping g{offsets, E, b_stride, bs_stride, 0};
+    fast::gemm_kernel<false, fast::kGroupRows><<<dim3(static_cast<unsigned>(mt * nt)), fast::kThreads, 0, stream>>>(
+        a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt, (int)nt,
+        c_vec, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
+                                 int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
+                                 uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream) {
+    if (!gemm_grouped_supported(true, N, K)) return hipErrorInvalidValue;
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0) && (c_stride % 4 == 0);
+    const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
+    const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
+    if (mt * nt > 0x7FFFFFFFLL || E > 65535) return hipErrorInvalidValue;
+    const fast::Grouping g{offsets, E, 0, 0, c_stride};
+    fast::gemm_kernel<true, fast::kGroupK><<<dim3(static_cast<unsigned>(mt * nt), static_cast<unsigned>(E)), fast::kThreads, 0, stream>>>(
+        a, lda, a_s, b, ldb, b_s, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec, g);
     return hipGetLastError();
 }
 

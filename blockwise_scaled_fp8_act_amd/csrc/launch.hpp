@@ -31,4 +31,17 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream);
 
+// Expert-grouped GEMMs (fast path only: K % 128 == 0; 128x128 scales: at most 512 K-blocks;
+// per-column scales: N % 4 == 0). offsets: E + 1 device int64 boundaries.
+bool gemm_grouped_supported(bool per_column, int64_t N, int64_t K);
+hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* a_s,
+                                    const uint8_t* b, int64_t ldb, int64_t b_stride, BScale bs,
+                                    int64_t bs_stride, const int64_t* offsets, int64_t E,
+                                    uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                    hipStream_t stream);
+hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
+                                 int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
+                                 uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream);
+
 }  // namespace bsfp8

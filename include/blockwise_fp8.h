@@ -151,6 +151,55 @@ int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s,
                      void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * gemm_1x128_128x128_grouped: the forward (or dgrad) GEMM of an expert-grouped (mixture-of-experts)
+ * layer in one launch. Tokens are sorted by expert: expert e owns rows [offsets[e], offsets[e+1])
+ * of A and C and multiplies them by its own B_e with its own 128x128 scales -- the grouped form of
+ * gemm_1x128_128x128 (the MoE path the ROCm page's description refers to, whose kernels it does not
+ * list; this is the plainest reading: per expert, exactly gemm_1x128_128x128 on its rows).
+ *   a, lda, a_s   all tokens: A [M, K] fp8, a_s column-major [M, ceil(K/128)] with ld M (one
+ *                 quantize_lhs over all tokens: 1x128 groups lie inside a token row).
+ *   b, ldb        B_e = b + e * b_stride (bytes), [N, K] rows of stride ldb. For stacked weights
+ *                 W [E, N, K] quantized as one [E*N, K] matrix (N % 128 == 0): forward b = q,
+ *                 b_stride = N * ldq; dgrad b = its transposed codes qT [K, E*N], b_stride = N bytes,
+ *                 ldb = ldqT.
+ *   b_s           scales of B_e at b_s + e * bs_stride (floats), (K-block kb, N-block nb) at
+ *                 [nb * bs_stride_nb + kb * bs_stride_kb], as in gemm_1x128_128x128.
+ *   offsets       E + 1 int64 in DEVICE memory, non-decreasing, in [0, M]. The kernel clamps them
+ *                 into [0, M] and to non-decreasing order; rows outside every range are not written.
+ *   c, ldc        C [M, N] bf16.
+ * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, at most 512 K-blocks; b_stride a
+ * multiple of 16 (else BSFP8_EALIGN); alignment and size limits as gemm_1x128_128x128.
+ * E == 0 or an empty M or N: no launch.
+ */
+int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s,
+                               const void* b, int64_t ldb, int64_t b_stride,
+                               const float* b_s, int64_t bs_stride,
+                               int64_t bs_stride_nb, int64_t bs_stride_kb,
+                               const int64_t* offsets, int64_t E,
+                               void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_1x128_128x1_grouped: the weight gradient of an expert-grouped layer in one launch: for every
+ * expert e, C_e = A_e B_e^T where A_e and B_e are the columns (tokens) [offsets[e], offsets[e+1])
+ * of A and B -- per expert, exactly gemm_1x128_128x1 over its own tokens.
+ *   a, lda, a_s   A [M, K] fp8 = quantize_rhs(dY) codes over all K tokens, a_s [ceil(K/128), M].
+ *   b, ldb, b_s   B [N, K] fp8 = quantize_rhs(X) codes, b_s [ceil(K/128), N].
+ *   offsets       E + 1 int64 token boundaries in DEVICE memory, multiples of 128: each expert's
+ *                 128x1 groups then lie inside its own tokens, so one quantize_rhs over all tokens
+ *                 is the per-expert quantization. Boundaries are clamped into [0, K] and to
+ *                 non-decreasing order and rounded down to a multiple of 128.
+ *   c, ldc        E outputs [M, N] bf16, expert e's at c + e * c_stride (elements).
+ * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, N % 4 == 0, E <= 65535,
+ * c_stride >= (M - 1) * ldc + N when E > 1; alignment and size limits as gemm_1x128_128x1.
+ * E == 0 or an empty M or N: no launch.
+ */
+int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s,
+                             const void* b, int64_t ldb, const float* b_s,
+                             const int64_t* offsets, int64_t E,
+                             void* c, int64_t ldc, int64_t c_stride,
+                             int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * encode_e4m3_f32: the quantizers' element conversion applied to n arbitrary fp32 values:
  *   q[i] = e4m3(clamp(x[i], -448, 448)), round to nearest even, sign kept. NaN inputs are outside
  *   the contract. Exposed so the device conversion can be checked over every fp32 pattern.

@@ -30,7 +30,8 @@ def test_every_declared_symbol_is_exported(L):
     names = _declared_functions()
     assert set(names) >= {"quantize_lhs", "quantize_rhs", "quantize_weight_128x128",
                           "gemm_1x128_128x128", "gemm_1x128_128x1", "bsfp8_status_string",
-                          "encode_e4m3_f32", "quantize_lhs_and_rhs"}
+                          "encode_e4m3_f32", "quantize_lhs_and_rhs",
+                          "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -65,6 +66,24 @@ def test_fused_quantizer_rejects_bad_arguments(L):
     assert f(P, 3, 64, 64, P, 64, None, P, 3, P, None) == 1       # a_s null
     assert f(P, 3, 64, 64, P, 64, P, None, 3, P, None) == 1       # qT null
     assert f(None, 0, 64, 64, None, 64, None, None, 0, None, None) == 0   # empty
+
+
+def test_grouped_gemms_reject_bad_arguments(L):
+    g = L.gemm_1x128_128x128_grouped
+    #      a   lda  a_s b  ldb  bstr a_s  bss nb kb off E  c  ldc  M    N    K
+    assert g(P, 128, P, P, 128, 0, P, 0, 1, 1, P, -1, P, 64, 256, 64, 128, None) == 1     # E < 0
+    assert g(P, 144, P, P, 144, 0, P, 0, 1, 1, P, 2, P, 64, 256, 64, 130, None) == 1      # K % 128
+    assert g(P, 128, P, P, 128, 0, P, 0, 1, 1, None, 2, P, 64, 256, 64, 128, None) == 1   # offsets
+    assert g(P, 128, P, P, 128, 8, P, 0, 1, 1, P, 2, P, 64, 256, 64, 128, None) == 2      # b_stride % 16
+    assert g(P, 128, P, P, 128, 0, P, -1, 1, 1, P, 2, P, 64, 256, 64, 128, None) == 1     # bs_stride < 0
+    assert g(None, 0, None, None, 0, 0, None, 0, 0, 0, None, 0, None, 0, 5, 5, 128, None) == 0  # E = 0
+    h = L.gemm_1x128_128x1_grouped
+    #      a   lda  a_s b  ldb  b_s off E  c  ldc cstr    M   N   K
+    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 64 * 64, 64, 64, 130, None) == 1          # K % 128
+    assert h(P, 256, P, P, 256, P, P, 2, P, 66, 64 * 66, 64, 66, 256, None) == 1          # N % 4
+    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 100, 64, 64, 256, None) == 1              # outputs overlap
+    assert h(P, 256, P, P, 256, P, None, 2, P, 64, 64 * 64, 64, 64, 256, None) == 1       # offsets
+    assert h(None, 0, None, None, 0, None, None, 0, None, 0, 0, 3, 4, 256, None) == 0     # E = 0
 
 
 def test_empty_problems_are_noops(L):
