@@ -593,7 +593,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (Kb > 0) {
-        // 128x128 B scales of the tile's two 128-column blocks for every K-block
+        auto stage_base = [&](int stage) { return op.lds + static_cast<uint32_t>(stage * kStageSize * 16); };
+        const int sw = swz(l16);  // the same for every fragment row 16 x + l16
+        const int pos_lo = (2 * lg) ^ sw;
+        const int pos_hi = (2 * lg + 1) ^ sw;
+
+        // prologue: block 0 into stage 0
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, M, N, wave);
+
+        // 128x128 B scales of the tile's two 128-column blocks for every K-block, fetched while
+        // block 0 is in flight (their wait covers both)
         if (!PER_COL) {
             for (int64_t c = tid; c < 2 * Kb; c += kThreads) {
                 const int half = c >= Kb;
@@ -603,15 +613,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                 bscale_lds[half][kb] = b_s[(nb * kGroup < N ? nb : 0) * bs_nb + kb * bs_kb];
             }
         }
-
-        auto stage_base = [&](int stage) { return op.lds + static_cast<uint32_t>(stage * kStageSize * 16); };
-        const int sw = swz(l16);  // the same for every fragment row 16 x + l16
-        const int pos_lo = (2 * lg) ^ sw;
-        const int pos_hi = (2 * lg + 1) ^ sw;
-
-        // prologue: block 0 into stage 0
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, M, N, wave);
         wait_own_loads<0>();
 
         // One loop body for both stages (stage = kb % 2 at run time): a body unrolled per stage
@@ -690,25 +691,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         for (int64_t kb = 0; kb < Kb; ++kb) step(kb);
     }
 
+    // Epilogue: each wave's 64 x 128 bf16 block goes through LDS (the stages are free once every
+    // wave has left the K-loop), so the global stores are 16 bytes per lane and whole 128-byte
+    // lines (a lane's own outputs are 4 columns of one row). Row r of a block holds 16 chunks of 16
+    // bytes, chunk c at position c ^ (r % 16), which keeps both LDS passes free of bank conflicts.
+    __syncthreads();
+    uint8_t* cblk = reinterpret_cast<uint8_t*>(smem) + wave * (kWM * kWN * 2);
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
-        const int64_t m = m0 + 64 * wm + 16 * i + l16;
-        if (m >= m_end) continue;
-        uint16_t* crow = C + m * ldc;
+        const int r = 16 * i + l16;
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
-            const int64_t n = n0 + 128 * wn + 16 * j + 4 * lg;
             const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            if (c_vec && n + 4 <= N) {
-                *reinterpret_cast<uint2*>(crow + n) = make_uint2(w0, w1);
-            } else {
-                const uint16_t h[4] = {static_cast<uint16_t>(w0 & 0xFFFF), static_cast<uint16_t>(w0 >> 16),
-                                       static_cast<uint16_t>(w1 & 0xFFFF), static_cast<uint16_t>(w1 >> 16)};
+            const int chunk = 2 * j + (lg >> 1);
+            *reinterpret_cast<uint2*>(cblk + r * 256 + ((chunk ^ (r & 15)) * 16) + 8 * (lg & 1)) =
+                make_uint2(w0, w1);
+        }
+    }
+    const int cc = lane & 15;  // 16-byte chunk (8 columns) of a row
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) crow[n + e] = h[e];
-            }
+    for (int p = 0; p < kWM / 4; ++p) {
+        const int r = 4 * p + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(cblk + r * 256 + ((cc ^ (r & 15)) * 16));
+        const int64_t m = m0 + 64 * wm + r;
+        if (m >= m_end) continue;
+        const int64_t n = n0 + 128 * wn + 8 * cc;
+        uint16_t* dst = C + m * ldc + n;
+        if (c_vec && n + 8 <= N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
         }
     }
 }
@@ -720,7 +736,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, hipStream_t stream) {
+    // vector stores: 8 bytes per lane in the general kernel, 16 in the fast one
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
     // Fast path: whole K-blocks; per-column scales read 4 columns at a time; 128x128 scales of a
     // tile's column staged in LDS (at most kMaxKbFast K-blocks).
     const bool fast_scales = bs.per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
@@ -732,11 +750,11 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
         const fast::Grouping none{nullptr, 0, 0, 0, 0};
         if (bs.per_column)
             fast::gemm_kernel<true, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec, none);
+                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
         else
             fast::gemm_kernel<false, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
                 a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt,
-                (int)nt, c_vec, none);
+                (int)nt, c_vec16, none);
         return hipGetLastError();
     }
     const int64_t mt = (M + kBM - 1) / kBM;
@@ -764,7 +782,7 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
                                     uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                     hipStream_t stream) {
     if (!gemm_grouped_supported(false, N, K)) return hipErrorInvalidValue;
-    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
     // every expert's last row tile may be partial: at most ceil(M / 256) + E row tiles
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM + E;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
@@ -781,7 +799,7 @@ hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s
                                  uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream) {
     if (!gemm_grouped_supported(true, N, K)) return hipErrorInvalidValue;
-    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0) && (c_stride % 4 == 0);
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0) && (c_stride % 8 == 0);
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL || E > 65535) return hipErrorInvalidValue;
