@@ -10,7 +10,8 @@ follow the GEMM-correctness table of "Enable blockwise FP8 dense training kernel
 (FP8 GEMM compared with a BF16 matmul by SQNR in dB).
 
 Array conventions:
-  bf16 tensors are ``np.uint16`` bit patterns; fp8 tensors are ``np.uint8`` e4m3fn codes.
+  bf16 tensors are ``np.uint16`` bit patterns; fp8 tensors are ``np.uint8`` codes in the format
+  ``fmt`` names: ``"e4m3fn"`` (default; finfo max 448) or ``"e4m3fnuz"`` (finfo max 240).
   ``a_s`` of the LHS quantizer is column-major [M, Kb]; it is returned as a C-contiguous numpy
   array of shape (Kb, M), which has the same bytes (element (m, kb) at kb * M + m).
 """
@@ -50,6 +51,16 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+FORMATS = {"e4m3fn": 0, "e4m3fnuz": 1}
+FP8_MAX = {"e4m3fn": 448.0, "e4m3fnuz": 240.0}
+
+
+def _fmt(fmt: str) -> int:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown fp8 format {fmt!r}; expected one of {sorted(FORMATS)}")
+    return FORMATS[fmt]
 
 
 def lib():
@@ -66,14 +77,23 @@ def lib():
         L.oracle_e4m3_encode_array.restype = None
         L.oracle_e4m3_encode_bits.argtypes = [ctypes.c_uint32, _u8p, _i64]
         L.oracle_e4m3_encode_bits.restype = None
-        L.oracle_quantize_lhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
-        L.oracle_quantize_rhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p]
+        L.oracle_e4m3fnuz_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3fnuz_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3fnuz_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3fnuz_decode.restype = ctypes.c_double
+        L.oracle_fp8_encode_array.argtypes = [_int, _f32p, _u8p, _i64]
+        L.oracle_fp8_encode_array.restype = None
+        L.oracle_fp8_encode_bits.argtypes = [_int, ctypes.c_uint32, _u8p, _i64]
+        L.oracle_fp8_encode_bits.restype = None
+        L.oracle_quantize_lhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _int]
+        L.oracle_quantize_rhs.argtypes = [_u16p, _i64, _i64, _i64, _u8p, _i64, _f32p, _int]
         L.oracle_quantize_weight_128x128.argtypes = [
-            _u16p, _i64, _i64, _i64, _u8p, _i64, _u8p, _i64, _f32p]
+            _u16p, _i64, _i64, _i64, _u8p, _i64, _u8p, _i64, _f32p, _int]
         L.oracle_gemm_1x128_128x128.argtypes = [
-            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64, _i64, _i64p, _i64, _f64p]
+            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64, _i64, _i64p, _i64, _f64p,
+            _int]
         L.oracle_gemm_1x128_128x1.argtypes = [
-            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64p, _i64, _f64p]
+            _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64p, _i64, _f64p, _int]
         for f in ("oracle_quantize_lhs", "oracle_quantize_rhs", "oracle_quantize_weight_128x128",
                   "oracle_gemm_1x128_128x128", "oracle_gemm_1x128_128x1", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -121,33 +141,55 @@ def e4m3_decode(codes) -> np.ndarray:
     return table[codes]
 
 
+def fp8_encode(v, fmt: str = "e4m3fn") -> np.ndarray:
+    """Round-to-nearest-even, saturating encode of fp32 values (finite inputs) in either format."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().oracle_fp8_encode_array(_fmt(fmt), _p(v, _f32p), _p(out, _u8p), v.size)
+    return out
+
+
+def fp8_encode_bits(first: int, n: int, fmt: str = "e4m3fn") -> np.ndarray:
+    """Codes of the fp32 bit patterns first .. first+n-1 (NaN patterns give 0xFF)."""
+    out = np.empty(n, dtype=np.uint8)
+    lib().oracle_fp8_encode_bits(_fmt(fmt), ctypes.c_uint32(first), _p(out, _u8p), n)
+    return out
+
+
+def fp8_decode(codes, fmt: str = "e4m3fn") -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    dec = lib().oracle_e4m3fnuz_decode if _fmt(fmt) == 1 else lib().oracle_e4m3_decode
+    table = np.array([dec(i) for i in range(256)], dtype=np.float64)
+    return table[codes]
+
+
 # ------------------------------------------------------------------ quantizers
 
-def quantize_lhs(x: np.ndarray):
+def quantize_lhs(x: np.ndarray, fmt: str = "e4m3fn"):
     """1x128 row-wise groups of x [M, K] (bf16 bits). Returns (q [M, K], a_s as (Kb, M))."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     M, K = x.shape
     Kb = cdiv(K, BLOCK)
     q = np.zeros((M, K), dtype=np.uint8)
     a_s = np.zeros((Kb, M), dtype=np.float32)
-    _check(lib().oracle_quantize_lhs(_p(x, _u16p), M, K, K, _p(q, _u8p), K, _p(a_s, _f32p)),
-           "quantize_lhs")
+    _check(lib().oracle_quantize_lhs(_p(x, _u16p), M, K, K, _p(q, _u8p), K, _p(a_s, _f32p),
+                                    _fmt(fmt)), "quantize_lhs")
     return q, a_s
 
 
-def quantize_rhs(x: np.ndarray):
+def quantize_rhs(x: np.ndarray, fmt: str = "e4m3fn"):
     """128x1 column-wise groups of x [K, N] (bf16 bits). Returns (qT [N, K], s [Kb, N])."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     K, N = x.shape
     Kb = cdiv(K, BLOCK)
     qT = np.zeros((N, K), dtype=np.uint8)
     s = np.zeros((Kb, N), dtype=np.float32)
-    _check(lib().oracle_quantize_rhs(_p(x, _u16p), K, N, N, _p(qT, _u8p), K, _p(s, _f32p)),
-           "quantize_rhs")
+    _check(lib().oracle_quantize_rhs(_p(x, _u16p), K, N, N, _p(qT, _u8p), K, _p(s, _f32p),
+                                    _fmt(fmt)), "quantize_rhs")
     return qT, s
 
 
-def quantize_weight_128x128(w: np.ndarray, want_qT: bool = True):
+def quantize_weight_128x128(w: np.ndarray, want_qT: bool = True, fmt: str = "e4m3fn"):
     """128x128 blocks of w [N, K] (bf16 bits). Returns (q [N, K], qT [K, N] or None, s [Nb, Kb])."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
     N, K = w.shape
@@ -156,7 +198,8 @@ def quantize_weight_128x128(w: np.ndarray, want_qT: bool = True):
     s = np.zeros((cdiv(N, BLOCK), cdiv(K, BLOCK)), dtype=np.float32)
     qTp = _p(qT, _u8p) if want_qT else None
     _check(lib().oracle_quantize_weight_128x128(_p(w, _u16p), N, K, K, _p(q, _u8p), K, qTp, N,
-                                                _p(s, _f32p)), "quantize_weight_128x128")
+                                                _p(s, _f32p), _fmt(fmt)),
+           "quantize_weight_128x128")
     return q, qT, s
 
 
@@ -168,7 +211,8 @@ def _rows_arg(rows, M):
     return np.ascontiguousarray(rows, dtype=np.int64)
 
 
-def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb, bs_stride_kb, rows=None) -> np.ndarray:
+def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb, bs_stride_kb, rows=None,
+                       fmt: str = "e4m3fn") -> np.ndarray:
     """fp64 C rows for A [M, K] codes, a_s (Kb, M), B [N, K] codes, 128x128 b_s via strides."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
@@ -181,12 +225,12 @@ def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb, bs_stride_kb, rows=None) ->
     out = np.zeros((rows.size, N), dtype=np.float64)
     _check(lib().oracle_gemm_1x128_128x128(
         _p(a, _u8p), K, _p(a_s, _f32p), _p(b, _u8p), K, _p(b_s, _f32p),
-        bs_stride_nb, bs_stride_kb, M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p)),
-        "gemm_1x128_128x128")
+        bs_stride_nb, bs_stride_kb, M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p),
+        _fmt(fmt)), "gemm_1x128_128x128")
     return out
 
 
-def gemm_1x128_128x1(a, a_s, b, b_s, rows=None) -> np.ndarray:
+def gemm_1x128_128x1(a, a_s, b, b_s, rows=None, fmt: str = "e4m3fn") -> np.ndarray:
     """fp64 C rows for A [M, K] codes, a_s (Kb, M), B [N, K] codes, per-column b_s [Kb, N]."""
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
@@ -199,7 +243,8 @@ def gemm_1x128_128x1(a, a_s, b, b_s, rows=None) -> np.ndarray:
     out = np.zeros((rows.size, N), dtype=np.float64)
     _check(lib().oracle_gemm_1x128_128x1(
         _p(a, _u8p), K, _p(a_s, _f32p), _p(b, _u8p), K, _p(b_s, _f32p),
-        M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p)), "gemm_1x128_128x1")
+        M, N, K, _p(rows, _i64p), rows.size, _p(out, _f64p), _fmt(fmt)),
+        "gemm_1x128_128x1")
     return out
 
 

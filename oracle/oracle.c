@@ -19,12 +19,20 @@
  *           no part.
  *   [OFP8]  The OCP 8-bit floating point specification, E4M3 encoding (bias 7, no infinities,
  *           S.1111.111 is NaN, max normal 448, min subnormal 2^-9).
+ *   [FNUZ]  The float8_e4m3fnuz format the ROCm page names for MI300X (its description and test
+ *           log: FP8 max 240): 1 sign, 4 exponent bits with bias 8, 3 mantissa bits, no
+ *           infinities and no negative zero -- the bit pattern 1.0000.000 (0x80) is the only NaN,
+ *           0x7F is the largest finite value 240, the smallest normal is 2^-7 and the smallest
+ *           subnormal 2^-10.
  *
  * Readings where the pages are silent (each is listed with its reason in the design notes):
  *   - eps clamp on the group amax: 1e-12f, applied before both divisions;
- *   - stored scale s = fl32(amax_c / 448), the dequantization multiplier ("reciprocal scale");
- *   - codes q = e4m3(clamp(fl32(x * fl32(448 / amax_c)), -448, 448)): multiply by the quantization
- *     multiplier, then round to nearest even and saturate;
+ *   - stored scale s = fl32(amax_c / FP8_MAX), the dequantization multiplier ("reciprocal scale");
+ *   - codes q = enc(clamp(fl32(x * fl32(FP8_MAX / amax_c)), -FP8_MAX, FP8_MAX)): multiply by the
+ *     quantization multiplier, then round to nearest even and saturate;
+ *   - FP8_MAX is the finfo max of the chosen element format: 448 for e4m3fn (the default), 240
+ *     for e4m3fnuz ([ROCm] description: the limits follow torch.finfo(dtype) and both formats are
+ *     accepted); every other step is the same for both;
  *   - partial groups at a tensor edge use only their valid elements.
  *
  * Build: gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off -fexcess-precision=standard -fopenmp.
@@ -39,7 +47,6 @@
 #include <omp.h>
 #endif
 
-#define FP8_MAX 448.0f /* [ROCm] description: finfo(float8_e4m3fn).max */
 #define GROUP_EPS 1e-12f /* reading: amax clamp so an all-zero group has a finite, non-zero scale */
 #define BLOCK 128        /* [ROCm] quantization table: block_size = 128 */
 
@@ -54,46 +61,74 @@ static float bf16_value(uint16_t bits)
     return f;
 }
 
-/* ---------------------------------------------------------------- e4m3fn codec [OFP8] */
+/* ---------------------------------------------------------------- element codecs */
 
-double oracle_e4m3_decode(uint8_t code)
+/*
+ * The two 8-bit formats differ only in their exponent bias, their largest finite code and their
+ * treatment of zero and NaN:
+ *                 bias  largest finite       NaN codes          zero codes
+ *   e4m3fn [OFP8]   7   0x7E = 448           0x7F, 0xFF         0x00 (+0), 0x80 (-0)
+ *   e4m3fnuz[FNUZ]  8   0x7F = 240           0x80               0x00 only
+ */
+struct e4m3_format {
+    int bias;
+    uint8_t max_code;
+    double max_value;
+    int negative_zero;      /* 1: a negative value that rounds to zero keeps its sign (0x80) */
+};
+
+static const struct e4m3_format FMT_FN = {7, 0x7E, 448.0, 1};
+static const struct e4m3_format FMT_FNUZ = {8, 0x7F, 240.0, 0};
+
+static const struct e4m3_format* format_of(int fmt)
+{
+    return fmt == ORACLE_FMT_E4M3FNUZ ? &FMT_FNUZ : &FMT_FN;
+}
+
+static double decode_generic(uint8_t code, const struct e4m3_format* f)
 {
     int sign = code >> 7;
     int e = (code >> 3) & 0xF;
     int m = code & 0x7;
     double mag;
-    if (e == 0xF && m == 0x7)
-        return NAN;                          /* S.1111.111 */
+    if (f->negative_zero) {
+        if (e == 0xF && m == 0x7)
+            return NAN;                              /* [OFP8] S.1111.111 */
+    } else if (code == 0x80) {
+        return NAN;                                  /* [FNUZ] the negative-zero pattern */
+    }
     if (e == 0)
-        mag = ldexp((double)m, -9);          /* subnormal: m/8 * 2^(1-7) */
+        mag = ldexp((double)m, 1 - f->bias - 3);     /* subnormal: m/8 * 2^(1 - bias) */
     else
-        mag = ldexp(1.0 + m / 8.0, e - 7);   /* normal: (1 + m/8) * 2^(e-7) */
+        mag = ldexp(1.0 + m / 8.0, e - f->bias);     /* normal: (1 + m/8) * 2^(e - bias) */
     return sign ? -mag : mag;
 }
 
 /*
  * Round-to-nearest-even, saturating encode of a finite binary32 value.
- * The representable magnitudes in the binade [2^e, 2^(e+1)) are spaced 2^(e-3) apart for e >= -6;
- * below 2^-6 the spacing stays 2^-9 (subnormals). Magnitudes >= 448 saturate to 448.
+ * With emin = 1 - bias the smallest normal exponent, the representable magnitudes in the binade
+ * [2^e, 2^(e+1)) are spaced 2^(e-3) apart for e >= emin; below 2^emin the spacing stays
+ * 2^(emin-3) (subnormals). Magnitudes >= the largest finite value saturate to it.
  */
-uint8_t oracle_e4m3_encode(float v)
+static uint8_t encode_generic(float v, const struct e4m3_format* f)
 {
+    const int emin = 1 - f->bias;
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
     double a = fabs((double)v);
-    int e, ex;
+    int e, ex, code;
     double quantum, r, fl, frac;
     int64_t n;
 
-    if (a >= 448.0)
-        return (uint8_t)(sign | 0x7E);
+    if (a >= f->max_value)
+        return (uint8_t)(sign | f->max_code);
 
     if (a == 0.0) {
-        e = -6;
+        e = emin;
     } else {
-        (void)frexp(a, &ex);    /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+        (void)frexp(a, &ex);    /* a = g * 2^ex, g in [0.5, 1): floor(log2 a) = ex - 1 */
         e = ex - 1;
-        if (e < -6)
-            e = -6;
+        if (e < emin)
+            e = emin;
     }
     quantum = ldexp(1.0, e - 3);
     r = a / quantum;            /* exact: a has 24 significant bits, quantum is a power of two */
@@ -107,49 +142,66 @@ uint8_t oracle_e4m3_encode(float v)
         n = 8;
         e += 1;
     }
-    /* Now n in [8, 15] is a normal significand (1 + (n-8)/8) at exponent e, or e == -6 and
-     * n in [0, 7] is a subnormal. Both map to code ((e + 7) << 3) + n - 8 for e >= -6 with the
-     * subnormal case landing on e_field 0. */
-    {
-        int code;
-        if (n < 8)
-            code = (int)n;                              /* e == -6, subnormal or zero */
-        else
-            code = ((e + 7) << 3) + (int)(n - 8);
-        /* a < 448 and the rounding above cannot pass 448 (the next step, 480, needs a >= 464). */
-        return (uint8_t)(sign | code);
+    /* Now n in [8, 15] is a normal significand (1 + (n-8)/8) at exponent e, or e == emin and
+     * n in [0, 7] is a subnormal (or zero), whose exponent field is 0. Rounding cannot pass the
+     * largest finite value: a is below it and the next step above it needs a half step more. */
+    if (n < 8)
+        code = (int)n;
+    else
+        code = ((e + f->bias) << 3) + (int)(n - 8);
+    if (code == 0 && !f->negative_zero)
+        return 0x00;            /* [FNUZ] zero has no sign */
+    return (uint8_t)(sign | code);
+}
+
+double oracle_e4m3_decode(uint8_t code) { return decode_generic(code, &FMT_FN); }
+uint8_t oracle_e4m3_encode(float v) { return encode_generic(v, &FMT_FN); }
+double oracle_e4m3fnuz_decode(uint8_t code) { return decode_generic(code, &FMT_FNUZ); }
+uint8_t oracle_e4m3fnuz_encode(float v) { return encode_generic(v, &FMT_FNUZ); }
+
+void oracle_fp8_encode_array(int fmt, const float* v, uint8_t* codes, int64_t n)
+{
+    const struct e4m3_format* f = format_of(fmt);
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        codes[i] = encode_generic(v[i], f);
+}
+
+void oracle_fp8_encode_bits(int fmt, uint32_t first, uint8_t* codes, int64_t n)
+{
+    const struct e4m3_format* f = format_of(fmt);
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) {
+        uint32_t u = first + (uint32_t)i;
+        float x;
+        memcpy(&x, &u, sizeof x);
+        codes[i] = isnan(x) ? 0xFF : encode_generic(x, f);
     }
 }
 
 void oracle_e4m3_encode_array(const float* v, uint8_t* codes, int64_t n)
 {
-    int64_t i;
-#pragma omp parallel for schedule(static)
-    for (i = 0; i < n; ++i)
-        codes[i] = oracle_e4m3_encode(v[i]);
+    oracle_fp8_encode_array(ORACLE_FMT_E4M3FN, v, codes, n);
 }
 
 void oracle_e4m3_encode_bits(uint32_t first, uint8_t* codes, int64_t n)
 {
-    int64_t i;
-#pragma omp parallel for schedule(static)
-    for (i = 0; i < n; ++i) {
-        uint32_t u = first + (uint32_t)i;
-        float f;
-        memcpy(&f, &u, sizeof f);
-        codes[i] = isnan(f) ? 0xFF : oracle_e4m3_encode(f);
-    }
+    oracle_fp8_encode_bits(ORACLE_FMT_E4M3FN, first, codes, n);
 }
 
 /* ---------------------------------------------------------------- one group */
 
 /*
  * The per-group quantization step shared by all three groupings: the group's n valid values are
- * given in vals[]; their codes are written to codes[] and the stored (dequantization) scale is
- * returned.
+ * given in vals[]; their codes (in format f) are written to codes[] and the stored
+ * (dequantization) scale is returned.
  */
-static float quantize_group(const float* vals, int64_t n, uint8_t* codes)
+static float quantize_group(const float* vals, int64_t n, uint8_t* codes,
+                            const struct e4m3_format* f)
 {
+    const float FP8_MAX = (float)f->max_value; /* [ROCm] description: finfo(dtype).max */
     float amax = 0.0f, amax_c, s, m;
     int64_t i;
     for (i = 0; i < n; ++i) {
@@ -166,7 +218,7 @@ static float quantize_group(const float* vals, int64_t n, uint8_t* codes)
             v = FP8_MAX;
         if (v < -FP8_MAX)
             v = -FP8_MAX;
-        codes[i] = oracle_e4m3_encode(v);
+        codes[i] = encode_generic(v, f);
     }
     return s;
 }
@@ -174,8 +226,9 @@ static float quantize_group(const float* vals, int64_t n, uint8_t* codes)
 /* ---------------------------------------------------------------- quantizers */
 
 int oracle_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                        uint8_t* q, int64_t ldq, float* a_s)
+                        uint8_t* q, int64_t ldq, float* a_s, int fmt)
 {
+    const struct e4m3_format* f = format_of(fmt);
     int64_t Kb, m;
     if (M < 0 || K < 0 || ldx < K || ldq < K)
         return -1;
@@ -195,7 +248,7 @@ int oracle_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
             for (k = 0; k < n; ++k)
                 vals[k] = bf16_value(x[m * ldx + k0 + k]);
             /* column-major [M, Kb]: element (m, kb) lives at kb * M + m */
-            a_s[kb * M + m] = quantize_group(vals, n, codes);
+            a_s[kb * M + m] = quantize_group(vals, n, codes, f);
             for (k = 0; k < n; ++k)
                 q[m * ldq + k0 + k] = codes[k];
         }
@@ -204,8 +257,9 @@ int oracle_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 }
 
 int oracle_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx,
-                        uint8_t* qT, int64_t ldqT, float* s)
+                        uint8_t* qT, int64_t ldqT, float* s, int fmt)
 {
+    const struct e4m3_format* f = format_of(fmt);
     int64_t Kb, col;
     if (K < 0 || N < 0 || ldx < N || ldqT < K)
         return -1;
@@ -224,7 +278,7 @@ int oracle_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx,
             int64_t n = (K - k0) < BLOCK ? (K - k0) : BLOCK;
             for (k = 0; k < n; ++k)
                 vals[k] = bf16_value(x[(k0 + k) * ldx + col]);
-            s[kb * N + col] = quantize_group(vals, n, codes);
+            s[kb * N + col] = quantize_group(vals, n, codes, f);
             for (k = 0; k < n; ++k)
                 qT[col * ldqT + k0 + k] = codes[k];
         }
@@ -233,8 +287,10 @@ int oracle_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx,
 }
 
 int oracle_quantize_weight_128x128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                                   uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s)
+                                   uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                                   int fmt)
 {
+    const struct e4m3_format* f = format_of(fmt);
     int64_t Nb, Kb, blk;
     if (N < 0 || K < 0 || ldw < K || ldq < K || (qT && ldqT < N))
         return -1;
@@ -256,7 +312,7 @@ int oracle_quantize_weight_128x128(const uint16_t* w, int64_t N, int64_t K, int6
         for (i = 0; i < rn; ++i)
             for (j = 0; j < rk; ++j)
                 vals[i * rk + j] = bf16_value(w[(n0 + i) * ldw + k0 + j]);
-        s[nb * Kb + kb] = quantize_group(vals, rn * rk, codes);
+        s[nb * Kb + kb] = quantize_group(vals, rn * rk, codes, f);
         for (i = 0; i < rn; ++i)
             for (j = 0; j < rk; ++j) {
                 q[(n0 + i) * ldq + k0 + j] = codes[i * rk + j];
@@ -273,17 +329,18 @@ int oracle_quantize_weight_128x128(const uint16_t* w, int64_t N, int64_t K, int6
 
 /*
  * C[m, n] = sum over K-blocks kb of  a_s[m, kb] * b_scale(kb, n) * sum_{k in kb, k < K} A[m,k] B[n,k]
- * with A, B the decoded fp8 values. Products of two e4m3 values are exact in fp64 and a K-block's
- * partial sum of at most 128 of them is exact too (their magnitudes span under 2^45); only the
- * outer sum over K-blocks rounds, at fp64.
+ * with A, B the decoded fp8 values (both in format fmt). Products of two e4m3 values are exact in
+ * fp64 and a K-block's partial sum of at most 128 of them is exact too (their magnitudes span under
+ * 2^45); only the outer sum over K-blocks rounds, at fp64.
  * bscale_kind 0: 128x128 blocks via (stride_nb, stride_kb); 1: per column, b_s[kb * N + n].
  */
 static int gemm_rows(const uint8_t* a, int64_t lda, const float* a_s,
                      const uint8_t* b, int64_t ldb, const float* b_s,
                      int bscale_kind, int64_t bs_stride_nb, int64_t bs_stride_kb,
                      int64_t M, int64_t N, int64_t K,
-                     const int64_t* rows, int64_t nrows, double* out)
+                     const int64_t* rows, int64_t nrows, double* out, int fmt)
 {
+    const struct e4m3_format* f = format_of(fmt);
     int64_t Kb, r;
     double* bdec;
     double table[256];
@@ -305,7 +362,7 @@ static int gemm_rows(const uint8_t* a, int64_t lda, const float* a_s,
         return -1;
     Kb = cdiv(K, BLOCK);
     for (i = 0; i < 256; ++i)
-        table[i] = oracle_e4m3_decode((uint8_t)i);
+        table[i] = decode_generic((uint8_t)i, f);
 
     /* decode B once: [N, K] doubles */
     bdec = (double*)malloc(sizeof(double) * N * K);
@@ -356,18 +413,18 @@ int oracle_gemm_1x128_128x128(const uint8_t* a, int64_t lda, const float* a_s,
                               const uint8_t* b, int64_t ldb, const float* b_s,
                               int64_t bs_stride_nb, int64_t bs_stride_kb,
                               int64_t M, int64_t N, int64_t K,
-                              const int64_t* rows, int64_t nrows, double* out)
+                              const int64_t* rows, int64_t nrows, double* out, int fmt)
 {
     return gemm_rows(a, lda, a_s, b, ldb, b_s, 0, bs_stride_nb, bs_stride_kb, M, N, K,
-                     rows, nrows, out);
+                     rows, nrows, out, fmt);
 }
 
 int oracle_gemm_1x128_128x1(const uint8_t* a, int64_t lda, const float* a_s,
                             const uint8_t* b, int64_t ldb, const float* b_s,
                             int64_t M, int64_t N, int64_t K,
-                            const int64_t* rows, int64_t nrows, double* out)
+                            const int64_t* rows, int64_t nrows, double* out, int fmt)
 {
-    return gemm_rows(a, lda, a_s, b, ldb, b_s, 1, 0, 0, M, N, K, rows, nrows, out);
+    return gemm_rows(a, lda, a_s, b, ldb, b_s, 1, 0, 0, M, N, K, rows, nrows, out, fmt);
 }
 
 int oracle_num_threads(void)

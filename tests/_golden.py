@@ -16,10 +16,10 @@ def _float(tok):
     return float.fromhex(tok) if "0x" in tok.lower() else float(tok)
 
 
-def hand_groups():
+def hand_groups(name="hand_groups.txt"):
     """-> list of dicts {name, x: [float], q: [int], s_bits: int, fill: float}."""
     cases, cur = [], None
-    for line in _lines("hand_groups.txt"):
+    for line in _lines(name):
         key, _, rest = line.partition(" ")
         if key == "case":
             cur = {"name": rest.strip(), "fill": 0.0}
