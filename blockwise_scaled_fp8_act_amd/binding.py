@@ -5,7 +5,9 @@ current stream. There is no CPU fallback: if the library is missing, loading rai
 
 Tensor conventions (torch, on the GPU):
   bf16 inputs       torch.bfloat16 (or int16/uint16 holding bf16 bits)
-  fp8 codes         torch.uint8 (``.view(torch.float8_e4m3fn)`` gives the same bytes as fp8)
+  fp8 codes         torch.uint8 (``.view(torch.float8_e4m3fn)`` gives the same bytes as fp8);
+                    with ``fmt="e4m3fnuz"`` (or torch.float8_e4m3fnuz) the codes are
+                    float8_e4m3fnuz and FP8_MAX is 240 instead of 448
   LHS scales a_s    torch.float32 of shape (Kb, M), C-contiguous == column-major [M, Kb], ld M
   RHS scales s      torch.float32 (Kb, N) row-major
   weight scales s   torch.float32 (Nb, Kb) row-major
@@ -59,8 +61,15 @@ def lib():
         L.gemm_1x128_128x1_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                                                _i64, _i64, _i64, _i64, _vp]
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
+                  "gemm_1x128_128x1", "quantize_lhs_and_rhs", "encode_e4m3_f32"):
+            fz = getattr(L, f.replace("e4m3", "e4m3fnuz") if f.startswith("encode") else f + "_fnuz")
+            fz.argtypes = getattr(L, f).argtypes
+        for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
                   "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs",
-                  "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped"):
+                  "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
+                  "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
+                  "gemm_1x128_128x128_fnuz", "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
+                  "quantize_lhs_and_rhs_fnuz"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -93,29 +102,51 @@ def cdiv(a, b):
     return (a + b - 1) // b
 
 
-def quantize_lhs(x, q=None, a_s=None, stream=None):
+FORMATS = ("e4m3fn", "e4m3fnuz")
+
+
+def fp8_format(fmt) -> str:
+    """Normalise an FP8 element-format choice: "e4m3fn" / "e4m3fnuz" or the torch dtypes
+    torch.float8_e4m3fn / torch.float8_e4m3fnuz."""
+    if fmt is torch.float8_e4m3fn:
+        return "e4m3fn"
+    if fmt is torch.float8_e4m3fnuz:
+        return "e4m3fnuz"
+    if fmt in FORMATS:
+        return fmt
+    raise ValueError(f"unsupported FP8 format {fmt!r}: expected one of {FORMATS} or the matching "
+                     "torch float8 dtype")
+
+
+def _entry(fn, fmt):
+    return fn + "_fnuz" if fp8_format(fmt) == "e4m3fnuz" else fn
+
+
+def quantize_lhs(x, q=None, a_s=None, stream=None, fmt="e4m3fn"):
     """1x128 row-wise quantization of x [M, K]. Returns (q [M, K] uint8, a_s (Kb, M) fp32)."""
     M, K = x.shape
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if a_s is None:
         a_s = torch.empty((cdiv(K, BLOCK), M), dtype=torch.float32, device=x.device)
-    _call("quantize_lhs", _ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(a_s), _stream(stream))
+    _call(_entry("quantize_lhs", fmt), _ptr(x), M, K, _ld(x), _ptr(q), _ld(q), _ptr(a_s),
+          _stream(stream))
     return q, a_s
 
 
-def quantize_rhs(x, qT=None, s=None, stream=None):
+def quantize_rhs(x, qT=None, s=None, stream=None, fmt="e4m3fn"):
     """128x1 column-wise quantization of x [K, N]. Returns (qT [N, K] uint8, s (Kb, N) fp32)."""
     K, N = x.shape
     if qT is None:
         qT = torch.empty((N, K), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((cdiv(K, BLOCK), N), dtype=torch.float32, device=x.device)
-    _call("quantize_rhs", _ptr(x), K, N, _ld(x), _ptr(qT), _ld(qT), _ptr(s), _stream(stream))
+    _call(_entry("quantize_rhs", fmt), _ptr(x), K, N, _ld(x), _ptr(qT), _ld(qT), _ptr(s),
+          _stream(stream))
     return qT, s
 
 
-def quantize_lhs_and_rhs(x, q=None, a_s=None, qT=None, s=None, stream=None):
+def quantize_lhs_and_rhs(x, q=None, a_s=None, qT=None, s=None, stream=None, fmt="e4m3fn"):
     """Both activation quantizations of x [R, C] in one pass. Returns (q [R, C], a_s (Kb_C, R),
     qT [C, R], s (Kb_R, C)): the outputs of quantize_lhs(x) and of quantize_rhs(x)."""
     R, C = x.shape
@@ -127,12 +158,13 @@ def quantize_lhs_and_rhs(x, q=None, a_s=None, qT=None, s=None, stream=None):
         qT = torch.empty((C, R), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((cdiv(R, BLOCK), C), dtype=torch.float32, device=x.device)
-    _call("quantize_lhs_and_rhs", _ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(a_s), _ptr(qT),
-          _ld(qT), _ptr(s), _stream(stream))
+    _call(_entry("quantize_lhs_and_rhs", fmt), _ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(a_s),
+          _ptr(qT), _ld(qT), _ptr(s), _stream(stream))
     return q, a_s, qT, s
 
 
-def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=None):
+def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=None,
+                            fmt="e4m3fn"):
     """128x128 block quantization of w [N, K]. Returns (q [N, K], qT [K, N] or None, s (Nb, Kb))."""
     N, K = w.shape
     if q is None:
@@ -142,16 +174,16 @@ def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=Non
     if s is None:
         s = torch.empty((cdiv(N, BLOCK), cdiv(K, BLOCK)), dtype=torch.float32, device=w.device)
     ldqT = _ld(qT) if qT is not None else 0
-    _call("quantize_weight_128x128", _ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(qT), ldqT,
-          _ptr(s), _stream(stream))
+    _call(_entry("quantize_weight_128x128", fmt), _ptr(w), N, K, _ld(w), _ptr(q), _ld(q), _ptr(qT),
+          ldqT, _ptr(s), _stream(stream))
     return q, qT, s
 
 
 def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb=None, bs_stride_kb=None, c=None, K=None,
-                       stream=None):
+                       stream=None, fmt="e4m3fn"):
     """C = A B^T, A [M, K] codes with a_s (Kb, M); B [N, K] codes with 128x128 scales.
     ``b_s`` is addressed as b_s[nb * bs_stride_nb + kb * bs_stride_kb]; the default strides treat it
-    as the weight quantizer's (Nb, Kb) tensor."""
+    as the weight quantizer's (Nb, Kb) tensor. ``fmt`` is the element format of both operands."""
     M = a.shape[0]
     N = b.shape[0]
     K = a.shape[1] if K is None else K
@@ -159,20 +191,21 @@ def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb=None, bs_stride_kb=None, c=N
         bs_stride_nb, bs_stride_kb = b_s.stride(0), b_s.stride(1)
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    _call("gemm_1x128_128x128", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
+    _call(_entry("gemm_1x128_128x128", fmt), _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
           bs_stride_nb, bs_stride_kb, _ptr(c), _ld(c), M, N, K, _stream(stream))
     return c
 
 
-def gemm_1x128_128x1(a, a_s, b, b_s, c=None, K=None, stream=None):
-    """C = A B^T, A [M, K] codes with a_s (Kb, M); B [N, K] codes with per-column b_s (Kb, N)."""
+def gemm_1x128_128x1(a, a_s, b, b_s, c=None, K=None, stream=None, fmt="e4m3fn"):
+    """C = A B^T, A [M, K] codes with a_s (Kb, M); B [N, K] codes with per-column b_s (Kb, N).
+    ``fmt`` is the element format of both operands."""
     M = a.shape[0]
     N = b.shape[0]
     K = a.shape[1] if K is None else K
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    _call("gemm_1x128_128x1", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s), _ptr(c),
-          _ld(c), M, N, K, _stream(stream))
+    _call(_entry("gemm_1x128_128x1", fmt), _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
+          _ptr(c), _ld(c), M, N, K, _stream(stream))
     return c
 
 
@@ -182,6 +215,16 @@ def encode_e4m3_f32(x, q=None, stream=None):
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _call("encode_e4m3_f32", _ptr(x), _ptr(q), n, _stream(stream))
+    return q
+
+
+def encode_e4m3fnuz_f32(x, q=None, stream=None):
+    """The quantizers' float8_e4m3fnuz conversion (RNE) of fp32 values with
+    |x| <= 240 (1 + 2^-21)."""
+    n = x.numel()
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _call("encode_e4m3fnuz_f32", _ptr(x), _ptr(q), n, _stream(stream))
     return q
 
 

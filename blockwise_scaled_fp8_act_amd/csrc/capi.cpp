@@ -57,6 +57,99 @@ int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, i
     return BSFP8_OK;
 }
 
+int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
+                      float* a_s, bool fnuz, void* stream) {
+    if (M < 0 || K < 0) return BSFP8_EINVAL;
+    if (M == 0 || K == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr || a_s == nullptr) return BSFP8_EINVAL;
+    if (ldx < K || ldq < K) return BSFP8_EINVAL;
+    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_lhs(static_cast<const uint16_t*>(x), M, K, ldx,
+                                             static_cast<uint8_t*>(q), ldq, a_s, fnuz,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int quantize_rhs_impl(const void* x, int64_t K, int64_t N, int64_t ldx, void* qT, int64_t ldqT,
+                      float* s, bool fnuz, void* stream) {
+    if (K < 0 || N < 0) return BSFP8_EINVAL;
+    if (K == 0 || N == 0) return BSFP8_OK;
+    if (x == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldx < N || ldqT < K) return BSFP8_EINVAL;
+    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_rhs(static_cast<const uint16_t*>(x), K, N, ldx,
+                                             static_cast<uint8_t*>(qT), ldqT, s, fnuz,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int quantize_weight_impl(const void* w, int64_t N, int64_t K, int64_t ldw, void* q, int64_t ldq,
+                         void* qT, int64_t ldqT, float* s, bool fnuz, void* stream) {
+    if (N < 0 || K < 0) return BSFP8_EINVAL;
+    if (N == 0 || K == 0) return BSFP8_OK;
+    if (w == nullptr || q == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldw < K || ldq < K || (qT != nullptr && ldqT < N)) return BSFP8_EINVAL;
+    if (cdiv(N, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_weight(static_cast<const uint16_t*>(w), N, K, ldw,
+                                                static_cast<uint8_t*>(q), ldq,
+                                                static_cast<uint8_t*>(qT), ldqT, s, fnuz,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int quantize_dual_impl(const void* x, int64_t R, int64_t C, int64_t ldx, void* q, int64_t ldq,
+                       float* a_s, void* qT, int64_t ldqT, float* s, bool fnuz, void* stream) {
+    if (R < 0 || C < 0) return BSFP8_EINVAL;
+    if (R == 0 || C == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr || a_s == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
+    if (ldx < C || ldq < C || ldqT < R) return BSFP8_EINVAL;
+    if (cdiv(R, kGroupEdge) > kMaxGridY || cdiv(C, kGroupEdge) > 0x7FFFFFFFLL) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_dual(static_cast<const uint16_t*>(x), R, C, ldx,
+                                              static_cast<uint8_t*>(q), ldq, a_s,
+                                              static_cast<uint8_t*>(qT), ldqT, s, fnuz,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int gemm_128x128_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                      const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz, void* stream) {
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (bs_stride_nb < 0 || bs_stride_kb < 0) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
+    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
+                                     static_cast<const uint8_t*>(b), ldb, bs,
+                                     static_cast<uint16_t*>(c), ldc, M, N, K, fnuz,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int gemm_128x1_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                    const float* b_s, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                    bool fnuz, void* stream) {
+    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
+    if (M == 0 || N == 0) return BSFP8_OK;
+    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    bsfp8::BScale bs{b_s, 0, 0, 1};
+    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
+                                     static_cast<const uint8_t*>(b), ldb, bs,
+                                     static_cast<uint16_t*>(c), ldc, M, N, K, fnuz,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int encode_impl(const float* x, void* q, int64_t n, bool fnuz, void* stream) {
+    if (n < 0) return BSFP8_EINVAL;
+    if (n == 0) return BSFP8_OK;
+    if (x == nullptr || q == nullptr) return BSFP8_EINVAL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 3) != 0) return BSFP8_EALIGN;
+    if ((n + 1023) / 1024 > 0x7FFFFFFFLL) return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_encode(x, static_cast<uint8_t*>(q), n, fnuz,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,84 +167,70 @@ const char* bsfp8_status_string(int status) {
 
 int quantize_lhs(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
                  float* a_s, void* stream) {
-    if (M < 0 || K < 0) return BSFP8_EINVAL;
-    if (M == 0 || K == 0) return BSFP8_OK;
-    if (x == nullptr || q == nullptr || a_s == nullptr) return BSFP8_EINVAL;
-    if (ldx < K || ldq < K) return BSFP8_EINVAL;
-    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    return finish(bsfp8::launch_quantize_lhs(static_cast<const uint16_t*>(x), M, K, ldx,
-                                             static_cast<uint8_t*>(q), ldq, a_s,
-                                             static_cast<hipStream_t>(stream)));
+    return quantize_lhs_impl(x, M, K, ldx, q, ldq, a_s, false, stream);
+}
+
+int quantize_lhs_fnuz(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
+                      float* a_s, void* stream) {
+    return quantize_lhs_impl(x, M, K, ldx, q, ldq, a_s, true, stream);
 }
 
 int quantize_rhs(const void* x, int64_t K, int64_t N, int64_t ldx, void* qT, int64_t ldqT,
                  float* s, void* stream) {
-    if (K < 0 || N < 0) return BSFP8_EINVAL;
-    if (K == 0 || N == 0) return BSFP8_OK;
-    if (x == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
-    if (ldx < N || ldqT < K) return BSFP8_EINVAL;
-    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    return finish(bsfp8::launch_quantize_rhs(static_cast<const uint16_t*>(x), K, N, ldx,
-                                             static_cast<uint8_t*>(qT), ldqT, s,
-                                             static_cast<hipStream_t>(stream)));
+    return quantize_rhs_impl(x, K, N, ldx, qT, ldqT, s, false, stream);
+}
+
+int quantize_rhs_fnuz(const void* x, int64_t K, int64_t N, int64_t ldx, void* qT, int64_t ldqT,
+                      float* s, void* stream) {
+    return quantize_rhs_impl(x, K, N, ldx, qT, ldqT, s, true, stream);
 }
 
 int quantize_weight_128x128(const void* w, int64_t N, int64_t K, int64_t ldw, void* q,
                             int64_t ldq, void* qT, int64_t ldqT, float* s, void* stream) {
-    if (N < 0 || K < 0) return BSFP8_EINVAL;
-    if (N == 0 || K == 0) return BSFP8_OK;
-    if (w == nullptr || q == nullptr || s == nullptr) return BSFP8_EINVAL;
-    if (ldw < K || ldq < K || (qT != nullptr && ldqT < N)) return BSFP8_EINVAL;
-    if (cdiv(N, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    return finish(bsfp8::launch_quantize_weight(static_cast<const uint16_t*>(w), N, K, ldw,
-                                                static_cast<uint8_t*>(q), ldq,
-                                                static_cast<uint8_t*>(qT), ldqT, s,
-                                                static_cast<hipStream_t>(stream)));
+    return quantize_weight_impl(w, N, K, ldw, q, ldq, qT, ldqT, s, false, stream);
+}
+
+int quantize_weight_128x128_fnuz(const void* w, int64_t N, int64_t K, int64_t ldw, void* q,
+                                 int64_t ldq, void* qT, int64_t ldqT, float* s, void* stream) {
+    return quantize_weight_impl(w, N, K, ldw, q, ldq, qT, ldqT, s, true, stream);
 }
 
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                        const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
                        int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
-    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
-    if (M == 0 || N == 0) return BSFP8_OK;
-    if (bs_stride_nb < 0 || bs_stride_kb < 0) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
-    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
-                                     static_cast<const uint8_t*>(b), ldb, bs,
-                                     static_cast<uint16_t*>(c), ldc, M, N, K,
-                                     static_cast<hipStream_t>(stream)));
+    return gemm_128x128_impl(a, lda, a_s, b, ldb, b_s, bs_stride_nb, bs_stride_kb, c, ldc, M, N, K,
+                             false, stream);
+}
+
+int gemm_1x128_128x128_fnuz(const void* a, int64_t lda, const float* a_s, const void* b,
+                            int64_t ldb, const float* b_s, int64_t bs_stride_nb,
+                            int64_t bs_stride_kb, void* c, int64_t ldc, int64_t M, int64_t N,
+                            int64_t K, void* stream) {
+    return gemm_128x128_impl(a, lda, a_s, b, ldb, b_s, bs_stride_nb, bs_stride_kb, c, ldc, M, N, K,
+                             true, stream);
 }
 
 int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                      const float* b_s, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                      void* stream) {
-    if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
-    if (M == 0 || N == 0) return BSFP8_OK;
-    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    bsfp8::BScale bs{b_s, 0, 0, 1};
-    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
-                                     static_cast<const uint8_t*>(b), ldb, bs,
-                                     static_cast<uint16_t*>(c), ldc, M, N, K,
-                                     static_cast<hipStream_t>(stream)));
+    return gemm_128x1_impl(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K, false, stream);
+}
+
+int gemm_1x128_128x1_fnuz(const void* a, int64_t lda, const float* a_s, const void* b,
+                          int64_t ldb, const float* b_s, void* c, int64_t ldc, int64_t M,
+                          int64_t N, int64_t K, void* stream) {
+    return gemm_128x1_impl(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K, true, stream);
 }
 
 int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx, void* q, int64_t ldq,
                          float* a_s, void* qT, int64_t ldqT, float* s, void* stream) {
-    if (R < 0 || C < 0) return BSFP8_EINVAL;
-    if (R == 0 || C == 0) return BSFP8_OK;
-    if (x == nullptr || q == nullptr || a_s == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
-    if (ldx < C || ldq < C || ldqT < R) return BSFP8_EINVAL;
-    if (cdiv(R, kGroupEdge) > kMaxGridY || cdiv(C, kGroupEdge) > 0x7FFFFFFFLL) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    return finish(bsfp8::launch_quantize_dual(static_cast<const uint16_t*>(x), R, C, ldx,
-                                              static_cast<uint8_t*>(q), ldq, a_s,
-                                              static_cast<uint8_t*>(qT), ldqT, s,
-                                              static_cast<hipStream_t>(stream)));
+    return quantize_dual_impl(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s, false, stream);
+}
+
+int quantize_lhs_and_rhs_fnuz(const void* x, int64_t R, int64_t C, int64_t ldx, void* q,
+                              int64_t ldq, float* a_s, void* qT, int64_t ldqT, float* s,
+                              void* stream) {
+    return quantize_dual_impl(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s, true, stream);
 }
 
 int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s, const void* b,
@@ -192,14 +271,11 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const
 }
 
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream) {
-    if (n < 0) return BSFP8_EINVAL;
-    if (n == 0) return BSFP8_OK;
-    if (x == nullptr || q == nullptr) return BSFP8_EINVAL;
-    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 3) != 0) return BSFP8_EALIGN;
-    if ((n + 1023) / 1024 > 0x7FFFFFFFLL) return BSFP8_EINVAL;
-    if (int rc = check_device()) return rc;
-    return finish(bsfp8::launch_encode(x, static_cast<uint8_t*>(q), n,
-                                       static_cast<hipStream_t>(stream)));
+    return encode_impl(x, q, n, false, stream);
+}
+
+int encode_e4m3fnuz_f32(const float* x, void* q, int64_t n, void* stream) {
+    return encode_impl(x, q, n, true, stream);
 }
 
 }  // extern "C"

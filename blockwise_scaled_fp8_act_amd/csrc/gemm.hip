@@ -19,6 +19,15 @@
 //     columns < N.
 // The fast kernel (namespace fast) serves K % 128 == 0; the general kernel also handles a ragged
 // last K-block (bytes past K are zeroed).
+//
+// float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240) run on the
+// general kernel: gfx950's FP8 matrix instructions read e4m3fn, and no power-of-two rescaling
+// maps every fnuz value onto an e4m3fn value (fnuz spans 2^-10 .. 240, e4m3fn 2^-9 .. 448, and
+// 2 x 240 = 480 is not an e4m3fn value). Each fnuz code is instead widened exactly to f16 in
+// registers (its 7 magnitude bits placed under the f16 exponent field, then a multiply by 2^7
+// rebiases the exponent and normalises the subnormals) and a K-block is four
+// v_mfma_f32_16x16x32_f16 instead of one FP8 instruction -- products of two 4-significant-bit
+// values are exact in fp32 either way, so the per-K-block partials equal the fn path's arithmetic.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -29,6 +38,9 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef short s2v __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256;      // workgroup rows (M)
 constexpr int kBN = 128;      // workgroup columns (N)
@@ -45,6 +57,44 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
     // Format selectors 0/0 = float8_e4m3fn for both operands; scale operands 0 select the
     // unscaled instruction.
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Two float8_e4m3fnuz codes (bytes 0,1 of w for HALF 0, bytes 2,3 for HALF 1) as two exact f16
+// values. Each code c = s eeee mmm is moved to bits 15..8 of its 16-bit half; an arithmetic
+// shift by one leaves s in bit 15 (and a copy in bit 14, cleared next), e in the low four bits of
+// the f16 exponent field and m at the top of the f16 mantissa. That f16 is
+// (1 + m/8) 2^(e - 15), or (m/8) 2^-14 for e = 0, i.e. the fnuz value times 2^-7; the multiply by
+// 2^7 is exact and normalises the subnormals. Every fnuz value (2^-10 .. 240) is a normal f16.
+template <int HALF>
+__device__ __forceinline__ uint32_t fnuz2_to_f16x2(uint32_t w) {
+    const uint32_t p = __builtin_amdgcn_perm(w, w, HALF ? 0x030C020Cu : 0x010C000Cu);
+    s2v v = __builtin_bit_cast(s2v, p);
+    v = v >> 1;
+    const uint32_t u = __builtin_bit_cast(uint32_t, v) & 0xBFFFBFFFu;
+    const h2v h = __builtin_bit_cast(h2v, u) * h2v{static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f)};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// A 32-code FP8 fragment (the lane's operand of one 16x16x128 instruction) as the operands of four
+// 16x16x32 f16 instructions: instruction q takes the lane's codes 8q .. 8q + 7. The lane-to-k
+// assignment is the same for both operands, so the four instructions together sum over exactly the
+// K-block's 128 products.
+__device__ __forceinline__ void fnuz_frag_to_f16(const v8i& f, h8v (&out)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = static_cast<uint32_t>(f[2 * q]);
+        const uint32_t w1 = static_cast<uint32_t>(f[2 * q + 1]);
+        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+        const u4 h = {fnuz2_to_f16x2<0>(w0), fnuz2_to_f16x2<1>(w0), fnuz2_to_f16x2<0>(w1), fnuz2_to_f16x2<1>(w1)};
+        out[q] = __builtin_bit_cast(h8v, h);
+    }
+}
+
+__device__ __forceinline__ v4f mfma_f16_kblock(const h8v (&b)[4], const h8v (&a)[4]) {
+    v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[q], a[q], c, 0, 0, 0);
+    return c;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -203,7 +253,7 @@ __device__ __forceinline__ void load_scales(float (&as)[kMSub], u32x4 (&bsv)[kNS
     }
 }
 
-template <bool PER_COL>
+template <bool PER_COL, bool FNUZ>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s,
@@ -288,15 +338,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             constexpr int nxt = cur ^ 1;
             const bool more = kb + 1 < Kb;
             const bool next_full = kb + 1 < Kfull;
-            if (more) {
-                if (next_full) {
-                    dma_b(sB[nxt], op, kb + 1, wave);
-                    load_a<true>(af[nxt], op, kb + 1, K, lg);
-                } else {
-                    load_a<false>(af[nxt], op, kb + 1, K, lg);
+            auto issue_next = [&]() {
+                if (more) {
+                    if (next_full) {
+                        dma_b(sB[nxt], op, kb + 1, wave);
+                        load_a<true>(af[nxt], op, kb + 1, K, lg);
+                    } else {
+                        load_a<false>(af[nxt], op, kb + 1, K, lg);
+                    }
+                    load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, M, N, tn);
                 }
-                load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, M, N, tn);
-            }
+            };
+            // fnuz: the next block's loads are issued once this block's A codes are all widened
+            // (half way through, see below), so the two never hold registers together
+            constexpr int kHalf = kMSub / 2;
+            h8v ac[FNUZ ? kHalf : 1][4];
+            if constexpr (!FNUZ) issue_next();
             // this K-block: partial products of every 16x16 subtile, rescaled into the totals.
             // Software pipeline over the 8 column subtiles: the B fragment of subtile j+1 is read
             // from LDS while subtile j's four MFMAs run, and subtile j-1's partials are rescaled
@@ -322,17 +379,59 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                     }
                 }
             };
-            v8i bf[2];
-            v4f pp[2][kMSub];
-            bf[0] = read_bf(0);
+            if constexpr (FNUZ) {
+                // A widened to f16 takes twice the registers of its codes, so the wave's 64 rows are
+                // done as two halves of 32: per half, the two A fragments are widened once and each
+                // B fragment is read and widened once; one B fragment and one set of partials are
+                // live at a time (the other wave of the SIMD covers the latencies).
 #pragma unroll
-            for (int j = 0; j < kNSub; ++j) {
-                if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
+                for (int h = 0; h < 2; ++h) {
+                    if (h == 1) {
+                        // the B fragments are read again rather than kept widened from the first
+                        // half (the clobbers keep the compiler from merging the two reads), and the
+                        // second half's A fragments pass through an empty asm here so that their
+                        // widening cannot be hoisted into the first half
+                        asm volatile("" ::: "memory");
 #pragma unroll
-                for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[cur][i]);
-                if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
+                        for (int i = kHalf; i < kMSub; ++i)
+#pragma unroll
+                            for (int d = 0; d < 8; ++d) asm volatile("" : "+v"(af[cur][i][d]));
+                    }
+#pragma unroll
+                    for (int i = 0; i < kHalf; ++i) fnuz_frag_to_f16(af[cur][h * kHalf + i], ac[i]);
+                    if (h == 1) issue_next();
+#pragma unroll
+                    for (int j = 0; j < kNSub; ++j) {
+                        // one B fragment in flight at a time (a memory clobber stops the compiler
+                        // from hoisting the next fragment's read above this one's use)
+                        if (j > 0) asm volatile("" ::: "memory");
+                        h8v bc[4];
+                        fnuz_frag_to_f16(read_bf(j), bc);
+#pragma unroll
+                        for (int i = 0; i < kHalf; ++i) {
+                            const v4f p = mfma_f16_kblock(bc, ac[i]);
+                            const int ii = h * kHalf + i;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float fe = PER_COL ? f[ii] * __uint_as_float(bsv[cur][j][e]) : f[ii];
+                                acc[ii][j][e] = fmaf(p[e], fe, acc[ii][j][e]);
+                            }
+                        }
+                    }
+                }
+            } else {
+                v8i bf[2];
+                v4f pp[2][kMSub];
+                bf[0] = read_bf(0);
+#pragma unroll
+                for (int j = 0; j < kNSub; ++j) {
+                    if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
+#pragma unroll
+                    for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[cur][i]);
+                    if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
+                }
+                rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
             }
-            rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
             if (more && !next_full) {  // ragged last K-block: masked register path
                 u32x4 bst[2];
                 load_b<false>(bst, op, kb + 1, K, tid);
@@ -735,14 +834,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
-                       int64_t K, hipStream_t stream) {
+                       int64_t K, bool fnuz, hipStream_t stream) {
     // vector stores: 8 bytes per lane in the general kernel, 16 in the fast one
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
     const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
     // Fast path: whole K-blocks; per-column scales read 4 columns at a time; 128x128 scales of a
     // tile's column staged in LDS (at most kMaxKbFast K-blocks).
     const bool fast_scales = bs.per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
-    if (K % kGroup == 0 && fast_scales) {
+    if (!fnuz && K % kGroup == 0 && fast_scales) {
         const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
         if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
@@ -761,13 +860,20 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
     const int64_t nt = (N + kBN - 1) / kBN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(mt * nt));
-    if (bs.per_column)
-        gemm_kernel<true><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc,
-                                                         M, N, K, (int)mt, (int)nt, c_vec);
-    else
-        gemm_kernel<false><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb,
-                                                          bs.stride_kb, c, ldc, M, N, K, (int)mt,
-                                                          (int)nt, c_vec);
+    const int64_t nb_stride = bs.per_column ? 0 : bs.stride_nb;
+    const int64_t kb_stride = bs.per_column ? 0 : bs.stride_kb;
+#define BSFP8_GG(PC, FZ)                                                                          \
+    gemm_kernel<PC, FZ><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, nb_stride,    \
+                                                       kb_stride, c, ldc, M, N, K, (int)mt,       \
+                                                       (int)nt, c_vec)
+    if (bs.per_column) {
+        if (fnuz) BSFP8_GG(true, true);
+        else BSFP8_GG(true, false);
+    } else {
+        if (fnuz) BSFP8_GG(false, true);
+        else BSFP8_GG(false, false);
+    }
+#undef BSFP8_GG
     return hipGetLastError();
 }
 

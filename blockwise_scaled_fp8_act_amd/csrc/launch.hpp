@@ -6,17 +6,18 @@
 
 namespace bsfp8 {
 
+// fnuz: float8_e4m3fnuz codes (FP8_MAX 240) instead of float8_e4m3fn (FP8_MAX 448).
 hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                               int64_t ldq, float* a_s, hipStream_t stream);
+                               int64_t ldq, float* a_s, bool fnuz, hipStream_t stream);
 hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
                                 int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
-                                hipStream_t stream);
+                                bool fnuz, hipStream_t stream);
 hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
-                               int64_t ldqT, float* s, hipStream_t stream);
+                               int64_t ldqT, float* s, bool fnuz, hipStream_t stream);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
-                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool fnuz,
                                   hipStream_t stream);
-hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
+hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, bool fnuz, hipStream_t stream);
 
 // b-scale addressing of the GEMM: kind 0 = one scale per (K-block, 128-column block) at
 // b_s[nb * stride_nb + kb * stride_kb]; kind 1 = one scale per (K-block, column) at b_s[kb * N + n].
@@ -27,9 +28,10 @@ struct BScale {
     int per_column;
 };
 
+// fnuz: both operands hold float8_e4m3fnuz codes (general kernel, f16 matrix instructions).
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
-                       int64_t K, hipStream_t stream);
+                       int64_t K, bool fnuz, hipStream_t stream);
 
 // Expert-grouped GEMMs (fast path only: K % 128 == 0; 128x128 scales: at most 512 K-blocks;
 // per-column scales: N % 4 == 0). offsets: E + 1 device int64 boundaries.

@@ -1,4 +1,4 @@
-// gfx950 group quantizers: bf16 -> float8_e4m3fn codes + fp32 scales.
+// gfx950 group quantizers: bf16 -> float8_e4m3fn (or float8_e4m3fnuz) codes + fp32 scales.
 //
 //   quantize_lhs             1x128 groups along K (act_quant_lhs), scales column-major [M, Kb]
 //   quantize_rhs             128x1 groups down each column (act_quant_rhs), codes written transposed
@@ -7,6 +7,9 @@
 // Operations as listed in the quantization-correctness table of "Enable blockwise FP8 dense
 // training kernels on ROCm" (block_size 128); the column-major scale layout and the rule that a
 // scale store of a row >= M must be dropped come from that page's root-cause comment.
+//
+// Every kernel is instantiated for both element formats (FNUZ = false: e4m3fn, FP8_MAX 448;
+// true: e4m3fnuz, FP8_MAX 240); only the scale pair and the final code conversion differ.
 //
 // All three are HBM-bound: every input byte is read once with 16-byte loads, every output byte is
 // written once, 16-lane (1x128) or LDS (128x1, 128x128) max reductions run on data already in
@@ -93,7 +96,7 @@ constexpr int kLhsRowsPerTeam = 4;
 constexpr int kLhsRows = 16 * kLhsRowsPerTeam;
 constexpr int kLhsBlocks = 2;
 
-template <bool VEC_X, bool VEC_Q>
+template <bool FNUZ, bool VEC_X, bool VEC_Q>
 __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s) {
@@ -122,9 +125,9 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[r][j]));
         am = umax_row16(am);
-        const GroupScale g = group_scale(__uint_as_float(am));
-        const uint32_t w0 = encode4_in_range(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
-        const uint32_t w1 = encode4_in_range(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
+        const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
+        const uint32_t w0 = encode4_in_range<FNUZ>(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
+        const uint32_t w1 = encode4_in_range<FNUZ>(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
         const int64_t m = mbase + r * 16 + team;
         if (m < M) {  // rows >= M store neither codes nor scales
             store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
 // written out as 128 contiguous bytes per output row.
 constexpr int kRhsCols = 64;
 
-template <bool VEC_X, bool VEC_Q>
+template <bool FNUZ, bool VEC_X, bool VEC_Q>
 __global__ __launch_bounds__(256) void quantize_rhs_kernel(
     const uint16_t* __restrict__ x, int64_t K, int64_t N, int64_t ldx,
     uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ s) {
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
         uint32_t am = 0;
 #pragma unroll 8
         for (int r = 0; r < 32; ++r) am = max(am, red[r][t]);
-        const GroupScale g = group_scale(__uint_as_float(am));
+        const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
         mult[t] = g.m;
         if (n0 + t < N) s[kb * N + n0 + t] = g.s;
     }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float mj = mult[cg * 8 + j];
-        const uint32_t w = encode4_in_range(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
+        const uint32_t w = encode4_in_range<FNUZ>(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
         const int cl = cg * 8 + j;
         const int chunk = (rq >> 2) ^ (cl >> 3);
         tw[cl * 32 + chunk * 4 + (rq & 3)] = w;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
 // 128x128 blocks: one workgroup per block; thread t holds rows 8*(t/16) .. +8 x columns
 // 8*(t%16) .. +8 (64 values in registers, read once). The block max is a wave reduction plus a
 // 4-entry LDS combine. The optional transposed copy goes through a swizzled LDS tile.
-template <bool VEC_W, bool VEC_Q, bool VEC_QT>
+template <bool FNUZ, bool VEC_W, bool VEC_Q, bool VEC_QT>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT,
@@ -248,14 +251,14 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
     if ((t & 63) == 0) wmax[t >> 6] = am;
     __syncthreads();
     am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    const GroupScale g = group_scale(__uint_as_float(am));
+    const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
     if (t == 0) s[nb * Kb + kb] = g.s;
 
     uint32_t code[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        code[i][0] = encode4_in_range(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
-        code[i][1] = encode4_in_range(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
+        code[i][0] = encode4_in_range<FNUZ>(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
+        code[i][1] = encode4_in_range<FNUZ>(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
         const int64_t n = n0 + rg * 8 + i;
         if (n < N) store8<VEC_Q>(q + n * ldq, c, K, code[i][0], code[i][1]);
     }
@@ -312,7 +315,7 @@ __device__ __forceinline__ float bcast_row16(float v, int l) {
 // Thread t holds rows 8 (t / 16) .. + 8 x columns 8 (t % 16) .. + 8; the 16 lanes of a DPP row
 // share the rows, so a row maximum is one 16-lane DPP reduction; column maxima combine the 16 row
 // groups through LDS. The transposed codes go through a swizzled LDS tile as in the weight kernel.
-template <bool VEC_X, bool VEC_Q, bool VEC_QT>
+template <bool FNUZ, bool VEC_X, bool VEC_Q, bool VEC_QT>
 __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s,
@@ -374,13 +377,13 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
     uint32_t mine = rmax[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mine = (cg & 7) == i ? rmax[i] : mine;
-    const GroupScale gm = group_scale(__uint_as_float(mine));
+    const GroupScale gm = group_scale<FNUZ>(__uint_as_float(mine));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float m = bcast_row16(gm.m, i);
         const float sc = bcast_row16(gm.s, i);
-        const uint32_t w0 = encode4_in_range(val(i, 0) * m, val(i, 1) * m, val(i, 2) * m, val(i, 3) * m);
-        const uint32_t w1 = encode4_in_range(val(i, 4) * m, val(i, 5) * m, val(i, 6) * m, val(i, 7) * m);
+        const uint32_t w0 = encode4_in_range<FNUZ>(val(i, 0) * m, val(i, 1) * m, val(i, 2) * m, val(i, 3) * m);
+        const uint32_t w1 = encode4_in_range<FNUZ>(val(i, 4) * m, val(i, 5) * m, val(i, 6) * m, val(i, 7) * m);
         const int64_t r = r0 + rg * 8 + i;
         if (r < R) {  // rows >= R store neither codes nor scales
             store8<VEC_Q>(q + r * ldq, c, C, w0, w1);
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
         uint32_t am = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) am = max(am, red[r][t]);
-        const GroupScale g = group_scale(__uint_as_float(am));
+        const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
         colm[t] = g.m;
         if (c0 + t < C) s[rb * C + c0 + t] = g.s;
     }
@@ -409,8 +412,8 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float mj = colm[cg * 8 + j];
-        const uint32_t lo = encode4_in_range(val(0, j) * mj, val(1, j) * mj, val(2, j) * mj, val(3, j) * mj);
-        const uint32_t hi = encode4_in_range(val(4, j) * mj, val(5, j) * mj, val(6, j) * mj, val(7, j) * mj);
+        const uint32_t lo = encode4_in_range<FNUZ>(val(0, j) * mj, val(1, j) * mj, val(2, j) * mj, val(3, j) * mj);
+        const uint32_t hi = encode4_in_range<FNUZ>(val(4, j) * mj, val(5, j) * mj, val(6, j) * mj, val(7, j) * mj);
         const int cl = cg * 8 + j;
         const int chunk = (rg >> 1) ^ (cg & 7);
         *reinterpret_cast<uint2*>(tw + cl * 32 + chunk * 4 + (rg & 1) * 2) = make_uint2(lo, hi);
@@ -431,60 +434,69 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// The element conversion on its own, for exhaustive checks: e4m3fn codes of arbitrary fp32 values
+// (clamped to +-448), or the quantizers' float8_e4m3fnuz conversion (encode4_in_range<true> of
+// twice the value) of values within the range a group multiplier produces.
+template <bool FNUZ>
+__device__ __forceinline__ uint32_t encode_one4(float a, float b, float c, float d) {
+    return FNUZ ? encode4_in_range<true>(2.0f * a, 2.0f * b, 2.0f * c, 2.0f * d) : encode4(a, b, c, d);
+}
+
+template <bool FNUZ>
 __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x,
                                                      uint8_t* __restrict__ q, int64_t n) {
     const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (i0 + 4 <= n) {
         const float4 v = *reinterpret_cast<const float4*>(x + i0);
-        const uint32_t w = encode4(v.x, v.y, v.z, v.w);
+        const uint32_t w = encode_one4<FNUZ>(v.x, v.y, v.z, v.w);
         *reinterpret_cast<uint32_t*>(q + i0) = w;
     } else {
-        for (int64_t i = i0; i < n; ++i) q[i] = static_cast<uint8_t>(encode4(x[i], 0.f, 0.f, 0.f) & 0xFF);
+        for (int64_t i = i0; i < n; ++i)
+            q[i] = static_cast<uint8_t>(encode_one4<FNUZ>(x[i], 0.f, 0.f, 0.f) & 0xFF);
     }
 }
 
 bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                               int64_t ldq, float* a_s, hipStream_t stream) {
+template <bool FNUZ>
+hipError_t quantize_lhs_impl(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                             int64_t ldq, float* a_s, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const dim3 grid(static_cast<unsigned>((M + kLhsRows - 1) / kLhsRows),
                     static_cast<unsigned>((Kb + kLhsBlocks - 1) / kLhsBlocks));
     const bool vx = aligned(x, 16) && (ldx % 8 == 0);
     const bool vq = aligned(q, 8) && (ldq % 8 == 0);
-    if (vx && vq)
-        quantize_lhs_kernel<true, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
-    else if (vx)
-        quantize_lhs_kernel<true, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
-    else if (vq)
-        quantize_lhs_kernel<false, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
-    else
-        quantize_lhs_kernel<false, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s);
+#define BSFP8_QL(A, B) \
+    quantize_lhs_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s)
+    if (vx && vq) BSFP8_QL(true, true);
+    else if (vx) BSFP8_QL(true, false);
+    else if (vq) BSFP8_QL(false, true);
+    else BSFP8_QL(false, false);
+#undef BSFP8_QL
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
-                               int64_t ldqT, float* s, hipStream_t stream) {
+template <bool FNUZ>
+hipError_t quantize_rhs_impl(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
+                             int64_t ldqT, float* s, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const dim3 grid(static_cast<unsigned>((N + kRhsCols - 1) / kRhsCols), static_cast<unsigned>(Kb));
     const bool vx = aligned(x, 16) && (ldx % 8 == 0);
     const bool vq = aligned(qT, 16) && (ldqT % 16 == 0);
-    if (vx && vq)
-        quantize_rhs_kernel<true, true><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
-    else if (vx)
-        quantize_rhs_kernel<true, false><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
-    else if (vq)
-        quantize_rhs_kernel<false, true><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
-    else
-        quantize_rhs_kernel<false, false><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s);
+#define BSFP8_QR(A, B) \
+    quantize_rhs_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s)
+    if (vx && vq) BSFP8_QR(true, true);
+    else if (vx) BSFP8_QR(true, false);
+    else if (vq) BSFP8_QR(false, true);
+    else BSFP8_QR(false, false);
+#undef BSFP8_QR
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
-                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
-                                  hipStream_t stream) {
+template <bool FNUZ>
+hipError_t quantize_weight_impl(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
+                                hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const int64_t Nb = (N + kGroup - 1) / kGroup;
     const dim3 grid(static_cast<unsigned>(Kb), static_cast<unsigned>(Nb));
@@ -492,7 +504,7 @@ hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64
     const bool vq = aligned(q, 8) && (ldq % 8 == 0);
     const bool vt = qT != nullptr && aligned(qT, 16) && (ldqT % 16 == 0);
 #define BSFP8_QW(A, B, C) \
-    quantize_weight_kernel<A, B, C><<<grid, 256, 0, stream>>>(w, N, K, ldw, q, ldq, qT, ldqT, s, Kb)
+    quantize_weight_kernel<FNUZ, A, B, C><<<grid, 256, 0, stream>>>(w, N, K, ldw, q, ldq, qT, ldqT, s, Kb)
     if (vw && vq && vt) BSFP8_QW(true, true, true);
     else if (vw && vq) BSFP8_QW(true, true, false);
     else if (vw && vt) BSFP8_QW(true, false, true);
@@ -505,15 +517,16 @@ hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
-                                int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
-                                hipStream_t stream) {
+template <bool FNUZ>
+hipError_t quantize_dual_impl(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
+                              int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
+                              hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((C + kGroup - 1) / kGroup), static_cast<unsigned>((R + kGroup - 1) / kGroup));
     const bool vx = aligned(x, 16) && (ldx % 8 == 0);
     const bool vq = aligned(q, 8) && (ldq % 8 == 0);
     const bool vt = aligned(qT, 16) && (ldqT % 16 == 0);
 #define BSFP8_QD(A, B, D) \
-    quantize_dual_kernel<A, B, D><<<grid, 256, 0, stream>>>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s)
+    quantize_dual_kernel<FNUZ, A, B, D><<<grid, 256, 0, stream>>>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s)
     if (vx && vq && vt) BSFP8_QD(true, true, true);
     else if (vx && vq) BSFP8_QD(true, true, false);
     else if (vx && vt) BSFP8_QD(true, false, true);
@@ -526,11 +539,42 @@ hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t
     return hipGetLastError();
 }
 
-hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                               int64_t ldq, float* a_s, bool fnuz, hipStream_t stream) {
+    return fnuz ? quantize_lhs_impl<true>(x, M, K, ldx, q, ldq, a_s, stream)
+                : quantize_lhs_impl<false>(x, M, K, ldx, q, ldq, a_s, stream);
+}
+
+hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
+                               int64_t ldqT, float* s, bool fnuz, hipStream_t stream) {
+    return fnuz ? quantize_rhs_impl<true>(x, K, N, ldx, qT, ldqT, s, stream)
+                : quantize_rhs_impl<false>(x, K, N, ldx, qT, ldqT, s, stream);
+}
+
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                  int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool fnuz,
+                                  hipStream_t stream) {
+    return fnuz ? quantize_weight_impl<true>(w, N, K, ldw, q, ldq, qT, ldqT, s, stream)
+                : quantize_weight_impl<false>(w, N, K, ldw, q, ldq, qT, ldqT, s, stream);
+}
+
+hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
+                                int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
+                                bool fnuz, hipStream_t stream) {
+    return fnuz ? quantize_dual_impl<true>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s, stream)
+                : quantize_dual_impl<false>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s, stream);
+}
+
+hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, bool fnuz, hipStream_t stream) {
     if (!aligned(x, 16) || !aligned(q, 4)) return hipErrorInvalidValue;
     const int64_t threads = (n + 3) / 4;
     const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
-    encode_kernel<<<grid, 256, 0, stream>>>(x, q, n);
+    if (fnuz)
+        encode_kernel<true><<<grid, 256, 0, stream>>>(x, q, n);
+    else
+        encode_kernel<false><<<grid, 256, 0, stream>>>(x, q, n);
     return hipGetLastError();
 }
 

@@ -14,7 +14,9 @@ quantization-correctness table lists which quantizer feeds which GEMM):
                                                           gemm_1x128_128x1
 
 X and dY each feed two GEMMs, so each is quantized once by quantize_lhs_and_rhs (both groupings in
-one pass). Every step runs in the library's kernels; this module only allocates outputs, orders the
+one pass). The FP8 element format is float8_e4m3fn by default; ``fmt="e4m3fnuz"`` (or
+torch.float8_e4m3fnuz) runs every quantizer and GEMM in float8_e4m3fnuz with FP8_MAX 240, the
+dtype choice the same page adds for MI300X. Every step runs in the library's kernels; this module only allocates outputs, orders the
 calls and keeps the forward's quantized operands for the backward (torch.autograd plumbing). All
 tensors are bf16 on the GPU; outputs are bf16.
 """
@@ -32,59 +34,64 @@ def _codes(rows: int, cols: int, device) -> torch.Tensor:
     return torch.empty((rows, ld), dtype=torch.uint8, device=device)[:, :cols]
 
 
-def _quantize_act(t: torch.Tensor):
+def _quantize_act(t: torch.Tensor, fmt: str):
     R, C = t.shape
-    return _b.quantize_lhs_and_rhs(t, q=_codes(R, C, t.device), qT=_codes(C, R, t.device))
+    return _b.quantize_lhs_and_rhs(t, q=_codes(R, C, t.device), qT=_codes(C, R, t.device), fmt=fmt)
 
 
 class _BlockwiseFp8LinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, fmt: str) -> torch.Tensor:
         if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
             raise TypeError("blockwise FP8 linear expects bf16 activations and weights")
         if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
             raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}")
         x = x.contiguous()
         w = w.contiguous()
-        qx, sx, qxT, sxT = _quantize_act(x)
+        qx, sx, qxT, sxT = _quantize_act(x, fmt)
         need_dgrad = ctx.needs_input_grad[0]
         d_out, d_in = w.shape
         qw, qwT, sw = _b.quantize_weight_128x128(
             w, q=_codes(d_out, d_in, w.device), qT=_codes(d_in, d_out, w.device) if need_dgrad else None,
-            want_qT=need_dgrad)
-        y = _b.gemm_1x128_128x128(qx, sx, qw, sw)
+            want_qT=need_dgrad, fmt=fmt)
+        y = _b.gemm_1x128_128x128(qx, sx, qw, sw, fmt=fmt)
         ctx.save_for_backward(qxT, sxT, qwT if need_dgrad else None, sw)
         ctx.shapes = (x.shape[0], x.shape[1], w.shape[0])
+        ctx.fmt = fmt
         return y
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
         qxT, sxT, qwT, sw = ctx.saved_tensors
         T, d_in, d_out = ctx.shapes
+        fmt = ctx.fmt
         dy = dy.to(torch.bfloat16).contiguous()
-        qdy, sdy, qdyT, sdyT = _quantize_act(dy)
+        qdy, sdy, qdyT, sdyT = _quantize_act(dy, fmt)
         dx = dw = None
         if ctx.needs_input_grad[0]:
             # B = W^T codes [d_in, d_out]; its (K-block over d_out, N-block over d_in) scale is the
             # weight scale s[kb][nb] of the [d_out/128, d_in/128] tensor: strides (1, d_in blocks)
-            dx = _b.gemm_1x128_128x128(qdy, sdy, qwT, sw, 1, sw.shape[1])
+            dx = _b.gemm_1x128_128x128(qdy, sdy, qwT, sw, 1, sw.shape[1], fmt=fmt)
         if ctx.needs_input_grad[1]:
-            dw = _b.gemm_1x128_128x1(qdyT, sdyT, qxT, sxT)
-        return dx, dw
+            dw = _b.gemm_1x128_128x1(qdyT, sdyT, qxT, sxT, fmt=fmt)
+        return dx, dw, None
 
 
-def blockwise_fp8_linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
-    """Y = X W^T (no bias) with the blockwise-FP8 forward and backward; x [T, in], w [out, in]."""
-    return _BlockwiseFp8LinearFn.apply(x, w)
+def blockwise_fp8_linear(x: torch.Tensor, w: torch.Tensor, fmt="e4m3fn") -> torch.Tensor:
+    """Y = X W^T (no bias) with the blockwise-FP8 forward and backward; x [T, in], w [out, in].
+    ``fmt``: FP8 element format ("e4m3fn", "e4m3fnuz" or the torch float8 dtype)."""
+    return _BlockwiseFp8LinearFn.apply(x, w, _b.fp8_format(fmt))
 
 
 class BlockwiseFp8Linear(torch.nn.Module):
     """nn.Linear replacement (bf16 parameters) whose forward and backward GEMMs run in blockwise
     FP8. A bias, if any, is added in bf16 after the FP8 GEMM."""
 
-    def __init__(self, in_features: int, out_features: int, bias: bool = False, device=None):
+    def __init__(self, in_features: int, out_features: int, bias: bool = False, device=None,
+                 fmt="e4m3fn"):
         super().__init__()
         self.in_features, self.out_features = in_features, out_features
+        self.fmt = _b.fp8_format(fmt)
         self.weight = torch.nn.Parameter(
             torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device))
         self.bias = (torch.nn.Parameter(torch.zeros(out_features, dtype=torch.bfloat16, device=device))
@@ -93,7 +100,7 @@ class BlockwiseFp8Linear(torch.nn.Module):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
-        y = blockwise_fp8_linear(x.reshape(-1, self.in_features), self.weight)
+        y = blockwise_fp8_linear(x.reshape(-1, self.in_features), self.weight, self.fmt)
         if self.bias is not None:
             y = y + self.bias
         return y.reshape(*lead, self.out_features)

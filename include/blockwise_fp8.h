@@ -13,14 +13,18 @@
  * Element formats
  *   bf16   : 16-bit bfloat16 bit patterns (uint16).
  *   fp8    : OCP float8_e4m3fn codes (uint8): bias 7, largest finite 448, no infinities.
+ *            The *_fnuz entry points use float8_e4m3fnuz codes instead (the format of the ROCm
+ *            page's MI300X runs): bias 8, largest finite 0x7F = 240, no infinities, no negative
+ *            zero (0x80 is its only NaN and is never produced). Their FP8_MAX is 240.
  *   scales : IEEE fp32.
  *
  * Quantization of one group g (1x128, 128x1 or 128x128 elements; a group at a tensor edge has only
  * its in-range elements):
  *   amax = max |x| over g;  amax_c = max(amax, 1e-12f);
- *   s    = amax_c / 448      (IEEE fp32 division; the stored, dequantizing scale: x ~= dec(q) * s)
- *   m    = 448 / amax_c      (IEEE fp32 division)
- *   q    = e4m3( clamp(fl32(x * m), -448, 448) )   round to nearest, ties to even; sign kept.
+ *   s    = amax_c / FP8_MAX  (IEEE fp32 division; the stored, dequantizing scale: x ~= dec(q) * s)
+ *   m    = FP8_MAX / amax_c  (IEEE fp32 division)
+ *   q    = enc( clamp(fl32(x * m), -FP8_MAX, FP8_MAX) )   round to nearest, ties to even;
+ *   FP8_MAX = 448 (e4m3fn; the sign of a zero result is kept) or 240 (e4m3fnuz; zero is 0x00).
  *
  * Scaled GEMM (C = A B^T with both operands K-contiguous):
  *   C[m,n] = sum_kb  a_s[m,kb] * b_s(kb,n) * sum_{k in block kb, k < K} dec(A[m,k]) dec(B[n,k])
@@ -206,6 +210,41 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s,
  *   Alignment (else BSFP8_EALIGN): x 16-byte aligned, q 4-byte aligned.
  */
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream);
+
+/*
+ * float8_e4m3fnuz variants ("Enable blockwise FP8 dense training kernels on ROCm", description:
+ * FP8_MAX follows torch.finfo(dtype) and both float8_e4m3fn and float8_e4m3fnuz are accepted; its
+ * MI300X log runs e4m3fnuz with FP8 max 240). Each takes exactly the arguments of the entry point
+ * it is named after, with the same layouts, limits, alignment rules and return codes; the codes
+ * it writes or reads are e4m3fnuz and FP8_MAX is 240.
+ *   Quantizers: the same kernels as the e4m3fn ones.
+ *   GEMMs: gfx950's FP8 matrix instructions read e4m3fn only, and e4m3fnuz values (2^-10 .. 240)
+ *     are not all e4m3fn values under any one power-of-two scaling, so these widen each code
+ *     exactly to f16 in registers and run the K-block as four 16x16x32 f16 matrix instructions
+ *     (fp32 accumulation, the same per-K-block rescale and bf16 rounding). Both operands must be
+ *     e4m3fnuz; the expert-grouped GEMMs have no e4m3fnuz variant.
+ *   encode_e4m3fnuz_f32: q[i] = e4m3fnuz(x[i]) by the quantizers' conversion, for
+ *     |x[i]| <= 240 (1 + 2^-21) -- the range a group multiplier produces; larger magnitudes are
+ *     outside the contract. Exposed so the device conversion can be checked exhaustively.
+ */
+int quantize_lhs_fnuz(const void* x, int64_t M, int64_t K, int64_t ldx,
+                      void* q, int64_t ldq, float* a_s, void* stream);
+int quantize_rhs_fnuz(const void* x, int64_t K, int64_t N, int64_t ldx,
+                      void* qT, int64_t ldqT, float* s, void* stream);
+int quantize_weight_128x128_fnuz(const void* w, int64_t N, int64_t K, int64_t ldw,
+                                 void* q, int64_t ldq, void* qT, int64_t ldqT, float* s,
+                                 void* stream);
+int quantize_lhs_and_rhs_fnuz(const void* x, int64_t R, int64_t C, int64_t ldx,
+                              void* q, int64_t ldq, float* a_s,
+                              void* qT, int64_t ldqT, float* s, void* stream);
+int gemm_1x128_128x128_fnuz(const void* a, int64_t lda, const float* a_s,
+                            const void* b, int64_t ldb,
+                            const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb,
+                            void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+int gemm_1x128_128x1_fnuz(const void* a, int64_t lda, const float* a_s,
+                          const void* b, int64_t ldb, const float* b_s,
+                          void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+int encode_e4m3fnuz_f32(const float* x, void* q, int64_t n, void* stream);
 
 #ifdef __cplusplus
 }

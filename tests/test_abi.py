@@ -31,7 +31,10 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) >= {"quantize_lhs", "quantize_rhs", "quantize_weight_128x128",
                           "gemm_1x128_128x128", "gemm_1x128_128x1", "bsfp8_status_string",
                           "encode_e4m3_f32", "quantize_lhs_and_rhs",
-                          "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped"}
+                          "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
+                          "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
+                          "quantize_lhs_and_rhs_fnuz", "gemm_1x128_128x128_fnuz",
+                          "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -119,3 +122,28 @@ def test_gemms_reject_sizes_past_32bit_offsets(L):
     assert g(P, 128, P, P, big_ld, P, 1, 1, P, 64, 4, 64, 128, None) == 1
     assert g(P, 128, P, P, 128, P, 1, 1, P, 64, 2**30, 64, 128, None) == 1   # 4 M Kb >= 2^32
     assert h(P, 128, P, P, 128, P, P, 2**30, 4, 2**30, 128, None) == 1     # 4 N Kb >= 2^32
+
+
+def test_fnuz_variants_validate_like_their_e4m3fn_twins(L):
+    """Each *_fnuz entry point takes its twin's arguments and rejects the same bad ones, before any
+    HIP call; empty problems are no-ops."""
+    assert L.quantize_lhs_fnuz(None, 4, 128, 128, P, 128, P, None) == 1
+    assert L.quantize_lhs_fnuz(P, 4, 128, 127, P, 128, P, None) == 1
+    assert L.quantize_lhs_fnuz(P, 0, 128, 128, P, 128, P, None) == 0
+    assert L.quantize_rhs_fnuz(P, 128, 64, 63, P, 128, P, None) == 1
+    assert L.quantize_rhs_fnuz(P, 128, 0, 64, P, 128, P, None) == 0
+    assert L.quantize_weight_128x128_fnuz(P, 64, 64, 64, P, 64, P, 10, P, None) == 1
+    assert L.quantize_lhs_and_rhs_fnuz(P, 64, 64, 64, P, 64, P, P, 63, P, None) == 1  # ldqT < R
+    assert L.quantize_lhs_and_rhs_fnuz(P, 0, 64, 64, P, 64, P, P, 64, P, None) == 0
+    odd = ctypes.c_void_p(16 * 1024 + 8)
+    # gemm_1x128_128x128_fnuz(a, lda, a_s, b, ldb, b_s, nb, kb, c, ldc, M, N, K, stream)
+    assert L.gemm_1x128_128x128_fnuz(P, 100, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1
+    assert L.gemm_1x128_128x128_fnuz(odd, 128, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 2
+    assert L.gemm_1x128_128x128_fnuz(P, 128, P, P, 128, P, -1, 1, P, 64, 4, 64, 128, None) == 1
+    assert L.gemm_1x128_128x128_fnuz(P, 128, P, P, 128, P, 1, 1, P, 64, 0, 64, 128, None) == 0
+    # gemm_1x128_128x1_fnuz(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K, stream)
+    assert L.gemm_1x128_128x1_fnuz(P, 128, P, P, 128, None, P, 64, 4, 64, 128, None) == 1
+    assert L.gemm_1x128_128x1_fnuz(P, 128, P, P, 144, P, P, 63, 4, 64, 128, None) == 1  # ldc < N
+    assert L.gemm_1x128_128x1_fnuz(P, 128, P, P, 120, P, P, 64, 4, 64, 128, None) == 1  # ldb < K
+    assert L.encode_e4m3fnuz_f32(odd, P, 16, None) == 2
+    assert L.encode_e4m3fnuz_f32(None, None, 0, None) == 0
