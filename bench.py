@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense f16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 BLOCK = 128
 
@@ -298,12 +299,12 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     (16384 x 5120 x 5120) shapes, each rotating over buffer sets larger than the cache."""
     out = []
 
-    def add(name, shape, avg, work, unit):
+    def add(name, shape, avg, work, unit, peak=None):
         rate = work / (avg * 1e-3)
         if unit == "GB/s":
-            r, peak = rate / 1e9, PEAK_HBM_GBS
+            r, peak = rate / 1e9, peak or PEAK_HBM_GBS
         else:
-            r, peak = rate / 1e12, PEAK_FP8_TFLOPS
+            r, peak = rate / 1e12, peak or PEAK_FP8_TFLOPS
         out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2), unit: round(r, 1),
                     "frac": round(r / peak, 4)})
 
@@ -369,6 +370,22 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
 
     a = _time_kernel(train_step, reps, stream, torch)
     add("linear fwd+dgrad+wgrad (autograd, all quantizers)", [T, D, D], a, 3 * fl, "TFLOP/s")
+
+    # float8_e4m3fnuz (FP8_MAX 240): the same quantizers; the GEMMs widen the codes to f16 and run
+    # on the f16 matrix instructions, so their peak is the dense f16 one
+    fz = "e4m3fnuz"
+    a = _time_kernel(lambda i: bf.quantize_lhs_and_rhs(X[j(i)], qx[j(i)], sx[j(i)], qxT[j(i)], sxT[j(i)],
+                                                      stream=stream, fmt=fz), reps, stream, torch)
+    add("quantize_lhs_and_rhs e4m3fnuz", [T, D], a, dual_bytes(T, D), "GB/s")
+    a = _time_kernel(lambda i: bf.quantize_weight_128x128(W[j(i)], qw[j(i)], qwT[j(i)], sw[j(i)], stream=stream,
+                                                             fmt=fz), reps, stream, torch)
+    add("quantize_weight_128x128(+qT) e4m3fnuz", [D, D], a, weight_bytes(D, D, True), "GB/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qx[j(i)], sx[j(i)], qw[j(i)], sw[j(i)], c=out_c[j(i)],
+                                                        stream=stream, fmt=fz), reps, stream, torch)
+    add("gemm_1x128_128x128 fwd e4m3fnuz (f16 MFMA)", [T, D, D], a, fl, "TFLOP/s", PEAK_F16_TFLOPS)
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)], sdyT[j(i)], qxT[j(i)], sxT[j(i)], c=dw[j(i)],
+                                                      stream=stream, fmt=fz), reps, stream, torch)
+    add("gemm_1x128_128x1 wgrad e4m3fnuz (f16 MFMA)", [D, D, T], a, fl, "TFLOP/s", PEAK_F16_TFLOPS)
     del X, dY, W, qx, sx, qxT, sxT, qdy, sdy, qdyT, sdyT, qw, qwT, sw, out_c, dw, Xg, Wg, dYg
     torch.cuda.empty_cache()
 
