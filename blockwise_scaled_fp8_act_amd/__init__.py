@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     gemm_1x128_128x128_grouped,
     quantize_lhs,
     quantize_lhs_and_rhs,
+    quantize_lhs_and_weight,
     quantize_rhs,
     quantize_weight_128x128,
 )

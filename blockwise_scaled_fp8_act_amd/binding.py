@@ -60,8 +60,11 @@ def lib():
                                                  _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]
         L.gemm_1x128_128x1_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
                                                _i64, _i64, _i64, _i64, _vp]
+        L.quantize_lhs_and_weight.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
+                                              _i64, _vp, _i64, _vp, _i64, _vp, _vp]
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
-                  "gemm_1x128_128x1", "quantize_lhs_and_rhs", "encode_e4m3_f32"):
+                  "gemm_1x128_128x1", "quantize_lhs_and_rhs", "encode_e4m3_f32",
+                  "quantize_lhs_and_weight"):
             fz = getattr(L, f.replace("e4m3", "e4m3fnuz") if f.startswith("encode") else f + "_fnuz")
             fz.argtypes = getattr(L, f).argtypes
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
@@ -69,7 +72,8 @@ def lib():
                   "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
                   "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
                   "gemm_1x128_128x128_fnuz", "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
-                  "quantize_lhs_and_rhs_fnuz"):
+                  "quantize_lhs_and_rhs_fnuz", "quantize_lhs_and_weight",
+                  "quantize_lhs_and_weight_fnuz"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -161,6 +165,29 @@ def quantize_lhs_and_rhs(x, q=None, a_s=None, qT=None, s=None, stream=None, fmt=
     _call(_entry("quantize_lhs_and_rhs", fmt), _ptr(x), R, C, _ld(x), _ptr(q), _ld(q), _ptr(a_s),
           _ptr(qT), _ld(qT), _ptr(s), _stream(stream))
     return q, a_s, qT, s
+
+
+def quantize_lhs_and_weight(x, w, qx=None, sx=None, qw=None, qwT=None, sw=None, want_qT=False,
+                            stream=None, fmt="e4m3fn"):
+    """quantize_lhs(x) and quantize_weight_128x128(w) in one launch (the two quantizations of a
+    linear layer's forward step). Returns (qx [M, K], sx (Kb, M), qw [N, Kw], qwT [Kw, N] or None,
+    sw (Nb, Kbw)), byte-identical to the two separate calls."""
+    M, K = x.shape
+    N, Kw = w.shape
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if sx is None:
+        sx = torch.empty((cdiv(K, BLOCK), M), dtype=torch.float32, device=x.device)
+    if qw is None:
+        qw = torch.empty((N, Kw), dtype=torch.uint8, device=w.device)
+    if qwT is None and want_qT:
+        qwT = torch.empty((Kw, N), dtype=torch.uint8, device=w.device)
+    if sw is None:
+        sw = torch.empty((cdiv(N, BLOCK), cdiv(Kw, BLOCK)), dtype=torch.float32, device=w.device)
+    ldqwT = _ld(qwT) if qwT is not None else 0
+    _call(_entry("quantize_lhs_and_weight", fmt), _ptr(x), M, K, _ld(x), _ptr(qx), _ld(qx), _ptr(sx),
+          _ptr(w), N, Kw, _ld(w), _ptr(qw), _ld(qw), _ptr(qwT), ldqwT, _ptr(sw), _stream(stream))
+    return qx, sx, qw, qwT, sw
 
 
 def quantize_weight_128x128(w, q=None, qT=None, s=None, want_qT=True, stream=None,

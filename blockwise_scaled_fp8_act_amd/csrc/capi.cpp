@@ -111,6 +111,27 @@ int quantize_dual_impl(const void* x, int64_t R, int64_t C, int64_t ldx, void* q
                                               static_cast<hipStream_t>(stream)));
 }
 
+int quantize_step_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* qx, int64_t ldqx,
+                       float* sx, const void* w, int64_t N, int64_t Kw, int64_t ldw, void* qw,
+                       int64_t ldqw, void* qwT, int64_t ldqwT, float* sw, bool fnuz, void* stream) {
+    if (M < 0 || K < 0 || N < 0 || Kw < 0) return BSFP8_EINVAL;
+    const bool x_empty = M == 0 || K == 0, w_empty = N == 0 || Kw == 0;
+    if (!x_empty && (x == nullptr || qx == nullptr || sx == nullptr || ldx < K || ldqx < K)) return BSFP8_EINVAL;
+    if (!w_empty && (w == nullptr || qw == nullptr || sw == nullptr || ldw < Kw || ldqw < Kw ||
+                     (qwT != nullptr && ldqwT < N)))
+        return BSFP8_EINVAL;
+    if (x_empty && w_empty) return BSFP8_OK;
+    if (x_empty) return quantize_weight_impl(w, N, Kw, ldw, qw, ldqw, qwT, ldqwT, sw, fnuz, stream);
+    if (w_empty) return quantize_lhs_impl(x, M, K, ldx, qx, ldqx, sx, fnuz, stream);
+    if (cdiv(M, kGroupEdge) * cdiv(K, kGroupEdge) + cdiv(N, kGroupEdge) * cdiv(Kw, kGroupEdge) > 0x7FFFFFFFLL)
+        return BSFP8_EINVAL;
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_step(
+        static_cast<const uint16_t*>(x), M, K, ldx, static_cast<uint8_t*>(qx), ldqx, sx,
+        static_cast<const uint16_t*>(w), N, Kw, ldw, static_cast<uint8_t*>(qw), ldqw,
+        static_cast<uint8_t*>(qwT), ldqwT, sw, fnuz, static_cast<hipStream_t>(stream)));
+}
+
 int gemm_128x128_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                       const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
                       int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz, void* stream) {
@@ -268,6 +289,21 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const
     return finish(bsfp8::launch_gemm_grouped_k(
         static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b), ldb, b_s, offsets,
         E, static_cast<uint16_t*>(c), ldc, c_stride, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int quantize_lhs_and_weight(const void* x, int64_t M, int64_t K, int64_t ldx, void* qx, int64_t ldqx,
+                            float* sx, const void* w, int64_t N, int64_t Kw, int64_t ldw, void* qw,
+                            int64_t ldqw, void* qwT, int64_t ldqwT, float* sw, void* stream) {
+    return quantize_step_impl(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw, qwT, ldqwT, sw, false,
+                              stream);
+}
+
+int quantize_lhs_and_weight_fnuz(const void* x, int64_t M, int64_t K, int64_t ldx, void* qx,
+                                 int64_t ldqx, float* sx, const void* w, int64_t N, int64_t Kw,
+                                 int64_t ldw, void* qw, int64_t ldqw, void* qwT, int64_t ldqwT,
+                                 float* sw, void* stream) {
+    return quantize_step_impl(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw, qwT, ldqwT, sw, true,
+                              stream);
 }
 
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream) {

@@ -17,6 +17,11 @@ hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t 
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                   int64_t ldq, uint8_t* qT, int64_t ldqT, float* s, bool fnuz,
                                   hipStream_t stream);
+// quantize_lhs(x) and quantize_weight_128x128(w) in one launch
+hipError_t launch_quantize_step(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qx,
+                                int64_t ldqx, float* sx, const uint16_t* w, int64_t N, int64_t Kw,
+                                int64_t ldw, uint8_t* qw, int64_t ldqw, uint8_t* qwT, int64_t ldqwT,
+                                float* sw, bool fnuz, hipStream_t stream);
 hipError_t launch_encode(const float* x, uint8_t* q, int64_t n, bool fnuz, hipStream_t stream);
 
 // b-scale addressing of the GEMM: kind 0 = one scale per (K-block, 128-column block) at

@@ -212,6 +212,24 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s,
 int encode_e4m3_f32(const float* x, void* q, int64_t n, void* stream);
 
 /*
+ * quantize_lhs_and_weight: quantize_lhs(x) and quantize_weight_128x128(w) in one launch -- the two
+ * quantizations of a linear layer's forward step (Y = X W^T: the 1x128 groups of the activation
+ * and the 128x128 blocks of the weight, "Enable blockwise FP8 dense training kernels on ROCm",
+ * quantization-correctness table). The outputs are byte-identical to the two separate calls with
+ * the same arguments:
+ *   x [M, K] bf16 (ldx), qx [M, K] (ldqx), sx column-major [M, ceil(K/128)] with ld M;
+ *   w [N, Kw] bf16 (ldw), qw [N, Kw] (ldqw), qwT nullable [Kw, N] (ldqwT), sw [Nb, Kbw] row-major.
+ * Either tensor may be empty (then only the other one is quantized). With 16-byte bf16 rows,
+ * 8-byte code rows and 16-byte qwT rows both run in one persistent kernel; otherwise the two
+ * single-purpose kernels run one after the other. Errors as for the two calls.
+ */
+int quantize_lhs_and_weight(const void* x, int64_t M, int64_t K, int64_t ldx,
+                            void* qx, int64_t ldqx, float* sx,
+                            const void* w, int64_t N, int64_t Kw, int64_t ldw,
+                            void* qw, int64_t ldqw, void* qwT, int64_t ldqwT, float* sw,
+                            void* stream);
+
+/*
  * float8_e4m3fnuz variants ("Enable blockwise FP8 dense training kernels on ROCm", description:
  * FP8_MAX follows torch.finfo(dtype) and both float8_e4m3fn and float8_e4m3fnuz are accepted; its
  * MI300X log runs e4m3fnuz with FP8 max 240). Each takes exactly the arguments of the entry point
@@ -237,6 +255,11 @@ int quantize_weight_128x128_fnuz(const void* w, int64_t N, int64_t K, int64_t ld
 int quantize_lhs_and_rhs_fnuz(const void* x, int64_t R, int64_t C, int64_t ldx,
                               void* q, int64_t ldq, float* a_s,
                               void* qT, int64_t ldqT, float* s, void* stream);
+int quantize_lhs_and_weight_fnuz(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                 void* qx, int64_t ldqx, float* sx,
+                                 const void* w, int64_t N, int64_t Kw, int64_t ldw,
+                                 void* qw, int64_t ldqw, void* qwT, int64_t ldqwT, float* sw,
+                                 void* stream);
 int gemm_1x128_128x128_fnuz(const void* a, int64_t lda, const float* a_s,
                             const void* b, int64_t ldb,
                             const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb,

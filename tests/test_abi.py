@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(L):
                           "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
                           "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
                           "quantize_lhs_and_rhs_fnuz", "gemm_1x128_128x128_fnuz",
-                          "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32"}
+                          "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
+                          "quantize_lhs_and_weight", "quantize_lhs_and_weight_fnuz"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -147,3 +148,15 @@ def test_fnuz_variants_validate_like_their_e4m3fn_twins(L):
     assert L.gemm_1x128_128x1_fnuz(P, 128, P, P, 120, P, P, 64, 4, 64, 128, None) == 1  # ldb < K
     assert L.encode_e4m3fnuz_f32(odd, P, 16, None) == 2
     assert L.encode_e4m3fnuz_f32(None, None, 0, None) == 0
+
+
+def test_fused_step_quantizer_rejects_bad_arguments(L):
+    # quantize_lhs_and_weight(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw, qwT, ldqwT, sw, s)
+    for f in (L.quantize_lhs_and_weight, L.quantize_lhs_and_weight_fnuz):
+        assert f(P, -1, 128, 128, P, 128, P, P, 64, 64, 64, P, 64, None, 0, P, None) == 1
+        assert f(P, 4, 128, 127, P, 128, P, P, 64, 64, 64, P, 64, None, 0, P, None) == 1  # ldx < K
+        assert f(P, 4, 128, 128, P, 128, None, P, 64, 64, 64, P, 64, None, 0, P, None) == 1
+        assert f(P, 4, 128, 128, P, 128, P, P, 64, 64, 63, P, 64, None, 0, P, None) == 1  # ldw < Kw
+        assert f(P, 4, 128, 128, P, 128, P, P, 64, 64, 64, P, 64, P, 10, P, None) == 1   # ldqwT < N
+        assert f(P, 4, 128, 128, P, 128, P, None, 64, 64, 64, P, 64, None, 0, P, None) == 1
+        assert f(P, 0, 128, 128, P, 128, P, P, 0, 64, 64, P, 64, None, 0, P, None) == 0  # both empty
