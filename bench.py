@@ -194,14 +194,17 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
+    # the GEMM of every EVERY-th step is bracketed by an event pair (each pair costs ~1 us of
+    # stream time, so not every step carries one)
+    EVERY = 5
     for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
+        step(sets[i % len(sets)], evs[i] if i % EVERY == 0 else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    gemm_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    gemm_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(0, args.steps, EVERY)])
 
     # per-kernel duration of the quantizer launch: a separate pass of the same steps with every
     # kernel bracketed (not part of the timed region)
@@ -209,9 +212,9 @@ def main():
         step(sets[i % len(sets)], evs[i], per_kernel=True)
     torch.cuda.synchronize()
     k_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in evs])
-    k_ms[:, 1] = gemm_ms  # the GEMM column is the timed region's
     k_avg = k_ms.mean(axis=0)
     k_med = np.median(k_ms, axis=0)
+    k_avg[1], k_med[1] = gemm_ms.mean(), np.median(gemm_ms)  # the GEMM figures are the timed region's
 
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (k_avg[1] * 1e-3) / 1e12
