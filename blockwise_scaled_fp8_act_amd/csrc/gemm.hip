@@ -17,8 +17,10 @@
 //   * operands are read through buffer resources that end at the matrix edge: rows >= M / >= N read
 //     as zero, and their outputs are never stored; every scale read is limited to rows < M,
 //     columns < N.
-// The fast kernel (namespace fast) serves K % 128 == 0; the general kernel also handles a ragged
-// last K-block (bytes past K are zeroed).
+// The fast kernel (namespace fast) serves every float8_e4m3fn GEMM whose B scales it can stage
+// (per-column: N % 4 == 0; 128x128: at most 512 K-blocks), a partial last K-block included; the
+// general kernel serves the rest and the float8_e4m3fnuz operands. Both zero the bytes of a
+// partial last K-block that lie at or past K.
 //
 // float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240) run on the
 // general kernel: gfx950's FP8 matrix instructions read e4m3fn, and no power-of-two rescaling
@@ -28,6 +30,8 @@
 // rebiases the exponent and normalises the subnormals) and a K-block is four
 // v_mfma_f32_16x16x32_f16 instead of one FP8 instruction -- products of two 4-significant-bit
 // values are exact in fp32 either way, so the per-K-block partials equal the fn path's arithmetic.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -470,9 +474,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 }
 
 // ==============================================================================================
-// Fast path for K % 128 == 0 (and, with per-column scales, N % 4 == 0): a 256 x 256 workgroup tile
-// of 8 waves, two per SIMD, each wave owning a 64 x 128 block of the tile (128 fp32 totals in
-// VGPRs).
+// Fast path (per-column scales: N % 4 == 0; 128x128 scales: at most 512 K-blocks): a 256 x 256
+// workgroup tile of 8 waves, two per SIMD, each wave owning a 64 x 128 block of the tile (128 fp32
+// totals in VGPRs).
 //   * Every K-block's A tile (256 x 128 bytes), B tile (256 x 128 bytes) and scale slices go
 //     global -> LDS by direct buffer loads (no registers) into one of two LDS stages, one K-block
 //     ahead of the block being multiplied. Each wave loads 1/8 of every tile; the workgroup barrier
@@ -621,7 +625,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     int64_t m0 = static_cast<int64_t>(tm) * kBM;  // this tile's rows are [m0, min(m0 + kBM, m_end))
     int64_t m_end = M;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
-    int64_t Kb = K / kGroup;
+    // K-blocks (the last one may be partial: only for the ungrouped GEMMs, whose callers allow it)
+    int64_t Kb = (K + kGroup - 1) / kGroup;
     if (GROUP == kGroupRows) {
         // tm indexes the concatenated row tiles of the experts; expert e owns rows
         // [offsets[e], offsets[e + 1]) of A and C (clamped to [0, M] and made non-decreasing) and
@@ -714,9 +719,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         }
         wait_own_loads<0>();
 
+        // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its DMA loads read whole
+        // 128-byte rows, so bytes at and past K (row padding, or the start of the next row) are
+        // zeroed in the fragment registers of that block: lane group lg holds bytes
+        // [32 lg, 32 lg + 32) of both operands' rows.
+        const int krem = static_cast<int>(K - (Kb - 1) * kGroup);
+        const int lane_keep = krem - 32 * lg;
+        auto tail_mask = [&](v8i v) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                const int keep = lane_keep - 4 * d;
+                const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+                v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & m);
+            }
+            return v;
+        };
+
         // One loop body for both stages (stage = kb % 2 at run time): a body unrolled per stage
-        // makes the register allocator spill.
-        auto step = [&](int64_t kb) {
+        // makes the register allocator spill. TAIL: the partial last K-block (fragments masked).
+        auto step = [&](int64_t kb, auto tail_tag) {
+            constexpr bool TAIL = decltype(tail_tag)::value;
             const int cur = static_cast<int>(kb & 1);
             const int nxt = cur ^ 1;
             // every wave's block-kb loads are in LDS, and every wave is done with block kb-1
@@ -729,7 +751,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             const float* sbs = reinterpret_cast<const float*>(st + kStageSB) + 128 * wn;
             auto read_bf = [&](int j) {
                 const int r = 128 * wn + 16 * j + l16;
-                return to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
+                const v8i v = to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
+                return TAIL ? tail_mask(v) : v;
             };
             // B fragments are read two subtiles ahead of their MFMAs (three in registers); the
             // first MFMA needs only bf[0] and af[0], so those are read first
@@ -740,6 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             for (int i = 0; i < kMSub; ++i) {
                 const int r = 64 * wm + 16 * i + l16;
                 af[i] = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
+                if (TAIL) af[i] = tail_mask(af[i]);
             }
             bf[1] = read_bf(1);
             const float bsc = PER_COL ? 1.0f : bscale_lds[wn][kb];
@@ -787,7 +811,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             wait_own_loads<0>();  // this wave's loads of block kb+1 have landed
         };
 
-        for (int64_t kb = 0; kb < Kb; ++kb) step(kb);
+        const int64_t Kb_full = krem == kGroup ? Kb : Kb - 1;
+        for (int64_t kb = 0; kb < Kb_full; ++kb) step(kb, std::false_type{});
+        if (Kb_full < Kb) step(Kb_full, std::true_type{});
     }
 
     // Epilogue: each wave's 64 x 128 bf16 block goes through LDS (the stages are free once every
@@ -838,10 +864,10 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
     // vector stores: 8 bytes per lane in the general kernel, 16 in the fast one
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
     const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
-    // Fast path: whole K-blocks; per-column scales read 4 columns at a time; 128x128 scales of a
+    // Fast path: per-column scales read 4 columns at a time; 128x128 scales of a
     // tile's column staged in LDS (at most kMaxKbFast K-blocks).
-    const bool fast_scales = bs.per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
-    if (!fnuz && K % kGroup == 0 && fast_scales) {
+    const bool fast_scales = bs.per_column ? (N % 4 == 0) : ((K + kGroup - 1) / kGroup <= fast::kMaxKbFast);
+    if (!fnuz && fast_scales) {
         const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
         if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;

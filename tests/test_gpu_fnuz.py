@@ -281,3 +281,33 @@ def test_linear_layer_fnuz():
            oracle.gemm_1x128_128x128(qdy, sdy, qwT, sw, 1, kbw, fmt=FMT), "dgrad")
     _check(w.grad.float().cpu().numpy(),
            oracle.gemm_1x128_128x1(qdyT, sdyT, qxT, sxT, fmt=FMT), "wgrad")
+
+
+@pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
+def test_gemm_fnuz_partial_last_block_ignores_nan_padding(per_col):
+    """Ragged K (300) with the NaN pattern 0x80 in every byte at and past K of the operand rows;
+    the operands are the oracle's fnuz quantization of Gaussian data."""
+    M, N, K, ld = 200, 136, 300, 320
+    g = np.random.Generator(np.random.PCG64(5))
+    ah, sa = oracle.quantize_lhs(inputs.bf16_bits_from_f64(g.standard_normal((M, K))), fmt=FMT)
+    if per_col:
+        bh, sb = oracle.quantize_rhs(inputs.bf16_bits_from_f64(g.standard_normal((K, N))), fmt=FMT)
+    else:
+        bh, _, sb = oracle.quantize_weight_128x128(
+            inputs.bf16_bits_from_f64(g.standard_normal((N, K)) * 0.02), want_qT=False, fmt=FMT)
+
+    def nan_padded(h):
+        buf = torch.full((h.shape[0] + 1, ld), 0x80, dtype=torch.uint8, device=DEV)
+        buf[:h.shape[0], :K] = torch.from_numpy(h).to(DEV)
+        return buf[:h.shape[0], :K]
+
+    a, b = nan_padded(ah), nan_padded(bh)
+    if per_col:
+        c = bf.gemm_1x128_128x1(a, to_dev(sa), b, to_dev(sb), fmt=FMT)
+        co = oracle.gemm_1x128_128x1(ah, sa, bh, sb, fmt=FMT)
+    else:
+        c = bf.gemm_1x128_128x128(a, to_dev(sa), b, to_dev(sb), fmt=FMT)
+        co = oracle.gemm_1x128_128x128(ah, sa, bh, sb, sb.shape[1], 1, fmt=FMT)
+    got = c.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    _check(got, co, "fnuz partial last K-block")

@@ -261,3 +261,37 @@ def test_training_step_full_size_sampled():
     ref_dw = dyf.T[rows_w] @ xf
     assert oracle.sqnr_db(ref_dx, dx.float().cpu().numpy()[rows]) >= 28.0
     assert oracle.sqnr_db(ref_dw, dw.float().cpu().numpy()[rows_w]) >= 28.0
+
+
+@pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
+@pytest.mark.parametrize("M,N,K,ld", [(300, 260, 200, 208), (257, 384, 1000, 1008), (64, 128, 1, 16),
+                                      (130, 512, 1280 - 40, 1248)], ids=lambda v: str(v))
+def test_gemm_partial_last_block_ignores_nan_padding(M, N, K, ld, per_col):
+    """A partial last K-block: the bytes at and past K of every operand row (row padding, and for
+    the last row the next allocation) hold the NaN code 0x7F; none of it may reach C."""
+    g = np.random.Generator(np.random.PCG64(M + K))
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    ah = g.choice(finite, size=(M, K))
+    bh = g.choice(finite, size=(N, K))
+    Kb = _cdiv(K, 128)
+
+    def nan_padded(h):
+        buf = torch.full((h.shape[0] + 1, ld), 0x7F, dtype=torch.uint8, device=DEV)
+        buf[:h.shape[0], :K] = torch.from_numpy(h).to(DEV)
+        return buf[:h.shape[0], :K]
+
+    a, b = nan_padded(ah), nan_padded(bh)
+    a_s = _scales((Kb, M), 21)
+    if per_col:
+        b_s = _scales((Kb, N), 22)
+        got = _run_guarded(lambda c: bf.gemm_1x128_128x1(a, to_dev(a_s), b, to_dev(b_s), c=c), M, N, N)
+        co = oracle.gemm_1x128_128x1(ah, a_s, bh, b_s)
+        c_abs = oracle.gemm_1x128_128x1(_abs_codes(ah), a_s, _abs_codes(bh), b_s)
+    else:
+        b_s = _scales((_cdiv(N, 128), Kb), 23)
+        got = _run_guarded(lambda c: bf.gemm_1x128_128x128(a, to_dev(a_s), b, to_dev(b_s), Kb, 1, c=c),
+                           M, N, N)
+        co = oracle.gemm_1x128_128x128(ah, a_s, bh, b_s, Kb, 1)
+        c_abs = oracle.gemm_1x128_128x128(_abs_codes(ah), a_s, _abs_codes(bh), b_s, Kb, 1)
+    assert np.all(np.isfinite(got))
+    _assert_dot_bound(got, co, c_abs, "partial last K-block")
