@@ -31,6 +31,10 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 BLOCK = 128
 
 
+def _cdiv(a, b):
+    return (a + b - 1) // b
+
+
 def lhs_bytes(M, K):
     """Algorithmic bytes of a 1x128 / 128x1 activation quantizer: read 2 B, write 1 B per element,
     plus one fp32 scale per 128 elements."""
@@ -370,6 +374,20 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
 
     a = _time_kernel(train_step, reps, stream, torch)
     add("linear fwd+dgrad+wgrad (autograd, all quantizers)", [T, D, D], a, 3 * fl, "TFLOP/s")
+
+    # token counts off the 128 grid: the last K-block is partial (8000 tokens: wgrad K = 8000;
+    # forward with 4000 input features)
+    Tr, Kr = 8000, 4000
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x1(qdyT[j(i)][:, :Tr], sdyT[j(i)][:_cdiv(Tr, BLOCK)],
+                                                      qxT[j(i)][:, :Tr], sxT[j(i)][:_cdiv(Tr, BLOCK)],
+                                                      c=dw[j(i)], K=Tr, stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x1 wgrad, 8000 tokens (partial last K-block)", [D, D, Tr], a, 2.0 * D * D * Tr,
+        "TFLOP/s")
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qx[j(i)][:, :Kr], sx[j(i)][:_cdiv(Kr, BLOCK)],
+                                                        qw[j(i)][:, :Kr], sw[j(i)], Kb, 1, c=out_c[j(i)],
+                                                        K=Kr, stream=stream), reps, stream, torch)
+    add("gemm_1x128_128x128 fwd, K = 4000 (partial last K-block)", [T, D, Kr], a, 2.0 * T * D * Kr,
+        "TFLOP/s")
 
     # float8_e4m3fnuz (FP8_MAX 240): the same quantizers; the GEMMs widen the codes to f16 and run
     # on the f16 matrix instructions, so their peak is the dense f16 one

@@ -160,3 +160,32 @@ def test_fused_step_quantizer_rejects_bad_arguments(L):
         assert f(P, 4, 128, 128, P, 128, P, P, 64, 64, 64, P, 64, P, 10, P, None) == 1   # ldqwT < N
         assert f(P, 4, 128, 128, P, 128, P, None, 64, 64, 64, P, 64, None, 0, P, None) == 1
         assert f(P, 0, 128, 128, P, 128, P, P, 0, 64, 64, P, 64, None, 0, P, None) == 0  # both empty
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/blockwise_fp8.h declares a C ABI: it compiles as C99 and as C++ without warnings, and
+    a C caller links against the library's exported symbols."""
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include "blockwise_fp8.h"\n'
+        "#include <stdio.h>\n"
+        "int main(void) {\n"
+        "    /* argument checks only: no GPU work is launched */\n"
+        "    int rc = quantize_lhs(0, 4, 128, 128, 0, 128, 0, 0);\n"
+        '    printf("%d %s\\n", rc, bsfp8_status_string(rc));\n'
+        "    return rc == BSFP8_EINVAL ? 0 : 1;\n"
+        "}\n")
+    inc = os.path.join(ROOT, "include")
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-x", "c" if cc == "gcc" else "c++",
+                            "-I", inc, "-c", str(src), "-o", str(tmp_path / f"use_{cc}.o")],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+    exe = tmp_path / "use"
+    r = subprocess.run(["gcc", str(tmp_path / "use_gcc.o"), binding.LIB_PATH,
+                        f"-Wl,-rpath,{os.path.dirname(binding.LIB_PATH)}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("1 invalid argument"), (r.stdout, r.stderr)
