@@ -26,10 +26,10 @@
 // general kernel: gfx950's FP8 matrix instructions read e4m3fn, and no power-of-two rescaling
 // maps every fnuz value onto an e4m3fn value (fnuz spans 2^-10 .. 240, e4m3fn 2^-9 .. 448, and
 // 2 x 240 = 480 is not an e4m3fn value). Each fnuz code is instead widened exactly to f16 in
-// registers (its 7 magnitude bits placed under the f16 exponent field, then a multiply by 2^7
-// rebiases the exponent and normalises the subnormals) and a K-block is four
-// v_mfma_f32_16x16x32_f16 instead of one FP8 instruction -- products of two 4-significant-bit
-// values are exact in fp32 either way, so the per-K-block partials equal the fn path's arithmetic.
+// registers (its 7 magnitude bits placed under the f16 exponent field: the value times 2^-7, the
+// smallest ones as f16 subnormals) and a K-block is four v_mfma_f32_16x16x32_f16 instead of one
+// FP8 instruction -- products of two 4-significant-bit values are exact in fp32 either way, so the
+// per-K-block partials equal the fn path's arithmetic up to the exact factor 2^-14.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -43,7 +43,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef short s2v __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256;      // workgroup rows (M)
@@ -64,19 +63,18 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
 }
 
 // Two float8_e4m3fnuz codes (bytes 0,1 of w for HALF 0, bytes 2,3 for HALF 1) as two exact f16
-// values. Each code c = s eeee mmm is moved to bits 15..8 of its 16-bit half; an arithmetic
-// shift by one leaves s in bit 15 (and a copy in bit 14, cleared next), e in the low four bits of
-// the f16 exponent field and m at the top of the f16 mantissa. That f16 is
-// (1 + m/8) 2^(e - 15), or (m/8) 2^-14 for e = 0, i.e. the fnuz value times 2^-7; the multiply by
-// 2^7 is exact and normalises the subnormals. Every fnuz value (2^-10 .. 240) is a normal f16.
+// values scaled by 2^-7. Each code c = s eeee mmm is moved to bits 15..8 of its 16-bit half; an
+// arithmetic shift by one leaves s in bit 15 (and a copy in bit 14, cleared next), e in the low four
+// bits of the f16 exponent field and m at the top of the f16 mantissa. That f16 is
+// (1 + m/8) 2^(e - 15), or (m/8) 2^-14 for e = 0 (an f16 subnormal), i.e. exactly the fnuz value
+// times 2^-7. The matrix instructions take f16 subnormal inputs exactly (every code's value comes
+// back exact through the GEMM), so the 2^14 of a product is folded into the per-K-block factor.
 template <int HALF>
 __device__ __forceinline__ uint32_t fnuz2_to_f16x2(uint32_t w) {
     const uint32_t p = __builtin_amdgcn_perm(w, w, HALF ? 0x030C020Cu : 0x010C000Cu);
     s2v v = __builtin_bit_cast(s2v, p);
     v = v >> 1;
-    const uint32_t u = __builtin_bit_cast(uint32_t, v) & 0xBFFFBFFFu;
-    const h2v h = __builtin_bit_cast(h2v, u) * h2v{static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f)};
-    return __builtin_bit_cast(uint32_t, h);
+    return __builtin_bit_cast(uint32_t, v) & 0xBFFFBFFFu;
 }
 
 // A 32-code FP8 fragment (the lane's operand of one 16x16x128 instruction) as the operands of four
@@ -365,7 +363,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             const u32x4* sb = sB[cur];
             float f[kMSub];
 #pragma unroll
-            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? as[cur][i] : as[cur][i] * bscal[cur];
+            for (int i = 0; i < kMSub; ++i) {
+                f[i] = PER_COL ? as[cur][i] : as[cur][i] * bscal[cur];
+                if (FNUZ) f[i] *= 16384.0f;  // 2^14: both widened operands carry 2^-7
+            }
             auto read_bf = [&](int j) {
                 const int r = kWN * wn + 16 * j + l16;
                 return to_v8i(sb[r * 8 + ((2 * lg) ^ (r & 7))], sb[r * 8 + ((2 * lg + 1) ^ (r & 7))]);
