@@ -12,8 +12,8 @@
 //   * the MFMA takes B as its first operand, so a lane's four outputs are four consecutive columns n
 //     of one row m: the 128x128 rescale factor is one scalar per (lane, 16-row subtile) and the bf16
 //     epilogue writes 8 contiguous bytes per lane;
-//   * tiles are staged in LDS with a 16-byte-chunk XOR swizzle (chunk ^ row % 8), so the fragment
-//     reads (16 rows x 32 bytes per 16 lanes) are bank-conflict free;
+//   * the fast kernel stages tiles in LDS with a 16-byte-chunk XOR swizzle and reads its fragments
+//     bank-conflict free (its layout is described there);
 //   * operands are read through buffer resources that end at the matrix edge: rows >= M / >= N read
 //     as zero, and their outputs are never stored; every scale read is limited to rows < M,
 //     columns < N.
@@ -699,9 +699,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
     if (Kb > 0) {
         auto stage_base = [&](int stage) { return op.lds + static_cast<uint32_t>(stage * kStageSize * 16); };
+        // Fragment lane (l16, lg) holds 16-byte chunks lg and lg + 4 of its row (row bytes
+        // [16 lg, 16 lg + 16) and [64 + 16 lg, 64 + 16 lg + 16)). Any assignment of a row's 128
+        // bytes to the four lane groups' 32 operand bytes gives the same dot product as long as A
+        // and B use the same one; this one makes every ds_read_b128 conflict free at the full LDS
+        // rate (4 cycles per instruction on gfx950, where chunks 2 lg and 2 lg + 1 take 8).
         const int sw = swz(l16);  // the same for every fragment row 16 x + l16
-        const int pos_lo = (2 * lg) ^ sw;
-        const int pos_hi = (2 * lg + 1) ^ sw;
+        const int pos_lo = lg ^ sw;
+        const int pos_hi = (lg + 4) ^ sw;
 
         // prologue: block 0 into stage 0
 #pragma unroll
@@ -722,14 +727,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
         // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its DMA loads read whole
         // 128-byte rows, so bytes at and past K (row padding, or the start of the next row) are
-        // zeroed in the fragment registers of that block: lane group lg holds bytes
-        // [32 lg, 32 lg + 32) of both operands' rows.
+        // zeroed in the fragment registers of that block: register d of lane group lg holds row
+        // bytes from 16 lg + 4 d (d < 4) and from 64 + 16 lg + 4 (d - 4) (d >= 4), in both operands.
         const int krem = static_cast<int>(K - (Kb - 1) * kGroup);
-        const int lane_keep = krem - 32 * lg;
+        const int lane_keep = krem - 16 * lg;
         auto tail_mask = [&](v8i v) {
 #pragma unroll
             for (int d = 0; d < 8; ++d) {
-                const int keep = lane_keep - 4 * d;
+                const int keep = lane_keep - (d < 4 ? 4 * d : 64 + 4 * (d - 4));
                 const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
                 v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & m);
             }
