@@ -63,7 +63,6 @@ int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
     if (M == 0 || K == 0) return BSFP8_OK;
     if (x == nullptr || q == nullptr || a_s == nullptr) return BSFP8_EINVAL;
     if (ldx < K || ldq < K) return BSFP8_EINVAL;
-    if (cdiv(K, kGroupEdge) > kMaxGridY) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     return finish(bsfp8::launch_quantize_lhs(static_cast<const uint16_t*>(x), M, K, ldx,
                                              static_cast<uint8_t*>(q), ldq, a_s, fnuz,

@@ -23,48 +23,55 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 consecutive bf16 of one row starting at column c; columns >= ncols read as +0.
+// 8 consecutive bf16 of row r (of nrows, row stride ld) starting at column c, as 4 packed dwords
+// (element 2d in the low half of dword d); rows >= nrows and columns >= ncols read as +0.
+// VEC (16-byte aligned rows and ncols % 8 == 0, so a lane's 8 columns are all in range or all
+// out): one 16-byte load with no branch around it -- an out-of-range lane loads from x[0] and
+// keeps zeros -- so the loads of a whole tile are in flight together. (A load inside a per-lane
+// branch is followed by a wait for it before the branch joins: one memory round trip per load.)
 template <bool VEC>
-__device__ __forceinline__ void load8(const uint16_t* __restrict__ row, int64_t c, int64_t ncols,
-                                      float f[8]) {
-    if (VEC && c + 8 <= ncols) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
-        f[0] = bf16_lo(v[0]); f[1] = bf16_hi(v[0]);
-        f[2] = bf16_lo(v[1]); f[3] = bf16_hi(v[1]);
-        f[4] = bf16_lo(v[2]); f[5] = bf16_hi(v[2]);
-        f[6] = bf16_lo(v[3]); f[7] = bf16_hi(v[3]);
+__device__ __forceinline__ void load8_packed(const uint16_t* __restrict__ x, int64_t ld, int64_t r,
+                                             int64_t nrows, int64_t c, int64_t ncols, uint32_t w[4]) {
+    if (VEC) {
+        const bool in = r < nrows && c < ncols;
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (in ? r * ld + c : 0)));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d] = in ? v[d] : 0u;
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            f[j] = (c + j < ncols) ? bf16_to_f32(row[c + j]) : 0.0f;
-    }
-}
-
-// The same 8 bf16 as 4 packed dwords (element 2d in the low half of dword d); columns >= ncols are
-// +0.
-template <bool VEC>
-__device__ __forceinline__ void load8_packed(const uint16_t* __restrict__ row, int64_t c, int64_t ncols,
-                                             uint32_t w[4]) {
-    if (VEC && c + 8 <= ncols) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c));
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-    } else {
+        for (int d = 0; d < 4; ++d) w[d] = 0u;
+        if (r < nrows) {
+            const uint16_t* row = x + r * ld;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t lo = (c + 2 * d < ncols) ? row[c + 2 * d] : 0u;
-            const uint32_t hi = (c + 2 * d + 1 < ncols) ? row[c + 2 * d + 1] : 0u;
-            w[d] = lo | (hi << 16);
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t lo = (c + 2 * d < ncols) ? row[c + 2 * d] : 0u;
+                const uint32_t hi = (c + 2 * d + 1 < ncols) ? row[c + 2 * d + 1] : 0u;
+                w[d] = lo | (hi << 16);
+            }
         }
     }
 }
 
+// The same 8 values as fp32 (exact).
+template <bool VEC>
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ x, int64_t ld, int64_t r, int64_t nrows,
+                                      int64_t c, int64_t ncols, float f[8]) {
+    uint32_t w[4];
+    load8_packed<VEC>(x, ld, r, nrows, c, ncols, w);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        f[2 * d] = bf16_lo(w[d]);
+        f[2 * d + 1] = bf16_hi(w[d]);
+    }
+}
+
 // Store 8 code bytes (w0 = bytes 0..3, w1 = bytes 4..7) at row[c ..]; bytes at columns >= ncols
-// are not written.
+// are not written. VEC (8-byte aligned rows, ncols % 8 == 0): one 8-byte store or none.
 template <bool VEC>
 __device__ __forceinline__ void store8(uint8_t* __restrict__ row, int64_t c, int64_t ncols,
                                        uint32_t w0, uint32_t w1) {
-    if (VEC && c + 8 <= ncols) {
-        *reinterpret_cast<uint2*>(row + c) = make_uint2(w0, w1);
+    if (VEC) {
+        if (c < ncols) *reinterpret_cast<uint2*>(row + c) = make_uint2(w0, w1);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -73,12 +80,13 @@ __device__ __forceinline__ void store8(uint8_t* __restrict__ row, int64_t c, int
     }
 }
 
-// Store 16 code bytes at row[c ..], masked at ncols.
+// Store 16 code bytes at row[c ..], masked at ncols. VEC (16-byte aligned rows, ncols % 16 == 0):
+// one 16-byte store or none.
 template <bool VEC>
 __device__ __forceinline__ void store16(uint8_t* __restrict__ row, int64_t c, int64_t ncols,
                                         uint4 v) {
-    if (VEC && c + 16 <= ncols) {
-        *reinterpret_cast<uint4*>(row + c) = v;
+    if (VEC) {
+        if (c < ncols) *reinterpret_cast<uint4*>(row + c) = v;
     } else {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -89,35 +97,32 @@ __device__ __forceinline__ void store16(uint8_t* __restrict__ row, int64_t c, in
 }
 
 // ------------------------------------------------------------------------------------------
-// 1x128: a 16-lane team owns one (row, K-block) group, 8 elements per lane; a workgroup covers
-// kLhsRows consecutive rows of kLhsBlocks consecutive K-blocks (one after the other), so its scale
-// stores form contiguous runs of the column-major scale columns.
+// 1x128: a 16-lane team owns one (row, K-block) group, 8 elements per lane. A unit of work is
+// kLhsRows consecutive rows of one K-block, so its scale stores are one contiguous run of a
+// column-major scale column. Units are numbered K-block fastest: the workgroups running at one
+// time read neighbouring 256-byte pieces of the same rows, i.e. contiguous stretches of x, which
+// keeps DRAM pages open (numbering them row block fastest cost 10-15% of the bandwidth). The grid
+// holds at most kLhsWgPerCu workgroups per CU; each walks the units with stride gridDim.x.
 constexpr int kLhsRowsPerTeam = 4;
 constexpr int kLhsRows = 16 * kLhsRowsPerTeam;
-constexpr int kLhsBlocks = 2;
+constexpr int kLhsWgPerCu = 8;
 
 template <bool FNUZ, bool VEC_X, bool VEC_Q>
 __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s) {
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ a_s, int64_t Kb, int64_t units) {
     const int lane16 = threadIdx.x & 15;
     const int team = threadIdx.x >> 4;
-    const int64_t mbase = static_cast<int64_t>(blockIdx.x) * kLhsRows;
-    for (int kk = 0; kk < kLhsBlocks; ++kk) {
-    const int64_t kb = static_cast<int64_t>(blockIdx.y) * kLhsBlocks + kk;
-    if (kb * kGroup >= K) break;  // uniform over the workgroup
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t rb = u / Kb;
+    const int64_t kb = u - rb * Kb;
+    const int64_t mbase = rb * kLhsRows;
     const int64_t c = kb * kGroup + lane16 * 8;
 
     float f[kLhsRowsPerTeam][8];
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) {
-        const int64_t m = mbase + r * 16 + team;
-        if (m < M) {
-            load8<VEC_X>(x + m * ldx, c, K, f[r]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[r][j] = 0.0f;
-        }
+        load8<VEC_X>(x, ldx, mbase + r * 16 + team, M, c, K, f[r]);
     }
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) {
@@ -163,13 +168,7 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
     float f[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t k = k0 + rq * 4 + i;
-        if (k < K) {
-            load8<VEC_X>(x + k * ldx, col, N, f[i]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
-        }
+        load8<VEC_X>(x, ldx, k0 + rq * 4 + i, K, col, N, f[i]);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -234,13 +233,7 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
     float f[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t n = n0 + rg * 8 + i;
-        if (n < N) {
-            load8<VEC_W>(w + n * ldw, c, K, f[i]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[i][j] = 0.0f;
-        }
+        load8<VEC_W>(w, ldw, n0 + rg * 8 + i, N, c, K, f[i]);
     }
     uint32_t am = 0;
 #pragma unroll
@@ -340,13 +333,7 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
     uint32_t w[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t r = r0 + rg * 8 + i;
-        if (r < R) {
-            load8_packed<VEC_X>(x + r * ldx, c, C, w[i]);
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) w[i][d] = 0u;
-        }
+        load8_packed<VEC_X>(x, ldx, r0 + rg * 8 + i, R, c, C, w[i]);
     }
     // element j (0..7) of row i as fp32, and its magnitude's bit pattern
     auto val = [&](int i, int j) { return (j & 1) ? bf16_hi(w[i][j >> 1]) : bf16_lo(w[i][j >> 1]); };
@@ -437,12 +424,12 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
 // The two quantizations of a linear layer's forward step in one persistent launch: the 1x128
 // row-wise groups of the activation x [M, K] (quantize_lhs) and the 128x128 blocks of the weight
 // w [N, Kw] (quantize_weight_128x128, optional transposed copy). Both are cut into 128 x 128 tiles
-// -- an activation tile holds one 1x128 group per row, a weight tile is one block -- and four
-// resident workgroups per CU walk the joint tile list (activation tiles first). The workgroups of
-// a CU drift apart, so one's loads overlap another's stores, and the two tensors share one ramp
-// and one drain instead of paying two (4096 x 4096 each: 20.2 us against 24 us for the two
-// kernels back to back). Thread t holds rows 8 (t / 16) .. + 8 x columns 8 (t % 16) .. + 8 of a
-// tile as packed bf16 pairs, as in quantize_dual_kernel.
+// -- an activation tile holds one 1x128 group per row, a weight tile is one block -- and the
+// resident workgroups (two or three per CU) walk the joint tile list (activation tiles first).
+// The workgroups of a CU drift apart, so one's loads overlap another's stores, and the two
+// tensors share one ramp and one drain instead of paying two (4096 x 4096 each: 19.3-20 us
+// against 21.7 us for the two kernels back to back). Thread t holds rows 8 (t / 16) .. + 8 x
+// columns 8 (t % 16) .. + 8 of a tile as packed bf16 pairs, as in quantize_dual_kernel.
 struct TileSrc {
     const uint16_t* base;
     int64_t ld, rows, cols, r0, c0;
@@ -451,19 +438,17 @@ struct TileSrc {
 __device__ __forceinline__ void load_tile(const TileSrc& t, int rg, int cg, uint32_t (&w)[8][4]) {
     const int64_t c = t.c0 + cg * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t r = t.r0 + rg * 8 + i;
-        if (r < t.rows) {
-            load8_packed<true>(t.base + r * t.ld, c, t.cols, w[i]);
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) w[i][d] = 0u;
-        }
-    }
+    for (int i = 0; i < 8; ++i) load8_packed<true>(t.base, t.ld, t.r0 + rg * 8 + i, t.rows, c, t.cols, w[i]);
 }
 
+// Resident workgroups per CU: the kernel needs ~155 VGPRs (three waves per SIMD), ~183 with the
+// transposed weight copy (two); bounding it to four workgroups per CU (128 VGPRs) made it spill,
+// and the waits on the scratch traffic serialised each workgroup's tiles.
+constexpr int kStepWgPerCu = 3;
+constexpr int kStepWgPerCuQT = 2;
+
 template <bool FNUZ, bool WANT_QT>
-__global__ __launch_bounds__(256, 4) void quantize_step_kernel(
+__global__ __launch_bounds__(256, 2) void quantize_step_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ qx,
     int64_t ldqx, float* __restrict__ sx, const uint16_t* __restrict__ w, int64_t N, int64_t Kw,
     int64_t ldw, uint8_t* __restrict__ qw, int64_t ldqw, uint8_t* __restrict__ qwT, int64_t ldqwT,
@@ -605,16 +590,26 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
 
 bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Compute units of the current device (256 on MI355X if the query fails).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return cus;
+}
+
 template <bool FNUZ>
 hipError_t quantize_lhs_impl(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                              int64_t ldq, float* a_s, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
-    const dim3 grid(static_cast<unsigned>((M + kLhsRows - 1) / kLhsRows),
-                    static_cast<unsigned>((Kb + kLhsBlocks - 1) / kLhsBlocks));
-    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
-    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
+    const int64_t units = (M + kLhsRows - 1) / kLhsRows * Kb;
+    const int64_t most = static_cast<int64_t>(device_cus()) * kLhsWgPerCu;
+    const dim3 grid(static_cast<unsigned>(units < most ? units : most));
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0) && (K % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0) && (K % 8 == 0);
 #define BSFP8_QL(A, B) \
-    quantize_lhs_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s)
+    quantize_lhs_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, M, K, ldx, q, ldq, a_s, Kb, units)
     if (vx && vq) BSFP8_QL(true, true);
     else if (vx) BSFP8_QL(true, false);
     else if (vq) BSFP8_QL(false, true);
@@ -628,8 +623,8 @@ hipError_t quantize_rhs_impl(const uint16_t* x, int64_t K, int64_t N, int64_t ld
                              int64_t ldqT, float* s, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const dim3 grid(static_cast<unsigned>((N + kRhsCols - 1) / kRhsCols), static_cast<unsigned>(Kb));
-    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
-    const bool vq = aligned(qT, 16) && (ldqT % 16 == 0);
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0) && (N % 8 == 0);
+    const bool vq = aligned(qT, 16) && (ldqT % 16 == 0) && (K % 16 == 0);
 #define BSFP8_QR(A, B) \
     quantize_rhs_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, K, N, ldx, qT, ldqT, s)
     if (vx && vq) BSFP8_QR(true, true);
@@ -647,9 +642,9 @@ hipError_t quantize_weight_impl(const uint16_t* w, int64_t N, int64_t K, int64_t
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const int64_t Nb = (N + kGroup - 1) / kGroup;
     const dim3 grid(static_cast<unsigned>(Kb), static_cast<unsigned>(Nb));
-    const bool vw = aligned(w, 16) && (ldw % 8 == 0);
-    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
-    const bool vt = qT != nullptr && aligned(qT, 16) && (ldqT % 16 == 0);
+    const bool vw = aligned(w, 16) && (ldw % 8 == 0) && (K % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0) && (K % 8 == 0);
+    const bool vt = qT != nullptr && aligned(qT, 16) && (ldqT % 16 == 0) && (N % 16 == 0);
 #define BSFP8_QW(A, B, C) \
     quantize_weight_kernel<FNUZ, A, B, C><<<grid, 256, 0, stream>>>(w, N, K, ldw, q, ldq, qT, ldqT, s, Kb)
     if (vw && vq && vt) BSFP8_QW(true, true, true);
@@ -669,9 +664,9 @@ hipError_t quantize_dual_impl(const uint16_t* x, int64_t R, int64_t C, int64_t l
                               int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
                               hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>((C + kGroup - 1) / kGroup), static_cast<unsigned>((R + kGroup - 1) / kGroup));
-    const bool vx = aligned(x, 16) && (ldx % 8 == 0);
-    const bool vq = aligned(q, 8) && (ldq % 8 == 0);
-    const bool vt = aligned(qT, 16) && (ldqT % 16 == 0);
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0) && (C % 8 == 0);
+    const bool vq = aligned(q, 8) && (ldq % 8 == 0) && (C % 8 == 0);
+    const bool vt = aligned(qT, 16) && (ldqT % 16 == 0) && (R % 16 == 0);
 #define BSFP8_QD(A, B, D) \
     quantize_dual_kernel<FNUZ, A, B, D><<<grid, 256, 0, stream>>>(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s)
     if (vx && vq && vt) BSFP8_QD(true, true, true);
@@ -694,12 +689,7 @@ hipError_t quantize_step_impl(const uint16_t* x, int64_t M, int64_t K, int64_t l
     const int64_t kb_x = (K + kGroup - 1) / kGroup, kb_w = (Kw + kGroup - 1) / kGroup;
     const int64_t tiles_x = (M + kGroup - 1) / kGroup * kb_x;
     const int64_t tiles_w = (N + kGroup - 1) / kGroup * kb_w;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
-    }
-    const int64_t want = static_cast<int64_t>(cus) * 4;  // four resident workgroups per CU
+    const int64_t want = static_cast<int64_t>(device_cus()) * (qwT != nullptr ? kStepWgPerCuQT : kStepWgPerCu);
     const dim3 grid(static_cast<unsigned>(tiles_x + tiles_w < want ? tiles_x + tiles_w : want));
     if (qwT != nullptr)
         quantize_step_kernel<FNUZ, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw,
@@ -742,11 +732,13 @@ hipError_t launch_quantize_step(const uint16_t* x, int64_t M, int64_t K, int64_t
                                 int64_t ldqx, float* sx, const uint16_t* w, int64_t N, int64_t Kw,
                                 int64_t ldw, uint8_t* qw, int64_t ldqw, uint8_t* qwT, int64_t ldqwT,
                                 float* sw, bool fnuz, hipStream_t stream) {
-    // the fused kernel takes the vector paths only: 16-byte bf16 rows, 8-byte code rows,
-    // 16-byte transposed rows; anything else runs the two kernels one after the other
-    const bool vec = aligned(x, 16) && ldx % 8 == 0 && aligned(w, 16) && ldw % 8 == 0 && aligned(qx, 8) &&
+    // the fused kernel takes the vector paths only: 16-byte bf16 rows with row lengths that are
+    // multiples of 8, 8-byte code rows, 16-byte transposed rows; anything else runs the two
+    // kernels one after the other
+    const bool vec = aligned(x, 16) && ldx % 8 == 0 && K % 8 == 0 && aligned(w, 16) && ldw % 8 == 0 &&
+                     Kw % 8 == 0 && aligned(qx, 8) &&
                      ldqx % 8 == 0 && aligned(qw, 8) && ldqw % 8 == 0 &&
-                     (qwT == nullptr || (aligned(qwT, 16) && ldqwT % 16 == 0));
+                     (qwT == nullptr || (aligned(qwT, 16) && ldqwT % 16 == 0 && N % 16 == 0));
     if (!vec) {
         const hipError_t e = launch_quantize_lhs(x, M, K, ldx, qx, ldqx, sx, fnuz, stream);
         if (e != hipSuccess) return e;
