@@ -119,20 +119,20 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     const int64_t mbase = rb * kLhsRows;
     const int64_t c = kb * kGroup + lane16 * 8;
 
-    float f[kLhsRowsPerTeam][8];
+    uint32_t w[kLhsRowsPerTeam][4];  // packed bf16 pairs
 #pragma unroll
-    for (int r = 0; r < kLhsRowsPerTeam; ++r) {
-        load8<VEC_X>(x, ldx, mbase + r * 16 + team, M, c, K, f[r]);
-    }
+    for (int r = 0; r < kLhsRowsPerTeam; ++r) load8_packed<VEC_X>(x, ldx, mbase + r * 16 + team, M, c, K, w[r]);
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) {
         uint32_t am = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[r][j]));
+        for (int d = 0; d < 4; ++d) am = max(am, max((w[r][d] << 16) & 0x7FFFFFFFu, w[r][d] & 0x7FFF0000u));
         am = umax_row16(am);
         const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
-        const uint32_t w0 = encode4_in_range<FNUZ>(f[r][0] * g.m, f[r][1] * g.m, f[r][2] * g.m, f[r][3] * g.m);
-        const uint32_t w1 = encode4_in_range<FNUZ>(f[r][4] * g.m, f[r][5] * g.m, f[r][6] * g.m, f[r][7] * g.m);
+        const uint32_t w0 = encode4_in_range<FNUZ>(bf16_lo(w[r][0]) * g.m, bf16_hi(w[r][0]) * g.m,
+                                                   bf16_lo(w[r][1]) * g.m, bf16_hi(w[r][1]) * g.m);
+        const uint32_t w1 = encode4_in_range<FNUZ>(bf16_lo(w[r][2]) * g.m, bf16_hi(w[r][2]) * g.m,
+                                                   bf16_lo(w[r][3]) * g.m, bf16_hi(w[r][3]) * g.m);
         const int64_t m = mbase + r * 16 + team;
         if (m < M) {  // rows >= M store neither codes nor scales
             store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
