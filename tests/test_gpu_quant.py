@@ -118,6 +118,9 @@ def test_quantize_lhs_workloads_full_size(idx):
 RHS_SHAPES = [
     (128, 64, 64, 128), (130, 70, 72, 144), (300, 129, 136, 304), (1, 5, 5, 1),
     (256, 384, 390, 260), (4096, 1024, 1024, 4096), (2048, 8192, 8192, 2048),
+    # more workgroups than one round of residents (65 x 33 > 8 per CU): K-block-fastest order,
+    # with K and N tails and padded strides
+    (8200, 2056, 2064, 8208),
 ]
 
 
