@@ -59,6 +59,9 @@ GEMM_SHAPES = [
     (2, 512, 128, 128, 512), (130, 512, 1280, 1280, 512), (1, 1, 1, 16, 1), (3, 5, 300, 304, 5),
     (128, 128, 128, 128, 128), (129, 130, 129, 144, 131), (257, 384, 520, 528, 384),
     (64, 200, 4096, 4096, 200), (300, 260, 256, 256, 262),
+    # 513 K-blocks, the last one partial: beyond the 128x128 fast path's staged B scales (general
+    # kernel); the per-column variant stays on the fast path
+    (40, 96, 65600, 65600, 96),
 ]
 
 
