@@ -32,7 +32,9 @@ STEP_SHAPES = [
     (4096, 4096, 4096, 4096, 4096, 4096, False),   # the forward step's shapes
     (2, 128, 128, 512, 128, 128, False),           # small forward case
     (130, 1280, 1280, 5120, 1280, 1280, True),     # M tail, weight with qT
-    (300, 200, 208, 130, 300, 304, True),          # ragged K, N and Kw
+    (300, 200, 208, 130, 300, 304, True),          # ragged K, N and Kw (Kw % 8 != 0: two kernels)
+    (300, 200, 208, 144, 296, 304, True),          # ragged K, N and Kw in one launch
+    (2100, 4000, 4008, 2192, 4000, 4008, True),    # several tiles per workgroup, every edge ragged
     (5, 7, 8, 3, 9, 16, False),                    # sub-group sizes
     (129, 256, 263, 256, 129, 131, True),          # odd strides: the two single-purpose kernels
 ]
@@ -69,7 +71,7 @@ def test_quantize_lhs_and_weight_parity(M, K, ldx, N, Kw, ldw, want_qT):
     _run(M, K, ldx, N, Kw, ldw, want_qT, "e4m3fn", seed=M + 3 * K + N)
 
 
-@pytest.mark.parametrize("shape", [STEP_SHAPES[2], STEP_SHAPES[3]], ids=lambda v: str(v))
+@pytest.mark.parametrize("shape", [STEP_SHAPES[2], STEP_SHAPES[3], STEP_SHAPES[4]], ids=lambda v: str(v))
 def test_quantize_lhs_and_weight_fnuz_parity(shape):
     _run(*shape, "e4m3fnuz", seed=17)
 
