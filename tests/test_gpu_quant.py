@@ -59,6 +59,7 @@ LHS_SHAPES = [
     (130, 1280, 1280, 1280),   # M tail: rows 128, 129 of the second 64-row tile
     (1, 1, 1, 1), (3, 127, 128, 127), (7, 129, 136, 129), (5, 200, 203, 211),
     (64, 256, 256, 256), (65, 384, 392, 400), (129, 4100, 4104, 4112),
+    (67, 200, 208, 208),       # vector loads and stores with a partial last K-block and an M tail
 ]
 LHS_SHAPES += [(int(m), int(k), int(k), int(k)) for m, k in _golden.table("pages_quant_shapes.txt")]
 
@@ -121,6 +122,7 @@ RHS_SHAPES = [
     # more workgroups than one round of residents (65 x 33 > 8 per CU): K-block-fastest order,
     # with K and N tails and padded strides
     (8200, 2056, 2064, 8208),
+    (208, 136, 136, 208),      # vector loads and stores, K and N tails
 ]
 
 
@@ -155,6 +157,7 @@ DUAL_SHAPES = [
     (128, 128, 128, 128, 128), (130, 1280, 1288, 1296, 144), (1, 1, 1, 1, 1),
     (257, 300, 304, 312, 272), (300, 129, 136, 144, 304), (129, 257, 264, 264, 129),
     (5, 200, 203, 211, 5), (2048, 2048, 2048, 2048, 2048), (384, 640, 640, 640, 390),
+    (272, 264, 264, 272, 272),  # vector loads and both vector stores, R and C tails
 ]
 
 
@@ -218,6 +221,7 @@ def test_quantize_lhs_and_rhs_outliers_and_zero_groups():
 W_SHAPES = [
     (512, 128, 128, 128, 512), (5120, 1280, 1280, 1280, 5120), (130, 300, 304, 312, 144),
     (5, 1, 8, 16, 16), (256, 257, 264, 272, 256), (129, 129, 130, 131, 133),
+    (144, 264, 264, 272, 144),  # vector loads and stores (qT too), N and K tails
 ]
 
 
