@@ -80,7 +80,8 @@ const char* bsfp8_status_string(int status);
  *   a_s column-major [M, ceil(K/128)] fp32 with leading dimension exactly M: the scale of row m,
  *       K-block kb is a_s[kb * M + m] (the layout of the ROCm page's root-cause comment; nothing
  *       past M * ceil(K/128) floats is written).
- * Any alignment is accepted; 16-byte-aligned rows take the vector path.
+ * Any alignment and row length are accepted; 16-byte-aligned rows whose length is a multiple of 8
+ * take the vector path (the others load and store element by element).
  */
 int quantize_lhs(const void* x, int64_t M, int64_t K, int64_t ldx,
                  void* q, int64_t ldq, float* a_s, void* stream);
