@@ -122,6 +122,10 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     uint32_t w[kLhsRowsPerTeam][4];  // packed bf16 pairs
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) load8_packed<VEC_X>(x, ldx, mbase + r * 16 + team, M, c, K, w[r]);
+    // every row is encoded before the first store: a store issued while loads are outstanding
+    // makes the wait for the next row's load also wait for that store
+    uint32_t code[kLhsRowsPerTeam][2];
+    float scale[kLhsRowsPerTeam];
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) {
         uint32_t am = 0;
@@ -129,14 +133,18 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
         for (int d = 0; d < 4; ++d) am = max(am, max((w[r][d] << 16) & 0x7FFFFFFFu, w[r][d] & 0x7FFF0000u));
         am = umax_row16(am);
         const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
-        const uint32_t w0 = encode4_in_range<FNUZ>(bf16_lo(w[r][0]) * g.m, bf16_hi(w[r][0]) * g.m,
-                                                   bf16_lo(w[r][1]) * g.m, bf16_hi(w[r][1]) * g.m);
-        const uint32_t w1 = encode4_in_range<FNUZ>(bf16_lo(w[r][2]) * g.m, bf16_hi(w[r][2]) * g.m,
-                                                   bf16_lo(w[r][3]) * g.m, bf16_hi(w[r][3]) * g.m);
+        code[r][0] = encode4_in_range<FNUZ>(bf16_lo(w[r][0]) * g.m, bf16_hi(w[r][0]) * g.m,
+                                            bf16_lo(w[r][1]) * g.m, bf16_hi(w[r][1]) * g.m);
+        code[r][1] = encode4_in_range<FNUZ>(bf16_lo(w[r][2]) * g.m, bf16_hi(w[r][2]) * g.m,
+                                            bf16_lo(w[r][3]) * g.m, bf16_hi(w[r][3]) * g.m);
+        scale[r] = g.s;
+    }
+#pragma unroll
+    for (int r = 0; r < kLhsRowsPerTeam; ++r) {
         const int64_t m = mbase + r * 16 + team;
         if (m < M) {  // rows >= M store neither codes nor scales
-            store8<VEC_Q>(q + m * ldq, c, K, w0, w1);
-            if (lane16 == 0) a_s[kb * M + m] = g.s;
+            store8<VEC_Q>(q + m * ldq, c, K, code[r][0], code[r][1]);
+            if (lane16 == 0) a_s[kb * M + m] = scale[r];
         }
     }
     }
