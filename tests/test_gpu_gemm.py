@@ -15,6 +15,7 @@ import torch
 import blockwise_scaled_fp8_act_amd as bf
 import oracle
 from blockwise_scaled_fp8_act_amd import inputs
+from tests import _golden
 from tests._gpu import DEV, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -208,6 +209,23 @@ def test_forward_small_workloads_full(idx):
     # the 2x512x128 case has a seed-dependent SQNR near 28 dB even for an exact path; the
     # 0.05 dB agreement with the oracle is the check there
     _forward_check(d["A"], d["W"], np.arange(M), sqnr_min=27.5 if idx == 0 else 28.0)
+
+
+@pytest.mark.parametrize("row", _golden.table("pages_sqnr_table.txt"),
+                         ids=lambda r: "x".join(str(int(v)) for v in r[:3]))
+def test_sqnr_at_pages_table_shapes(row):
+    """The GPU path at every shape of the ROCm page's GEMM-correctness table (SQNR 28.6-28.8 dB
+    against a BF16 matmul): within the table's band of the printed value (1.2 dB for the tiny M = 2,
+    4 outputs, 0.3 dB otherwise, as for the oracle path) and within 0.05 dB of the oracle path on
+    the same inputs (A ~ N(0,1), W ~ N(0, 0.02^2), seed 0)."""
+    M, N, K, db = int(row[0]), int(row[1]), int(row[2]), row[3]
+    g = inputs.rng(0)
+    a_h = inputs.normal_bf16(g, (M, K))
+    w_h = inputs.normal_bf16(g, (N, K), 0.02)
+    rows = np.arange(M) if M <= 128 else np.linspace(0, M - 1, 64).astype(np.int64)
+    band = 1.2 if M * N < 100000 else 0.3
+    s_gpu, _ = _forward_check(a_h, w_h, rows, sqnr_min=db - band)
+    assert abs(s_gpu - db) <= band, s_gpu
 
 
 def test_forward_4096_sampled():
