@@ -243,16 +243,16 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
     const int64_t k0 = kb * kGroup;
     const int64_t c = k0 + cg * 8;
 
-    float f[8][8];
+    // the block stays packed as bf16 pairs (32 registers rather than 64 floats), so more
+    // workgroups fit per CU
+    uint32_t wv[8][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        load8<VEC_W>(w, ldw, n0 + rg * 8 + i, N, c, K, f[i]);
-    }
+    for (int i = 0; i < 8; ++i) load8_packed<VEC_W>(w, ldw, n0 + rg * 8 + i, N, c, K, wv[i]);
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) am = max(am, abs_bits(f[i][j]));
+        for (int d = 0; d < 4; ++d) am = max(am, max((wv[i][d] << 16) & 0x7FFFFFFFu, wv[i][d] & 0x7FFF0000u));
     am = umax_wave(am);
     if ((t & 63) == 0) wmax[t >> 6] = am;
     __syncthreads();
@@ -263,8 +263,10 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
     uint32_t code[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        code[i][0] = encode4_in_range<FNUZ>(f[i][0] * g.m, f[i][1] * g.m, f[i][2] * g.m, f[i][3] * g.m);
-        code[i][1] = encode4_in_range<FNUZ>(f[i][4] * g.m, f[i][5] * g.m, f[i][6] * g.m, f[i][7] * g.m);
+        code[i][0] = encode4_in_range<FNUZ>(bf16_lo(wv[i][0]) * g.m, bf16_hi(wv[i][0]) * g.m,
+                                            bf16_lo(wv[i][1]) * g.m, bf16_hi(wv[i][1]) * g.m);
+        code[i][1] = encode4_in_range<FNUZ>(bf16_lo(wv[i][2]) * g.m, bf16_hi(wv[i][2]) * g.m,
+                                            bf16_lo(wv[i][3]) * g.m, bf16_hi(wv[i][3]) * g.m);
         const int64_t n = n0 + rg * 8 + i;
         if (n < N) store8<VEC_Q>(q + n * ldq, c, K, code[i][0], code[i][1]);
     }
