@@ -3,6 +3,8 @@
 //   quantize_lhs             1x128 groups along K (act_quant_lhs), scales column-major [M, Kb]
 //   quantize_rhs             128x1 groups down each column (act_quant_rhs), codes written transposed
 //   quantize_weight_128x128  128x128 blocks (weight_quant_rhs), optional transposed copy
+//   quantize_lhs_and_rhs     the 1x128 and the transposed 128x1 outputs of one tensor, one read
+//   quantize_lhs_and_weight  quantize_lhs(x) and quantize_weight_128x128(w) in one launch
 //
 // Operations as listed in the quantization-correctness table of "Enable blockwise FP8 dense
 // training kernels on ROCm" (block_size 128); the column-major scale layout and the rule that a
@@ -11,10 +13,10 @@
 // Every kernel is instantiated for both element formats (FNUZ = false: e4m3fn, FP8_MAX 448;
 // true: e4m3fnuz, FP8_MAX 240); only the scale pair and the final code conversion differ.
 //
-// All three are HBM-bound: every input byte is read once with 16-byte loads, every output byte is
-// written once, 16-lane (1x128) or LDS (128x1, 128x128) max reductions run on data already in
-// registers, and the transposing variants turn the tile around in LDS so global stores stay
-// contiguous along the output rows.
+// All are HBM-bound: every input byte is read once with 16-byte loads, all of a tile's loads are in
+// flight before the first wait, every output byte is written once, 16-lane (1x128) or LDS (128x1,
+// 128x128) max reductions run on data already in registers, and the transposing variants turn the
+// tile around in LDS so global stores stay contiguous along the output rows.
 #include "device_common.hpp"
 #include "launch.hpp"
 
