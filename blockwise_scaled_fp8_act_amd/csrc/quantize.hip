@@ -442,68 +442,59 @@ __global__ __launch_bounds__(256, 4) void quantize_dual_kernel(
 // row-wise groups of the activation x [M, K] (quantize_lhs) and the 128x128 blocks of the weight
 // w [N, Kw] (quantize_weight_128x128, optional transposed copy). Both are cut into 128 x 128 tiles
 // -- an activation tile holds one 1x128 group per row, a weight tile is one block -- and the
-// resident workgroups (two or three per CU) walk the joint tile list (activation tiles first).
-// The workgroups of a CU drift apart, so one's loads overlap another's stores, and the two
-// tensors share one ramp and one drain instead of paying two (4096 x 4096 each: 19.3-20 us
-// against 21.7 us for the two kernels back to back). Thread t holds rows 8 (t / 16) .. + 8 x
-// columns 8 (t % 16) .. + 8 of a tile as packed bf16 pairs, as in quantize_dual_kernel.
+// resident workgroups (two per CU, 512 threads each) walk the joint tile list (activation tiles
+// first). The workgroups of a CU drift apart, so one's loads overlap another's stores, and the two
+// tensors share one ramp and one drain instead of paying two (4096 x 4096 each: 18.8 us against
+// 21.7 us for the two kernels back to back). Thread t holds rows 4 (t / 16) .. + 4 x columns
+// 8 (t % 16) .. + 8 of a tile as packed bf16 pairs (16 registers; with 256 threads and 8 rows
+// each the kernel needed ~155 VGPRs and ran 4% slower at three workgroups per CU).
 struct TileSrc {
     const uint16_t* base;
     int64_t ld, rows, cols, r0, c0;
 };
 
-__device__ __forceinline__ void load_tile(const TileSrc& t, int rg, int cg, uint32_t (&w)[8][4]) {
-    const int64_t c = t.c0 + cg * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) load8_packed<true>(t.base, t.ld, t.r0 + rg * 8 + i, t.rows, c, t.cols, w[i]);
-}
-
-// Resident workgroups per CU: the kernel needs ~155 VGPRs (three waves per SIMD), ~183 with the
-// transposed weight copy (two); bounding it to four workgroups per CU (128 VGPRs) made it spill,
-// and the waits on the scratch traffic serialised each workgroup's tiles.
-constexpr int kStepWgPerCu = 3;
-constexpr int kStepWgPerCuQT = 2;
+constexpr int kStepThreads = 512;
+constexpr int kStepRows = 4;        // rows per thread
+constexpr int kStepWgPerCu = 2;
 
 template <bool FNUZ, bool WANT_QT>
-__global__ __launch_bounds__(256, 2) void quantize_step_kernel(
+__global__ __launch_bounds__(kStepThreads, 1) void quantize_step_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ qx,
     int64_t ldqx, float* __restrict__ sx, const uint16_t* __restrict__ w, int64_t N, int64_t Kw,
     int64_t ldw, uint8_t* __restrict__ qw, int64_t ldqw, uint8_t* __restrict__ qwT, int64_t ldqwT,
     float* __restrict__ sw, int64_t kb_x, int64_t tiles_x, int64_t kb_w, int64_t tiles_w) {
     __shared__ uint4 tileT[kGroup * 8];  // transposed weight codes, [column][8 chunks], swizzled
-    __shared__ uint32_t wmax[4];
+    __shared__ uint32_t wmax[kStepThreads / 64];
 
     const int t = threadIdx.x;
-    const int cg = t & 15;
-    const int rg = t >> 4;
+    const int cg = t & 15;   // columns 8 cg .. 8 cg + 7 of the tile
+    const int rg = t >> 4;   // rows 4 rg .. 4 rg + 3
     const int64_t total = tiles_x + tiles_w;
 
-    auto source = [&](int64_t tile) {
-        TileSrc s;
+    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        TileSrc src;
         if (tile < tiles_x) {
-            s = TileSrc{x, ldx, M, K, (tile / kb_x) * kGroup, (tile % kb_x) * kGroup};
+            src = TileSrc{x, ldx, M, K, (tile / kb_x) * kGroup, (tile % kb_x) * kGroup};
         } else {
             const int64_t b = tile - tiles_x;
-            s = TileSrc{w, ldw, N, Kw, (b / kb_w) * kGroup, (b % kb_w) * kGroup};
+            src = TileSrc{w, ldw, N, Kw, (b / kb_w) * kGroup, (b % kb_w) * kGroup};
         }
-        return s;
-    };
-
-    uint32_t cur[8][4];
-    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        const TileSrc src = source(tile);
-        load_tile(src, rg, cg, cur);
+        const int64_t c = src.c0 + cg * 8;
+        uint32_t cur[kStepRows][4];
+#pragma unroll
+        for (int i = 0; i < kStepRows; ++i)
+            load8_packed<true>(src.base, src.ld, src.r0 + rg * kStepRows + i, src.rows, c, src.cols, cur[i]);
         auto val = [&](int i, int j) { return (j & 1) ? bf16_hi(cur[i][j >> 1]) : bf16_lo(cur[i][j >> 1]); };
         auto mag = [&](int i, int j) {
             return (j & 1) ? (cur[i][j >> 1] & 0x7FFF0000u) : ((cur[i][j >> 1] << 16) & 0x7FFFFFFFu);
         };
-        const int64_t c = src.c0 + cg * 8;
+        uint32_t code[kStepRows][2];
         if (tile < tiles_x) {
             // 1x128 groups: one per tile row; the row maximum is a 16-lane DPP reduction, lane
-            // cg % 8 divides for row cg % 8 and every lane takes its rows' pairs by row broadcast
-            uint32_t rmax[8];
+            // cg % 4 divides for row cg % 4 and every lane takes its rows' pairs by row broadcast
+            uint32_t rmax[kStepRows];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kStepRows; ++i) {
                 uint32_t am = 0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) am = max(am, mag(i, j));
@@ -511,65 +502,73 @@ __global__ __launch_bounds__(256, 2) void quantize_step_kernel(
             }
             uint32_t mine = rmax[0];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) mine = (cg & 7) == i ? rmax[i] : mine;
+            for (int i = 1; i < kStepRows; ++i) mine = (cg & (kStepRows - 1)) == i ? rmax[i] : mine;
             const GroupScale gm = group_scale<FNUZ>(__uint_as_float(mine));
             const int64_t kb = src.c0 / kGroup;
+            float sc[kStepRows];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kStepRows; ++i) {
                 const float m = bcast_row16(gm.m, i);
-                const float sc = bcast_row16(gm.s, i);
-                const uint32_t w0 = encode4_in_range<FNUZ>(val(i, 0) * m, val(i, 1) * m, val(i, 2) * m, val(i, 3) * m);
-                const uint32_t w1 = encode4_in_range<FNUZ>(val(i, 4) * m, val(i, 5) * m, val(i, 6) * m, val(i, 7) * m);
-                const int64_t r = src.r0 + rg * 8 + i;
+                sc[i] = bcast_row16(gm.s, i);
+                code[i][0] = encode4_in_range<FNUZ>(val(i, 0) * m, val(i, 1) * m, val(i, 2) * m, val(i, 3) * m);
+                code[i][1] = encode4_in_range<FNUZ>(val(i, 4) * m, val(i, 5) * m, val(i, 6) * m, val(i, 7) * m);
+            }
+#pragma unroll
+            for (int i = 0; i < kStepRows; ++i) {
+                const int64_t r = src.r0 + rg * kStepRows + i;
                 if (r < M) {  // rows >= M store neither codes nor scales
-                    store8<true>(qx + r * ldqx, c, K, w0, w1);
-                    if (cg == 0) sx[kb * M + r] = sc;
+                    store8<true>(qx + r * ldqx, c, K, code[i][0], code[i][1]);
+                    if (cg == 0) sx[kb * M + r] = sc[i];
                 }
             }
         } else {
             // one 128x128 block: wave maxima combined through LDS
             uint32_t am = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kStepRows; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) am = max(am, mag(i, j));
             am = umax_wave(am);
             if ((t & 63) == 0) wmax[t >> 6] = am;
             __syncthreads();
-            am = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+            am = wmax[0];
+#pragma unroll
+            for (int v = 1; v < kStepThreads / 64; ++v) am = max(am, wmax[v]);
             const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
             const int64_t nb = src.r0 / kGroup, kb = src.c0 / kGroup;
             if (t == 0) sw[nb * kb_w + kb] = g.s;
-            uint32_t code[8][2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kStepRows; ++i) {
                 code[i][0] = encode4_in_range<FNUZ>(val(i, 0) * g.m, val(i, 1) * g.m, val(i, 2) * g.m, val(i, 3) * g.m);
                 code[i][1] = encode4_in_range<FNUZ>(val(i, 4) * g.m, val(i, 5) * g.m, val(i, 6) * g.m, val(i, 7) * g.m);
-                const int64_t n = src.r0 + rg * 8 + i;
+            }
+#pragma unroll
+            for (int i = 0; i < kStepRows; ++i) {
+                const int64_t n = src.r0 + rg * kStepRows + i;
                 if (n < N) store8<true>(qw + n * ldqw, c, Kw, code[i][0], code[i][1]);
             }
             if (WANT_QT) {
-                // 8x8 byte transpose through LDS as in quantize_weight_kernel
+                // column j of my 8 columns collects byte j of my 4 rows: one dword, rows 4 rg ..
+                // 4 rg + 3 of column 8 cg + j, i.e. dword rg % 4 of 16-byte row chunk rg / 4; the
+                // chunk is stored at position chunk ^ (column / 8) % 8
                 uint32_t* tw = reinterpret_cast<uint32_t*>(tileT);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int wsel = j >> 2;
                     const int sh = 8 * (j & 3);
-                    uint32_t lo = 0, hi = 0;
+                    uint32_t d = 0;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        lo |= ((code[i][wsel] >> sh) & 0xFFu) << (8 * i);
-                        hi |= ((code[i + 4][wsel] >> sh) & 0xFFu) << (8 * i);
-                    }
+                    for (int i = 0; i < kStepRows; ++i) d |= ((code[i][wsel] >> sh) & 0xFFu) << (8 * i);
                     const int cl = cg * 8 + j;
-                    const int chunk = (rg >> 1) ^ (cg & 7);
-                    *reinterpret_cast<uint2*>(tw + cl * 32 + chunk * 4 + (rg & 1) * 2) = make_uint2(lo, hi);
+                    const int chunk = (rg >> 2) ^ (cg & 7);
+                    tw[cl * 32 + chunk * 4 + (rg & 3)] = d;
                 }
                 __syncthreads();
+                // 8 consecutive lanes write one qT row's 128 bytes
                 const int chunk = t & 7;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const int cl = p * 32 + (t >> 3);
+                for (int p = 0; p < kGroup / (kStepThreads / 8); ++p) {
+                    const int cl = p * (kStepThreads / 8) + (t >> 3);
                     const int64_t k = src.c0 + cl;
                     if (k < Kw) {
                         const uint4 v = tileT[cl * 8 + (chunk ^ ((cl >> 3) & 7))];
@@ -709,13 +708,13 @@ hipError_t quantize_step_impl(const uint16_t* x, int64_t M, int64_t K, int64_t l
     const int64_t kb_x = (K + kGroup - 1) / kGroup, kb_w = (Kw + kGroup - 1) / kGroup;
     const int64_t tiles_x = (M + kGroup - 1) / kGroup * kb_x;
     const int64_t tiles_w = (N + kGroup - 1) / kGroup * kb_w;
-    const int64_t want = static_cast<int64_t>(device_cus()) * (qwT != nullptr ? kStepWgPerCuQT : kStepWgPerCu);
+    const int64_t want = static_cast<int64_t>(device_cus()) * kStepWgPerCu;
     const dim3 grid(static_cast<unsigned>(tiles_x + tiles_w < want ? tiles_x + tiles_w : want));
     if (qwT != nullptr)
-        quantize_step_kernel<FNUZ, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw,
+        quantize_step_kernel<FNUZ, true><<<grid, kStepThreads, 0, stream>>>(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw,
                                                                    qwT, ldqwT, sw, kb_x, tiles_x, kb_w, tiles_w);
     else
-        quantize_step_kernel<FNUZ, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw,
+        quantize_step_kernel<FNUZ, false><<<grid, kStepThreads, 0, stream>>>(x, M, K, ldx, qx, ldqx, sx, w, N, Kw, ldw, qw, ldqw,
                                                                     qwT, ldqwT, sw, kb_x, tiles_x, kb_w, tiles_w);
     return hipGetLastError();
 }
