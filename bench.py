@@ -255,12 +255,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3fn x fp8_e4m3fn -> fp32 accumulate, bf16 in/out",
+        "dtype": "fp8_e4m3fn",
         "data": "synthetic (seeded numpy PCG64, bf16 RNE)",
         "config": {
             "workload": "forward 4096^3: quantize_lhs A[4096,4096] + quantize_weight_128x128 "
                         "W[4096,4096] (one launch) + gemm_1x128_128x128 (A~N(0,1), W~N(0,0.02^2))",
             "M": M, "N": N, "K": K, "rotated_sets": len(sets),
+            "arithmetic": "bf16 in; float8_e4m3fn codes with fp32 scales; fp8 x fp8 matrix-core "
+                          "products, fp32 per-K-block rescale and accumulation; bf16 out",
             "rotated_bytes": set_bytes * len(sets),
         },
         "roofline": {
