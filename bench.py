@@ -111,6 +111,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=8, help="rotated buffer sets (cold cache)")
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="run the step for at least this long before the warm-up steps, so the "
+                        "GPU clock has settled under sustained load")
     p.add_argument("--no-rows", action="store_true", help="omit the per-kernel shape table")
     p.add_argument("--no-cpu-baseline", action="store_true", help="omit the CPU oracle leg")
     p.add_argument("--cpu-rows", type=int, default=4096, help="GEMM rows in the CPU oracle sample")
@@ -188,13 +191,15 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
+    # the chip's clock takes ~10-20 ms of sustained load to settle after an idle period (it dips
+    # first, then rises: a 4096^3 GEMM launch takes ~79 us in the first few ms and ~63 us once
+    # settled), so the steps run for at least --settle-ms before the W counted warm-up steps
     evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     t_start = TimingEvent()
     t_end = TimingEvent()
+    settle(lambda i: step(sets[i % len(sets)]), args.settle_ms, torch)
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
@@ -295,12 +300,28 @@ def main():
     print(json.dumps(out))
 
 
+def settle(fn, min_ms, torch, chunk=50):
+    """Run fn(0), fn(1), ... until at least min_ms of wall time has passed (synchronizing every
+    `chunk` calls), so the GPU's clock has settled under sustained load before timing starts."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(chunk):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return i
+
+
+SETTLE_ROW_MS = 30.0
+
+
 def _time_kernel(fn, reps, stream, torch):
     """Average duration (ms) of fn(i) over reps back-to-back launches: one HIP event pair on
-    `stream` around the whole batch, so host-side launch cost never shows as GPU time."""
-    for i in range(3):
-        fn(i)
-    torch.cuda.synchronize()
+    `stream` around the whole batch, so host-side launch cost never shows as GPU time. The
+    launches first run for SETTLE_ROW_MS so the clock has settled after the host-side set-up."""
+    settle(fn, SETTLE_ROW_MS, torch, chunk=10)
     e0, e1 = TimingEvent(), TimingEvent()
     e0.record(stream)
     for i in range(reps):
