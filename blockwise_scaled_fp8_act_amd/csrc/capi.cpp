@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -35,10 +36,32 @@ int check_device() {
 
 int finish(hipError_t e) { return e == hipSuccess ? BSFP8_OK : BSFP8_EHIP; }
 
+// Compute units per device ordinal, queried once (0 = not yet known).
+std::atomic<int> g_cus[64];
+
+}  // namespace
+
+int bsfp8::device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int cus = g_cus[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        g_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-constexpr int64_t kMaxOffset = 0xFFFFFFFFLL;
-constexpr int64_t kMaxOperandLd = kMaxOffset / 256;
+// The GEMM kernels read every operand and scale tensor through buffer resources of at most 2^31
+// bytes (a 256-row band of an operand, a whole scale tensor), so that an out-of-range lane offset
+// (2^31 plus a per-K-block advance below 2^31) is always past the end.
+constexpr int64_t kMaxRange = 0x80000000LL;
+constexpr int64_t kMaxOperandLd = kMaxRange / 256;
 
 int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                   const float* b_s, const void* c, int64_t ldc, int64_t M, int64_t N, int64_t K) {
@@ -49,12 +72,67 @@ int validate_gemm(const void* a, int64_t lda, const float* a_s, const void* b, i
     if (K == 0) return BSFP8_OK;
     if (a == nullptr || b == nullptr || a_s == nullptr || b_s == nullptr) return BSFP8_EINVAL;
     if (lda < K || ldb < K) return BSFP8_EINVAL;
-    // the kernels address a 256-row band of each operand and the scale arrays with 32-bit byte
-    // offsets
     if (lda > kMaxOperandLd || ldb > kMaxOperandLd) return BSFP8_EINVAL;
-    if (4 * M * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
+    if (4 * M * cdiv(K, kGroupEdge) > kMaxRange) return BSFP8_EINVAL;
     if (!aligned16(a) || !aligned16(b) || (lda % 16) != 0 || (ldb % 16) != 0) return BSFP8_EALIGN;
     return BSFP8_OK;
+}
+
+// Split-K workspaces (shapes whose output tiles cannot fill the chip) come from a per-device
+// stream-ordered memory pool whose memory is never returned to the system, so a call allocates
+// from the driver only until the pool has grown to its largest workspace, and calls on different
+// streams never share a buffer.
+constexpr int64_t kMaxSplitWorkspace = 256LL << 20;
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[64];
+
+hipError_t device_pool(hipMemPool_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_pool_mutex);
+    if (g_pools[dev] == nullptr) {
+        hipMemPoolProps props;
+        std::memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if ((e = hipMemPoolCreate(&pool, &props)) != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        if ((e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) return e;
+        g_pools[dev] = pool;
+    }
+    *out = g_pools[dev];
+    return hipSuccess;
+}
+
+// The GEMM with its K split when the plan asks for it: the workspace is allocated and freed in
+// stream order around the two kernels.
+hipError_t run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                    bsfp8::BScale bs, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz,
+                    hipStream_t stream) {
+    const int cus = bsfp8::device_cus();
+    const bsfp8::SplitPlan plan = bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+    float* ws = nullptr;
+    if (plan.S > 1) {
+        hipMemPool_t pool = nullptr;
+        hipError_t e = device_pool(&pool);
+        if (e != hipSuccess) return e;
+        if ((e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.bytes), pool,
+                                        stream)) != hipSuccess)
+            return e;
+    }
+    const hipError_t e = bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b),
+                                            ldb, bs, static_cast<uint16_t*>(c), ldc, M, N, K, fnuz, plan, ws,
+                                            cus, stream);
+    if (ws != nullptr) {
+        const hipError_t f = hipFreeAsync(ws, stream);
+        if (e == hipSuccess && f != hipSuccess) return f;
+    }
+    return e;
 }
 
 int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
@@ -131,18 +209,21 @@ int quantize_step_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q
         static_cast<uint8_t*>(qwT), ldqwT, sw, fnuz, static_cast<hipStream_t>(stream)));
 }
 
+// Floats a strided 128x128 scale tensor spans (the largest index read, plus one).
+int64_t bscale_extent(int64_t N, int64_t K, int64_t bs_nb, int64_t bs_kb) {
+    return (cdiv(N, kGroupEdge) - 1) * bs_nb + (cdiv(K, kGroupEdge) - 1) * bs_kb + 1;
+}
+
 int gemm_128x128_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                       const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
                       int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz, void* stream) {
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (M == 0 || N == 0) return BSFP8_OK;
     if (bs_stride_nb < 0 || bs_stride_kb < 0) return BSFP8_EINVAL;
+    if (K > 0 && 4 * bscale_extent(N, K, bs_stride_nb, bs_stride_kb) > kMaxRange) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
-    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
-                                     static_cast<const uint8_t*>(b), ldb, bs,
-                                     static_cast<uint16_t*>(c), ldc, M, N, K, fnuz,
-                                     static_cast<hipStream_t>(stream)));
+    return finish(run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, static_cast<hipStream_t>(stream)));
 }
 
 int gemm_128x1_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
@@ -150,13 +231,10 @@ int gemm_128x1_impl(const void* a, int64_t lda, const float* a_s, const void* b,
                     bool fnuz, void* stream) {
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (M == 0 || N == 0) return BSFP8_OK;
-    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
+    if (4 * N * cdiv(K, kGroupEdge) > kMaxRange) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, 0, 0, 1};
-    return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s,
-                                     static_cast<const uint8_t*>(b), ldb, bs,
-                                     static_cast<uint16_t*>(c), ldc, M, N, K, fnuz,
-                                     static_cast<hipStream_t>(stream)));
+    return finish(run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, static_cast<hipStream_t>(stream)));
 }
 
 int encode_impl(const float* x, void* q, int64_t n, bool fnuz, void* stream) {
@@ -260,10 +338,11 @@ int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s, con
                                void* stream) {
     if (E < 0 || K < 0) return BSFP8_EINVAL;
     if (E == 0 || M == 0 || N == 0) return M < 0 || N < 0 ? BSFP8_EINVAL : BSFP8_OK;
-    if (K == 0 || K % kGroupEdge != 0 || K / kGroupEdge > 512) return BSFP8_EINVAL;
+    if (K == 0 || K % kGroupEdge != 0) return BSFP8_EINVAL;
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (offsets == nullptr || b_stride < 0 || bs_stride < 0 || bs_stride_nb < 0 || bs_stride_kb < 0)
         return BSFP8_EINVAL;
+    if (4 * bscale_extent(N, K, bs_stride_nb, bs_stride_kb) > kMaxRange) return BSFP8_EINVAL;
     if (b_stride % 16 != 0) return BSFP8_EALIGN;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
@@ -279,9 +358,9 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const
                              int64_t K, void* stream) {
     if (E < 0 || K < 0) return BSFP8_EINVAL;
     if (E == 0 || M == 0 || N == 0) return M < 0 || N < 0 ? BSFP8_EINVAL : BSFP8_OK;
-    if (K == 0 || K % kGroupEdge != 0 || N % 4 != 0 || E > 65535) return BSFP8_EINVAL;
+    if (K == 0 || K % kGroupEdge != 0 || E > 65535) return BSFP8_EINVAL;
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
-    if (4 * N * cdiv(K, kGroupEdge) > kMaxOffset) return BSFP8_EINVAL;
+    if (4 * N * cdiv(K, kGroupEdge) > kMaxRange) return BSFP8_EINVAL;
     if (offsets == nullptr) return BSFP8_EINVAL;
     if (E > 1 && c_stride < (M - 1) * ldc + N) return BSFP8_EINVAL;  // expert outputs must not overlap
     if (int rc = check_device()) return rc;

@@ -10,29 +10,30 @@
 //   * the partial is multiplied by a_s[m,kb] * b_s(kb,n) and added into fp32 totals (one FMA per
 //     element per K-block) before the next K-block, as the method prescribes;
 //   * the MFMA takes B as its first operand, so a lane's four outputs are four consecutive columns n
-//     of one row m: the 128x128 rescale factor is one scalar per (lane, 16-row subtile) and the bf16
-//     epilogue writes 8 contiguous bytes per lane;
-//   * the fast kernel stages tiles in LDS with a 16-byte-chunk XOR swizzle and reads its fragments
-//     bank-conflict free (its layout is described there);
-//   * operands are read through buffer resources that end at the matrix edge: rows >= M / >= N read
-//     as zero, and their outputs are never stored; every scale read is limited to rows < M,
-//     columns < N.
-// The fast kernel (namespace fast) serves every float8_e4m3fn GEMM whose B scales it can stage
-// (per-column: N % 4 == 0; 128x128: at most 512 K-blocks), a partial last K-block included; the
-// general kernel serves the rest and the float8_e4m3fnuz operands. Both zero the bytes of a
-// partial last K-block that lie at or past K.
+//     of one row m: the 128x128 rescale factor is one scalar per (lane, 16-row subtile) and a lane
+//     holds 8 contiguous bytes of a bf16 output row;
+//   * every operand and scale is read through a raw buffer resource with the whole offset in the
+//     per-lane register, and a lane whose row, column or scale lies outside the tensor gets an
+//     out-of-range offset (geometry.hpp, whose arithmetic the CPU tests enumerate lane by lane);
+//     outputs of rows >= M or columns >= N are never stored.
+// The fast kernel (namespace fast) serves every float8_e4m3fn GEMM, a partial last K-block
+// included, and for short-and-wide shapes whose few output tiles leave most CUs idle splits K over
+// several workgroups per tile (fp32 partial tiles, summed by a second kernel; gemm_split_plan). The general kernel (namespace
+// gen) serves the float8_e4m3fnuz operands. Both zero the bytes of a partial last K-block that lie
+// at or past K.
 //
-// float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240) run on the
-// general kernel: gfx950's FP8 matrix instructions read e4m3fn, and no power-of-two rescaling
-// maps every fnuz value onto an e4m3fn value (fnuz spans 2^-10 .. 240, e4m3fn 2^-9 .. 448, and
-// 2 x 240 = 480 is not an e4m3fn value). Each fnuz code is instead widened exactly to f16 in
-// registers (its 7 magnitude bits placed under the f16 exponent field: the value times 2^-7, the
-// smallest ones as f16 subnormals) and a K-block is four v_mfma_f32_16x16x32_f16 instead of one
-// FP8 instruction -- products of two 4-significant-bit values are exact in fp32 either way, so the
-// per-K-block partials equal the fn path's arithmetic up to the exact factor 2^-14.
+// float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240): gfx950's FP8
+// matrix instructions read e4m3fn, and no power-of-two rescaling maps every fnuz value onto an
+// e4m3fn value (fnuz spans 2^-10 .. 240, e4m3fn 2^-9 .. 448, and 2 x 240 = 480 is not an e4m3fn
+// value). Each fnuz code is instead widened exactly to f16 in registers (its 7 magnitude bits placed
+// under the f16 exponent field: the value times 2^-7, the smallest ones as f16 subnormals) and a
+// K-block is four v_mfma_f32_16x16x32_f16 instead of one FP8 instruction -- products of two
+// 4-significant-bit values are exact in fp32 either way, so the per-K-block partials equal the fn
+// path's arithmetic up to the exact factor 2^-14.
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "geometry.hpp"
 #include "launch.hpp"
 
 namespace bsfp8 {
@@ -44,16 +45,7 @@ typedef float f2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef short s2v __attribute__((ext_vector_type(2)));
-
-constexpr int kBM = 256;      // workgroup rows (M)
-constexpr int kBN = 128;      // workgroup columns (N)
-constexpr int kWM = 64;       // rows per wave
-constexpr int kWN = 64;       // columns per wave
-constexpr int kWavesM = kBM / kWM;  // 4
-constexpr int kWavesN = kBN / kWN;  // 2
-constexpr int kThreads = 64 * kWavesM * kWavesN;  // 512: two waves per SIMD
-constexpr int kMSub = kWM / 16;   // 16-row subtiles per wave
-constexpr int kNSub = kWN / 16;   // 16-column subtiles per wave
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -86,8 +78,7 @@ __device__ __forceinline__ void fnuz_frag_to_f16(const v8i& f, h8v (&out)[4]) {
     for (int q = 0; q < 4; ++q) {
         const uint32_t w0 = static_cast<uint32_t>(f[2 * q]);
         const uint32_t w1 = static_cast<uint32_t>(f[2 * q + 1]);
-        typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-        const u4 h = {fnuz2_to_f16x2<0>(w0), fnuz2_to_f16x2<1>(w0), fnuz2_to_f16x2<0>(w1), fnuz2_to_f16x2<1>(w1)};
+        const u32x4 h = {fnuz2_to_f16x2<0>(w0), fnuz2_to_f16x2<1>(w0), fnuz2_to_f16x2<0>(w1), fnuz2_to_f16x2<1>(w1)};
         out[q] = __builtin_bit_cast(h8v, h);
     }
 }
@@ -109,34 +100,11 @@ struct IntTag {
     static constexpr int value = V;
 };
 
-// Workgroup -> output tile. Workgroups are dispatched round-robin over the 8 XCDs; consecutive
-// logical tiles are given to the same XCD, and logical tiles are ordered in groups of kGroupRows
-// tile-rows so the workgroups one XCD runs at the same time share A rows and B columns in its L2.
-constexpr int kXcds = 8;
-constexpr int kGroupRows = 4;
-
-__device__ __forceinline__ void tile_of(int bid, int mt, int nt, int& tm, int& tn) {
-    const int total = mt * nt;
-    int logical = bid;
-    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
-    const int per_group = kGroupRows * nt;
-    const int group = logical / per_group;
-    const int first_m = group * kGroupRows;
-    const int gsize = min(mt - first_m, kGroupRows);
-    const int in_group = logical - group * per_group;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+// Raw buffer resource over [base, base + bytes): loads at per-lane offsets >= bytes return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes),
                                              0x00020000);
 }
-
-constexpr uint32_t kOob = 0x80000000u;  // an offset past every buffer this kernel builds
 
 // Zero the bytes of a 16-byte chunk that lie at or past `valid` (valid counted from the chunk start).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int64_t valid) {
@@ -153,31 +121,43 @@ __device__ __forceinline__ v8i to_v8i(u32x4 lo, u32x4 hi) {
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// Per-workgroup addressing state. Tensors are read through buffer resources whose extent stops at
-// the last row of the matrix, so rows >= M (A) or >= N (B) read as zero; per-lane offsets are
-// 32-bit and block/subtile steps are uniform (scalar) offsets.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// ==============================================================================================
+// General kernel (float8_e4m3fnuz operands): a 256 x 128 workgroup tile of 8 waves, each a 64 x 64
+// block; A fragments and scales are loaded into registers, B tiles through LDS.
+namespace gen {
+
+constexpr int kBM = geom::kGenBM;
+constexpr int kBN = geom::kGenBN;
+constexpr int kWM = 64;
+constexpr int kWN = 64;
+constexpr int kThreads = 512;   // two waves per SIMD
+constexpr int kMSub = kWM / 16;
+constexpr int kNSub = kWN / 16;
+
+// Per-workgroup addressing state (geometry.hpp): A subtile i, B register rows p and B direct-load q
+// read through resources that start at their first tile row and end at the matrix edge; scale
+// reads carry a per-lane base (kOob outside the tensor) plus a per-K-block advance.
 struct Operands {
-    __amdgpu_buffer_rsrc_t a, b, as, bs;
-    uint32_t a_lane;          // (wave rows + l16) * lda + 32 lg  within the A tile
-    uint32_t b_lane;          // (tid / 8) * ldb + 16 (tid % 8)   within the B tile
-    uint32_t b_dma_lane;      // direct-to-LDS B load: row 16 wave + lane / 8, chunk (lane % 8) ^ (lane / 8)
-    uint32_t as_off[kMSub];   // 4 * m, or kOob for m >= M
-    uint32_t bs_off[kNSub];   // 4 * n for the per-column scales (n = first of the lane's 4), or kOob
+    __amdgpu_buffer_rsrc_t a[kMSub], b_reg[2], b_dma[2], as, bs;
+    uint32_t a_lane, b_lane, bdma_lane;
+    uint32_t as_base[kMSub];  // geom::gen_ascale_base
+    uint32_t bs_base[kNSub];  // geom::gen_bscale_base (per-column scales)
     uint32_t bs_partial;      // bit j: the lane's 4 columns of subtile j straddle column N
-    uint32_t a_sub;           // 16 * lda: A offset between consecutive 16-row subtiles
-    uint32_t b_half;          // 64 * ldb: B offset between the 2 row halves a thread loads
-    uint32_t b_eighth;        // 8 * ldb
+    int64_t M, N;
 };
 
 // A operand of K-block kb for this lane: subtile i covers rows 16 i + l16 of the wave's 64 rows and
 // bytes [32 lg, 32 lg + 32) of the block, exactly the MFMA's per-lane operand layout.
 template <bool FULL>
-__device__ __forceinline__ void load_a(v8i (&af)[kMSub], const Operands& op, int64_t kb, int64_t K, int lg) {
+__device__ __forceinline__ void load_a(v8i (&af)[kMSub], const Operands& op, int64_t kb, int64_t K, int lane) {
+    const int lg = lane >> 4;
+    const uint32_t off = op.a_lane + static_cast<uint32_t>(kb * kGroup);
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
-        const uint32_t so = static_cast<uint32_t>(i) * op.a_sub + static_cast<uint32_t>(kb * kGroup);
-        u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(op.a, op.a_lane, so, 0);
-        u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(op.a, op.a_lane + 16, so, 0);
+        u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(op.a[i], off, 0, 0);
+        u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(op.a[i], off + 16, 0, 0);
         if (!FULL) {
             const int64_t valid = K - (kb * kGroup + 32 * lg);
             lo = mask_tail(lo, valid);
@@ -187,16 +167,12 @@ __device__ __forceinline__ void load_a(v8i (&af)[kMSub], const Operands& op, int
     }
 }
 
-// B tile of K-block kb (128 rows x 128 bytes) into registers: thread t holds rows t/8 + 64 p,
-// 16-byte chunk t % 8.
-template <bool FULL>
-__device__ __forceinline__ void load_b(u32x4 (&bst)[2], const Operands& op, int64_t kb, int64_t K, int tid) {
+// B tile of a partial K-block (128 rows x 128 bytes) into registers, bytes past K zeroed.
+__device__ __forceinline__ void load_b_tail(u32x4 (&bst)[2], const Operands& op, int64_t kb, int64_t K, int tid) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const uint32_t so = static_cast<uint32_t>(p) * op.b_half + static_cast<uint32_t>(kb * kGroup);
-        u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(op.b, op.b_lane, so, 0);
-        if (!FULL) v = mask_tail(v, K - (kb * kGroup + 16 * (tid & 7)));
-        bst[p] = v;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(op.b_reg[p], op.b_lane + static_cast<uint32_t>(kb * kGroup), 0, 0);
+        bst[p] = mask_tail(v, K - (kb * kGroup + 16 * (tid & 7)));
     }
 }
 
@@ -205,57 +181,52 @@ __device__ __forceinline__ void load_b(u32x4 (&bst)[2], const Operands& op, int6
 __device__ __forceinline__ void store_b(u32x4* __restrict__ sb, const u32x4 (&bst)[2], int tid) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const int r = (tid >> 3) + 64 * p;
+        const int r = geom::gen_b_row(tid, p);
         const int ch = tid & 7;
         sb[r * 8 + (ch ^ (r & 7))] = bst[p];
     }
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // B tile of a full K-block straight from global memory into its LDS image (no registers): wave w
-// fills tile rows [16 w, 16 w + 16) with two 1 KB loads; lane i of load q lands at 16-byte position
-// (16 w + 8 q) * 8 + i, i.e. row 16 w + 8 q + i / 8, chunk position i % 8, which holds logical chunk
-// (i % 8) ^ (i / 8) of that row -- the same swizzled image store_b writes.
+// fills tile rows [16 w, 16 w + 16) with two 1 KB loads.
 __device__ __forceinline__ void dma_b(u32x4* __restrict__ sb, const Operands& op, int64_t kb, int wave) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         lds_void_t* dst = (lds_void_t*)(sb + (16 * wave + 8 * q) * 8);
-        const uint32_t so = static_cast<uint32_t>(q) * op.b_eighth + static_cast<uint32_t>(kb * kGroup);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b, dst, 16, op.b_dma_lane, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(op.b_dma[q], dst, 16, op.bdma_lane + static_cast<uint32_t>(kb * kGroup), 0, 0, 0);
     }
 }
 
 template <bool PER_COL>
 __device__ __forceinline__ void load_scales(float (&as)[kMSub], u32x4 (&bsv)[kNSub], float& bscal,
                                             const Operands& op, const float* __restrict__ b_s,
-                                            int64_t bs_nb, int64_t bs_kb, int64_t kb, int64_t M,
-                                            int64_t N, int tn) {
-    const uint32_t col = static_cast<uint32_t>(kb * M * 4);
+                                            int64_t bs_nb, int64_t bs_kb, int64_t kb, int tn) {
+    const uint32_t acol = static_cast<uint32_t>(4 * kb * op.M);
 #pragma unroll
     for (int i = 0; i < kMSub; ++i)
-        as[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(op.as, op.as_off[i], col, 0));
+        as[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(op.as, op.as_base[i] + acol, 0, 0));
     if (PER_COL) {
-        const uint32_t row = static_cast<uint32_t>(kb * N * 4);
+        const uint32_t brow = static_cast<uint32_t>(4 * kb * op.N);
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
             if (op.bs_partial & (1u << j)) {  // the quad straddles column N: per-element loads
-                const int64_t n = op.bs_off[j] / 4;
+                const int64_t n = op.bs_base[j] / 4;
                 u32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[e] = (n + e < N) ? __builtin_amdgcn_raw_buffer_load_b32(op.bs, op.bs_off[j] + 4 * e, row, 0) : 0u;
+                    v[e] = (n + e < op.N) ? __builtin_amdgcn_raw_buffer_load_b32(op.bs, op.bs_base[j] + 4 * e + brow, 0, 0) : 0u;
                 bsv[j] = v;
             } else {
-                bsv[j] = __builtin_amdgcn_raw_buffer_load_b128(op.bs, op.bs_off[j], row, 0);
+                bsv[j] = __builtin_amdgcn_raw_buffer_load_b128(op.bs, op.bs_base[j] + brow, 0, 0);
             }
         }
     } else {
+        // the tile's one 128-column block (tiles exist only for columns below N)
         bscal = b_s[static_cast<int64_t>(tn) * bs_nb + kb * bs_kb];
     }
 }
 
-template <bool PER_COL, bool FNUZ>
+template <bool PER_COL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s,
@@ -269,13 +240,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     int tm, tn;
-    tile_of(blockIdx.x, mt, nt, tm, tn);
+    geom::tile_of(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * kBM;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int64_t mw = m0 + kWM * wm;
-    const int64_t nw = n0 + kWN * wn;
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const int64_t Kfull = K / kGroup;  // K-blocks with all 128 columns in range
 
@@ -283,28 +252,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     {
         const int64_t arows = (M - m0) < kBM ? (M - m0) : kBM;
         const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
-        op.a = make_rsrc(A + m0 * lda, static_cast<uint32_t>(arows * lda));
-        op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
-        op.as = make_rsrc(a_s, static_cast<uint32_t>(M * Kb * 4));
-        op.bs = make_rsrc(b_s, PER_COL ? static_cast<uint32_t>(N * Kb * 4) : 0u);
-        op.a_lane = static_cast<uint32_t>((kWM * wm + l16) * lda + 32 * lg);
-        op.b_lane = static_cast<uint32_t>((tid >> 3) * ldb + 16 * (tid & 7));
-        op.a_sub = static_cast<uint32_t>(16 * lda);
-        op.b_half = static_cast<uint32_t>(64 * ldb);
-        op.b_eighth = static_cast<uint32_t>(8 * ldb);
-        op.b_dma_lane = static_cast<uint32_t>((16 * wave + (lane >> 3)) * ldb + 16 * ((lane & 7) ^ (lane >> 3)));
 #pragma unroll
-        for (int i = 0; i < kMSub; ++i) {
-            const int64_t m = mw + 16 * i + l16;
-            op.as_off[i] = m < M ? static_cast<uint32_t>(4 * m) : kOob;
+        for (int i = 0; i < kMSub; ++i)
+            op.a[i] = make_rsrc(A + (m0 + geom::gen_a_first_row(i)) * lda, geom::gen_a_range(i, arows, lda));
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            op.b_reg[p] = make_rsrc(B + (n0 + geom::gen_b_first_row(p)) * ldb, geom::gen_b_range(p, brows, ldb));
+            op.b_dma[p] = make_rsrc(B + (n0 + geom::gen_bdma_first_row(p)) * ldb, geom::gen_bdma_range(p, brows, ldb));
         }
+        op.as = make_rsrc(a_s, M * Kb * 4);
+        op.bs = make_rsrc(b_s, PER_COL ? N * Kb * 4 : 0);
+        op.a_lane = geom::gen_a_lane(wm, lane, lda);
+        op.b_lane = geom::gen_b_lane(tid, ldb);
+        op.bdma_lane = geom::gen_bdma_lane(wave, lane, ldb);
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) op.as_base[i] = geom::gen_ascale_base(m0, wm, i, lane, M);
         op.bs_partial = 0u;
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
-            const int64_t n = nw + 16 * j + 4 * lg;
-            op.bs_off[j] = n < N ? static_cast<uint32_t>(4 * n) : kOob;
-            if (n < N && n + 4 > N) op.bs_partial |= 1u << j;
+            const int64_t n = geom::gen_col(n0, wn, j, lane);
+            op.bs_base[j] = geom::gen_bscale_base(n, N);
+            if (geom::gen_bscale_straddles(n, N)) op.bs_partial |= 1u << j;
         }
+        op.M = M;
+        op.N = N;
     }
 
     v4f acc[kMSub][kNSub];
@@ -322,14 +293,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         // prologue: B(0) -> LDS[0]; A(0) and scales(0) -> registers
         if (Kfull > 0) {
             dma_b(sB[0], op, 0, wave);
-            load_a<true>(af[0], op, 0, K, lg);
+            load_a<true>(af[0], op, 0, K, lane);
         } else {
             u32x4 bst[2];
-            load_b<false>(bst, op, 0, K, tid);
+            load_b_tail(bst, op, 0, K, tid);
             store_b(sB[0], bst, tid);
-            load_a<false>(af[0], op, 0, K, lg);
+            load_a<false>(af[0], op, 0, K, lane);
         }
-        load_scales<PER_COL>(as[0], bsv[0], bscal[0], op, b_s, bs_nb, bs_kb, 0, M, N, tn);
+        load_scales<PER_COL>(as[0], bsv[0], bscal[0], op, b_s, bs_nb, bs_kb, 0, tn);
         __syncthreads();
 
         // One K-block; the buffer index is a compile-time constant so every register array stays
@@ -344,102 +315,70 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                 if (more) {
                     if (next_full) {
                         dma_b(sB[nxt], op, kb + 1, wave);
-                        load_a<true>(af[nxt], op, kb + 1, K, lg);
+                        load_a<true>(af[nxt], op, kb + 1, K, lane);
                     } else {
-                        load_a<false>(af[nxt], op, kb + 1, K, lg);
+                        load_a<false>(af[nxt], op, kb + 1, K, lane);
                     }
-                    load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, M, N, tn);
+                    load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, tn);
                 }
             };
-            // fnuz: the next block's loads are issued once this block's A codes are all widened
-            // (half way through, see below), so the two never hold registers together
+            // the next block's loads are issued once this block's A codes are all widened (half
+            // way through, see below), so the two never hold registers together
             constexpr int kHalf = kMSub / 2;
-            h8v ac[FNUZ ? kHalf : 1][4];
-            if constexpr (!FNUZ) issue_next();
-            // this K-block: partial products of every 16x16 subtile, rescaled into the totals.
-            // Software pipeline over the 8 column subtiles: the B fragment of subtile j+1 is read
-            // from LDS while subtile j's four MFMAs run, and subtile j-1's partials are rescaled
-            // into the totals between them (one MFMA, then four FMAs).
+            h8v ac[kHalf][4];
             const u32x4* sb = sB[cur];
             float f[kMSub];
 #pragma unroll
             for (int i = 0; i < kMSub; ++i) {
                 f[i] = PER_COL ? as[cur][i] : as[cur][i] * bscal[cur];
-                if (FNUZ) f[i] *= 16384.0f;  // 2^14: both widened operands carry 2^-7
+                f[i] *= 16384.0f;  // 2^14: both widened operands carry 2^-7
             }
             auto read_bf = [&](int j) {
                 const int r = kWN * wn + 16 * j + l16;
                 return to_v8i(sb[r * 8 + ((2 * lg) ^ (r & 7))], sb[r * 8 + ((2 * lg + 1) ^ (r & 7))]);
             };
-            auto rescale = [&](int j, const v4f (&pj)[kMSub]) {
+            // A widened to f16 takes twice the registers of its codes, so the wave's 64 rows are
+            // done as two halves of 32: per half, the two A fragments are widened once and each B
+            // fragment is read and widened once; one B fragment and one set of partials are live
+            // at a time (the other wave of the SIMD covers the latencies).
 #pragma unroll
-                for (int i = 0; i < kMSub; ++i) {
-                    if (PER_COL) {
+            for (int h = 0; h < 2; ++h) {
+                if (h == 1) {
+                    // the B fragments are read again rather than kept widened from the first half
+                    // (the clobbers keep the compiler from merging the two reads), and the second
+                    // half's A fragments pass through an empty asm here so that their widening
+                    // cannot be hoisted into the first half
+                    asm volatile("" ::: "memory");
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j][e] = fmaf(pj[i][e], f[i] * __uint_as_float(bsv[cur][j][e]), acc[i][j][e]);
-                    } else {
+                    for (int i = kHalf; i < kMSub; ++i)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(pj[i][e], f[i], acc[i][j][e]);
-                    }
+                        for (int d = 0; d < 8; ++d) asm volatile("" : "+v"(af[cur][i][d]));
                 }
-            };
-            if constexpr (FNUZ) {
-                // A widened to f16 takes twice the registers of its codes, so the wave's 64 rows are
-                // done as two halves of 32: per half, the two A fragments are widened once and each
-                // B fragment is read and widened once; one B fragment and one set of partials are
-                // live at a time (the other wave of the SIMD covers the latencies).
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    if (h == 1) {
-                        // the B fragments are read again rather than kept widened from the first
-                        // half (the clobbers keep the compiler from merging the two reads), and the
-                        // second half's A fragments pass through an empty asm here so that their
-                        // widening cannot be hoisted into the first half
-                        asm volatile("" ::: "memory");
+                for (int i = 0; i < kHalf; ++i) fnuz_frag_to_f16(af[cur][h * kHalf + i], ac[i]);
+                if (h == 1) issue_next();
 #pragma unroll
-                        for (int i = kHalf; i < kMSub; ++i)
+                for (int j = 0; j < kNSub; ++j) {
+                    // one B fragment in flight at a time (a memory clobber stops the compiler from
+                    // hoisting the next fragment's read above this one's use)
+                    if (j > 0) asm volatile("" ::: "memory");
+                    h8v bc[4];
+                    fnuz_frag_to_f16(read_bf(j), bc);
 #pragma unroll
-                            for (int d = 0; d < 8; ++d) asm volatile("" : "+v"(af[cur][i][d]));
-                    }
+                    for (int i = 0; i < kHalf; ++i) {
+                        const v4f p = mfma_f16_kblock(bc, ac[i]);
+                        const int ii = h * kHalf + i;
 #pragma unroll
-                    for (int i = 0; i < kHalf; ++i) fnuz_frag_to_f16(af[cur][h * kHalf + i], ac[i]);
-                    if (h == 1) issue_next();
-#pragma unroll
-                    for (int j = 0; j < kNSub; ++j) {
-                        // one B fragment in flight at a time (a memory clobber stops the compiler
-                        // from hoisting the next fragment's read above this one's use)
-                        if (j > 0) asm volatile("" ::: "memory");
-                        h8v bc[4];
-                        fnuz_frag_to_f16(read_bf(j), bc);
-#pragma unroll
-                        for (int i = 0; i < kHalf; ++i) {
-                            const v4f p = mfma_f16_kblock(bc, ac[i]);
-                            const int ii = h * kHalf + i;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float fe = PER_COL ? f[ii] * __uint_as_float(bsv[cur][j][e]) : f[ii];
-                                acc[ii][j][e] = fmaf(p[e], fe, acc[ii][j][e]);
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            const float fe = PER_COL ? f[ii] * __uint_as_float(bsv[cur][j][e]) : f[ii];
+                            acc[ii][j][e] = fmaf(p[e], fe, acc[ii][j][e]);
                         }
                     }
                 }
-            } else {
-                v8i bf[2];
-                v4f pp[2][kMSub];
-                bf[0] = read_bf(0);
-#pragma unroll
-                for (int j = 0; j < kNSub; ++j) {
-                    if (j + 1 < kNSub) bf[(j + 1) & 1] = read_bf(j + 1);
-#pragma unroll
-                    for (int i = 0; i < kMSub; ++i) pp[j & 1][i] = mfma_fp8_16x16x128(bf[j & 1], af[cur][i]);
-                    if (j > 0) rescale(j - 1, pp[(j - 1) & 1]);
-                }
-                rescale(kNSub - 1, pp[(kNSub - 1) & 1]);
             }
             if (more && !next_full) {  // ragged last K-block: masked register path
                 u32x4 bst[2];
-                load_b<false>(bst, op, kb + 1, K, tid);
+                load_b_tail(bst, op, kb + 1, K, tid);
                 store_b(sB[nxt], bst, tid);
             }
             __syncthreads();
@@ -453,12 +392,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     // epilogue: lane holds C[m][n .. n+3] of every subtile
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
-        const int64_t m = mw + 16 * i + l16;
+        const int64_t m = m0 + geom::gen_a_row(wm, i, lane);
         if (m >= M) continue;
         uint16_t* crow = C + m * ldc;
 #pragma unroll
         for (int j = 0; j < kNSub; ++j) {
-            const int64_t n = nw + 16 * j + 4 * lg;
+            const int64_t n = geom::gen_col(n0, wn, j, lane);
             const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
             if (c_vec && n + 4 <= N) {
@@ -474,14 +413,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     }
 }
 
+}  // namespace gen
+
 // ==============================================================================================
-// Fast path (per-column scales: N % 4 == 0; 128x128 scales: at most 512 K-blocks): a 256 x 256
-// workgroup tile of 8 waves, two per SIMD, each wave owning a 64 x 128 block of the tile (128 fp32
-// totals in VGPRs).
+// Fast kernel: a 256 x 256 workgroup tile of 8 waves, two per SIMD, each wave owning a 64 x 128
+// block of the tile (128 fp32 totals in VGPRs).
 //   * Every K-block's A tile (256 x 128 bytes), B tile (256 x 128 bytes) and scale slices go
-//     global -> LDS by direct buffer loads (no registers) into one of two LDS stages, one K-block
-//     ahead of the block being multiplied. Each wave loads 1/8 of every tile; the workgroup barrier
-//     that follows each wave's wait for its own loads makes the stage visible to all.
+//     global -> LDS by direct buffer loads (no registers) into one of two LDS stages. Each wave
+//     loads 1/8 of every tile; a workgroup barrier that follows each wave's wait for its own loads
+//     makes a stage visible to all.
 //   * Two waves per SIMD: while one waits at the barrier or for LDS data, the other keeps the
 //     matrix core busy. Per K-block and CU: 64 KB written to LDS and 192 KB read from it against
 //     2048 MFMA cycles per SIMD.
@@ -489,19 +429,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 //     read touches (per lane group) fall in 16 distinct groups of 4 banks.
 namespace fast {
 
-constexpr int kBM = 256;
-constexpr int kBN = 256;
+constexpr int kBM = geom::kFastBM;
+constexpr int kBN = geom::kFastBN;
 constexpr int kWM = 64;
 constexpr int kWN = 128;
-constexpr int kWaves = 8;              // 4 (M) x 2 (N): two per SIMD
-constexpr int kThreads = 64 * kWaves;  // 512
-constexpr int kMSub = kWM / 16;        // 4
-constexpr int kNSub = kWN / 16;        // 8
+constexpr int kWaves = geom::kFastWaves;  // 4 (M) x 2 (N): two per SIMD
+constexpr int kThreads = 64 * kWaves;     // 512
+constexpr int kMSub = kWM / 16;           // 4
+constexpr int kNSub = kWN / 16;           // 8
 constexpr int kStages = 2;
-constexpr int kMaxKbFast = 512;        // 128x128 B scales of the tile's columns, kept in LDS
 
 // LDS image of one stage (16-byte units): A tile rows 0..255, B tile rows 0..255, then the A scales
-// of the tile rows and the per-column B scales of the tile columns.
+// of the tile rows and the B scales (per column: of the tile columns; 128x128: of the tile's two
+// column blocks, floats 0 and 1).
 constexpr int kStageA = 0;
 constexpr int kStageB = kStageA + kBM * 8;
 constexpr int kStageSA = kStageB + kBN * 8;
@@ -509,86 +449,107 @@ constexpr int kStageSB = kStageSA + kBM / 4;
 constexpr int kStageSize = kStageSB + kBN / 4;  // 4224 x 16 B = 66 KB
 
 // vector-memory instructions each wave issues per stage: 4 A loads, 4 B loads (8 rows of 128 bytes
-// each), the A scales and (per-column) the B scales of 32 rows / columns
-constexpr int kLoadsPerStage(bool per_col) { return 4 + 4 + 1 + (per_col ? 1 : 0); }
+// each), the A scales of 32 rows, the B scales (32 columns, or the two column-block scales)
+constexpr int kLoads = 10;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-// Expert grouping of one launch (MoE): kGroupRows -- experts own row ranges of A and C and bring
-// their own B (forward, dgrad); kGroupK -- experts own token (K) ranges and write their own C
-// (weight gradient).
+// One launch's work split: kGroupRows -- experts own row ranges of A and C and bring their own B
+// (forward, dgrad); kGroupK -- experts own token (K) ranges and write their own C (weight
+// gradient); kSplitK -- slice blockIdx.y of gridDim.y owns a range of K-blocks and writes an fp32
+// partial tile (summed by split_reduce_kernel).
 constexpr int kGroupNone = 0;
 constexpr int kGroupRows = 1;
 constexpr int kGroupK = 2;
+constexpr int kSplitK = 3;
 struct Grouping {
     const int64_t* offsets;  // E + 1 boundaries (device memory)
     int64_t E;
     int64_t b_stride;   // bytes between consecutive experts' B            (kGroupRows)
     int64_t bs_stride;  // floats between consecutive experts' B scales    (kGroupRows)
-    int64_t c_stride;   // elements between consecutive experts' C         (kGroupK)
+    int64_t c_stride;   // elements between consecutive experts' C (kGroupK); floats per partial (kSplitK)
 };
 
 struct Ops {
-    __amdgpu_buffer_rsrc_t a, b, as, bs;
-    uint32_t a_lane[2];  // tile row 32 wave + lane / 8, chunk (lane % 8) ^ swz(row) for loads q even / odd
-    uint32_t b_lane[2];  // same for B
-    uint32_t as_lane;    // 4 (m0 + 32 wave + 4 lane): 4 A scales per lane (lanes 0..7)
-    uint32_t bs_lane;    // 4 (n0 + 32 wave + 4 lane): 4 B scales per lane (lanes 0..7)
-    uint32_t a_eighth;   // 8 lda
-    uint32_t b_eighth;   // 8 ldb
+    __amdgpu_buffer_rsrc_t a[4], b[4];  // operand load q reads through a[q] / b[q] (from tile row 8 q)
+    __amdgpu_buffer_rsrc_t as, bs;
+    uint32_t a_lane[2];  // geom::fast_operand_lane for loads of parity 0 / 1
+    uint32_t b_lane[2];
+    uint32_t as_base;    // geom::fast_ascale_base
+    uint32_t bs_base;    // geom::fast_bscale_col_base / fast_bscale_blk_base
+    int64_t as_step;     // bytes between K-blocks of the A scales (4 M)
+    int64_t bs_step;     // ... of the B scales (4 N per column; 4 bs_kb for 128x128)
     uint32_t lds;        // LDS byte address of stage 0
 };
 
-// One direct load, 16 bytes per lane to LDS address lds + 16 * lane; M0 is saved and restored.
-__device__ __forceinline__ void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff))
-        : "memory");
+// A wave-uniform 64-bit lane mask in scalar registers. readfirstlane returns a signed int: each half
+// goes through uint32_t so a low half with bit 31 set does not sign-extend into the high half.
+__device__ __forceinline__ uint64_t uniform_mask(uint64_t lanes) {
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(lanes >> 32)));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(lanes)));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// The same for lanes 0 .. 7 only. A direct load writes LDS for every active lane (lanes whose offset
-// is out of range write zeros), so the lanes beyond a scale slice are switched off; EXEC is changed
-// and restored inside the asm block rather than through a branch, which would split the K-block's
-// straight-line code.
-__device__ __forceinline__ void dma16_8lanes(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+// One direct load to LDS address lds + 16 * lane (16 bytes per lane), for the lanes set in both
+// EXEC and `lanes` (a wave-uniform mask); the scalar offset is zero. A direct load writes LDS for
+// every active lane (lanes whose offset is out of range write zeros), so every lane of a load that
+// is not wanted is switched off. EXEC and M0 are changed and restored inside the asm block rather
+// than through a branch, which would split the K-block's straight-line code (a uniform branch there
+// makes the register allocator spill).
+__device__ __forceinline__ void dma16(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint64_t lanes) {
     uint32_t saved_m0;
     uint64_t saved_exec;
     asm volatile(
         "s_mov_b64 %1, exec\n\t"
-        "s_mov_b32 exec_lo, 0xff\n\t"
-        "s_mov_b32 exec_hi, 0\n\t"
+        "s_and_b64 exec, exec, %5\n\t"
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
-        "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
+        "buffer_load_dwordx4 %3, %4, 0 offen lds\n\t"
         "s_mov_b32 m0, %0\n\t"
         "s_mov_b64 exec, %1"
         : "=&s"(saved_m0), "=&s"(saved_exec)
-        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r),
-          "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(uniform_mask(lanes))
         : "memory");
 }
 
-// Load number q of a stage, q = 0 .. kLoadsPerStage - 1: 0..3 A rows 32 wave + 8 q .., 4..7 B rows
-// 32 wave + 8 (q - 4) .., 8 the A scales of rows 32 wave .. + 32, 9 (per-column) the B scales of
-// columns 32 wave .. + 32. The loads of one stage can be spread over a K-block.
+// The same with 4 bytes per lane, to LDS address lds + 4 * lane.
+__device__ __forceinline__ void dma4(uint32_t lds, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint64_t lanes) {
+    uint32_t saved_m0;
+    uint64_t saved_exec;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\t"
+        "s_and_b64 exec, exec, %5\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "buffer_load_dword %3, %4, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_mov_b64 exec, %1"
+        : "=&s"(saved_m0), "=&s"(saved_exec)
+        : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r), "s"(uniform_mask(lanes))
+        : "memory");
+}
+
+// Load number q of a stage, q = 0 .. kLoads - 1: 0..3 A rows 32 wave + 8 q .., 4..7 B rows
+// 32 wave + 8 (q - 4) .., 8 the A scales of rows 32 wave .. + 32, 9 the B scales (per column: of
+// columns 32 wave .. + 32; 128x128: the two column-block scales, by wave 0). `on` (wave-uniform)
+// false: the load is issued with no lane enabled, so nothing is read or written. Every offset is
+// the lane's offset in the load's resource (a position in the tensor, or kOob for a scale outside
+// it) plus this K-block's advance.
 template <bool PER_COL>
-__device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb,
-                                           int64_t M, int64_t N, int wave) {
-    const uint32_t k = static_cast<uint32_t>(kb * kGroup);
+__device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb, int wave,
+                                           bool on = true) {
+    const uint32_t k = geom::fast_operand_advance(kb);
+    const uint64_t all = on ? ~0ull : 0ull;
+    const uint64_t half = on ? 0xFFFFFFFFull : 0ull;
     if (q < 4) {
-        dma16(stage_base + (kStageA + (32 * wave + 8 * q) * 8) * 16, op.a, op.a_lane[q & 1], q * op.a_eighth + k);
+        dma16(stage_base + (kStageA + (32 * wave + 8 * q) * 8) * 16, op.a[q], op.a_lane[q & 1] + k, all);
     } else if (q < 8) {
-        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 4)) * 8) * 16, op.b, op.b_lane[q & 1], (q - 4) * op.b_eighth + k);
+        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 4)) * 8) * 16, op.b[q - 4], op.b_lane[q & 1] + k, all);
     } else if (q == 8) {
-        dma16_8lanes(stage_base + (kStageSA + 8 * wave) * 16, op.as, op.as_lane, static_cast<uint32_t>(kb * M * 4));
-    } else if (PER_COL && q == 9) {
-        dma16_8lanes(stage_base + (kStageSB + 8 * wave) * 16, op.bs, op.bs_lane, static_cast<uint32_t>(kb * N * 4));
+        dma4(stage_base + kStageSA * 16 + 128 * wave, op.as, op.as_base + static_cast<uint32_t>(kb * op.as_step), half);
+    } else if (PER_COL) {
+        dma4(stage_base + kStageSB * 16 + 128 * wave, op.bs, op.bs_base + static_cast<uint32_t>(kb * op.bs_step), half);
+    } else {
+        dma4(stage_base + kStageSB * 16, op.bs, op.bs_base + static_cast<uint32_t>(kb * op.bs_step),
+             on && wave == 0 ? 0x3ull : 0ull);
     }
 }
 
@@ -612,7 +573,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt,
     int nt, int c_vec, Grouping grp) {
     __shared__ u32x4 smem[kStages * kStageSize];
-    __shared__ float bscale_lds[2][kMaxKbFast];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -622,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     int tm, tn;
-    tile_of(blockIdx.x, mt, nt, tm, tn);
+    geom::tile_of(blockIdx.x, mt, nt, tm, tn);
     int64_t m0 = static_cast<int64_t>(tm) * kBM;  // this tile's rows are [m0, min(m0 + kBM, m_end))
     int64_t m_end = M;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
@@ -655,7 +615,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         b_s += e * grp.bs_stride;
     } else if (GROUP == kGroupK) {
         // expert e = blockIdx.y owns the K-blocks [offsets[e] / 128, offsets[e + 1] / 128) of A and B
-        // (token ranges of the weight gradient) and writes its own C
+        // (token ranges of the weight gradient, multiples of 128) and writes its own C
         const int64_t e = blockIdx.y;
         const int64_t lo = min(max(grp.offsets[e], int64_t{0}), K);
         const int64_t hi = min(max(grp.offsets[e + 1], lo), K);
@@ -666,28 +626,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         a_s += kb0 * M;
         b_s += PER_COL ? kb0 * N : kb0 * bs_kb;
         C += e * grp.c_stride;
+    } else if (GROUP == kSplitK) {
+        // slice s owns K-blocks [kb0, kb1) of the whole K and stops at K in the last one
+        const int64_t KbT = Kb;
+        const int64_t kb0 = geom::split_begin(KbT, gridDim.y, blockIdx.y);
+        const int64_t kb1 = geom::split_begin(KbT, gridDim.y, blockIdx.y + 1);
+        Kb = kb1 - kb0;
+        K = min(K, kb1 * kGroup) - kb0 * kGroup;
+        A += kb0 * kGroup;
+        B += kb0 * kGroup;
+        a_s += kb0 * M;
+        b_s += PER_COL ? kb0 * N : kb0 * bs_kb;
     }
-    constexpr int kLoads = kLoadsPerStage(PER_COL);
 
     Ops op;
     {
         const int64_t arows = (m_end - m0) < kBM ? (m_end - m0) : kBM;
         const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
-        op.a = make_rsrc(A + m0 * lda, static_cast<uint32_t>(arows * lda));
-        op.b = make_rsrc(B + n0 * ldb, static_cast<uint32_t>(brows * ldb));
-        op.as = make_rsrc(a_s, static_cast<uint32_t>(M * Kb * 4));
-        op.bs = make_rsrc(b_s, PER_COL ? static_cast<uint32_t>(N * Kb * 4) : 0u);
-        // row 32 wave + 8 q + lane / 8 has swz = (4 q + lane / 16) % 8, which depends on q % 2
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            op.a[q] = make_rsrc(A + (m0 + geom::fast_operand_first_row(q)) * lda, geom::fast_operand_range(q, arows, lda));
+            op.b[q] = make_rsrc(B + (n0 + geom::fast_operand_first_row(q)) * ldb, geom::fast_operand_range(q, brows, ldb));
+        }
+        op.as = make_rsrc(a_s, M * Kb * 4);
+        op.bs = make_rsrc(b_s, PER_COL ? N * Kb * 4 : 4 * geom::bscale_blk_extent(N, Kb, bs_nb, bs_kb));
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
-            const int chunk = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
-            op.a_lane[par] = static_cast<uint32_t>((32 * wave + (lane >> 3)) * lda + 16 * chunk);
-            op.b_lane[par] = static_cast<uint32_t>((32 * wave + (lane >> 3)) * ldb + 16 * chunk);
+            op.a_lane[par] = geom::fast_operand_lane(wave, par, lane, lda);
+            op.b_lane[par] = geom::fast_operand_lane(wave, par, lane, ldb);
         }
-        op.as_lane = static_cast<uint32_t>(4 * (m0 + 32 * wave + 4 * lane));
-        op.bs_lane = static_cast<uint32_t>(4 * (n0 + 32 * wave + 4 * lane));
-        op.a_eighth = static_cast<uint32_t>(8 * lda);
-        op.b_eighth = static_cast<uint32_t>(8 * ldb);
+        op.as_base = geom::fast_ascale_base(m0, m_end, wave, lane);
+        op.as_step = 4 * M;
+        if (PER_COL) {
+            op.bs_base = geom::fast_bscale_col_base(n0, N, wave, lane);
+            op.bs_step = 4 * N;
+        } else {
+            op.bs_base = geom::fast_bscale_blk_base(tn, N, bs_nb, wave, lane);
+            op.bs_step = 4 * bs_kb;
+        }
         op.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
     }
 
@@ -704,122 +680,184 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         // bytes to the four lane groups' 32 operand bytes gives the same dot product as long as A
         // and B use the same one; this one makes every ds_read_b128 conflict free at the full LDS
         // rate (4 cycles per instruction on gfx950, where chunks 2 lg and 2 lg + 1 take 8).
-        const int sw = swz(l16);  // the same for every fragment row 16 x + l16
+        const int sw = geom::lds_swizzle(l16);  // the same for every fragment row 16 x + l16
         const int pos_lo = lg ^ sw;
         const int pos_hi = (lg + 4) ^ sw;
 
         // prologue: block 0 into stage 0
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, M, N, wave);
-
-        // 128x128 B scales of the tile's two 128-column blocks for every K-block, fetched while
-        // block 0 is in flight (their wait covers both)
-        if (!PER_COL) {
-            for (int64_t c = tid; c < 2 * Kb; c += kThreads) {
-                const int half = c >= Kb;
-                const int64_t kb = c - half * Kb;
-                const int64_t nb = 2 * static_cast<int64_t>(tn) + half;
-                // a column block past N is never stored; read block 0's scale instead
-                bscale_lds[half][kb] = b_s[(nb * kGroup < N ? nb : 0) * bs_nb + kb * bs_kb];
-            }
-        }
+        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, wave);
         wait_own_loads<0>();
 
-        // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its DMA loads read whole
+        // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its loads read whole
         // 128-byte rows, so bytes at and past K (row padding, or the start of the next row) are
-        // zeroed in the fragment registers of that block: register d of lane group lg holds row
-        // bytes from 16 lg + 4 d (d < 4) and from 64 + 16 lg + 4 (d - 4) (d >= 4), in both operands.
+        // zeroed in the fragment registers of that block (geom::tail_keep_mask).
         const int krem = static_cast<int>(K - (Kb - 1) * kGroup);
-        const int lane_keep = krem - 16 * lg;
+        const bool partial = krem != kGroup;
         auto tail_mask = [&](v8i v) {
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const int keep = lane_keep - (d < 4 ? 4 * d : 64 + 4 * (d - 4));
-                const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
-                v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & m);
-            }
+            for (int d = 0; d < 8; ++d) v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & geom::tail_keep_mask(krem, lg, d));
             return v;
         };
 
-        // One loop body for both stages (stage = kb % 2 at run time): a body unrolled per stage
-        // makes the register allocator spill. TAIL: the partial last K-block (fragments masked).
-        auto step = [&](int64_t kb, auto tail_tag) {
+        // block 0 is visible to every wave; block 1 goes into stage 1
+        lds_barrier();
+        if (Kb > 1) {
+#pragma unroll
+            for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(1), 1, wave);
+        }
+
+        auto read_a = [&](const u32x4* st, int i, bool tail) {
+            const int r = 64 * wm + 16 * i + l16;
+            const v8i v = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
+            return tail ? tail_mask(v) : v;
+        };
+        auto read_b = [&](const u32x4* st, int j, bool tail) {
+            const int r = 128 * wn + 16 * j + l16;
+            const v8i v = to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
+            return tail ? tail_mask(v) : v;
+        };
+        // per-column B scales of subtile j (four consecutive columns per lane)
+        auto read_bsj = [&](const u32x4* st, int j) {
+            const float* sbs = reinterpret_cast<const float*>(st + kStageSB) + 128 * wn;
+            return PER_COL ? *reinterpret_cast<const v4f*>(sbs + 16 * j + 4 * lg) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+        };
+        // the factor a_s[m, kb] (times the 128x128 B scale of the wave's column block) of each of
+        // the lane's four rows
+        auto read_factors = [&](const u32x4* st, float (&fo)[kMSub]) {
+            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wm;
+            const float bsc = PER_COL ? 1.0f : reinterpret_cast<const float*>(st + kStageSB)[wn];
+#pragma unroll
+            for (int i = 0; i < kMSub; ++i) fo[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
+        };
+
+        // Carried from one K-block to the next: the block's A fragments, its B fragments in a
+        // four-deep ring (subtile j in bf[j % 4], read two subtiles ahead of its MFMAs), its
+        // factors, and the partials of its last subtile column with their factors (rescaled just
+        // before the next block's first MFMAs overwrite them).
+        v8i af[kMSub];
+        v8i bf[4];
+        float f[kMSub];
+        v4f pp[kMSub];
+        v4f bsj_prev = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) {
+            af[i] = read_a(smem, i, false);
+            f[i] = 0.0f;
+            pp[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};  // a zero partial with a zero factor adds +0
+        }
+        bf[0] = read_b(smem, 0, false);
+        bf[1] = read_b(smem, 1, false);
+
+        // partial of subtile (i, j) times its factors, into the totals
+        auto rescale = [&](int i, int j, const v4f& p, const float (&fi)[kMSub], const v4f& bsj) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[i][j][e] = fmaf(p[e], PER_COL ? fi[i] * bsj[e] : fi[i], acc[i][j][e]);
+        };
+
+        // One K-block. Subtile columns 0..5 run on fragments read from this block's stage; before
+        // column 6 every fragment and scale of the block has been read, so one barrier there
+        // (after each wave's wait for its own loads of block kb+1) both publishes block kb+1 and
+        // frees this block's stage. Block kb+2 is then loaded into it -- four of the wave's loads
+        // right away, the rest two per column over the next block's columns 0..2, so the memory
+        // system never sees a whole block requested at once -- and block kb+1's first fragments
+        // are read while columns 6 and 7 keep the matrix cores busy; its A fragments replace this
+        // block's right after their last MFMA. TAIL: the partial last K-block, whose fragments are
+        // read again masked and which prefetches nothing. One body serves both stages (the stage
+        // index is a run-time value: a body unrolled per stage makes the allocator spill).
+        auto body = [&](int64_t kb, auto tail_tag) {
             constexpr bool TAIL = decltype(tail_tag)::value;
             const int cur = static_cast<int>(kb & 1);
-            const int nxt = cur ^ 1;
-            // every wave's block-kb loads are in LDS, and every wave is done with block kb-1
-            lds_barrier();
-            const uint32_t base_n = stage_base(nxt);
-            const int64_t kb_next = kb + 1 < Kb ? kb + 1 : kb;  // past the end: reload (unused)
-
             const u32x4* st = smem + cur * kStageSize;
-            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wm;
-            const float* sbs = reinterpret_cast<const float*>(st + kStageSB) + 128 * wn;
-            auto read_bf = [&](int j) {
-                const int r = 128 * wn + 16 * j + l16;
-                const v8i v = to_v8i(st[kStageB + r * 8 + pos_lo], st[kStageB + r * 8 + pos_hi]);
-                return TAIL ? tail_mask(v) : v;
-            };
-            // B fragments are read two subtiles ahead of their MFMAs (three in registers); the
-            // first MFMA needs only bf[0] and af[0], so those are read first
-            v8i bf[3];
-            v8i af[kMSub];
-            bf[0] = read_bf(0);
+            const u32x4* stn = smem + (cur ^ 1) * kStageSize;
+            v4f bsj6 = {1.0f, 1.0f, 1.0f, 1.0f}, bsj7 = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (TAIL) {
 #pragma unroll
-            for (int i = 0; i < kMSub; ++i) {
-                const int r = 64 * wm + 16 * i + l16;
-                af[i] = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
-                if (TAIL) af[i] = tail_mask(af[i]);
+                for (int i = 0; i < kMSub; ++i) af[i] = read_a(st, i, true);
+                bf[0] = read_b(st, 0, true);
+                bf[1] = read_b(st, 1, true);
             }
-            bf[1] = read_bf(1);
-            const float bsc = PER_COL ? 1.0f : bscale_lds[wn][kb];
-            float f[kMSub];
-#pragma unroll
-            for (int i = 0; i < kMSub; ++i) f[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
-
-            // partial of subtile (i, j) times its scales, into the totals
-            auto rescale = [&](int i, int j, const v4f& p, const v4f& bsj) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[i][j][e] = fmaf(p[e], PER_COL ? f[i] * bsj[e] : f[i], acc[i][j][e]);
-            };
-            auto read_bsj = [&](int j) {
-                return PER_COL ? *reinterpret_cast<const v4f*>(sbs + 16 * j + 4 * lg) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
-            };
-            v4f pp[kMSub];  // partials of the previous subtile until rescaled, then of the current one
-            v4f bsj_prev = {1.0f, 1.0f, 1.0f, 1.0f};
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNSub; ++j) {
-                // the next block's loads, spread over the first subtiles
-                if (2 * j < kLoads) issue_load<PER_COL>(2 * j, op, base_n, kb_next, M, N, wave);
-                if (2 * j + 1 < kLoads) issue_load<PER_COL>(2 * j + 1, op, base_n, kb_next, M, N, wave);
-                if (j + 2 < kNSub) bf[(j + 2) % 3] = read_bf(j + 2);
-                const v4f bsj = read_bsj(j);
-                // the previous subtile's partial of row block i is rescaled just before the MFMA
-                // that overwrites it (4 MFMAs after the one that produced it)
+                if (j == 6 && !TAIL) {
+                    wait_own_loads<0>();  // this wave's loads of block kb+1 have landed
+                    lds_barrier();        // ... every wave's; no wave reads stage cur any more
+                    // block kb+2 into this block's stage (none past the last block): loads 0..3 now,
+                    // the rest over the next block's first columns
+                    const bool more = kb + 2 < Kb;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        issue_load<PER_COL>(q, op, stage_base(cur), more ? kb + 2 : kb, wave, more);
+                    // slots 0 and 1 were last used by subtiles 4 and 5
+                    bf[0] = read_b(stn, 0, false);
+                    bf[1] = read_b(stn, 1, false);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (!TAIL && j < 3) {
+                    // the rest of block kb+1's loads, issued by the previous block after its barrier
+                    const bool pend = kb >= 1 && kb + 1 < Kb;
+                    if (4 + 2 * j < kLoads) issue_load<PER_COL>(4 + 2 * j, op, stage_base(cur ^ 1), pend ? kb + 1 : kb, wave, pend);
+                    if (5 + 2 * j < kLoads) issue_load<PER_COL>(5 + 2 * j, op, stage_base(cur ^ 1), pend ? kb + 1 : kb, wave, pend);
+                }
+                if (j + 2 < kNSub) bf[(j + 2) % 4] = read_b(st, j + 2, TAIL);
+                v4f bsj;
+                if (j < 6) {
+                    bsj = read_bsj(st, j);
+                    if (j == 5) {
+                        bsj6 = read_bsj(st, 6);
+                        bsj7 = read_bsj(st, 7);
+                    }
+                } else {
+                    bsj = j == 6 ? bsj6 : bsj7;
+                }
+                // the partial pp[i] holds (subtile (i, j-1); at j = 0 the previous block's (i, 7))
+                // is rescaled just before the MFMA that overwrites it
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) {
-                    if (j > 0) rescale(i, j - 1, pp[i], bsj_prev);
-                    pp[i] = mfma_fp8_16x16x128(bf[j % 3], af[i]);
+                    rescale(i, j == 0 ? kNSub - 1 : j - 1, pp[i], f, bsj_prev);
+                    pp[i] = mfma_fp8_16x16x128(bf[j % 4], af[i]);
+                    if (j == kNSub - 1 && !TAIL) af[i] = read_a(stn, i, false);
                 }
+                // this block's factors, once the previous block's last partials are rescaled
+                if (j == 0) read_factors(st, f);
                 bsj_prev = bsj;
                 if (j + 2 < kNSub) __builtin_amdgcn_sched_group_barrier(0x100, PER_COL ? 3 : 2, 0);
+                if (PER_COL && j == 5) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
                 for (int i = 0; i < kMSub; ++i) {
-                    if (j > 0) __builtin_amdgcn_sched_group_barrier(0x002, PER_COL ? 8 : 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, PER_COL ? 8 : 4, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (j == kNSub - 1 && !TAIL) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int i = 0; i < kMSub; ++i) rescale(i, kNSub - 1, pp[i], bsj_prev);
-            wait_own_loads<0>();  // this wave's loads of block kb+1 have landed
         };
 
-        const int64_t Kb_full = krem == kGroup ? Kb : Kb - 1;
-        for (int64_t kb = 0; kb < Kb_full; ++kb) step(kb, std::false_type{});
-        if (Kb_full < Kb) step(Kb_full, std::true_type{});
+        const int64_t Kb_full = partial ? Kb - 1 : Kb;
+        for (int64_t kb = 0; kb < Kb_full; ++kb) body(kb, std::false_type{});
+        if (partial) body(Kb - 1, std::true_type{});
+        // the last block's last subtile column
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) rescale(i, kNSub - 1, pp[i], f, bsj_prev);
+        wait_own_loads<0>();
+    }
+
+    if constexpr (GROUP == kSplitK) {
+        // fp32 partial tile of this K slice, straight from the totals: 16 bytes per lane
+        float* P = reinterpret_cast<float*>(C) + static_cast<int64_t>(blockIdx.y) * grp.c_stride;
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) {
+            const int64_t m = geom::fast_partial_row(m0, wm, i, lane);
+            if (m >= m_end) continue;
+#pragma unroll
+            for (int j = 0; j < kNSub; ++j) {
+                const int64_t n = geom::fast_partial_col(n0, wn, j, lane);
+                if (n < N) *reinterpret_cast<v4f*>(P + m * ldc + n) = acc[i][j];
+            }
+        }
+        return;
     }
 
     // Epilogue: each wave's 64 x 128 bf16 block goes through LDS (the stages are free once every
@@ -844,15 +882,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 #pragma unroll
     for (int p = 0; p < kWM / 4; ++p) {
         const int r = 4 * p + (lane >> 4);
-        const uint4 v = *reinterpret_cast<const uint4*>(cblk + r * 256 + ((cc ^ (r & 15)) * 16));
-        const int64_t m = m0 + 64 * wm + r;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(cblk + r * 256 + ((cc ^ (r & 15)) * 16));
+        const int64_t m = geom::fast_store_row(m0, wm, p, lane);
         if (m >= m_end) continue;
-        const int64_t n = n0 + 128 * wn + 8 * cc;
+        const int64_t n = geom::fast_store_col(n0, wn, lane);
         uint16_t* dst = C + m * ldc + n;
         if (c_vec && n + 8 <= N) {
-            *reinterpret_cast<uint4*>(dst) = v;
+            // streaming store: the output is not read again by this kernel, and lines that stay
+            // dirty in L2 would all be written back at the end of the launch
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
         } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// C[m, n] = bf16(sum over the S partial tiles of fp32 P[s][m][n]), slices summed in order 0 .. S-1.
+// Thread work item: 8 consecutive columns of one row (the partial rows are padded to a multiple
+// of 8 floats).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ P, int64_t ldp,
+                                                           int64_t slice, int S, uint16_t* __restrict__ C,
+                                                           int64_t ldc, int64_t M, int64_t N, int c_vec) {
+    const int64_t chunks = (N + 7) / 8;
+    const int64_t total = M * chunks;
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < total;
+         t += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t m = t / chunks;
+        const int64_t n = (t - m * chunks) * 8;
+        const float* p = P + m * ldp + n;
+        v4f s0 = *reinterpret_cast<const v4f*>(p);
+        v4f s1 = *reinterpret_cast<const v4f*>(p + 4);
+        for (int s = 1; s < S; ++s) {
+            s0 += *reinterpret_cast<const v4f*>(p + s * slice);
+            s1 += *reinterpret_cast<const v4f*>(p + s * slice + 4);
+        }
+        const uint32_t w[4] = {pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]), pack_bf16x2(s1[0], s1[1]),
+                               pack_bf16x2(s1[2], s1[3])};
+        uint16_t* dst = C + m * ldc + n;
+        if (c_vec && n + 8 <= N) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (n + e < N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
@@ -864,54 +936,94 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
 }  // namespace
 
+// When to split K, from measurements on MI355X (256 CUs; back-to-back launches, settled clock): a
+// slice costs its fp32 partial tile (written, then read by the sum) and the sum is a second launch,
+// so splitting pays only when few tiles leave most CUs idle, M is small and K is long -- 128 x 4096
+// x 4096: 46.7 us unsplit, 22.2 us with 12 slices; 512 x 4096 x 4096: 47.4 / 31.4 us with 4;
+// 2 x 5120 x 1280: 18.0 / 10.6 us with 6 -- while 130 x 5120 x 1280, 1024^3 and 2048 x 4096 x 4096
+// ran fastest unsplit. The slices always fit in one round of workgroups.
+SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
+    SplitPlan plan{1, 0, 0};
+    if (fnuz || M <= 0 || N <= 0 || K <= 0 || M > 512) return plan;
+    const int64_t tiles = ((M + fast::kBM - 1) / fast::kBM) * ((N + fast::kBN - 1) / fast::kBN);
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    if (4 * tiles > cus) return plan;
+    int64_t S = cus / tiles;  // one round of workgroups
+    if (M <= 64) {
+        if (S > Kb) S = Kb;
+    } else {
+        if (Kb <= 10) return plan;  // short K: the slice overhead outweighs the idle CUs
+        if (S > Kb / 2) S = Kb / 2;
+        if (S > (M <= 256 ? 12 : 4)) S = M <= 256 ? 12 : 4;
+    }
+    const int64_t ldp = (N + 7) / 8 * 8;
+    const int64_t slice_bytes = M * ldp * 4;
+    if (S * slice_bytes > max_bytes) S = max_bytes / slice_bytes;
+    if (S > 65535) S = 65535;
+    if (S < 2) return plan;
+    plan.S = static_cast<int>(S);
+    plan.ldp = ldp;
+    plan.bytes = S * slice_bytes;
+    return plan;
+}
+
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
-                       int64_t K, bool fnuz, hipStream_t stream) {
-    // vector stores: 8 bytes per lane in the general kernel, 16 in the fast one
-    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
-    const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
-    // Fast path: per-column scales read 4 columns at a time; 128x128 scales of a
-    // tile's column staged in LDS (at most kMaxKbFast K-blocks).
-    const bool fast_scales = bs.per_column ? (N % 4 == 0) : ((K + kGroup - 1) / kGroup <= fast::kMaxKbFast);
-    if (!fnuz && fast_scales) {
+                       int64_t K, bool fnuz, const SplitPlan& plan, float* workspace, int cus,
+                       hipStream_t stream) {
+    if (!fnuz) {
         const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
         const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
         if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+        const int64_t nb = bs.per_column ? 0 : bs.stride_nb;
+        const int64_t kbs = bs.per_column ? 0 : bs.stride_kb;
+        if (plan.S > 1) {
+            // K split over plan.S workgroups per tile: fp32 partial tiles, then their sum in bf16
+            if (workspace == nullptr) return hipErrorInvalidValue;
+            const fast::Grouping g{nullptr, 0, 0, 0, M * plan.ldp};
+            const dim3 grid(static_cast<unsigned>(mt * nt), static_cast<unsigned>(plan.S));
+            uint16_t* P = reinterpret_cast<uint16_t*>(workspace);
+            if (bs.per_column)
+                fast::gemm_kernel<true, fast::kSplitK><<<grid, fast::kThreads, 0, stream>>>(
+                    a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
+            else
+                fast::gemm_kernel<false, fast::kSplitK><<<grid, fast::kThreads, 0, stream>>>(
+                    a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
+            const int64_t items = M * ((N + 7) / 8);
+            int64_t wgs = (items + 255) / 256;
+            if (wgs > static_cast<int64_t>(cus) * 8) wgs = static_cast<int64_t>(cus) * 8;
+            fast::split_reduce_kernel<<<dim3(static_cast<unsigned>(wgs)), 256, 0, stream>>>(
+                workspace, plan.ldp, M * plan.ldp, plan.S, c, ldc, M, N, c_vec16);
+            return hipGetLastError();
+        }
+        const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
         const dim3 grid(static_cast<unsigned>(mt * nt));
         const fast::Grouping none{nullptr, 0, 0, 0, 0};
         if (bs.per_column)
             fast::gemm_kernel<true, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
+                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
         else
             fast::gemm_kernel<false, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt,
-                (int)nt, c_vec16, none);
+                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
         return hipGetLastError();
     }
-    const int64_t mt = (M + kBM - 1) / kBM;
-    const int64_t nt = (N + kBN - 1) / kBN;
+    // float8_e4m3fnuz: general kernel
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    const int64_t mt = (M + gen::kBM - 1) / gen::kBM;
+    const int64_t nt = (N + gen::kBN - 1) / gen::kBN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(mt * nt));
-    const int64_t nb_stride = bs.per_column ? 0 : bs.stride_nb;
-    const int64_t kb_stride = bs.per_column ? 0 : bs.stride_kb;
-#define BSFP8_GG(PC, FZ)                                                                          \
-    gemm_kernel<PC, FZ><<<grid, kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, nb_stride,    \
-                                                       kb_stride, c, ldc, M, N, K, (int)mt,       \
-                                                       (int)nt, c_vec)
-    if (bs.per_column) {
-        if (fnuz) BSFP8_GG(true, true);
-        else BSFP8_GG(true, false);
-    } else {
-        if (fnuz) BSFP8_GG(false, true);
-        else BSFP8_GG(false, false);
-    }
-#undef BSFP8_GG
+    if (bs.per_column)
+        gen::gemm_kernel<true><<<grid, gen::kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M,
+                                                                   N, K, (int)mt, (int)nt, c_vec);
+    else
+        gen::gemm_kernel<false><<<grid, gen::kThreads, 0, stream>>>(a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb,
+                                                                    bs.stride_kb, c, ldc, M, N, K, (int)mt,
+                                                                    (int)nt, c_vec);
     return hipGetLastError();
-}
-
-bool gemm_grouped_supported(bool per_column, int64_t N, int64_t K) {
-    if (K % kGroup != 0) return false;
-    return per_column ? (N % 4 == 0) : (K / kGroup <= fast::kMaxKbFast);
 }
 
 hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* a_s,
@@ -919,7 +1031,7 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
                                     int64_t bs_stride, const int64_t* offsets, int64_t E,
                                     uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                                     hipStream_t stream) {
-    if (!gemm_grouped_supported(false, N, K)) return hipErrorInvalidValue;
+    if (K % kGroup != 0) return hipErrorInvalidValue;
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
     // every expert's last row tile may be partial: at most ceil(M / 256) + E row tiles
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM + E;
@@ -936,7 +1048,7 @@ hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s
                                  int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
                                  uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream) {
-    if (!gemm_grouped_supported(true, N, K)) return hipErrorInvalidValue;
+    if (K % kGroup != 0) return hipErrorInvalidValue;
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0) && (c_stride % 8 == 0);
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;

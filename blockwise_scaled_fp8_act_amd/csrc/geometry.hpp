@@ -1,0 +1,207 @@
+// Index arithmetic of the gfx950 kernels: which rows, columns and scale elements each lane reads
+// and writes, and the byte offsets it hands to the buffer loads. The kernels call these functions;
+// tests/geometry_check.cpp compiles the same header for the CPU and enumerates every lane of every
+// launch on ragged shapes, checking that each read is either inside its buffer or out of range as a
+// whole, that every in-range element is read and written, and that nothing outside the tensors is
+// written -- the checks "Mask a_s/b_s scale loads in blockwise FP8 training GEMM kernels" (Test)
+// runs on its Triton kernels' offs_m / offs_n arithmetic, and the scale-store mask of the LHS
+// quantizer from the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm".
+//
+// Buffer loads: a raw buffer resource of num_records bytes returns zero for an access whose
+// per-lane offset (VGPR offset) lies at or past num_records (CDNA3/CDNA4 ISA, MUBUF out-of-range
+// behaviour for raw buffers: stride 0, range checked on the byte offset). Every GEMM load here
+// passes its whole offset in the VGPR (the scalar offset is always 0), every access is 16 bytes at a
+// 16-byte-aligned offset into a buffer whose size is a multiple of 16, or 4 bytes at a 4-byte-aligned
+// offset, so an access is entirely inside or entirely outside its buffer. A lane whose row, column
+// or scale lies outside the tensor gets the offset kOob, to which only a per-K-block advance below
+// 2^31 is added; the callers keep every buffer below kMaxRange bytes, so such an access is always
+// out of range and never wraps past 2^32.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define BSFP8_HD __host__ __device__ __forceinline__
+#else
+#define BSFP8_HD inline
+#endif
+
+namespace bsfp8 {
+namespace geom {
+
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int64_t kMaxRange = 0x80000000LL;  // buffer resources of the GEMMs span at most 2^31 bytes
+constexpr int kBlockK = 128;                 // K-block depth (one 1x128 / 128x1 / 128x128 group)
+
+// ---------------------------------------------------------------------------------------------
+// Workgroup -> output tile (both GEMM kernels). Workgroups are dispatched round-robin over the 8
+// XCDs; consecutive logical tiles go to one XCD, and logical tiles run in groups of kGroupRows
+// tile-rows so the workgroups one XCD runs together share A rows and B columns in its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupRows = 4;
+
+BSFP8_HD void tile_of(int bid, int mt, int nt, int& tm, int& tn) {
+    const int total = mt * nt;
+    int logical = bid;
+    if (total % kXcds == 0) logical = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    const int per_group = kGroupRows * nt;
+    const int group = logical / per_group;
+    const int first_m = group * kGroupRows;
+    const int gsize = (mt - first_m) < kGroupRows ? (mt - first_m) : kGroupRows;
+    const int in_group = logical - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fast GEMM kernel: 256 x 256 tile, 8 waves (wm = wave % 4 owns rows 64 wm.., wn = wave / 4
+// columns 128 wn..). Each K-block's operand tiles are loaded by the 8 waves together, 16 bytes
+// per lane, straight into LDS.
+constexpr int kFastBM = 256;
+constexpr int kFastBN = 256;
+constexpr int kFastWaves = 8;
+
+// Operand load q (0..3) of a wave: tile row 32 wave + 8 q + lane / 8, 16-byte chunk
+// (lane % 8) ^ swz(row) of the row's K-block, where swz(row) = (row / 2) % 8 is the LDS swizzle:
+// lane l lands at LDS unit (32 wave + 8 q) * 8 + l = row * 8 + l % 8, which thus holds logical chunk
+// (l % 8) ^ swz(row). Load q reads through its own buffer resource, which starts at tile row 8 q and
+// spans the tile's in-range rows from there (fast_operand_range), so the per-lane offset is the
+// same for q and q + 2 and a row past the matrix is past the end of its resource.
+BSFP8_HD int fast_operand_row(int wave, int q, int lane) { return 32 * wave + 8 * q + (lane >> 3); }
+BSFP8_HD int lds_swizzle(int row) { return (row >> 1) & 7; }
+BSFP8_HD int fast_operand_chunk(int q, int lane) { return (lane & 7) ^ ((4 * (q & 1) + (lane >> 4)) & 7); }
+// Per-lane offset of load q (depends on q only through q % 2) from the start of its resource,
+// before the K-block advance kb * 128.
+BSFP8_HD uint32_t fast_operand_lane(int wave, int q, int lane, int64_t ld) {
+    return static_cast<uint32_t>((32 * wave + (lane >> 3)) * ld + 16 * fast_operand_chunk(q, lane));
+}
+// Resource of load q: from tile row 8 q, (rows_in_range - 8 q) rows of ld bytes (none if negative).
+BSFP8_HD int64_t fast_operand_first_row(int q) { return 8 * q; }
+BSFP8_HD int64_t fast_operand_range(int q, int64_t rows_in_range, int64_t ld) {
+    return rows_in_range > 8 * q ? (rows_in_range - 8 * q) * ld : 0;
+}
+BSFP8_HD uint32_t fast_operand_advance(int64_t kb) { return static_cast<uint32_t>(kb * kBlockK); }
+
+// A scales of a K-block: lanes 0..31 of each wave load one fp32 each, tile row 32 wave + lane
+// (LDS float 32 wave + lane). a_s is column-major [M, Kb] with ld M: element (m, kb) at kb * M + m.
+BSFP8_HD uint32_t fast_ascale_base(int64_t m0, int64_t m_end, int wave, int lane) {
+    const int64_t m = m0 + 32 * wave + lane;
+    return (lane < 32 && m < m_end) ? static_cast<uint32_t>(4 * m) : kOob;
+}
+BSFP8_HD uint32_t fast_ascale_advance(int64_t kb, int64_t M) { return static_cast<uint32_t>(4 * kb * M); }
+
+// Per-column B scales of a K-block: lanes 0..31 of each wave, tile column 32 wave + lane;
+// b_s [Kb, N] row-major: element (kb, n) at kb * N + n.
+BSFP8_HD uint32_t fast_bscale_col_base(int64_t n0, int64_t N, int wave, int lane) {
+    const int64_t n = n0 + 32 * wave + lane;
+    return (lane < 32 && n < N) ? static_cast<uint32_t>(4 * n) : kOob;
+}
+BSFP8_HD uint32_t fast_bscale_col_advance(int64_t kb, int64_t N) { return static_cast<uint32_t>(4 * kb * N); }
+
+// 128x128 B scales of a K-block: lanes 0 and 1 of wave 0, column block 2 tn + lane (LDS float lane);
+// element (kb, nb) at nb * bs_nb + kb * bs_kb.
+BSFP8_HD uint32_t fast_bscale_blk_base(int tn, int64_t N, int64_t bs_nb, int wave, int lane) {
+    const int64_t nb = 2 * static_cast<int64_t>(tn) + lane;
+    return (wave == 0 && lane < 2 && nb * kBlockK < N) ? static_cast<uint32_t>(4 * nb * bs_nb) : kOob;
+}
+BSFP8_HD uint32_t fast_bscale_blk_advance(int64_t kb, int64_t bs_kb) { return static_cast<uint32_t>(4 * kb * bs_kb); }
+// floats a strided 128x128 scale tensor spans: the largest index read plus one
+BSFP8_HD int64_t bscale_blk_extent(int64_t N, int64_t Kb, int64_t bs_nb, int64_t bs_kb) {
+    const int64_t Nb = (N + kBlockK - 1) / kBlockK;
+    return (Nb - 1) * bs_nb + (Kb - 1) * bs_kb + 1;
+}
+
+// Bytes of the last K-block that lie below K and the fragment mask: register d of lane group lg
+// holds row bytes from 16 lg + 4 d (d < 4) and from 64 + 16 lg + 4 (d - 4) (d >= 4) in both
+// operands; bytes at and past krem are zeroed.
+BSFP8_HD int fragment_byte(int lg, int d) { return d < 4 ? 16 * lg + 4 * d : 64 + 16 * lg + 4 * (d - 4); }
+BSFP8_HD uint32_t tail_keep_mask(int krem, int lg, int d) {
+    const int keep = krem - fragment_byte(lg, d);
+    return keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+}
+
+// bf16 epilogue: pass p (0..15) of a wave stores 16 bytes per lane: row 64 wm + 4 p + lane / 16,
+// columns 128 wn + 8 (lane % 16) .. + 8 of the tile; element n + e is stored iff row < m_end and
+// n + e < N.
+BSFP8_HD int64_t fast_store_row(int64_t m0, int wm, int p, int lane) { return m0 + 64 * wm + 4 * p + (lane >> 4); }
+BSFP8_HD int64_t fast_store_col(int64_t n0, int wn, int lane) { return n0 + 128 * wn + 8 * (lane & 15); }
+
+// fp32 partial epilogue (split K): subtile (i, j) of a wave stores a lane's four totals at row
+// 64 wm + 16 i + lane % 16, columns 128 wn + 16 j + 4 (lane / 16) .. + 4 of the tile, iff the row is
+// below m_end and the first column below N (the partial rows are padded to a multiple of 4 floats).
+BSFP8_HD int64_t fast_partial_row(int64_t m0, int wm, int i, int lane) { return m0 + 64 * wm + 16 * i + (lane & 15); }
+BSFP8_HD int64_t fast_partial_col(int64_t n0, int wn, int j, int lane) { return n0 + 128 * wn + 16 * j + 4 * (lane >> 4); }
+
+// Split K: slice s of S owns K-blocks [split_begin(Kb, S, s), split_begin(Kb, S, s + 1)).
+BSFP8_HD int64_t split_begin(int64_t Kb, int64_t S, int64_t s) { return Kb * s / S; }
+
+// ---------------------------------------------------------------------------------------------
+// General GEMM kernel (float8_e4m3fnuz operands): 256 x 128 tile, 8 waves (wm = wave / 2 owns rows
+// 64 wm.., wn = wave % 2 columns 64 wn..), operands read through buffer loads into registers.
+constexpr int kGenBM = 256;
+constexpr int kGenBN = 128;
+
+// A fragment of subtile i (0..3): tile row 64 wm + 16 i + lane % 16, bytes [32 (lane / 16), +32)
+// of the K-block as two 16-byte loads (the second at +16). Subtile i reads through its own resource
+// from tile row 16 i (gen_a_range), so the lane offset is the same for every i.
+BSFP8_HD int gen_a_row(int wm, int i, int lane) { return 64 * wm + 16 * i + (lane & 15); }
+BSFP8_HD int64_t gen_a_first_row(int i) { return 16 * i; }
+BSFP8_HD int64_t gen_a_range(int i, int64_t rows_in_range, int64_t lda) {
+    return rows_in_range > 16 * i ? (rows_in_range - 16 * i) * lda : 0;
+}
+BSFP8_HD uint32_t gen_a_lane(int wm, int lane, int64_t lda) {
+    return static_cast<uint32_t>((64 * wm + (lane & 15)) * lda + 32 * (lane >> 4));
+}
+// B tile rows into registers (a partial last K-block): thread t (0..511) loads row t / 8 + 64 p
+// (p = 0, 1), 16-byte chunk t % 8, through the resource from tile row 64 p; LDS row r holds chunk c
+// at position c ^ (r % 8).
+BSFP8_HD int gen_b_row(int tid, int p) { return (tid >> 3) + 64 * p; }
+BSFP8_HD int64_t gen_b_first_row(int p) { return 64 * p; }
+BSFP8_HD int64_t gen_b_range(int p, int64_t rows_in_range, int64_t ldb) {
+    return rows_in_range > 64 * p ? (rows_in_range - 64 * p) * ldb : 0;
+}
+BSFP8_HD uint32_t gen_b_lane(int tid, int64_t ldb) { return static_cast<uint32_t>((tid >> 3) * ldb + 16 * (tid & 7)); }
+// B tile of a full K-block straight into LDS: load q (0, 1) of wave w, lane l: row 16 w + 8 q + l / 8,
+// LDS position l % 8 holding logical chunk (l % 8) ^ (row % 8) = (l % 8) ^ (l / 8), through the
+// resource from tile row 8 q.
+BSFP8_HD int gen_bdma_row(int wave, int q, int lane) { return 16 * wave + 8 * q + (lane >> 3); }
+BSFP8_HD int64_t gen_bdma_first_row(int q) { return 8 * q; }
+BSFP8_HD int64_t gen_bdma_range(int q, int64_t rows_in_range, int64_t ldb) {
+    return rows_in_range > 8 * q ? (rows_in_range - 8 * q) * ldb : 0;
+}
+BSFP8_HD uint32_t gen_bdma_lane(int wave, int lane, int64_t ldb) {
+    return static_cast<uint32_t>((16 * wave + (lane >> 3)) * ldb + 16 * ((lane & 7) ^ (lane >> 3)));
+}
+// A scale of subtile i's row (element (m, kb) of the column-major a_s at 4 (kb M + m)): the lane's
+// base, kOob for a row >= M; the K-block advance 4 kb M is added per load.
+BSFP8_HD uint32_t gen_ascale_base(int64_t m0, int wm, int i, int lane, int64_t M) {
+    const int64_t m = m0 + gen_a_row(wm, i, lane);
+    return m < M ? static_cast<uint32_t>(4 * m) : kOob;
+}
+// Per-column B scales of subtile j: columns n .. n + 3 with n = n0 + 64 wn + 16 j + 4 (lane / 16):
+// base 4 n (kOob for n >= N), advance 4 kb N; a quad that straddles N is read element by element,
+// only below N.
+BSFP8_HD int64_t gen_col(int64_t n0, int wn, int j, int lane) { return n0 + 64 * wn + 16 * j + 4 * (lane >> 4); }
+BSFP8_HD uint32_t gen_bscale_base(int64_t n, int64_t N) { return n < N ? static_cast<uint32_t>(4 * n) : kOob; }
+BSFP8_HD bool gen_bscale_straddles(int64_t n, int64_t N) { return n < N && n + 4 > N; }
+
+// ---------------------------------------------------------------------------------------------
+// Quantizer scale stores. Each function gives the scale element a thread writes and whether it
+// writes it; the kernels store exactly when the predicate holds.
+
+// quantize_lhs: unit u (kLhsRows rows of one K-block, K-block fastest) of a 256-thread workgroup;
+// team = thread / 16 (16 teams), r = 0..rows_per_team-1: row rb * 16 * rows_per_team + 16 r + team;
+// lane 0 of each team stores a_s[kb * M + row] iff row < M.
+BSFP8_HD void lhs_unit(int64_t u, int64_t Kb, int64_t& rb, int64_t& kb) {
+    rb = u / Kb;
+    kb = u - rb * Kb;
+}
+BSFP8_HD int64_t lhs_row(int64_t rb, int rows_per_team, int r, int team) {
+    return rb * 16 * rows_per_team + 16 * r + team;
+}
+BSFP8_HD int64_t colmajor_index(int64_t kb, int64_t M, int64_t m) { return kb * M + m; }
+// a row's codes and scale are stored only when the row is inside the tensor
+BSFP8_HD bool row_stored(int64_t m, int64_t M) { return m < M; }
+
+}  // namespace geom
+}  // namespace bsfp8

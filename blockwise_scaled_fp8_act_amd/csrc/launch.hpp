@@ -33,14 +33,27 @@ struct BScale {
     int per_column;
 };
 
+// Compute units of the current device (cached per device after the first query).
+int device_cus();
+
+// K split of a GEMM whose output tiles cannot fill the chip: S workgroups per tile each multiply a
+// range of K-blocks into an fp32 partial tile (rows of ldp floats, ldp = N rounded up to 8), and a
+// second kernel sums the S partials into C. S == 1: no split. bytes: the fp32 workspace it needs.
+struct SplitPlan {
+    int S;
+    int64_t ldp;
+    int64_t bytes;
+};
+SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes);
+
 // fnuz: both operands hold float8_e4m3fnuz codes (general kernel, f16 matrix instructions).
+// plan.S > 1 needs `workspace` (plan.bytes, 256-byte aligned, device memory) for the partial tiles.
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
-                       int64_t K, bool fnuz, hipStream_t stream);
+                       int64_t K, bool fnuz, const SplitPlan& plan, float* workspace, int cus,
+                       hipStream_t stream);
 
-// Expert-grouped GEMMs (fast path only: K % 128 == 0; 128x128 scales: at most 512 K-blocks;
-// per-column scales: N % 4 == 0). offsets: E + 1 device int64 boundaries.
-bool gemm_grouped_supported(bool per_column, int64_t N, int64_t K);
+// Expert-grouped GEMMs (fast kernel; K % 128 == 0). offsets: E + 1 device int64 boundaries.
 hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* a_s,
                                     const uint8_t* b, int64_t ldb, int64_t b_stride, BScale bs,
                                     int64_t bs_stride, const int64_t* offsets, int64_t E,

@@ -18,6 +18,7 @@
 // 128x128) max reductions run on data already in registers, and the transposing variants turn the
 // tile around in LDS so global stores stay contiguous along the output rows.
 #include "device_common.hpp"
+#include "geometry.hpp"
 #include "launch.hpp"
 
 namespace bsfp8 {
@@ -116,14 +117,13 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     const int lane16 = threadIdx.x & 15;
     const int team = threadIdx.x >> 4;
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int64_t rb = u / Kb;
-    const int64_t kb = u - rb * Kb;
-    const int64_t mbase = rb * kLhsRows;
+    int64_t rb, kb;
+    geom::lhs_unit(u, Kb, rb, kb);
     const int64_t c = kb * kGroup + lane16 * 8;
 
     uint32_t w[kLhsRowsPerTeam][4];  // packed bf16 pairs
 #pragma unroll
-    for (int r = 0; r < kLhsRowsPerTeam; ++r) load8_packed<VEC_X>(x, ldx, mbase + r * 16 + team, M, c, K, w[r]);
+    for (int r = 0; r < kLhsRowsPerTeam; ++r) load8_packed<VEC_X>(x, ldx, geom::lhs_row(rb, kLhsRowsPerTeam, r, team), M, c, K, w[r]);
     // every row is encoded before the first store: a store issued while loads are outstanding
     // makes the wait for the next row's load also wait for that store
     uint32_t code[kLhsRowsPerTeam][2];
@@ -143,10 +143,10 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
     }
 #pragma unroll
     for (int r = 0; r < kLhsRowsPerTeam; ++r) {
-        const int64_t m = mbase + r * 16 + team;
-        if (m < M) {  // rows >= M store neither codes nor scales
+        const int64_t m = geom::lhs_row(rb, kLhsRowsPerTeam, r, team);
+        if (geom::row_stored(m, M)) {  // rows >= M store neither codes nor scales
             store8<VEC_Q>(q + m * ldq, c, K, code[r][0], code[r][1]);
-            if (lane16 == 0) a_s[kb * M + m] = scale[r];
+            if (lane16 == 0) a_s[geom::colmajor_index(kb, M, m)] = scale[r];
         }
     }
     }
@@ -605,15 +605,6 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ x
 }
 
 bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// Compute units of the current device (256 on MI355X if the query fails).
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-    return cus;
-}
 
 template <bool FNUZ>
 hipError_t quantize_lhs_impl(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,

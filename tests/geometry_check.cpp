@@ -1,0 +1,384 @@
+// Host-side check of the GEMM kernels' index arithmetic (blockwise_scaled_fp8_act_amd/csrc/
+// geometry.hpp, the same header the kernels call), in the manner of the index test of "Mask a_s/b_s
+// scale loads in blockwise FP8 training GEMM kernels" (Test): for ragged M, N, K it enumerates every
+// lane of every workgroup and K-block and asserts
+//   * every buffer access is 16-byte (operands) or 4-byte (scales) aligned and lies wholly inside or
+//     wholly outside its buffer resource, offsets never wrap past 2^32, and an access inside its
+//     resource is inside the tensor it was built over;
+//   * a lane whose row / column / scale is outside the tensor is outside its resource (it reads zero);
+//   * every in-range operand chunk and scale is loaded exactly once per K-block, into the LDS slot
+//     the fragment reads expect;
+//   * every output element (m < M, n < N) is stored exactly once and nothing else is stored (bf16
+//     epilogue, split-K partial tiles), and the split slices partition the K-blocks;
+//   * the partial-K-block masks keep exactly the fragment bytes below K;
+//   * quantize_lhs stores each scale of the column-major [M, Kb] tensor exactly once and never a row
+//     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm").
+// Usage: geometry_check M N K [M N K ...]; prints one line per shape, exits 1 on the first failure.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "geometry.hpp"
+
+using namespace bsfp8::geom;
+
+static int g_fail = 0;
+#define CHECK(cond, ...)                                              \
+    do {                                                              \
+        if (!(cond)) {                                                \
+            std::printf("FAIL %s:%d: %s -- ", __FILE__, __LINE__, #cond); \
+            std::printf(__VA_ARGS__);                                 \
+            std::printf("\n");                                        \
+            g_fail = 1;                                               \
+            return false;                                             \
+        }                                                             \
+    } while (0)
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// One access of `size` bytes at 64-bit offset `off` (the value the lane hands the hardware, reduced
+// to 32 bits) into a resource of `range` bytes: returns true if it reads memory (in range).
+static bool access(uint64_t off, int64_t range, int size, bool& ok) {
+    ok = off < (1ull << 32) && off % size == 0 && range % size == 0;
+    return static_cast<int64_t>(off) < range;
+}
+
+// ---------------------------------------------------------------------------------------------
+static bool check_tiles(int mt, int nt) {
+    std::vector<int> seen(static_cast<size_t>(mt) * nt, 0);
+    for (int bid = 0; bid < mt * nt; ++bid) {
+        int tm, tn;
+        tile_of(bid, mt, nt, tm, tn);
+        CHECK(tm >= 0 && tm < mt && tn >= 0 && tn < nt, "bid %d -> (%d, %d) of %d x %d", bid, tm, tn, mt, nt);
+        CHECK(++seen[static_cast<size_t>(tm) * nt + tn] == 1, "tile (%d, %d) twice", tm, tn);
+    }
+    return true;
+}
+
+// Fast kernel operand loads of one tile and K-block: rows [0, rows) of a tile starting at row r0 of an
+// operand with `total_rows` rows of K bytes at row stride ld. A chunk that holds bytes below K must be
+// read at its address; a chunk wholly at or past K (masked to zero in the fragments) may read the
+// following bytes of the operand or nothing, but never outside it.
+static bool check_fast_operand(int64_t r0, int64_t rows, int64_t total_rows, int64_t ld, int64_t K, int64_t kb) {
+    std::vector<uint8_t> got(256 * 8, 0);
+    for (int q = 0; q < 4; ++q) {
+        const int64_t range = fast_operand_range(q, rows, ld);
+        const int64_t first = r0 + fast_operand_first_row(q);
+        for (int wave = 0; wave < kFastWaves; ++wave)
+            for (int lane = 0; lane < 64; ++lane) {
+                const uint64_t off = static_cast<uint64_t>(fast_operand_lane(wave, q, lane, ld)) + fast_operand_advance(kb);
+                bool ok;
+                const bool in = access(off, range, 16, ok);
+                CHECK(ok, "operand offset %llu (range %lld)", (unsigned long long)off, (long long)range);
+                const int r = fast_operand_row(wave, q, lane);
+                const int c = fast_operand_chunk(q, lane);
+                // LDS slot of the lane: unit (32 wave + 8 q) * 8 + lane = row r, position lane % 8,
+                // which the fragment reads take as logical chunk (lane % 8) ^ swizzle(r)
+                CHECK((32 * wave + 8 * q) * 8 + lane == r * 8 + (lane & 7), "LDS unit");
+                CHECK(((lane & 7) ^ lds_swizzle(r)) == c, "LDS chunk position");
+                const bool needed = kb * kBlockK + 16 * c < K;
+                if (r < rows) {
+                    CHECK(static_cast<int64_t>(off) == (r - 8 * q) * ld + kb * kBlockK + 16 * c, "operand address");
+                    if (needed) {
+                        CHECK(in, "row %d chunk %d below K not read (q %d wave %d lane %d)", r, c, q, wave, lane);
+                        CHECK(++got[r * 8 + c] == 1, "row %d chunk %d loaded twice", r, c);
+                    }
+                } else {
+                    CHECK(!in, "row %d past the tile's %lld rows is read", r, (long long)rows);
+                }
+                if (in) CHECK(first * ld + static_cast<int64_t>(off) + 16 <= total_rows * ld, "read past the operand");
+            }
+    }
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < 8; ++c)
+            if (kb * kBlockK + 16 * c < K) CHECK(got[r * 8 + c] == 1, "row %d chunk %d not loaded", r, c);
+    return true;
+}
+
+static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    const int mt = static_cast<int>(cdiv(M, kFastBM)), nt = static_cast<int>(cdiv(N, kFastBN));
+    const int64_t Kb = cdiv(K, kBlockK);
+    if (!check_tiles(mt, nt)) return false;
+    // 128x128 B scales read with the forward strides (Kb, 1) and the dgrad strides (1, Nb)
+    const int64_t Nb = cdiv(N, kBlockK);
+    const int64_t strides[2][2] = {{Kb, 1}, {1, Nb}};
+    std::vector<uint8_t> stored(static_cast<size_t>(M) * N, 0);
+    for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < nt; ++tn) {
+            const int64_t m0 = static_cast<int64_t>(tm) * kFastBM, n0 = static_cast<int64_t>(tn) * kFastBN;
+            const int64_t arows = M - m0 < kFastBM ? M - m0 : kFastBM;
+            const int64_t brows = N - n0 < kFastBN ? N - n0 : kFastBN;
+            for (int64_t kb = 0; kb < Kb; ++kb) {
+                if (!check_fast_operand(m0, arows, M, lda, K, kb)) return false;
+                if (!check_fast_operand(n0, brows, N, ldb, K, kb)) return false;
+                // A scales: lanes 0..31 of each wave (the others are switched off)
+                std::vector<uint8_t> sa(256, 0), sbc(256, 0);
+                for (int wave = 0; wave < kFastWaves; ++wave)
+                    for (int lane = 0; lane < 32; ++lane) {
+                        const uint64_t off = static_cast<uint64_t>(fast_ascale_base(m0, M, wave, lane)) + fast_ascale_advance(kb, M);
+                        bool ok;
+                        const bool in = access(off, 4 * M * Kb, 4, ok);
+                        CHECK(ok, "a_s offset");
+                        const int64_t m = m0 + 32 * wave + lane;
+                        if (m < M) {
+                            CHECK(in && static_cast<int64_t>(off) == 4 * (kb * M + m), "a_s[%lld, %lld] address", (long long)m, (long long)kb);
+                            ++sa[32 * wave + lane];
+                        } else {
+                            CHECK(!in, "a_s row %lld >= M read", (long long)m);
+                        }
+                        // per-column B scales
+                        const uint64_t offb = static_cast<uint64_t>(fast_bscale_col_base(n0, N, wave, lane)) + fast_bscale_col_advance(kb, N);
+                        const bool inb = access(offb, 4 * N * Kb, 4, ok);
+                        CHECK(ok, "b_s offset");
+                        const int64_t n = n0 + 32 * wave + lane;
+                        if (n < N) {
+                            CHECK(inb && static_cast<int64_t>(offb) == 4 * (kb * N + n), "b_s[%lld, %lld] address", (long long)kb, (long long)n);
+                            ++sbc[32 * wave + lane];
+                        } else {
+                            CHECK(!inb, "b_s column %lld >= N read", (long long)n);
+                        }
+                    }
+                for (int r = 0; r < arows; ++r) CHECK(sa[r] == 1, "a_s row %lld not loaded once", (long long)(m0 + r));
+                for (int r = 0; r < brows; ++r) CHECK(sbc[r] == 1, "b_s column %lld not loaded once", (long long)(n0 + r));
+                // 128x128 B scales: wave 0, lanes 0 and 1 (the other lanes and waves switched off)
+                for (const auto& st : strides) {
+                    const int64_t ext = bscale_blk_extent(N, Kb, st[0], st[1]);
+                    for (int lane = 0; lane < 2; ++lane) {
+                        const uint64_t off = static_cast<uint64_t>(fast_bscale_blk_base(tn, N, st[0], 0, lane)) + fast_bscale_blk_advance(kb, st[1]);
+                        bool ok;
+                        const bool in = access(off, 4 * ext, 4, ok);
+                        CHECK(ok, "128x128 b_s offset");
+                        const int64_t nb = 2 * static_cast<int64_t>(tn) + lane;
+                        if (nb * kBlockK < N) {
+                            CHECK(in && static_cast<int64_t>(off) == 4 * (nb * st[0] + kb * st[1]), "128x128 b_s address");
+                        } else {
+                            CHECK(!in, "128x128 b_s block %lld past N read", (long long)nb);
+                        }
+                    }
+                }
+            }
+            // bf16 epilogue
+            for (int wave = 0; wave < kFastWaves; ++wave)
+                for (int p = 0; p < 16; ++p)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int64_t m = fast_store_row(m0, wave & 3, p, lane);
+                        const int64_t n = fast_store_col(n0, wave >> 2, lane);
+                        if (m >= M) continue;
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < N) CHECK(++stored[m * N + n + e] == 1, "C[%lld, %lld] stored twice", (long long)m, (long long)(n + e));
+                    }
+        }
+    for (int64_t i = 0; i < M * N; ++i) CHECK(stored[i] == 1, "C element %lld not stored", (long long)i);
+    return true;
+}
+
+// Split K: slices partition the K-blocks; each slice's fp32 partial tile covers every output once.
+static bool check_split(int64_t M, int64_t N, int64_t K) {
+    const int64_t Kb = cdiv(K, kBlockK);
+    for (int64_t S = 1; S <= Kb && S <= 40; ++S) {
+        int64_t next = 0;
+        for (int64_t s = 0; s < S; ++s) {
+            const int64_t b = split_begin(Kb, S, s), e = split_begin(Kb, S, s + 1);
+            CHECK(b == next && e > b, "slice %lld of %lld: [%lld, %lld)", (long long)s, (long long)S, (long long)b, (long long)e);
+            next = e;
+        }
+        CHECK(next == Kb, "slices end at %lld of %lld", (long long)next, (long long)Kb);
+    }
+    const int64_t ldp = (N + 7) / 8 * 8;
+    std::vector<uint8_t> stored(static_cast<size_t>(M) * ldp, 0);
+    const int mt = static_cast<int>(cdiv(M, kFastBM)), nt = static_cast<int>(cdiv(N, kFastBN));
+    for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < nt; ++tn)
+            for (int wave = 0; wave < kFastWaves; ++wave)
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 8; ++j)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int64_t m = fast_partial_row(static_cast<int64_t>(tm) * kFastBM, wave & 3, i, lane);
+                            const int64_t n = fast_partial_col(static_cast<int64_t>(tn) * kFastBN, wave >> 2, j, lane);
+                            if (m >= M || n >= N) continue;
+                            CHECK(n % 4 == 0 && n + 4 <= ldp, "partial store past the padded row");
+                            for (int e = 0; e < 4; ++e) CHECK(++stored[m * ldp + n + e] == 1, "partial stored twice");
+                        }
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) CHECK(stored[m * ldp + n] == 1, "partial (%lld, %lld) not stored", (long long)m, (long long)n);
+    return true;
+}
+
+static bool check_tail_masks() {
+    for (int krem = 1; krem <= kBlockK; ++krem)
+        for (int lg = 0; lg < 4; ++lg)
+            for (int d = 0; d < 8; ++d) {
+                const uint32_t m = tail_keep_mask(krem, lg, d);
+                for (int b = 0; b < 4; ++b) {
+                    const bool keep = ((m >> (8 * b)) & 0xFF) == 0xFF;
+                    const bool zero = ((m >> (8 * b)) & 0xFF) == 0;
+                    CHECK(keep || zero, "partial byte mask");
+                    CHECK(keep == (fragment_byte(lg, d) + b < krem), "krem %d lg %d d %d byte %d", krem, lg, d, b);
+                }
+            }
+    // the fragment bytes of the four lane groups are each row byte exactly once
+    std::vector<int> hit(128, 0);
+    for (int lg = 0; lg < 4; ++lg)
+        for (int d = 0; d < 8; ++d)
+            for (int b = 0; b < 4; ++b) ++hit[fragment_byte(lg, d) + b];
+    for (int i = 0; i < 128; ++i) CHECK(hit[i] == 1, "fragment byte %d", i);
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// General (float8_e4m3fnuz) kernel: 256 x 128 tiles, 8 waves of 64 x 64.
+static bool check_gen(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    const int mt = static_cast<int>(cdiv(M, kGenBM)), nt = static_cast<int>(cdiv(N, kGenBN));
+    const int64_t Kb = cdiv(K, kBlockK);
+    if (!check_tiles(mt, nt)) return false;
+    std::vector<uint8_t> stored(static_cast<size_t>(M) * N, 0);
+    for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < nt; ++tn) {
+            const int64_t m0 = static_cast<int64_t>(tm) * kGenBM, n0 = static_cast<int64_t>(tn) * kGenBN;
+            const int64_t arows = M - m0 < kGenBM ? M - m0 : kGenBM;
+            const int64_t brows = N - n0 < kGenBN ? N - n0 : kGenBN;
+            for (int64_t kb = 0; kb < Kb; ++kb) {
+                std::vector<uint8_t> ga(2 * 256 * 8, 0), gb(128 * 8, 0), gbd(128 * 8, 0);  // A: once per column half (wave % 2)
+                for (int wave = 0; wave < 8; ++wave)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        bool ok;
+                        // A: subtile i, two 16-byte halves
+                        for (int i = 0; i < 4; ++i)
+                            for (int h = 0; h < 2; ++h) {
+                                const uint64_t off = static_cast<uint64_t>(gen_a_lane(wave >> 1, lane, lda)) + kb * kBlockK + 16 * h;
+                                const int64_t range = gen_a_range(i, arows, lda);
+                                const bool in = access(off, range, 16, ok);
+                                CHECK(ok, "gen A offset");
+                                const int r = gen_a_row(wave >> 1, i, lane);
+                                const int c = 2 * (lane >> 4) + h;
+                                if (r < arows) {
+                                    CHECK(static_cast<int64_t>(off) == (r - gen_a_first_row(i)) * lda + kb * kBlockK + 16 * c, "gen A address");
+                                    if (kb * kBlockK + 16 * c < K) {
+                                        CHECK(in, "gen A row %d not read", r);
+                                        CHECK(++ga[(wave & 1) * 2048 + r * 8 + c] == 1, "gen A chunk twice");
+                                    }
+                                } else {
+                                    CHECK(!in, "gen A row %d past the tile read", r);
+                                }
+                                if (in) CHECK((m0 + gen_a_first_row(i)) * lda + static_cast<int64_t>(off) + 16 <= M * lda, "gen A past the operand");
+                            }
+                        // A scales
+                        for (int i = 0; i < 4; ++i) {
+                            const uint64_t off = static_cast<uint64_t>(gen_ascale_base(m0, wave >> 1, i, lane, M)) + 4 * kb * M;
+                            const bool in = access(off, 4 * M * Kb, 4, ok);
+                            CHECK(ok, "gen a_s offset");
+                            const int64_t m = m0 + gen_a_row(wave >> 1, i, lane);
+                            CHECK(in == (m < M), "gen a_s row %lld", (long long)m);
+                            if (in) CHECK(static_cast<int64_t>(off) == 4 * (kb * M + m), "gen a_s address");
+                        }
+                        // per-column B scales
+                        for (int j = 0; j < 4; ++j) {
+                            const int64_t n = gen_col(n0, wave & 1, j, lane);
+                            const uint32_t base = gen_bscale_base(n, N);
+                            if (gen_bscale_straddles(n, N)) {
+                                for (int e = 0; e < 4; ++e) {
+                                    if (n + e >= N) continue;  // not read
+                                    const uint64_t off = static_cast<uint64_t>(base) + 4 * e + 4 * kb * N;
+                                    const bool in = access(off, 4 * N * Kb, 4, ok);
+                                    CHECK(ok && in && static_cast<int64_t>(off) == 4 * (kb * N + n + e), "gen b_s element");
+                                }
+                            } else {
+                                const uint64_t off = static_cast<uint64_t>(base) + 4 * kb * N;
+                                const bool in = access(off, 4 * N * Kb, 16, ok);
+                                CHECK(off < (1ull << 32) && off % 4 == 0, "gen b_s quad offset");
+                                if (n < N) {
+                                    CHECK(in && static_cast<int64_t>(off) + 16 <= 4 * N * Kb, "gen b_s quad in range");
+                                } else {
+                                    CHECK(static_cast<int64_t>(off) >= 4 * N * Kb, "gen b_s column %lld >= N read", (long long)n);
+                                }
+                            }
+                        }
+                        // B through registers (partial K-block) and straight into LDS
+                        const int tid = 64 * wave + lane;
+                        for (int p = 0; p < 2; ++p) {
+                            const uint64_t off = static_cast<uint64_t>(gen_b_lane(tid, ldb)) + kb * kBlockK;
+                            const bool in = access(off, gen_b_range(p, brows, ldb), 16, ok);
+                            CHECK(ok, "gen B offset");
+                            const int r = gen_b_row(tid, p);
+                            if (r < brows) {
+                                if (kb * kBlockK + 16 * (tid & 7) < K) CHECK(in && ++gb[r * 8 + (tid & 7)] == 1, "gen B row %d", r);
+                            } else {
+                                CHECK(!in, "gen B row %d past the tile read", r);
+                            }
+                        }
+                        for (int q = 0; q < 2; ++q) {
+                            const uint64_t off = static_cast<uint64_t>(gen_bdma_lane(wave, lane, ldb)) + kb * kBlockK;
+                            const bool in = access(off, gen_bdma_range(q, brows, ldb), 16, ok);
+                            CHECK(ok, "gen B DMA offset");
+                            const int r = gen_bdma_row(wave, q, lane);
+                            const int c = (lane & 7) ^ (lane >> 3);
+                            CHECK(c == ((lane & 7) ^ (r & 7)), "gen B LDS chunk position");
+                            if (r < brows) {
+                                // the direct load serves full K-blocks only
+                                if ((kb + 1) * kBlockK <= K) CHECK(in && ++gbd[r * 8 + c] == 1, "gen B DMA row %d", r);
+                            } else {
+                                CHECK(!in, "gen B DMA row %d past the tile read", r);
+                            }
+                        }
+                    }
+                for (int r = 0; r < arows; ++r)
+                    for (int c = 0; c < 8; ++c)
+                        if (kb * kBlockK + 16 * c < K) CHECK(ga[r * 8 + c] == 1 && ga[2048 + r * 8 + c] == 1, "gen A row %d chunk %d", r, c);
+                for (int r = 0; r < brows; ++r)
+                    for (int c = 0; c < 8; ++c) {
+                        if (kb * kBlockK + 16 * c < K) CHECK(gb[r * 8 + c] == 1, "gen B row %d chunk %d", r, c);
+                        if ((kb + 1) * kBlockK <= K) CHECK(gbd[r * 8 + c] == 1, "gen B DMA row %d chunk %d", r, c);
+                    }
+            }
+            for (int wave = 0; wave < 8; ++wave)
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 4; ++j)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int64_t m = m0 + gen_a_row(wave >> 1, i, lane);
+                            const int64_t n = gen_col(n0, wave & 1, j, lane);
+                            if (m >= M) continue;
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N) CHECK(++stored[m * N + n + e] == 1, "gen C stored twice");
+                        }
+        }
+    for (int64_t i = 0; i < M * N; ++i) CHECK(stored[i] == 1, "gen C element %lld not stored", (long long)i);
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// quantize_lhs scale stores (units of 64 rows of one K-block, 16 teams x 4 rows per unit).
+static bool check_lhs_scales(int64_t M, int64_t K) {
+    const int64_t Kb = cdiv(K, kBlockK);
+    const int rows_per_team = 4;
+    const int64_t units = cdiv(M, 16 * rows_per_team) * Kb;
+    std::vector<uint8_t> w(static_cast<size_t>(M) * Kb, 0);
+    for (int64_t u = 0; u < units; ++u) {
+        int64_t rb, kb;
+        lhs_unit(u, Kb, rb, kb);
+        CHECK(kb >= 0 && kb < Kb, "unit K-block");
+        for (int team = 0; team < 16; ++team)
+            for (int r = 0; r < rows_per_team; ++r) {
+                const int64_t m = lhs_row(rb, rows_per_team, r, team);
+                if (!row_stored(m, M)) continue;  // the kernel's store predicate
+                const int64_t idx = colmajor_index(kb, M, m);
+                CHECK(m < M && idx >= 0 && idx < M * Kb, "a_s store of row %lld (index %lld)", (long long)m, (long long)idx);
+                CHECK(++w[idx] == 1, "a_s[%lld] stored twice", (long long)idx);
+            }
+    }
+    for (int64_t i = 0; i < M * Kb; ++i) CHECK(w[i] == 1, "a_s[%lld] not stored", (long long)i);
+    return true;
+}
+
+int main(int argc, char** argv) {
+    if (!check_tail_masks()) return 1;
+    for (int a = 1; a + 2 < argc; a += 3) {
+        const int64_t M = std::atoll(argv[a]), N = std::atoll(argv[a + 1]), K = std::atoll(argv[a + 2]);
+        const int64_t ld = (K + 15) / 16 * 16;  // the GEMMs' 16-byte row rule
+        bool ok = check_fast(M, N, K, ld, ld) && check_fast(M, N, K, ld + 16, ld + 48) && check_split(M, N, K) &&
+                  check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);
+        std::printf("%s M=%lld N=%lld K=%lld\n", ok ? "ok" : "FAILED", (long long)M, (long long)N, (long long)K);
+        if (!ok) return 1;
+    }
+    return g_fail;
+}
