@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -109,13 +110,25 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
+// BSFP8_GEMM_SPLIT (environment, read at each call): a slice count that replaces the automatic
+// choice of gemm_split_plan (1 = never split), so tests and benchmarks can run the split path on any
+// shape. Unset or empty: automatic.
+int forced_split() {
+    const char* v = std::getenv("BSFP8_GEMM_SPLIT");
+    if (v == nullptr || *v == 0) return 0;
+    const long s = std::strtol(v, nullptr, 10);
+    return s < 1 ? 1 : (s > 65535 ? 65535 : static_cast<int>(s));
+}
+
 // The GEMM with its K split when the plan asks for it: the workspace is allocated and freed in
 // stream order around the two kernels.
 hipError_t run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                     bsfp8::BScale bs, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz,
                     hipStream_t stream) {
     const int cus = bsfp8::device_cus();
-    const bsfp8::SplitPlan plan = bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+    const int forced = forced_split();
+    const bsfp8::SplitPlan plan = forced ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, forced, kMaxSplitWorkspace)
+                                         : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
     float* ws = nullptr;
     if (plan.S > 1) {
         hipMemPool_t pool = nullptr;

@@ -967,6 +967,24 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, i
     return plan;
 }
 
+// A slice count chosen by the caller: clamped to the K-blocks and to the workspace bound; fewer than
+// two slices means no split.
+SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int S, int64_t max_bytes) {
+    SplitPlan plan{1, 0, 0};
+    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const int64_t ldp = (N + 7) / 8 * 8;
+    const int64_t slice_bytes = M * ldp * 4;
+    int64_t s = S > Kb ? Kb : S;
+    if (s * slice_bytes > max_bytes) s = max_bytes / slice_bytes;
+    if (s > 65535) s = 65535;
+    if (s < 2) return plan;
+    plan.S = static_cast<int>(s);
+    plan.ldp = ldp;
+    plan.bytes = s * slice_bytes;
+    return plan;
+}
+
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, bool fnuz, const SplitPlan& plan, float* workspace, int cus,

@@ -45,6 +45,9 @@ struct SplitPlan {
     int64_t bytes;
 };
 SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes);
+// A plan with S slices chosen by the caller (clamped to the K-block count and to max_bytes of
+// workspace; fewer than two: no split), so the split path can run on any shape.
+SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int S, int64_t max_bytes);
 
 // fnuz: both operands hold float8_e4m3fnuz codes (general kernel, f16 matrix instructions).
 // plan.S > 1 needs `workspace` (plan.bytes, 256-byte aligned, device memory) for the partial tiles.

@@ -316,3 +316,44 @@ def test_gemm_partial_last_block_ignores_nan_padding(M, N, K, ld, per_col):
         c_abs = oracle.gemm_1x128_128x128(_abs_codes(ah), a_s, _abs_codes(bh), b_s, Kb, 1)
     assert np.all(np.isfinite(got))
     _assert_dot_bound(got, co, c_abs, "partial last K-block")
+
+
+# ------------------------------------------------------------------ the split-K path
+
+SPLIT_SHAPES = [
+    # M, N, K, ld: ragged tiles, a partial last K-block, one tile, several tiles
+    (130, 300, 1000, 1008), (1, 40, 4096, 4096), (257, 513, 2000, 2000), (64, 256, 384, 384),
+]
+
+
+@pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
+@pytest.mark.parametrize("S", [2, 3, 7])
+@pytest.mark.parametrize("M,N,K,ld", SPLIT_SHAPES, ids=lambda v: str(v))
+def test_gemm_forced_split(M, N, K, ld, S, per_col, monkeypatch):
+    """K split over S slices (BSFP8_GEMM_SPLIT) on ragged shapes: fp32 partial tiles summed by the
+    second kernel, against the oracle in full; the fixed summation order makes two calls agree bit
+    for bit."""
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + N + K + S, per_col)
+    monkeypatch.setenv("BSFP8_GEMM_SPLIT", str(S))
+    if per_col:
+        fn = lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x1(oqa, osa, oqb, osb)
+    else:
+        fn = lambda c: bf.gemm_1x128_128x128(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x128(oqa, osa, oqb, osb, osb.shape[1], 1)
+    got = _run_guarded(fn, M, N, N + 3)
+    again = _run_guarded(fn, M, N, N + 3)
+    assert np.array_equal(got, again)
+    _assert_close(got, co, f"split {S}")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2, 5120, 1280),
+                                   (4, 3584, 640)], ids=lambda v: str(v))
+def test_forward_split_shapes_full(M, N, K, monkeypatch):
+    """The pages' short-and-wide GEMM shapes, where the automatic plan splits K: every output row
+    against the oracle, and the SQNR against the fp64 matmul of the bf16 inputs."""
+    monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
+    g = inputs.rng(0)
+    a_h = inputs.normal_bf16(g, (M, K))
+    w_h = inputs.normal_bf16(g, (N, K), 0.02)
+    _forward_check(a_h, w_h, np.arange(M), sqnr_min=27.5)
