@@ -34,8 +34,12 @@
  *   the next block; C is rounded to bf16 (RNE).
  *
  * Memory and ownership
- *   Every tensor pointer is a DEVICE pointer owned by the caller. The library never allocates,
- *   frees or retains memory and keeps no state besides a per-device architecture check.
+ *   Every tensor pointer is a DEVICE pointer owned by the caller; the library retains none of
+ *   them. Its state per device: the architecture check, the compute-unit count, and a
+ *   stream-ordered memory pool for the K-split workspace of gemm_1x128_128x128 and
+ *   gemm_1x128_128x1 (fp32 partial tiles, at most 256 MiB per call, allocated and freed on the
+ *   call's stream around its two kernels; the pool keeps freed memory for reuse until the process
+ *   ends). No other entry point allocates.
  *   Row-major tensors take a row stride "ld" in elements (bytes for fp8).
  *   Outputs must not overlap inputs. Every in-range output element is written; nothing outside the
  *   in-range elements (padding between rows, rows >= M, ...) is written.
@@ -134,9 +138,18 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  *       scales read transposed: strides (1, Nb_of_weight)). Strides must be >= 0.
  *   c   [M, N] bf16, row stride ldc >= N.
  * Alignment (else BSFP8_EALIGN): a and b 16-byte aligned, lda and ldb multiples of 16.
- * Size limits (else BSFP8_EINVAL; operands are addressed with 32-bit byte offsets):
- *   256 * lda and 256 * ldb below 2^32, and 4 * M * ceil(K/128) below 2^32.
+ * Size limits (else BSFP8_EINVAL; every operand and scale read goes through a buffer resource of
+ * at most 2^31 bytes, and a lane whose row, column or K-block is out of range is given an offset
+ * past that resource's end, which the hardware reads as zero):
+ *   256 * lda, 256 * ldb, 4 * M * ceil(K/128) and 4 * (the b_s elements the strides span) at most
+ *   2^31; ceil(M/128) at most 65535.
  * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
+ * Schedule: one workgroup per 256 x 256 output tile. When few tiles leave most compute units idle
+ * (M <= 512 and at most a quarter as many tiles as compute units, on a long enough K) the K-blocks
+ * are split over S workgroups per tile, which write fp32 partial tiles to the pooled workspace, and
+ * a second kernel sums the S partials in a fixed order into C (same result on every call). The
+ * environment variable BSFP8_GEMM_SPLIT, read at each call, forces S (1 = never split; S is
+ * clamped to ceil(K/128) and to the workspace bound).
  */
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
                        const void* b, int64_t ldb, const float* b_s,
@@ -148,8 +161,8 @@ int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
  * (wgrad dW = dY^T X, contracting over tokens: A and B are quantize_rhs outputs).
  *   a, lda, a_s as above;  b [N, K] fp8, row stride ldb;
  *   b_s [ceil(K/128), N] fp32 row-major: the scale of (kb, n) is b_s[kb * N + n].
- *   c   [M, N] bf16, row stride ldc >= N.  Alignment and size limits as for gemm_1x128_128x128,
- *   and also 4 * N * ceil(K/128) below 2^32.
+ *   c   [M, N] bf16, row stride ldc >= N.  Alignment, size limits and schedule as for
+ *   gemm_1x128_128x128 (4 * N * ceil(K/128) at most 2^31 in place of the b_s span).
  */
 int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s,
                      const void* b, int64_t ldb, const float* b_s,
@@ -172,8 +185,8 @@ int gemm_1x128_128x1(const void* a, int64_t lda, const float* a_s,
  *   offsets       E + 1 int64 in DEVICE memory, non-decreasing, in [0, M]. The kernel clamps them
  *                 into [0, M] and to non-decreasing order; rows outside every range are not written.
  *   c, ldc        C [M, N] bf16.
- * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, at most 512 K-blocks; b_stride a
- * multiple of 16 (else BSFP8_EALIGN); alignment and size limits as gemm_1x128_128x128.
+ * Requirements (else BSFP8_EINVAL): K a positive multiple of 128; b_stride a multiple of 16 (else
+ * BSFP8_EALIGN); alignment and size limits as gemm_1x128_128x128. Never split; allocates nothing.
  * E == 0 or an empty M or N: no launch.
  */
 int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s,
@@ -194,8 +207,9 @@ int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s,
  *                 is the per-expert quantization. Boundaries are clamped into [0, K] and to
  *                 non-decreasing order and rounded down to a multiple of 128.
  *   c, ldc        E outputs [M, N] bf16, expert e's at c + e * c_stride (elements).
- * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, N % 4 == 0, E <= 65535,
+ * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, E <= 65535,
  * c_stride >= (M - 1) * ldc + N when E > 1; alignment and size limits as gemm_1x128_128x1.
+ * Never split; allocates nothing.
  * E == 0 or an empty M or N: no launch.
  */
 int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s,
