@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     gemm_1x128_128x1_grouped,
     gemm_1x128_128x128,
     gemm_1x128_128x128_grouped,
+    gemm_1x128_128x128_noalloc,
     quantize_lhs,
     quantize_lhs_and_rhs,
     quantize_lhs_and_weight,

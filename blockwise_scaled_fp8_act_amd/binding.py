@@ -52,6 +52,7 @@ def lib():
         L.quantize_weight_128x128.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
         L.gemm_1x128_128x128.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _i64,
                                          _i64, _i64, _i64, _vp]
+        L.gemm_1x128_128x128_noalloc.argtypes = L.gemm_1x128_128x128.argtypes
         L.gemm_1x128_128x1.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
                                        _vp]
         L.encode_e4m3_f32.argtypes = [_vp, _vp, _i64, _vp]
@@ -70,6 +71,7 @@ def lib():
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
                   "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs",
                   "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
+                  "gemm_1x128_128x128_noalloc",
                   "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
                   "gemm_1x128_128x128_fnuz", "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
                   "quantize_lhs_and_rhs_fnuz", "quantize_lhs_and_weight",
@@ -219,6 +221,20 @@ def gemm_1x128_128x128(a, a_s, b, b_s, bs_stride_nb=None, bs_stride_kb=None, c=N
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _call(_entry("gemm_1x128_128x128", fmt), _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
+          bs_stride_nb, bs_stride_kb, _ptr(c), _ld(c), M, N, K, _stream(stream))
+    return c
+
+
+def gemm_1x128_128x128_noalloc(a, a_s, b, b_s, c, bs_stride_nb=None, bs_stride_kb=None, K=None,
+                               stream=None):
+    """gemm_1x128_128x128 (e4m3fn) into a caller-provided ``c``, with the K-split partial tiles in
+    the library's static scratch: the call allocates no device memory."""
+    M = a.shape[0]
+    N = b.shape[0]
+    K = a.shape[1] if K is None else K
+    if bs_stride_nb is None:
+        bs_stride_nb, bs_stride_kb = b_s.stride(0), b_s.stride(1)
+    _call("gemm_1x128_128x128_noalloc", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
           bs_stride_nb, bs_stride_kb, _ptr(c), _ld(c), M, N, K, _stream(stream))
     return c
 

@@ -120,32 +120,37 @@ int forced_split() {
     return s < 1 ? 1 : (s > 65535 ? 65535 : static_cast<int>(s));
 }
 
-// The GEMM with its K split when the plan asks for it: the workspace is allocated and freed in
-// stream order around the two kernels.
-hipError_t run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
-                    bsfp8::BScale bs, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz,
-                    hipStream_t stream) {
+// The GEMM with its K split when the plan asks for it. The workspace is allocated and freed in
+// stream order around the two kernels, or, with use_scratch, is the library's static scratch
+// (nothing allocated; a plan larger than the scratch is BSFP8_ESCRATCH).
+int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+             bsfp8::BScale bs, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz,
+             bool use_scratch, hipStream_t stream) {
     const int cus = bsfp8::device_cus();
     const int forced = forced_split();
     const bsfp8::SplitPlan plan = forced ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, forced, kMaxSplitWorkspace)
                                          : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+    if (use_scratch) {
+        if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
+        float* ws = nullptr;
+        if (plan.S > 1 && bsfp8::gemm_scratch(&ws) != hipSuccess) return BSFP8_EHIP;
+        return finish(bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b),
+                                         ldb, bs, static_cast<uint16_t*>(c), ldc, M, N, K, fnuz, plan, ws, cus,
+                                         stream));
+    }
     float* ws = nullptr;
     if (plan.S > 1) {
         hipMemPool_t pool = nullptr;
-        hipError_t e = device_pool(&pool);
-        if (e != hipSuccess) return e;
-        if ((e = hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.bytes), pool,
-                                        stream)) != hipSuccess)
-            return e;
+        if (device_pool(&pool) != hipSuccess) return BSFP8_EHIP;
+        if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(plan.bytes), pool, stream) !=
+            hipSuccess)
+            return BSFP8_EHIP;
     }
     const hipError_t e = bsfp8::launch_gemm(static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b),
                                             ldb, bs, static_cast<uint16_t*>(c), ldc, M, N, K, fnuz, plan, ws,
                                             cus, stream);
-    if (ws != nullptr) {
-        const hipError_t f = hipFreeAsync(ws, stream);
-        if (e == hipSuccess && f != hipSuccess) return f;
-    }
-    return e;
+    const hipError_t f = ws != nullptr ? hipFreeAsync(ws, stream) : hipSuccess;
+    return finish(e != hipSuccess ? e : f);
 }
 
 int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
@@ -229,25 +234,26 @@ int64_t bscale_extent(int64_t N, int64_t K, int64_t bs_nb, int64_t bs_kb) {
 
 int gemm_128x128_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                       const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
-                      int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz, void* stream) {
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz, void* stream,
+                      bool use_scratch = false) {
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (M == 0 || N == 0) return BSFP8_OK;
     if (bs_stride_nb < 0 || bs_stride_kb < 0) return BSFP8_EINVAL;
     if (K > 0 && 4 * bscale_extent(N, K, bs_stride_nb, bs_stride_kb) > kMaxRange) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, bs_stride_nb, bs_stride_kb, 0};
-    return finish(run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, static_cast<hipStream_t>(stream)));
+    return run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, use_scratch, static_cast<hipStream_t>(stream));
 }
 
 int gemm_128x1_impl(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
                     const float* b_s, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                    bool fnuz, void* stream) {
+                    bool fnuz, void* stream, bool use_scratch = false) {
     if (int rc = validate_gemm(a, lda, a_s, b, ldb, b_s, c, ldc, M, N, K)) return rc;
     if (M == 0 || N == 0) return BSFP8_OK;
     if (4 * N * cdiv(K, kGroupEdge) > kMaxRange) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     bsfp8::BScale bs{b_s, 0, 0, 1};
-    return finish(run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, static_cast<hipStream_t>(stream)));
+    return run_gemm(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, fnuz, use_scratch, static_cast<hipStream_t>(stream));
 }
 
 int encode_impl(const float* x, void* q, int64_t n, bool fnuz, void* stream) {
@@ -272,6 +278,7 @@ const char* bsfp8_status_string(int status) {
         case BSFP8_EALIGN: return "operand rows not 16-byte aligned";
         case BSFP8_EDEVICE: return "current device is not gfx950";
         case BSFP8_EHIP: return "HIP call or kernel launch failed";
+        case BSFP8_ESCRATCH: return "the K-split workspace exceeds the allocation-free scratch";
         default: return "unknown status";
     }
 }
@@ -311,6 +318,13 @@ int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s, const void*
                        int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
     return gemm_128x128_impl(a, lda, a_s, b, ldb, b_s, bs_stride_nb, bs_stride_kb, c, ldc, M, N, K,
                              false, stream);
+}
+
+int gemm_1x128_128x128_noalloc(const void* a, int64_t lda, const float* a_s, const void* b, int64_t ldb,
+                               const float* b_s, int64_t bs_stride_nb, int64_t bs_stride_kb, void* c,
+                               int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+    return gemm_128x128_impl(a, lda, a_s, b, ldb, b_s, bs_stride_nb, bs_stride_kb, c, ldc, M, N, K,
+                             false, stream, true);
 }
 
 int gemm_1x128_128x128_fnuz(const void* a, int64_t lda, const float* a_s, const void* b,

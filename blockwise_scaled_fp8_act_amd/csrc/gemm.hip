@@ -30,6 +30,7 @@
 // K-block is four v_mfma_f32_16x16x32_f16 instead of one FP8 instruction -- products of two
 // 4-significant-bit values are exact in fp32 either way, so the per-K-block partials equal the fn
 // path's arithmetic up to the exact factor 2^-14.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -935,6 +936,36 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 }  // namespace fast
 
 }  // namespace
+
+// Scratch of the allocation-free GEMM entry point: the split-K partial tiles, in a file-scope device
+// array (each GPU holds its own copy for the life of the process). In host code the array's name is
+// a stand-in, not a device address: host code uses only the address hipGetSymbolAddress returns for
+// the current device, looked up on the first use on that device and kept. 64 MiB covers every plan
+// gemm_split_plan makes (at most one slice per CU of a 256 x 256 fp32 tile: 256 x 256 KiB).
+constexpr int64_t kScratchBytes = 64LL << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+namespace {
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[64];
+}  // namespace
+
+int64_t gemm_scratch_bytes() { return kScratchBytes; }
+
+hipError_t gemm_scratch(float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // When to split K, from measurements on MI355X (256 CUs; back-to-back launches, settled clock): a
 // slice costs its fp32 partial tile (written, then read by the sum) and the sum is a second launch,

@@ -49,6 +49,11 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, i
 // workspace; fewer than two: no split), so the split path can run on any shape.
 SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int S, int64_t max_bytes);
 
+// The allocation-free GEMM's scratch: a device array of gemm_scratch_bytes() bytes per device;
+// gemm_scratch gives its address on the current device (looked up once per device).
+int64_t gemm_scratch_bytes();
+hipError_t gemm_scratch(float** out);
+
 // fnuz: both operands hold float8_e4m3fnuz codes (general kernel, f16 matrix instructions).
 // plan.S > 1 needs `workspace` (plan.bytes, 256-byte aligned, device memory) for the partial tiles.
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,

@@ -53,7 +53,8 @@
  *   size, ld smaller than the row length, a stride out of range, a GEMM beyond its size limits;
  *   BSFP8_EALIGN (2) a GEMM operand
  *   row is not 16-byte aligned (see the GEMMs); BSFP8_EDEVICE (3) the current device is not gfx950;
- *   BSFP8_EHIP (4) a HIP call or launch failed. Argument checks happen before any HIP call, so
+ *   BSFP8_EHIP (4) a HIP call or launch failed; BSFP8_ESCRATCH (5) gemm_1x128_128x128_noalloc's
+ *   split workspace would exceed its scratch. Argument checks happen before any HIP call, so
  *   codes 1 and 2 need no GPU. Empty problems (a zero extent) return BSFP8_OK without launching,
  *   except that a GEMM with K == 0 and M, N > 0 writes C = 0.
  */
@@ -71,7 +72,8 @@ enum {
     BSFP8_EINVAL = 1,
     BSFP8_EALIGN = 2,
     BSFP8_EDEVICE = 3,
-    BSFP8_EHIP = 4
+    BSFP8_EHIP = 4,
+    BSFP8_ESCRATCH = 5
 };
 
 /* Text for a return code (static storage). */
@@ -155,6 +157,22 @@ int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
                        const void* b, int64_t ldb, const float* b_s,
                        int64_t bs_stride_nb, int64_t bs_stride_kb,
                        void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * gemm_1x128_128x128_noalloc: gemm_1x128_128x128 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, result, limits and split schedule; the K-split partial tiles live in a static scratch
+ * array of 64 MiB that each GPU holds for the life of the process, so the call allocates nothing
+ * (no hipMalloc, no pool). 64 MiB covers every automatic split plan; a plan forced larger through
+ * BSFP8_GEMM_SPLIT returns BSFP8_ESCRATCH before any launch. Every call on one GPU shares that
+ * GPU's scratch: calls on one stream are ordered, but calls that overlap in time on one GPU (other
+ * streams, other threads) race on it. No part of the scratch needs clearing (each slice writes its
+ * whole partial tile before the sum reads it).
+ */
+int gemm_1x128_128x128_noalloc(const void* a, int64_t lda, const float* a_s,
+                               const void* b, int64_t ldb, const float* b_s,
+                               int64_t bs_stride_nb, int64_t bs_stride_kb,
+                               void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * gemm_1x128_128x1: C = A B^T with 1x128 scales on A and per-column 128x1 scales on B
