@@ -42,14 +42,22 @@ def normal_bf16(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return bf16_bits_from_f64(g.standard_normal(shape) * std)
 
 
-def _apply_outliers(g: np.random.Generator, a: np.ndarray, n_channels: int,
-                    zero_group_frac: float) -> np.ndarray:
+def _apply_outliers(g: np.random.Generator, a: np.ndarray, n_channels: int, zero_frac: float,
+                    zero_whole_groups: bool) -> np.ndarray:
+    """Multiply n_channels random K-channels by 100, then set a zero_frac share to exactly zero:
+    single elements drawn at random over the tensor, or (zero_whole_groups) whole 1x128 groups,
+    whose all-zero amax takes the eps clamp."""
     M, K = a.shape
     cols = g.choice(K, size=n_channels, replace=False)
     a[:, cols] *= 100.0
+    if not zero_whole_groups:
+        n_zero = int(round(zero_frac * M * K))
+        flat = g.choice(M * K, size=n_zero, replace=False)
+        a.reshape(-1)[flat] = 0.0
+        return a
     kb = (K + BLOCK - 1) // BLOCK
     n_groups = M * kb
-    n_zero = int(round(zero_group_frac * n_groups))
+    n_zero = int(round(zero_frac * n_groups))
     groups = g.choice(n_groups, size=n_zero, replace=False)
     for gid in groups:
         m, b = divmod(int(gid), kb)
@@ -62,16 +70,19 @@ WORKLOADS = {
     1: "fwd_tail: A[130,1280]~N(0,1), W[5120,1280]~N(0,0.02^2)",
     2: "fwd_4096: A[4096,4096]~N(0,1), W[4096,4096]~N(0,0.02^2)",
     3: "train_step: X[8192,4096]~N(0,1), W[4096,4096]~N(0,0.02^2), dY[8192,4096]~N(0,0.01^2)",
-    4: "fwd_outlier: A[16384,5120]~N(0,1) with 26 columns x100 and 1% of 1x128 groups zero, "
-       "W[5120,5120]~t(4)*0.02",
+    4: "fwd_outlier: A[16384,5120]~N(0,1) with 26 columns x100 and 1% of elements exactly zero, "
+       "W[5120,5120]~t(4)*0.02 (zero_groups=True: 1% of whole 1x128 groups zero instead, the eps "
+       "clamp case)",
 }
 
 
-def make_workload(idx: int, seed: int = 0, scale_down: int = 1) -> dict:
+def make_workload(idx: int, seed: int = 0, scale_down: int = 1, zero_groups: bool = False) -> dict:
     """Return the named bf16 tensors (uint16 bit patterns) of workload ``idx``.
 
     ``scale_down`` > 1 divides the token dimension (and, for the outlier case, nothing else) so
     CPU-only tests can use the same recipe at a smaller size; the full size is scale_down = 1.
+    ``zero_groups`` (outlier case only) zeroes 1% of whole 1x128 groups instead of 1% of the
+    elements, so the eps clamp of an all-zero group is exercised.
     """
     g = rng(seed)
     if idx == 0:
@@ -92,6 +103,7 @@ def make_workload(idx: int, seed: int = 0, scale_down: int = 1) -> dict:
         M, K, N = 16384 // scale_down, 5120, 5120
         a = g.standard_normal((M, K))
         w = g.standard_t(4.0, size=(N, K)) * 0.02
-        a = _apply_outliers(g, a, n_channels=int(round(0.005 * K)), zero_group_frac=0.01)
+        a = _apply_outliers(g, a, n_channels=int(round(0.005 * K)), zero_frac=0.01,
+                            zero_whole_groups=zero_groups)
         return {"A": bf16_bits_from_f64(a), "W": bf16_bits_from_f64(w)}
     raise ValueError(f"unknown workload {idx}")

@@ -1,8 +1,13 @@
 """Blockwise-FP8 linear layer for training, composed from the C-ABI kernels.
 
-The recipe of "Enable blockwise FP8 dense training kernels on ROCm" (description: the linear layer
-runs its forward and both backward GEMMs in FP8 with the 1x128 / 128x1 / 128x128 groupings; the
-quantization-correctness table lists which quantizer feeds which GEMM):
+"Enable blockwise FP8 dense training kernels on ROCm" names the parts but not their wiring: its
+quantization-correctness table lists three quantizers (act_quant_lhs, act_quant_rhs,
+weight_quant_rhs, block_size 128), its description mentions the blockwise linear module
+(Float8BlockwiseLinear) and the dense training kernels, and "Mask a_s/b_s scale loads in blockwise
+FP8 training GEMM kernels" names the two GEMMs (1x128_128x128, 1x128_128x1). Which quantizer feeds
+which GEMM of a training step is this module's reading -- the one the groupings force, since the
+1x128 and 128x128 groups run along the contracted dimension of the forward and dgrad products and
+the 128x1 groups along the tokens the weight gradient contracts over:
 
     forward   Y  = X W^T      A = quantize_lhs(X)        (1x128 along in_features)
                               B = quantize_weight(W)     (128x128), gemm_1x128_128x128

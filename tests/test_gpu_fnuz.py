@@ -145,7 +145,7 @@ def test_quantize_lhs_and_rhs_fnuz_parity(R, C, ldx, ldq, ldqT):
 def test_quantize_fnuz_outliers_zero_groups_and_negative_tiny():
     """Outlier columns, all-zero groups (eps clamp), and groups of -0.0 and of tiny negatives that
     round to zero: fnuz has no negative zero, so no 0x80 may appear."""
-    d = inputs.make_workload(4, scale_down=8)
+    d = inputs.make_workload(4, scale_down=8, zero_groups=True)
     xh = d["A"].copy()
     xh[0, :128] = 0x8000                                  # -0.0
     xh[1, :128] = inputs.bf16_bits_from_f64(np.full(128, -1e-30))

@@ -86,8 +86,8 @@ def test_linear_layer_training_step_sampled():
     d = inputs.make_workload(3)
     xh, wh, dyh = d["X"], d["W"], d["dY"]
     y, dx, dw = _run_layer(xh, wh, dyh)
-    rows_t = _sample_rows(xh.shape[0], 40)
-    rows_w = _sample_rows(wh.shape[0], 40)
+    rows_t = _sample_rows(xh.shape[0], 256)
+    rows_w = _sample_rows(wh.shape[0], 256)
     oy, odx, odw = _oracle_layer(xh, wh, dyh, rows_t, rows_w)
     _check(y[rows_t], oy, "forward")
     _check(dx[rows_t], odx, "dgrad")

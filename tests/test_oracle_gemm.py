@@ -158,3 +158,54 @@ def test_sqnr_negative_control_scale_store_bug():
     bad = oracle.gemm_1x128_128x128(qa, flat[: M * 2].reshape(2, M), qw, sw, sw.shape[1], 1)
     assert oracle.sqnr_db(ref, good) > 27.0
     assert 2.0 <= oracle.sqnr_db(ref, bad) <= 10.0
+
+
+# ------------------------------------------------------------------ the acceptance criterion itself
+
+def test_tolerance_report_elementwise_bound_both_sides():
+    """|C - C_o| <= 2e-2 (|C_o| + 1): a difference on the bound passes, one just past it fails
+    (checked where |C_o| is 0, moderate and large, and for both signs of the difference)."""
+    co = np.array([[0.0, 3.0, -250.0, 1e4]])
+    bound = 2e-2 * (np.abs(co) + 1.0)
+    # inside the Frobenius limit: put the elementwise probe on one element of a large, exact matrix
+    big = np.full((64, 64), 1e3)
+    for j in range(co.shape[1]):
+        for sign in (1.0, -1.0):
+            c_o = big.copy()
+            c_o[0, 0] = co[0, j]
+            at = c_o.copy()
+            at[0, 0] += sign * bound[0, j] * (1 - 1e-12)
+            rep = oracle.gemm_tolerance_report(at, c_o)
+            assert rep["n_bad"] == 0 and rep["ok"], (j, sign, rep)
+            past = c_o.copy()
+            past[0, 0] += sign * bound[0, j] * (1 + 1e-9)
+            rep = oracle.gemm_tolerance_report(past, c_o)
+            assert rep["n_bad"] == 1 and not rep["ok"] and rep["max_excess"] > 0, (j, sign, rep)
+
+
+def test_tolerance_report_frobenius_bound_both_sides():
+    """||C - C_o||_F / ||C_o||_F <= 4e-3, with every element well inside its own bound."""
+    g = np.random.Generator(np.random.PCG64(5))
+    c_o = g.standard_normal((128, 96)) * 50.0
+    d = c_o * np.where(g.random(c_o.shape) < 0.5, -1.0, 1.0)   # |d| = |C_o|: ||d||_F = ||C_o||_F
+    for ratio, ok in [(4e-3 * (1 - 1e-9), True), (4e-3 * (1 + 1e-9), False), (3e-3, True), (5e-3, False)]:
+        c = c_o + ratio * d
+        rep = oracle.gemm_tolerance_report(c, c_o)
+        assert rep["n_bad"] == 0, rep                       # the elementwise test passes throughout
+        assert abs(rep["rel_frobenius"] - ratio) <= 1e-12 * ratio + 1e-15
+        assert rep["ok"] is ok, (ratio, rep)
+
+
+def test_tolerance_report_zero_oracle_and_empty():
+    """An all-zero C_o: the relative error falls back to ||C||_F (so any C within 4e-3 of zero in
+    norm passes, an error of 1 fails); an empty pair passes."""
+    z = np.zeros((3, 3))
+    assert oracle.gemm_tolerance_report(z, z)["ok"]
+    small = z.copy()
+    small[1, 1] = 1e-3
+    assert oracle.gemm_tolerance_report(small, z)["ok"]
+    one = z.copy()
+    one[1, 1] = 1e-2                                        # inside 2e-2 elementwise, 1e-2 > 4e-3
+    rep = oracle.gemm_tolerance_report(one, z)
+    assert rep["n_bad"] == 0 and not rep["ok"]
+    assert oracle.gemm_tolerance_report(np.zeros((0, 4)), np.zeros((0, 4)))["ok"]

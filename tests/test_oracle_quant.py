@@ -208,9 +208,23 @@ def test_weight_block_with_amax_in_every_row_matches_lhs():
     assert np.all(sl == sw[0, 0])
 
 
-def test_outlier_workload_takes_eps_path():
-    """The outlier recipe zeroes 1% of 1x128 groups, so the eps clamp is really exercised."""
+def test_outlier_workload_zeroes_one_percent_of_elements():
+    """The outlier recipe as stated: 1% of the elements exactly zero (scattered, so no group is
+    all zero and the eps clamp is not taken), 0.5% of the channels scaled by 100."""
     d = inputs.make_workload(4, scale_down=64)  # 256 x 5120
+    a = oracle.bf16_bits_to_f64(d["A"])
+    n = a.size
+    # N(0,1) draws are never exactly zero in bf16 except through the recipe's zeroing
+    assert abs(int(np.count_nonzero(a == 0.0)) - round(0.01 * n)) <= 2
+    big = np.abs(a).max(axis=0) > 50.0
+    assert int(np.count_nonzero(big)) == round(0.005 * 5120)
+    q, a_s = oracle.quantize_lhs(d["A"])
+    assert int(np.count_nonzero(a_s == np.float32(EPS / F448))) == 0
+
+
+def test_outlier_zero_group_variant_takes_eps_path():
+    """The eps variant zeroes 1% of whole 1x128 groups, so the eps clamp is really exercised."""
+    d = inputs.make_workload(4, scale_down=64, zero_groups=True)  # 256 x 5120
     q, a_s = oracle.quantize_lhs(d["A"])
     s_eps = np.float32(EPS / F448)
     n_zero_groups = int(round(0.01 * 256 * 40))
