@@ -228,7 +228,7 @@ def main():
     # the quantizer launch's own duration: the step's quantizer launched back to back over the
     # rotating sets, one event pair per batch (an event pair around a single launch also spans its
     # dispatch, as the in-step figure above does)
-    q_batch_ms = _time_kernel(
+    q_batch_ms, q_p10, q_p90 = _time_kernel(
         lambda i: bf.quantize_lhs_and_weight(sets[i % len(sets)]["A"], sets[i % len(sets)]["W"],
                                              sets[i % len(sets)]["qa"], sets[i % len(sets)]["sa"],
                                              sets[i % len(sets)]["qw"], None, sets[i % len(sets)]["sw"],
@@ -247,7 +247,10 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(A_h, W_h, args.cpu_rows)
+        s0 = sets[0]
+        gpu = {k: s0[k].cpu().numpy() for k in ("qa", "sa", "qw", "sw")}
+        gpu["c"] = s0["c"].float().cpu().numpy()
+        cpu = cpu_baseline(A_h, W_h, args.cpu_rows, gpu)
 
     out = {
         "metric": "blockwise-FP8 GEMM TFLOPS @4096^3 (% FP8 MFMA peak) + quantizer GB/s (% HBM)",
@@ -282,12 +285,16 @@ def main():
         },
         "step_kernels": {
             "quantize_lhs_and_weight": {"avg_us": round(q_batch_ms * 1e3, 2),
+                                        "p10_us": round(q_p10 * 1e3, 2),
+                                        "p90_us": round(q_p90 * 1e3, 2),
                                         "in_step_avg_us": round(k_avg[0] * 1e3, 2),
                                         "in_step_median_us": round(k_med[0] * 1e3, 2),
                                         "GB/s": round(q_gbs, 1),
                                         "frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4)},
             "gemm_1x128_128x128": {"avg_us": round(k_avg[1] * 1e3, 2),
                                    "median_us": round(k_med[1] * 1e3, 2),
+                                   "p10_us": round(float(np.percentile(gemm_ms, 10)) * 1e3, 2),
+                                   "p90_us": round(float(np.percentile(gemm_ms, 90)) * 1e3, 2),
                                    "TFLOP/s": round(gemm_tflops, 1),
                                    "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4)},
         },
@@ -317,33 +324,42 @@ def settle(fn, min_ms, torch, chunk=50):
 SETTLE_ROW_MS = 30.0
 
 
-def _time_kernel(fn, reps, stream, torch):
-    """Average duration (ms) of fn(i) over reps back-to-back launches: one HIP event pair on
-    `stream` around the whole batch, so host-side launch cost never shows as GPU time. The
-    launches first run for SETTLE_ROW_MS so the clock has settled after the host-side set-up."""
+def _time_kernel(fn, reps, stream, torch, batches=8):
+    """Duration (ms) of fn(i) over reps back-to-back launches, as (average, p10, p90): the launches
+    run in `batches` consecutive batches, each bracketed by HIP events on `stream` (so host-side
+    launch cost never shows as GPU time); the average is over all launches, p10 and p90 over the
+    batches' per-launch averages. The launches first run for SETTLE_ROW_MS so the clock has
+    settled after the host-side set-up."""
     settle(fn, SETTLE_ROW_MS, torch, chunk=10)
-    e0, e1 = TimingEvent(), TimingEvent()
-    e0.record(stream)
-    for i in range(reps):
-        fn(i)
-    e1.record(stream)
+    per = max(1, reps // batches)
+    ev = [TimingEvent() for _ in range(batches + 1)]
+    i = 0
+    ev[0].record(stream)
+    for b in range(batches):
+        for _ in range(per):
+            fn(i)
+            i += 1
+        ev[b + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    ms = np.array([ev[b].elapsed_time(ev[b + 1]) / per for b in range(batches)])
+    return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
 
 
-def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
+def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     """Per-kernel timings on the training-step (8192 tokens, 4096x4096 weight) and outlier
     (16384 x 5120 x 5120) shapes, each rotating over buffer sets larger than the cache."""
     out = []
 
-    def add(name, shape, avg, work, unit, peak=None):
+    def add(name, shape, t, work, unit, peak=None, **extra):
+        avg, p10, p90 = t
         rate = work / (avg * 1e-3)
         if unit == "GB/s":
             r, peak = rate / 1e9, peak or PEAK_HBM_GBS
         else:
             r, peak = rate / 1e12, peak or PEAK_FP8_TFLOPS
-        out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2), unit: round(r, 1),
-                    "frac": round(r / peak, 4)})
+        out.append({"kernel": name, "shape": shape, "avg_us": round(avg * 1e3, 2),
+                    "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2), unit: round(r, 1),
+                    "frac": round(r / peak, 4), **extra})
 
     d3 = inputs.make_workload(3)
     T, D = d3["X"].shape
@@ -505,33 +521,125 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=20, nsets=4):
     add("gemm_1x128_128x128 outlier", [M4, N4, K4], a, 2.0 * M4 * N4 * K4, "TFLOP/s")
     del A4, W4, qa4, sa4, qw4, sw4, c4
     torch.cuda.empty_cache()
+
+    # the forward GEMM at every shape of the ROCm page's performance table (its FP8 Triton GEMM on
+    # MI300X, printed there as context: another chip, not a target). Operands from N(0,1) / N(0,
+    # 0.02^2) bf16 through the quantizers, copied into enough rotating sets to exceed the 256 MB
+    # last-level cache (at most 32 sets); shapes with few output tiles take the split-K schedule.
+    g8 = np.random.Generator(np.random.PCG64(8))
+    for (Mp, Np, Kp, page_tflops) in PAGES_GEMM_TABLE:
+        ap = dev_bf16(inputs.normal_bf16(g8, (Mp, Kp)))
+        wp = dev_bf16(inputs.normal_bf16(g8, (Np, Kp), 0.02))
+        qa0, sa0 = bf.quantize_lhs(ap)
+        qw0, _, sw0 = bf.quantize_weight_128x128(wp, want_qT=False)
+        del ap, wp
+        per_set = Mp * Kp + Np * Kp + 4 * (sa0.numel() + sw0.numel()) + 2 * Mp * Np
+        nsp = int(min(32, max(2, _cdiv(300 << 20, per_set))))
+        ops = [(qa0.clone(), sa0.clone(), qw0.clone(), sw0.clone(),
+                torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)) for _ in range(nsp)]
+        del qa0, sa0, qw0, sw0
+        a = _time_kernel(lambda i: bf.gemm_1x128_128x128(*ops[i % nsp][:4], c=ops[i % nsp][4], stream=stream),
+                         reps, stream, torch)
+        add(f"gemm_1x128_128x128 {Mp}x{Np}x{Kp} (pages' table shape)", [Mp, Np, Kp], a,
+            2.0 * Mp * Np * Kp, "TFLOP/s", pages_mi300x_fp8_tflops=page_tflops, rotated_sets=nsp)
+        del ops
+        torch.cuda.empty_cache()
+
+    # the smallest workload (2 x 512 x 128: one K-block, two output tiles): host-launch-bound, so
+    # it is timed like the others but only shows the launch floor
+    d0 = inputs.make_workload(0)
+    A0, W0 = dev_bf16(d0["A"]), dev_bf16(d0["W"])
+    qa_0, sa_0, qw_0, _, sw_0 = bf.quantize_lhs_and_weight(A0, W0)
+    c0 = torch.empty((A0.shape[0], W0.shape[0]), dtype=torch.bfloat16, device=dev)
+    a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa_0, sa_0, qw_0, sw_0, c=c0, stream=stream), reps,
+                     stream, torch)
+    add("gemm_1x128_128x128 2x512x128 (launch floor)", [2, 512, 128], a, 2.0 * 2 * 512 * 128, "TFLOP/s")
+    del A0, W0, qa_0, sa_0, qw_0, sw_0, c0
     return out
 
 
-def cpu_baseline(A_h, W_h, gemm_rows):
+# The ROCm page's GEMM performance table: M, N, K and its FP8 Triton TFLOP/s on MI300X.
+PAGES_GEMM_TABLE = [
+    (128, 4096, 4096, 54.6), (512, 4096, 4096, 220.3), (2048, 4096, 4096, 294.1),
+    (4096, 4096, 4096, 299.3), (8192, 4096, 4096, 306.2), (2048, 8192, 4096, 453.4),
+    (4096, 8192, 4096, 470.5), (4096, 5120, 5120, 525.0),
+]
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(A_h, W_h, gemm_rows, gpu):
     """The CPU oracle (as it stands) on a bounded sample of the step: both quantizers on the full
-    tensors, the GEMM on `gemm_rows` evenly spaced rows; scaled to the whole step."""
+    tensors, the GEMM on `gemm_rows` evenly spaced rows; scaled to the whole step. The same leg
+    checks the GPU step's outputs (`gpu`: host copies of one set's codes, scales and C) against
+    what the oracle computed: the codes and scales bit for bit, the sampled rows of C within the
+    GEMM tolerance, and the SQNR of both against the fp64 product of the bf16 inputs. It also times
+    the two quantizers on one thread."""
     import oracle
     M, K = A_h.shape
     N = W_h.shape[0]
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     qa, sa = oracle.quantize_lhs(A_h)
     qw, _, sw = oracle.quantize_weight_128x128(W_h, want_qT=False)
     t1 = time.perf_counter()
     rows = np.linspace(0, M - 1, gemm_rows).astype(np.int64)
-    oracle.gemm_1x128_128x128(qa, sa, qw, sw, sw.shape[1], 1, rows=rows)
+    c_or = oracle.gemm_1x128_128x128(qa, sa, qw, sw, sw.shape[1], 1, rows=rows)
     t2 = time.perf_counter()
     step_s = (t1 - t0) + (t2 - t1) * (M / gemm_rows)
+
+    # one thread: the quantizers over the same tensors
+    oracle.set_num_threads(1)
+    try:
+        t3 = time.perf_counter()
+        oracle.quantize_lhs(A_h)
+        oracle.quantize_weight_128x128(W_h, want_qT=False)
+        q1_s = time.perf_counter() - t3
+    finally:
+        oracle.set_num_threads(threads)
+    q_bytes = lhs_bytes(M, K) + weight_bytes(N, K, False)
+
+    parity = None
+    if gpu is not None:
+        quant_exact = bool(np.array_equal(gpu["qa"], qa) and np.array_equal(gpu["sa"].view(np.uint32), sa.view(np.uint32))
+                           and np.array_equal(gpu["qw"], qw) and np.array_equal(gpu["sw"].view(np.uint32), sw.view(np.uint32)))
+        c_gpu = gpu["c"][rows]
+        rep = oracle.gemm_tolerance_report(c_gpu, c_or)
+        ref = oracle.matmul_bf16_f64(A_h, W_h, rows=rows)
+        parity = {
+            "quantizers_bit_exact": quant_exact,
+            "gemm_rows_checked": int(rows.size),
+            "gemm_within_tolerance": rep["ok"],
+            "gemm_rel_frobenius": rep["rel_frobenius"],
+            "sqnr_gpu_db": round(oracle.sqnr_db(ref, c_gpu), 3),
+            "sqnr_oracle_db": round(oracle.sqnr_db(ref, c_or), 3),
+            "verdict": "pass" if quant_exact and rep["ok"] else "FAIL",
+        }
     return {
         "value": round(2.0 * M * N * K / step_s / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"quantize_lhs + quantize_weight_128x128 on the full 4096x4096 tensors, GEMM on "
                   f"{gemm_rows} of {M} rows; GEMM time scaled by {M / gemm_rows:g}",
         "measured_s": round(t2 - t0, 2),
         "quant_s": round(t1 - t0, 3),
         "gemm_sample_s": round(t2 - t1, 3),
+        "quant_1thread_s": round(q1_s, 3),
+        "quant_1thread_GB/s": round(q_bytes / q1_s / 1e9, 3),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+        "cpu_model": _cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count(),
+        "parity": parity,
     }
 
 

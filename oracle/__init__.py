@@ -94,6 +94,8 @@ def lib():
             _int]
         L.oracle_gemm_1x128_128x1.argtypes = [
             _u8p, _i64, _f32p, _u8p, _i64, _f32p, _i64, _i64, _i64, _i64p, _i64, _f64p, _int]
+        L.oracle_set_num_threads.argtypes = [_int]
+        L.oracle_set_num_threads.restype = None
         for f in ("oracle_quantize_lhs", "oracle_quantize_rhs", "oracle_quantize_weight_128x128",
                   "oracle_gemm_1x128_128x128", "oracle_gemm_1x128_128x1", "oracle_num_threads"):
             getattr(L, f).restype = ctypes.c_int
@@ -112,6 +114,11 @@ def _check(rc, what):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (for single-thread timings)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def cdiv(a: int, b: int) -> int:

@@ -427,6 +427,15 @@ int oracle_gemm_1x128_128x1(const uint8_t* a, int64_t lda, const float* a_s,
     return gemm_rows(a, lda, a_s, b, ldb, b_s, 1, 0, 0, M, N, K, rows, nrows, out, fmt);
 }
 
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

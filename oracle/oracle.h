@@ -70,6 +70,8 @@ int oracle_gemm_1x128_128x1(const uint8_t* a, int64_t lda, const float* a_s,
 
 /* Threads the OpenMP loops above use. */
 int oracle_num_threads(void);
+/* Threads the parallel loops use from now on (n > 0). */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
