@@ -110,11 +110,12 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// BSFP8_GEMM_SPLIT (environment, read at each call): a slice count that replaces the automatic
-// choice of gemm_split_plan (1 = never split), so tests and benchmarks can run the split path on any
-// shape. Unset or empty: automatic.
-int forced_split() {
-    const char* v = std::getenv("BSFP8_GEMM_SPLIT");
+// BSFP8_GEMM_SPLIT and BSFP8_GEMM_TILE_M (environment, read at each call): a slice count (1 =
+// never split) and a tile height (256 or 128) that replace the automatic choices of
+// gemm_split_plan, so tests and benchmarks can run every schedule on any shape. Unset or empty:
+// automatic.
+int env_int(const char* name) {
+    const char* v = std::getenv(name);
     if (v == nullptr || *v == 0) return 0;
     const long s = std::strtol(v, nullptr, 10);
     return s < 1 ? 1 : (s > 65535 ? 65535 : static_cast<int>(s));
@@ -127,9 +128,10 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
              bsfp8::BScale bs, void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, bool fnuz,
              bool use_scratch, hipStream_t stream) {
     const int cus = bsfp8::device_cus();
-    const int forced = forced_split();
-    const bsfp8::SplitPlan plan = forced ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, forced, kMaxSplitWorkspace)
-                                         : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+    const int forced_s = env_int("BSFP8_GEMM_SPLIT"), forced_bm = env_int("BSFP8_GEMM_TILE_M");
+    const bsfp8::SplitPlan plan =
+        forced_s || forced_bm ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, cus, forced_s, forced_bm, kMaxSplitWorkspace)
+                              : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
     if (use_scratch) {
         if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
         float* ws = nullptr;

@@ -17,10 +17,11 @@
 //     out-of-range offset (geometry.hpp, whose arithmetic the CPU tests enumerate lane by lane);
 //     outputs of rows >= M or columns >= N are never stored.
 // The fast kernel (namespace fast) serves every float8_e4m3fn GEMM, a partial last K-block
-// included, and for short-and-wide shapes whose few output tiles leave most CUs idle splits K over
-// several workgroups per tile (fp32 partial tiles, summed by a second kernel; gemm_split_plan). The general kernel (namespace
-// gen) serves the float8_e4m3fnuz operands. Both zero the bytes of a partial last K-block that lie
-// at or past K.
+// included, in 256 x 256 tiles, or in 128 x 256 tiles when the larger ones would leave CUs idle;
+// for short-and-wide shapes whose tiles still leave most CUs idle it splits K over several
+// workgroups per tile (fp32 partial tiles, summed by a second kernel; gemm_split_plan). The general
+// kernel (namespace gen) serves the float8_e4m3fnuz operands. Both zero the bytes of a partial last
+// K-block that lie at or past K.
 //
 // float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240): gfx950's FP8
 // matrix instructions read e4m3fn, and no power-of-two rescaling maps every fnuz value onto an
@@ -430,28 +431,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 //     read touches (per lane group) fall in 16 distinct groups of 4 banks.
 namespace fast {
 
-constexpr int kBM = geom::kFastBM;
 constexpr int kBN = geom::kFastBN;
 constexpr int kWM = 64;
 constexpr int kWN = 128;
-constexpr int kWaves = geom::kFastWaves;  // 4 (M) x 2 (N): two per SIMD
-constexpr int kThreads = 64 * kWaves;     // 512
 constexpr int kMSub = kWM / 16;           // 4
 constexpr int kNSub = kWN / 16;           // 8
 constexpr int kStages = 2;
 
-// LDS image of one stage (16-byte units): A tile rows 0..255, B tile rows 0..255, then the A scales
-// of the tile rows and the B scales (per column: of the tile columns; 128x128: of the tile's two
-// column blocks, floats 0 and 1).
-constexpr int kStageA = 0;
-constexpr int kStageB = kStageA + kBM * 8;
-constexpr int kStageSA = kStageB + kBN * 8;
-constexpr int kStageSB = kStageSA + kBM / 4;
-constexpr int kStageSize = kStageSB + kBN / 4;  // 4224 x 16 B = 66 KB
-
-// vector-memory instructions each wave issues per stage: 4 A loads, 4 B loads (8 rows of 128 bytes
-// each), the A scales of 32 rows, the B scales (32 columns, or the two column-block scales)
-constexpr int kLoads = 10;
+// Tile geometry for tile height BM: 256 rows (8 waves, 4 (M) x 2 (N), two per SIMD) or 128 rows
+// (4 waves, 2 x 2, one per SIMD, for problems whose 256-row tiles would leave compute units idle).
+// Every wave computes a 64 x 128 block either way.
+template <int BM>
+struct Cfg {
+    static constexpr int kWaves = BM / 32;
+    static constexpr int kWavesM = BM / 64;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBRows = kBN / kWaves;  // B rows (and per-column B scales) a wave loads: 32 or 64
+    static constexpr int kBLoads = kBRows / 8;
+    // LDS image of one stage (16-byte units): A tile rows 0..BM-1, B tile rows 0..255, then the A
+    // scales of the tile rows and the B scales (per column: of the tile columns; 128x128: of the
+    // tile's two column blocks, floats 0 and 1). BM 256: 4224 units (66 KB); BM 128: 3168 (49.5 KB).
+    static constexpr int kStageA = 0;
+    static constexpr int kStageB = kStageA + BM * 8;
+    static constexpr int kStageSA = kStageB + kBN * 8;
+    static constexpr int kStageSB = kStageSA + BM / 4;
+    static constexpr int kStageSize = kStageSB + kBN / 4;
+    // vector-memory instructions each wave issues per stage: 4 A loads and kBLoads B loads (8 rows
+    // of 128 bytes each), the A scales of 32 rows, the B scales (kBRows columns, or the two
+    // column-block scales)
+    static constexpr int kLoads = 4 + kBLoads + 2;
+    // a block's loads past the first four are issued two per subtile column over this many columns
+    static constexpr int kPendCols = (kLoads - 3) / 2;
+};
+constexpr int kBM = geom::kFastBM;
+constexpr int kBMSmall = geom::kFastBMSmall;
 
 // One launch's work split: kGroupRows -- experts own row ranges of A and C and bring their own B
 // (forward, dgrad); kGroupK -- experts own token (K) ranges and write their own C (weight
@@ -470,10 +483,10 @@ struct Grouping {
 };
 
 struct Ops {
-    __amdgpu_buffer_rsrc_t a[4], b[4];  // operand load q reads through a[q] / b[q] (from tile row 8 q)
+    __amdgpu_buffer_rsrc_t a[4], b[4];  // operand load q reads through a[q % 4] / b[q % 4] (from tile row 8 (q % 4))
     __amdgpu_buffer_rsrc_t as, bs;
-    uint32_t a_lane[2];  // geom::fast_operand_lane for loads of parity 0 / 1
-    uint32_t b_lane[2];
+    uint32_t a_lane[2];  // geom::fast_operand_lane for loads with q % 2 = 0 / 1
+    uint32_t b_lane[4];  // ... for B loads with q % 2 + 2 (q / 4) = 0 .. 3
     uint32_t as_base;    // geom::fast_ascale_base
     uint32_t bs_base;    // geom::fast_bscale_col_base / fast_bscale_blk_base
     int64_t as_step;     // bytes between K-blocks of the A scales (4 M)
@@ -528,28 +541,32 @@ __device__ __forceinline__ void dma4(uint32_t lds, __amdgpu_buffer_rsrc_t r, uin
         : "memory");
 }
 
-// Load number q of a stage, q = 0 .. kLoads - 1: 0..3 A rows 32 wave + 8 q .., 4..7 B rows
-// 32 wave + 8 (q - 4) .., 8 the A scales of rows 32 wave .. + 32, 9 the B scales (per column: of
-// columns 32 wave .. + 32; 128x128: the two column-block scales, by wave 0). `on` (wave-uniform)
-// false: the load is issued with no lane enabled, so nothing is read or written. Every offset is
-// the lane's offset in the load's resource (a position in the tensor, or kOob for a scale outside
-// it) plus this K-block's advance.
-template <bool PER_COL>
+// Load number q of a stage, q = 0 .. kLoads - 1: 0..3 A rows 32 wave + 8 q .., then kBLoads B loads
+// of rows kBRows wave + 8 (q - 4) .., then the A scales of rows 32 wave .. + 32, then the B scales
+// (per column: of columns kBRows wave .. + kBRows; 128x128: the two column-block scales, by wave
+// 0). `on` (wave-uniform) false: the load is issued with no lane enabled, so nothing is read or
+// written. Every offset is the lane's offset in the load's resource (a position in the tensor, or
+// kOob for a scale outside it) plus this K-block's advance.
+template <bool PER_COL, int BM>
 __device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb, int wave,
                                            bool on = true) {
+    using C = Cfg<BM>;
     const uint32_t k = geom::fast_operand_advance(kb);
     const uint64_t all = on ? ~0ull : 0ull;
     const uint64_t half = on ? 0xFFFFFFFFull : 0ull;
     if (q < 4) {
-        dma16(stage_base + (kStageA + (32 * wave + 8 * q) * 8) * 16, op.a[q], op.a_lane[q & 1] + k, all);
-    } else if (q < 8) {
-        dma16(stage_base + (kStageB + (32 * wave + 8 * (q - 4)) * 8) * 16, op.b[q - 4], op.b_lane[q & 1] + k, all);
-    } else if (q == 8) {
-        dma4(stage_base + kStageSA * 16 + 128 * wave, op.as, op.as_base + static_cast<uint32_t>(kb * op.as_step), half);
+        dma16(stage_base + (C::kStageA + (32 * wave + 8 * q) * 8) * 16, op.a[q], op.a_lane[q & 1] + k, all);
+    } else if (q < 4 + C::kBLoads) {
+        const int qb = q - 4;
+        dma16(stage_base + (C::kStageB + (C::kBRows * wave + 8 * qb) * 8) * 16, op.b[qb & 3],
+              op.b_lane[(qb & 1) + 2 * (qb >> 2)] + k, all);
+    } else if (q == 4 + C::kBLoads) {
+        dma4(stage_base + C::kStageSA * 16 + 128 * wave, op.as, op.as_base + static_cast<uint32_t>(kb * op.as_step), half);
     } else if (PER_COL) {
-        dma4(stage_base + kStageSB * 16 + 128 * wave, op.bs, op.bs_base + static_cast<uint32_t>(kb * op.bs_step), half);
+        dma4(stage_base + C::kStageSB * 16 + 4 * C::kBRows * wave, op.bs,
+             op.bs_base + static_cast<uint32_t>(kb * op.bs_step), C::kBRows == 64 ? all : half);
     } else {
-        dma4(stage_base + kStageSB * 16, op.bs, op.bs_base + static_cast<uint32_t>(kb * op.bs_step),
+        dma4(stage_base + C::kStageSB * 16, op.bs, op.bs_base + static_cast<uint32_t>(kb * op.bs_step),
              on && wave == 0 ? 0x3ull : 0ull);
     }
 }
@@ -567,24 +584,27 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool PER_COL, int GROUP>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+template <bool PER_COL, int GROUP, int BM>
+__global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb,
     int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt,
     int nt, int c_vec, Grouping grp) {
+    using Cf = Cfg<BM>;
+    constexpr int kStageA = Cf::kStageA, kStageB = Cf::kStageB, kStageSA = Cf::kStageSA, kStageSB = Cf::kStageSB;
+    constexpr int kStageSize = Cf::kStageSize, kLoads = Cf::kLoads;
     __shared__ u32x4 smem[kStages * kStageSize];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 3;   // rows 64 wm .. of the tile
-    const int wn = wave >> 2;  // columns 128 wn .. of the tile
+    const int wm = wave % Cf::kWavesM;  // rows 64 wm .. of the tile
+    const int wn = wave / Cf::kWavesM;  // columns 128 wn .. of the tile
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     int tm, tn;
     geom::tile_of(blockIdx.x, mt, nt, tm, tn);
-    int64_t m0 = static_cast<int64_t>(tm) * kBM;  // this tile's rows are [m0, min(m0 + kBM, m_end))
+    int64_t m0 = static_cast<int64_t>(tm) * BM;  // this tile's rows are [m0, min(m0 + BM, m_end))
     int64_t m_end = M;
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
     // K-blocks (the last one may be partial: only for the ungrouped GEMMs, whose callers allow it)
@@ -600,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             const int64_t a = min(max(grp.offsets[j], prev), M);
             const int64_t b = min(max(grp.offsets[j + 1], a), M);
             prev = b;
-            const int64_t tiles = (b - a + kBM - 1) / kBM;
+            const int64_t tiles = (b - a + BM - 1) / BM;
             if (tm < first + tiles) {
                 e = j;
                 lo = a;
@@ -610,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             first += tiles;
         }
         if (e < 0) return;  // a spare workgroup of the grid's upper bound: the whole group leaves
-        m0 = lo + (tm - first) * kBM;
+        m0 = lo + (tm - first) * BM;
         m_end = hi;
         B += e * grp.b_stride;
         b_s += e * grp.bs_stride;
@@ -642,24 +662,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
     Ops op;
     {
-        const int64_t arows = (m_end - m0) < kBM ? (m_end - m0) : kBM;
+        const int64_t arows = (m_end - m0) < BM ? (m_end - m0) : BM;
         const int64_t brows = (N - n0) < kBN ? (N - n0) : kBN;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q)
             op.a[q] = make_rsrc(A + (m0 + geom::fast_operand_first_row(q)) * lda, geom::fast_operand_range(q, arows, lda));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
             op.b[q] = make_rsrc(B + (n0 + geom::fast_operand_first_row(q)) * ldb, geom::fast_operand_range(q, brows, ldb));
-        }
         op.as = make_rsrc(a_s, M * Kb * 4);
         op.bs = make_rsrc(b_s, PER_COL ? N * Kb * 4 : 4 * geom::bscale_blk_extent(N, Kb, bs_nb, bs_kb));
 #pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            op.a_lane[par] = geom::fast_operand_lane(wave, par, lane, lda);
-            op.b_lane[par] = geom::fast_operand_lane(wave, par, lane, ldb);
-        }
+        for (int par = 0; par < 2; ++par) op.a_lane[par] = geom::fast_operand_lane(32, wave, par, lane, lda);
+#pragma unroll
+        for (int v = 0; v < (Cf::kBLoads > 4 ? 4 : 2); ++v)
+            op.b_lane[v] = geom::fast_operand_lane(Cf::kBRows, wave, (v & 1) + 4 * (v >> 1), lane, ldb);
         op.as_base = geom::fast_ascale_base(m0, m_end, wave, lane);
         op.as_step = 4 * M;
         if (PER_COL) {
-            op.bs_base = geom::fast_bscale_col_base(n0, N, wave, lane);
+            op.bs_base = geom::fast_bscale_col_base(Cf::kBRows, n0, N, wave, lane);
             op.bs_step = 4 * N;
         } else {
             op.bs_base = geom::fast_bscale_blk_base(tn, N, bs_nb, wave, lane);
@@ -687,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
         // prologue: block 0 into stage 0
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(0), 0, wave);
+        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM>(q, op, stage_base(0), 0, wave);
         wait_own_loads<0>();
 
         // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its loads read whole
@@ -705,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         lds_barrier();
         if (Kb > 1) {
 #pragma unroll
-            for (int q = 0; q < kLoads; ++q) issue_load<PER_COL>(q, op, stage_base(1), 1, wave);
+            for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM>(q, op, stage_base(1), 1, wave);
         }
 
         auto read_a = [&](const u32x4* st, int i, bool tail) {
@@ -761,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         // column 6 every fragment and scale of the block has been read, so one barrier there
         // (after each wave's wait for its own loads of block kb+1) both publishes block kb+1 and
         // frees this block's stage. Block kb+2 is then loaded into it -- four of the wave's loads
-        // right away, the rest two per column over the next block's columns 0..2, so the memory
+        // right away, the rest two per column over the next block's first columns, so the memory
         // system never sees a whole block requested at once -- and block kb+1's first fragments
         // are read while columns 6 and 7 keep the matrix cores busy; its A fragments replace this
         // block's right after their last MFMA. TAIL: the partial last K-block, whose fragments are
@@ -790,17 +811,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                     const bool more = kb + 2 < Kb;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        issue_load<PER_COL>(q, op, stage_base(cur), more ? kb + 2 : kb, wave, more);
+                        issue_load<PER_COL, BM>(q, op, stage_base(cur), more ? kb + 2 : kb, wave, more);
                     // slots 0 and 1 were last used by subtiles 4 and 5
                     bf[0] = read_b(stn, 0, false);
                     bf[1] = read_b(stn, 1, false);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if (!TAIL && j < 3) {
-                    // the rest of block kb+1's loads, issued by the previous block after its barrier
+                if (!TAIL && j < Cf::kPendCols) {
+                    // the rest of block kb+1's loads (its first four were issued by the previous
+                    // block after its barrier; block 0 issues none, the prologue loaded block 1)
                     const bool pend = kb >= 1 && kb + 1 < Kb;
-                    if (4 + 2 * j < kLoads) issue_load<PER_COL>(4 + 2 * j, op, stage_base(cur ^ 1), pend ? kb + 1 : kb, wave, pend);
-                    if (5 + 2 * j < kLoads) issue_load<PER_COL>(5 + 2 * j, op, stage_base(cur ^ 1), pend ? kb + 1 : kb, wave, pend);
+                    const int64_t pkb = pend ? kb + 1 : kb;
+                    if (4 + 2 * j < kLoads) issue_load<PER_COL, BM>(4 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
+                    if (5 + 2 * j < kLoads) issue_load<PER_COL, BM>(5 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
                 }
                 if (j + 2 < kNSub) bf[(j + 2) % 4] = read_b(st, j + 2, TAIL);
                 v4f bsj;
@@ -967,18 +990,22 @@ hipError_t gemm_scratch(float** out) {
     return hipSuccess;
 }
 
-// When to split K, from measurements on MI355X (256 CUs; back-to-back launches, settled clock): a
-// slice costs its fp32 partial tile (written, then read by the sum) and the sum is a second launch,
-// so splitting pays only when few tiles leave most CUs idle, M is small and K is long -- 128 x 4096
-// x 4096: 46.7 us unsplit, 22.2 us with 12 slices; 512 x 4096 x 4096: 47.4 / 31.4 us with 4;
-// 2 x 5120 x 1280: 18.0 / 10.6 us with 6 -- while 130 x 5120 x 1280, 1024^3 and 2048 x 4096 x 4096
-// ran fastest unsplit. The slices always fit in one round of workgroups.
+// Tile height and K split, from measurements on MI355X (256 CUs; back-to-back launches, settled
+// clock). 256-row tiles (8 waves, two per SIMD) run the K-loop fastest, so they are kept whenever
+// they give every CU a tile; a problem with fewer 256-row tiles than half the CUs takes 128-row
+// tiles (4 waves, one per SIMD; twice the tiles), as does any M <= 128, whose 256-row tile would be
+// at least half empty. A K split then costs its fp32 partial tiles (written, then read by the sum)
+// and a second launch, so it pays only when the tiles still leave most CUs idle and K is long. The
+// slices always fit in one round of workgroups.
 SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
-    SplitPlan plan{1, 0, 0};
-    if (fnuz || M <= 0 || N <= 0 || K <= 0 || M > 512) return plan;
-    const int64_t tiles = ((M + fast::kBM - 1) / fast::kBM) * ((N + fast::kBN - 1) / fast::kBN);
+    SplitPlan plan{1, 0, 0, fast::kBM};
+    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
+    const int64_t tiles256 = ((M + fast::kBM - 1) / fast::kBM) * nt;
+    if (M <= fast::kBMSmall || 2 * tiles256 <= cus) plan.bm = fast::kBMSmall;
+    const int64_t tiles = ((M + plan.bm - 1) / plan.bm) * nt;
     const int64_t Kb = (K + kGroup - 1) / kGroup;
-    if (4 * tiles > cus) return plan;
+    if (M > 512 || 4 * tiles > cus) return plan;
     int64_t S = cus / tiles;  // one round of workgroups
     if (M <= 64) {
         if (S > Kb) S = Kb;
@@ -998,11 +1025,17 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, i
     return plan;
 }
 
-// A slice count chosen by the caller: clamped to the K-blocks and to the workspace bound; fewer than
-// two slices means no split.
-SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int S, int64_t max_bytes) {
-    SplitPlan plan{1, 0, 0};
+// A slice count and tile height chosen by the caller: S clamped to the K-blocks and to the
+// workspace bound (fewer than two slices: no split); bm 0 keeps the automatic tile height.
+SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm,
+                                 int64_t max_bytes) {
+    SplitPlan plan = gemm_split_plan(M, N, K, fnuz, cus, max_bytes);
     if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    if (bm == fast::kBM || bm == fast::kBMSmall) plan.bm = bm;
+    if (S <= 0) return plan;  // tile height only
+    plan.S = 1;
+    plan.ldp = 0;
+    plan.bytes = 0;
     const int64_t Kb = (K + kGroup - 1) / kGroup;
     const int64_t ldp = (N + 7) / 8 * 8;
     const int64_t slice_bytes = M * ldp * 4;
@@ -1016,48 +1049,63 @@ SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int
     return plan;
 }
 
+namespace {
+
+// The fast kernel with tile height BM, unsplit or split over plan.S slices.
+template <int BM>
+hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
+                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                       const SplitPlan& plan, float* workspace, int cus, hipStream_t stream) {
+    constexpr int kThreads = fast::Cfg<BM>::kThreads;
+    const int64_t mt = (M + BM - 1) / BM;
+    const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
+    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const int64_t nb = bs.per_column ? 0 : bs.stride_nb;
+    const int64_t kbs = bs.per_column ? 0 : bs.stride_kb;
+    if (plan.S > 1) {
+        // K split over plan.S workgroups per tile: fp32 partial tiles, then their sum in bf16
+        if (workspace == nullptr) return hipErrorInvalidValue;
+        const fast::Grouping g{nullptr, 0, 0, 0, M * plan.ldp};
+        const dim3 grid(static_cast<unsigned>(mt * nt), static_cast<unsigned>(plan.S));
+        uint16_t* P = reinterpret_cast<uint16_t*>(workspace);
+        if (bs.per_column)
+            fast::gemm_kernel<true, fast::kSplitK, BM><<<grid, kThreads, 0, stream>>>(
+                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
+        else
+            fast::gemm_kernel<false, fast::kSplitK, BM><<<grid, kThreads, 0, stream>>>(
+                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
+        const int64_t items = M * ((N + 7) / 8);
+        int64_t wgs = (items + 255) / 256;
+        if (wgs > static_cast<int64_t>(cus) * 8) wgs = static_cast<int64_t>(cus) * 8;
+        fast::split_reduce_kernel<<<dim3(static_cast<unsigned>(wgs)), 256, 0, stream>>>(
+            workspace, plan.ldp, M * plan.ldp, plan.S, c, ldc, M, N, c_vec16);
+        return hipGetLastError();
+    }
+    const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
+    const dim3 grid(static_cast<unsigned>(mt * nt));
+    const fast::Grouping none{nullptr, 0, 0, 0, 0};
+    if (bs.per_column)
+        fast::gemm_kernel<true, fast::kGroupNone, BM><<<grid, kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
+    else
+        fast::gemm_kernel<false, fast::kGroupNone, BM><<<grid, kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                        int64_t ldb, BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N,
                        int64_t K, bool fnuz, const SplitPlan& plan, float* workspace, int cus,
                        hipStream_t stream) {
     if (!fnuz) {
-        const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
-        const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
-        if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-        const int64_t nb = bs.per_column ? 0 : bs.stride_nb;
-        const int64_t kbs = bs.per_column ? 0 : bs.stride_kb;
-        if (plan.S > 1) {
-            // K split over plan.S workgroups per tile: fp32 partial tiles, then their sum in bf16
-            if (workspace == nullptr) return hipErrorInvalidValue;
-            const fast::Grouping g{nullptr, 0, 0, 0, M * plan.ldp};
-            const dim3 grid(static_cast<unsigned>(mt * nt), static_cast<unsigned>(plan.S));
-            uint16_t* P = reinterpret_cast<uint16_t*>(workspace);
-            if (bs.per_column)
-                fast::gemm_kernel<true, fast::kSplitK><<<grid, fast::kThreads, 0, stream>>>(
-                    a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
-            else
-                fast::gemm_kernel<false, fast::kSplitK><<<grid, fast::kThreads, 0, stream>>>(
-                    a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
-            const int64_t items = M * ((N + 7) / 8);
-            int64_t wgs = (items + 255) / 256;
-            if (wgs > static_cast<int64_t>(cus) * 8) wgs = static_cast<int64_t>(cus) * 8;
-            fast::split_reduce_kernel<<<dim3(static_cast<unsigned>(wgs)), 256, 0, stream>>>(
-                workspace, plan.ldp, M * plan.ldp, plan.S, c, ldc, M, N, c_vec16);
-            return hipGetLastError();
-        }
-        const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
-        const dim3 grid(static_cast<unsigned>(mt * nt));
-        const fast::Grouping none{nullptr, 0, 0, 0, 0};
-        if (bs.per_column)
-            fast::gemm_kernel<true, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
-        else
-            fast::gemm_kernel<false, fast::kGroupNone><<<grid, fast::kThreads, 0, stream>>>(
-                a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
-        return hipGetLastError();
+        if (plan.bm == fast::kBMSmall)
+            return launch_fast<fast::kBMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
+        return launch_fast<fast::kBM>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
     }
     // float8_e4m3fnuz: general kernel
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
@@ -1087,7 +1135,7 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     const fast::Grouping g{offsets, E, b_stride, bs_stride, 0};
-    fast::gemm_kernel<false, fast::kGroupRows><<<dim3(static_cast<unsigned>(mt * nt)), fast::kThreads, 0, stream>>>(
+    fast::gemm_kernel<false, fast::kGroupRows, fast::kBM><<<dim3(static_cast<unsigned>(mt * nt)), fast::Cfg<fast::kBM>::kThreads, 0, stream>>>(
         a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt, (int)nt,
         c_vec, g);
     return hipGetLastError();
@@ -1103,7 +1151,7 @@ hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL || E > 65535) return hipErrorInvalidValue;
     const fast::Grouping g{offsets, E, 0, 0, c_stride};
-    fast::gemm_kernel<true, fast::kGroupK><<<dim3(static_cast<unsigned>(mt * nt), static_cast<unsigned>(E)), fast::kThreads, 0, stream>>>(
+    fast::gemm_kernel<true, fast::kGroupK, fast::kBM><<<dim3(static_cast<unsigned>(mt * nt), static_cast<unsigned>(E)), fast::Cfg<fast::kBM>::kThreads, 0, stream>>>(
         a, lda, a_s, b, ldb, b_s, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec, g);
     return hipGetLastError();
 }

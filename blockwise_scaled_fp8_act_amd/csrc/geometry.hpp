@@ -54,31 +54,42 @@ BSFP8_HD void tile_of(int bid, int mt, int nt, int& tm, int& tn) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fast GEMM kernel: 256 x 256 tile, 8 waves (wm = wave % 4 owns rows 64 wm.., wn = wave / 4
-// columns 128 wn..). Each K-block's operand tiles are loaded by the 8 waves together, 16 bytes
-// per lane, straight into LDS.
+// Fast GEMM kernel: BM x 256 tiles, BM = 256 (8 waves) or 128 (4 waves); wave w owns rows
+// 64 wm.. (wm = w % (BM / 64)) and columns 128 wn.. (wn = w / (BM / 64)) of the tile. Each
+// K-block's operand tiles are loaded by the waves together, 16 bytes per lane, straight into LDS:
+// every wave loads 32 rows of the A tile and 256 / waves rows (32 or 64) of the B tile.
 constexpr int kFastBM = 256;
 constexpr int kFastBN = 256;
 constexpr int kFastWaves = 8;
+constexpr int kFastBMSmall = 128;
+constexpr int kFastWavesSmall = 4;
+BSFP8_HD int fast_waves(int bm) { return bm == kFastBMSmall ? kFastWavesSmall : kFastWaves; }
+BSFP8_HD int fast_b_rows_per_wave(int bm) { return kFastBN / fast_waves(bm); }
 
-// Operand load q (0..3) of a wave: tile row 32 wave + 8 q + lane / 8, 16-byte chunk
+// Operand load q (0 .. rows_per_wave / 8 - 1) of a wave whose share of the tile is rows_per_wave
+// rows (32 for A; 32 or 64 for B): tile row rows_per_wave * wave + 8 q + lane / 8, 16-byte chunk
 // (lane % 8) ^ swz(row) of the row's K-block, where swz(row) = (row / 2) % 8 is the LDS swizzle:
-// lane l lands at LDS unit (32 wave + 8 q) * 8 + l = row * 8 + l % 8, which thus holds logical chunk
-// (l % 8) ^ swz(row). Load q reads through its own buffer resource, which starts at tile row 8 q and
-// spans the tile's in-range rows from there (fast_operand_range), so the per-lane offset is the
-// same for q and q + 2 and a row past the matrix is past the end of its resource.
-BSFP8_HD int fast_operand_row(int wave, int q, int lane) { return 32 * wave + 8 * q + (lane >> 3); }
+// lane l lands at LDS unit (rows_per_wave * wave + 8 q) * 8 + l = row * 8 + l % 8, which thus holds
+// logical chunk (l % 8) ^ swz(row) (rows_per_wave * wave is a multiple of 32, so swz depends on q
+// and l only). Load q reads through buffer resource q % 4, which starts at tile row 8 (q % 4) and
+// spans the tile's in-range rows from there (fast_operand_range); the lane offset from that start,
+// (rows_per_wave * wave + 32 (q / 4) + lane / 8) rows plus the chunk, depends on q only through
+// q % 2 and q / 4, and a row past the matrix is past the end of the resource.
+BSFP8_HD int fast_operand_row(int rows_per_wave, int wave, int q, int lane) {
+    return rows_per_wave * wave + 8 * q + (lane >> 3);
+}
 BSFP8_HD int lds_swizzle(int row) { return (row >> 1) & 7; }
 BSFP8_HD int fast_operand_chunk(int q, int lane) { return (lane & 7) ^ ((4 * (q & 1) + (lane >> 4)) & 7); }
-// Per-lane offset of load q (depends on q only through q % 2) from the start of its resource,
-// before the K-block advance kb * 128.
-BSFP8_HD uint32_t fast_operand_lane(int wave, int q, int lane, int64_t ld) {
-    return static_cast<uint32_t>((32 * wave + (lane >> 3)) * ld + 16 * fast_operand_chunk(q, lane));
+// Per-lane offset of load q from the start of its resource, before the K-block advance kb * 128.
+BSFP8_HD uint32_t fast_operand_lane(int rows_per_wave, int wave, int q, int lane, int64_t ld) {
+    return static_cast<uint32_t>((rows_per_wave * wave + 32 * (q >> 2) + (lane >> 3)) * ld +
+                                 16 * fast_operand_chunk(q, lane));
 }
-// Resource of load q: from tile row 8 q, (rows_in_range - 8 q) rows of ld bytes (none if negative).
-BSFP8_HD int64_t fast_operand_first_row(int q) { return 8 * q; }
+// Resource of load q: from tile row 8 (q % 4), (rows_in_range - 8 (q % 4)) rows of ld bytes (none
+// if negative).
+BSFP8_HD int64_t fast_operand_first_row(int q) { return 8 * (q & 3); }
 BSFP8_HD int64_t fast_operand_range(int q, int64_t rows_in_range, int64_t ld) {
-    return rows_in_range > 8 * q ? (rows_in_range - 8 * q) * ld : 0;
+    return rows_in_range > 8 * (q & 3) ? (rows_in_range - 8 * (q & 3)) * ld : 0;
 }
 BSFP8_HD uint32_t fast_operand_advance(int64_t kb) { return static_cast<uint32_t>(kb * kBlockK); }
 
@@ -90,11 +101,12 @@ BSFP8_HD uint32_t fast_ascale_base(int64_t m0, int64_t m_end, int wave, int lane
 }
 BSFP8_HD uint32_t fast_ascale_advance(int64_t kb, int64_t M) { return static_cast<uint32_t>(4 * kb * M); }
 
-// Per-column B scales of a K-block: lanes 0..31 of each wave, tile column 32 wave + lane;
+// Per-column B scales of a K-block: lanes 0 .. cols_per_wave - 1 of each wave (cols_per_wave =
+// 256 / waves: 32 or 64), tile column cols_per_wave * wave + lane (LDS float of the same index);
 // b_s [Kb, N] row-major: element (kb, n) at kb * N + n.
-BSFP8_HD uint32_t fast_bscale_col_base(int64_t n0, int64_t N, int wave, int lane) {
-    const int64_t n = n0 + 32 * wave + lane;
-    return (lane < 32 && n < N) ? static_cast<uint32_t>(4 * n) : kOob;
+BSFP8_HD uint32_t fast_bscale_col_base(int cols_per_wave, int64_t n0, int64_t N, int wave, int lane) {
+    const int64_t n = n0 + cols_per_wave * wave + lane;
+    return (lane < cols_per_wave && n < N) ? static_cast<uint32_t>(4 * n) : kOob;
 }
 BSFP8_HD uint32_t fast_bscale_col_advance(int64_t kb, int64_t N) { return static_cast<uint32_t>(4 * kb * N); }
 

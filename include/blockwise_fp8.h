@@ -146,12 +146,14 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  *   256 * lda, 256 * ldb, 4 * M * ceil(K/128) and 4 * (the b_s elements the strides span) at most
  *   2^31; ceil(M/128) at most 65535.
  * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
- * Schedule: one workgroup per 256 x 256 output tile. When few tiles leave most compute units idle
- * (M <= 512 and at most a quarter as many tiles as compute units, on a long enough K) the K-blocks
- * are split over S workgroups per tile, which write fp32 partial tiles to the pooled workspace, and
- * a second kernel sums the S partials in a fixed order into C (same result on every call). The
- * environment variable BSFP8_GEMM_SPLIT, read at each call, forces S (1 = never split; S is
- * clamped to ceil(K/128) and to the workspace bound).
+ * Schedule: one workgroup per 256 x 256 output tile, or per 128 x 256 tile when M <= 128 or the
+ * 256-row tiles number at most half the compute units. When the tiles still leave most compute
+ * units idle (M <= 512 and at most a quarter as many tiles as compute units, on a long enough K)
+ * the K-blocks are split over S workgroups per tile, which write fp32 partial tiles to the pooled
+ * workspace, and a second kernel sums the S partials in a fixed order into C (same result on every
+ * call). The environment variables BSFP8_GEMM_SPLIT and BSFP8_GEMM_TILE_M, read at each call,
+ * force S (1 = never split; S is clamped to ceil(K/128) and to the workspace bound) and the tile
+ * height (256 or 128).
  */
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
                        const void* b, int64_t ldb, const float* b_s,

@@ -13,6 +13,7 @@
 //   * the partial-K-block masks keep exactly the fragment bytes below K;
 //   * quantize_lhs stores each scale of the column-major [M, Kb] tensor exactly once and never a row
 //     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm").
+// Both tile heights of the fast kernel (256 rows, 8 waves; 128 rows, 4 waves) are enumerated.
 // Usage: geometry_check M N K [M N K ...]; prints one line per shape, exits 1 on the first failure.
 #include <cstdint>
 #include <cstdio>
@@ -60,26 +61,28 @@ static bool check_tiles(int mt, int nt) {
 // operand with `total_rows` rows of K bytes at row stride ld. A chunk that holds bytes below K must be
 // read at its address; a chunk wholly at or past K (masked to zero in the fragments) may read the
 // following bytes of the operand or nothing, but never outside it.
-static bool check_fast_operand(int64_t r0, int64_t rows, int64_t total_rows, int64_t ld, int64_t K, int64_t kb) {
-    std::vector<uint8_t> got(256 * 8, 0);
-    for (int q = 0; q < 4; ++q) {
+// rpw: rows each of the `waves` waves loads (8 per load instruction).
+static bool check_fast_operand(int64_t r0, int64_t rows, int64_t total_rows, int64_t ld, int64_t K, int64_t kb,
+                               int rpw, int waves) {
+    std::vector<uint8_t> got(static_cast<size_t>(rpw) * waves * 8, 0);
+    for (int q = 0; q < rpw / 8; ++q) {
         const int64_t range = fast_operand_range(q, rows, ld);
         const int64_t first = r0 + fast_operand_first_row(q);
-        for (int wave = 0; wave < kFastWaves; ++wave)
+        for (int wave = 0; wave < waves; ++wave)
             for (int lane = 0; lane < 64; ++lane) {
-                const uint64_t off = static_cast<uint64_t>(fast_operand_lane(wave, q, lane, ld)) + fast_operand_advance(kb);
+                const uint64_t off = static_cast<uint64_t>(fast_operand_lane(rpw, wave, q, lane, ld)) + fast_operand_advance(kb);
                 bool ok;
                 const bool in = access(off, range, 16, ok);
                 CHECK(ok, "operand offset %llu (range %lld)", (unsigned long long)off, (long long)range);
-                const int r = fast_operand_row(wave, q, lane);
+                const int r = fast_operand_row(rpw, wave, q, lane);
                 const int c = fast_operand_chunk(q, lane);
-                // LDS slot of the lane: unit (32 wave + 8 q) * 8 + lane = row r, position lane % 8,
+                // LDS slot of the lane: unit (rpw wave + 8 q) * 8 + lane = row r, position lane % 8,
                 // which the fragment reads take as logical chunk (lane % 8) ^ swizzle(r)
-                CHECK((32 * wave + 8 * q) * 8 + lane == r * 8 + (lane & 7), "LDS unit");
+                CHECK((rpw * wave + 8 * q) * 8 + lane == r * 8 + (lane & 7), "LDS unit");
                 CHECK(((lane & 7) ^ lds_swizzle(r)) == c, "LDS chunk position");
                 const bool needed = kb * kBlockK + 16 * c < K;
                 if (r < rows) {
-                    CHECK(static_cast<int64_t>(off) == (r - 8 * q) * ld + kb * kBlockK + 16 * c, "operand address");
+                    CHECK(static_cast<int64_t>(off) == (r - fast_operand_first_row(q)) * ld + kb * kBlockK + 16 * c, "operand address");
                     if (needed) {
                         CHECK(in, "row %d chunk %d below K not read (q %d wave %d lane %d)", r, c, q, wave, lane);
                         CHECK(++got[r * 8 + c] == 1, "row %d chunk %d loaded twice", r, c);
@@ -96,8 +99,10 @@ static bool check_fast_operand(int64_t r0, int64_t rows, int64_t total_rows, int
     return true;
 }
 
-static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
-    const int mt = static_cast<int>(cdiv(M, kFastBM)), nt = static_cast<int>(cdiv(N, kFastBN));
+// bm: the tile height (256: 8 waves; 128: 4 waves).
+static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bm) {
+    const int waves = fast_waves(bm), wms = bm / 64, cpw = fast_b_rows_per_wave(bm);
+    const int mt = static_cast<int>(cdiv(M, bm)), nt = static_cast<int>(cdiv(N, kFastBN));
     const int64_t Kb = cdiv(K, kBlockK);
     if (!check_tiles(mt, nt)) return false;
     // 128x128 B scales read with the forward strides (Kb, 1) and the dgrad strides (1, Nb)
@@ -106,37 +111,40 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
     std::vector<uint8_t> stored(static_cast<size_t>(M) * N, 0);
     for (int tm = 0; tm < mt; ++tm)
         for (int tn = 0; tn < nt; ++tn) {
-            const int64_t m0 = static_cast<int64_t>(tm) * kFastBM, n0 = static_cast<int64_t>(tn) * kFastBN;
-            const int64_t arows = M - m0 < kFastBM ? M - m0 : kFastBM;
+            const int64_t m0 = static_cast<int64_t>(tm) * bm, n0 = static_cast<int64_t>(tn) * kFastBN;
+            const int64_t arows = M - m0 < bm ? M - m0 : bm;
             const int64_t brows = N - n0 < kFastBN ? N - n0 : kFastBN;
             for (int64_t kb = 0; kb < Kb; ++kb) {
-                if (!check_fast_operand(m0, arows, M, lda, K, kb)) return false;
-                if (!check_fast_operand(n0, brows, N, ldb, K, kb)) return false;
-                // A scales: lanes 0..31 of each wave (the others are switched off)
+                if (!check_fast_operand(m0, arows, M, lda, K, kb, 32, waves)) return false;
+                if (!check_fast_operand(n0, brows, N, ldb, K, kb, cpw, waves)) return false;
+                // A scales: lanes 0..31 of each wave (the others are switched off); per-column B
+                // scales: lanes 0 .. cpw - 1
                 std::vector<uint8_t> sa(256, 0), sbc(256, 0);
-                for (int wave = 0; wave < kFastWaves; ++wave)
-                    for (int lane = 0; lane < 32; ++lane) {
-                        const uint64_t off = static_cast<uint64_t>(fast_ascale_base(m0, M, wave, lane)) + fast_ascale_advance(kb, M);
+                for (int wave = 0; wave < waves; ++wave)
+                    for (int lane = 0; lane < 64; ++lane) {
                         bool ok;
-                        const bool in = access(off, 4 * M * Kb, 4, ok);
-                        CHECK(ok, "a_s offset");
-                        const int64_t m = m0 + 32 * wave + lane;
-                        if (m < M) {
-                            CHECK(in && static_cast<int64_t>(off) == 4 * (kb * M + m), "a_s[%lld, %lld] address", (long long)m, (long long)kb);
-                            ++sa[32 * wave + lane];
-                        } else {
-                            CHECK(!in, "a_s row %lld >= M read", (long long)m);
+                        if (lane < 32) {
+                            const uint64_t off = static_cast<uint64_t>(fast_ascale_base(m0, M, wave, lane)) + fast_ascale_advance(kb, M);
+                            const bool in = access(off, 4 * M * Kb, 4, ok);
+                            CHECK(ok, "a_s offset");
+                            const int64_t m = m0 + 32 * wave + lane;
+                            if (m < M) {
+                                CHECK(in && static_cast<int64_t>(off) == 4 * (kb * M + m), "a_s[%lld, %lld] address", (long long)m, (long long)kb);
+                                ++sa[32 * wave + lane];
+                            } else {
+                                CHECK(!in, "a_s row %lld >= M read", (long long)m);
+                            }
                         }
                         // per-column B scales
-                        const uint64_t offb = static_cast<uint64_t>(fast_bscale_col_base(n0, N, wave, lane)) + fast_bscale_col_advance(kb, N);
+                        const uint64_t offb = static_cast<uint64_t>(fast_bscale_col_base(cpw, n0, N, wave, lane)) + fast_bscale_col_advance(kb, N);
                         const bool inb = access(offb, 4 * N * Kb, 4, ok);
                         CHECK(ok, "b_s offset");
-                        const int64_t n = n0 + 32 * wave + lane;
-                        if (n < N) {
+                        const int64_t n = n0 + cpw * wave + lane;
+                        if (lane < cpw && n < N) {
                             CHECK(inb && static_cast<int64_t>(offb) == 4 * (kb * N + n), "b_s[%lld, %lld] address", (long long)kb, (long long)n);
-                            ++sbc[32 * wave + lane];
+                            ++sbc[cpw * wave + lane];
                         } else {
-                            CHECK(!inb, "b_s column %lld >= N read", (long long)n);
+                            CHECK(!inb, "b_s lane %d (column %lld) read", lane, (long long)n);
                         }
                     }
                 for (int r = 0; r < arows; ++r) CHECK(sa[r] == 1, "a_s row %lld not loaded once", (long long)(m0 + r));
@@ -159,11 +167,11 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
                 }
             }
             // bf16 epilogue
-            for (int wave = 0; wave < kFastWaves; ++wave)
+            for (int wave = 0; wave < waves; ++wave)
                 for (int p = 0; p < 16; ++p)
                     for (int lane = 0; lane < 64; ++lane) {
-                        const int64_t m = fast_store_row(m0, wave & 3, p, lane);
-                        const int64_t n = fast_store_col(n0, wave >> 2, lane);
+                        const int64_t m = fast_store_row(m0, wave % wms, p, lane);
+                        const int64_t n = fast_store_col(n0, wave / wms, lane);
                         if (m >= M) continue;
                         for (int e = 0; e < 8; ++e)
                             if (n + e < N) CHECK(++stored[m * N + n + e] == 1, "C[%lld, %lld] stored twice", (long long)m, (long long)(n + e));
@@ -174,7 +182,8 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
 }
 
 // Split K: slices partition the K-blocks; each slice's fp32 partial tile covers every output once.
-static bool check_split(int64_t M, int64_t N, int64_t K) {
+static bool check_split(int64_t M, int64_t N, int64_t K, int bm) {
+    const int waves = fast_waves(bm), wms = bm / 64;
     const int64_t Kb = cdiv(K, kBlockK);
     for (int64_t S = 1; S <= Kb && S <= 40; ++S) {
         int64_t next = 0;
@@ -187,15 +196,15 @@ static bool check_split(int64_t M, int64_t N, int64_t K) {
     }
     const int64_t ldp = (N + 7) / 8 * 8;
     std::vector<uint8_t> stored(static_cast<size_t>(M) * ldp, 0);
-    const int mt = static_cast<int>(cdiv(M, kFastBM)), nt = static_cast<int>(cdiv(N, kFastBN));
+    const int mt = static_cast<int>(cdiv(M, bm)), nt = static_cast<int>(cdiv(N, kFastBN));
     for (int tm = 0; tm < mt; ++tm)
         for (int tn = 0; tn < nt; ++tn)
-            for (int wave = 0; wave < kFastWaves; ++wave)
+            for (int wave = 0; wave < waves; ++wave)
                 for (int i = 0; i < 4; ++i)
                     for (int j = 0; j < 8; ++j)
                         for (int lane = 0; lane < 64; ++lane) {
-                            const int64_t m = fast_partial_row(static_cast<int64_t>(tm) * kFastBM, wave & 3, i, lane);
-                            const int64_t n = fast_partial_col(static_cast<int64_t>(tn) * kFastBN, wave >> 2, j, lane);
+                            const int64_t m = fast_partial_row(static_cast<int64_t>(tm) * bm, wave % wms, i, lane);
+                            const int64_t n = fast_partial_col(static_cast<int64_t>(tn) * kFastBN, wave / wms, j, lane);
                             if (m >= M || n >= N) continue;
                             CHECK(n % 4 == 0 && n + 4 <= ldp, "partial store past the padded row");
                             for (int e = 0; e < 4; ++e) CHECK(++stored[m * ldp + n + e] == 1, "partial stored twice");
@@ -375,8 +384,11 @@ int main(int argc, char** argv) {
     for (int a = 1; a + 2 < argc; a += 3) {
         const int64_t M = std::atoll(argv[a]), N = std::atoll(argv[a + 1]), K = std::atoll(argv[a + 2]);
         const int64_t ld = (K + 15) / 16 * 16;  // the GEMMs' 16-byte row rule
-        bool ok = check_fast(M, N, K, ld, ld) && check_fast(M, N, K, ld + 16, ld + 48) && check_split(M, N, K) &&
-                  check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);
+        bool ok = true;
+        for (int bm : {kFastBM, kFastBMSmall})
+            ok = ok && check_fast(M, N, K, ld, ld, bm) && check_fast(M, N, K, ld + 16, ld + 48, bm) &&
+                 check_split(M, N, K, bm);
+        ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);
         std::printf("%s M=%lld N=%lld K=%lld\n", ok ? "ok" : "FAILED", (long long)M, (long long)N, (long long)K);
         if (!ok) return 1;
     }

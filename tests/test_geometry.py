@@ -87,8 +87,8 @@ def test_unmasked_scale_store_is_caught(tmp_path):
 def test_planted_operand_row_read_is_caught(tmp_path):
     """An operand resource that runs past the tile's in-range rows."""
     exe = _planted(tmp_path,
-                   "return rows_in_range > 8 * q ? (rows_in_range - 8 * q) * ld : 0;",
-                   "return (256 - 8 * q) * ld;", "planted_rows")
+                   "return rows_in_range > 8 * (q & 3) ? (rows_in_range - 8 * (q & 3)) * ld : 0;",
+                   "return (256 - 8 * (q & 3)) * ld;", "planted_rows")
     r = _run(exe, [(130, 256, 256)])
     assert r.returncode != 0, r.stdout
 

@@ -330,18 +330,21 @@ def test_gemm_partial_last_block_ignores_nan_padding(M, N, K, ld, per_col):
 SPLIT_SHAPES = [
     # M, N, K, ld: ragged tiles, a partial last K-block, one tile, several tiles
     (130, 300, 1000, 1008), (1, 40, 4096, 4096), (257, 513, 2000, 2000), (64, 256, 384, 384),
+    (300, 260, 200, 208),
 ]
 
 
 @pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
-@pytest.mark.parametrize("S", [2, 3, 7])
+@pytest.mark.parametrize("bm", [256, 128], ids=["tile256", "tile128"])
+@pytest.mark.parametrize("S", [1, 2, 3, 7])
 @pytest.mark.parametrize("M,N,K,ld", SPLIT_SHAPES, ids=lambda v: str(v))
-def test_gemm_forced_split(M, N, K, ld, S, per_col, monkeypatch):
-    """K split over S slices (BSFP8_GEMM_SPLIT) on ragged shapes: fp32 partial tiles summed by the
-    second kernel, against the oracle in full; the fixed summation order makes two calls agree bit
-    for bit."""
+def test_gemm_forced_schedule(M, N, K, ld, S, bm, per_col, monkeypatch):
+    """Every schedule on ragged shapes: tile height bm (BSFP8_GEMM_TILE_M) and K split over S
+    slices (BSFP8_GEMM_SPLIT; 1 = none): fp32 partial tiles summed by the second kernel, against the
+    oracle in full; the fixed summation order makes two calls agree bit for bit."""
     qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + N + K + S, per_col)
     monkeypatch.setenv("BSFP8_GEMM_SPLIT", str(S))
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", str(bm))
     if per_col:
         fn = lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c)
         co = oracle.gemm_1x128_128x1(oqa, osa, oqb, osb)
@@ -354,12 +357,14 @@ def test_gemm_forced_split(M, N, K, ld, S, per_col, monkeypatch):
     _assert_close(got, co, f"split {S}")
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2, 5120, 1280),
-                                   (4, 3584, 640)], ids=lambda v: str(v))
-def test_forward_split_shapes_full(M, N, K, monkeypatch):
-    """The pages' short-and-wide GEMM shapes, where the automatic plan splits K: every output row
-    against the oracle, and the SQNR against the fp64 matmul of the bf16 inputs."""
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2048, 4096, 4096),
+                                   (2, 5120, 1280), (4, 3584, 640)], ids=lambda v: str(v))
+def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):
+    """The pages' short-and-wide GEMM shapes, where the automatic plan takes 128-row tiles and / or
+    splits K: every output row against the oracle, and the SQNR against the fp64 matmul of the bf16
+    inputs."""
     monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
+    monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
     g = inputs.rng(0)
     a_h = inputs.normal_bf16(g, (M, K))
     w_h = inputs.normal_bf16(g, (N, K), 0.02)
