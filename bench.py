@@ -345,6 +345,37 @@ def _time_kernel(fn, reps, stream, torch, batches=8):
     return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
 
 
+def _time_graph(fn, per, torch, batches=8):
+    """Duration (ms) per launch of fn(i), i = 0 .. per-1, recorded once into a HIP graph (every
+    call on torch's current stream, which is the capture stream inside the capture) and replayed
+    `batches` times, each replay bracketed by HIP events: (average, p10, p90) over the replays. A
+    replay starts its kernels back to back, so the host's per-call cost does not show, as it does for
+    launches from Python when one kernel takes less time than one call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(per):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(per):
+            fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    settle(lambda i: graph.replay(), SETTLE_ROW_MS, torch, chunk=2)
+    ev = [TimingEvent() for _ in range(batches + 1)]
+    ev[0].record(stream)
+    for b in range(batches):
+        graph.replay()
+        ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[b].elapsed_time(ev[b + 1]) / per for b in range(batches)])
+    del graph
+    return float(ms.mean()), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+
+
 def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     """Per-kernel timings on the training-step (8192 tokens, 4096x4096 weight) and outlier
     (16384 x 5120 x 5120) shapes, each rotating over buffer sets larger than the cache."""
@@ -484,7 +515,7 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     del Am, Wm, dYm, qam, qwm, swm, qxTm, sxTm, qdyTm, sdyTm, cm, dwm
     torch.cuda.empty_cache()
 
-    # tail-masking workload (130 x 5120 x 1280): the GEMM has 20 output tiles for 256 CUs and a few
+    # tail-masking workload (130 x 5120 x 1280): the GEMM has 40 output tiles for 256 CUs and a few
     # MB of data, so it is occupancy-bound and served from cache; reported for completeness (its
     # quantizers finish faster than one launch from Python, so timing them here would time the host)
     d1 = inputs.make_workload(1)
@@ -496,7 +527,9 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     c1 = torch.empty((M1, N1), dtype=torch.bfloat16, device=dev)
     a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa1, sa1, qw1, sw1, c=c1, stream=stream), reps,
                      stream, torch)
-    add("gemm_1x128_128x128 tail (20 tiles, warm cache)", [M1, N1, K1], a, 2.0 * M1 * N1 * K1, "TFLOP/s")
+    gph = _time_graph(lambda i: bf.gemm_1x128_128x128_noalloc(qa1, sa1, qw1, sw1, c1), 16, torch)
+    add("gemm_1x128_128x128 tail (warm cache)", [M1, N1, K1], a, 2.0 * M1 * N1 * K1, "TFLOP/s",
+        graph_avg_us=round(gph[0] * 1e3, 2), graph_p10_us=round(gph[1] * 1e3, 2), graph_p90_us=round(gph[2] * 1e3, 2))
     del A1, W1, qa1, sa1, qw1, sw1, c1
 
     d4 = inputs.make_workload(4)
@@ -540,8 +573,15 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
         del qa0, sa0, qw0, sw0
         a = _time_kernel(lambda i: bf.gemm_1x128_128x128(*ops[i % nsp][:4], c=ops[i % nsp][4], stream=stream),
                          reps, stream, torch)
-        add(f"gemm_1x128_128x128 {Mp}x{Np}x{Kp} (pages' table shape)", [Mp, Np, Kp], a,
-            2.0 * Mp * Np * Kp, "TFLOP/s", pages_mi300x_fp8_tflops=page_tflops, rotated_sets=nsp)
+        # the same launches replayed from a HIP graph (the allocation-free entry point, same
+        # kernels and schedule): GPU time without the host's per-call cost
+        gph = _time_graph(lambda i: bf.gemm_1x128_128x128_noalloc(*ops[i % nsp][:4], ops[i % nsp][4]),
+                          2 * nsp, torch)
+        fl = 2.0 * Mp * Np * Kp
+        add(f"gemm_1x128_128x128 {Mp}x{Np}x{Kp} (pages' table shape)", [Mp, Np, Kp], a, fl, "TFLOP/s",
+            pages_mi300x_fp8_tflops=page_tflops, rotated_sets=nsp,
+            graph_avg_us=round(gph[0] * 1e3, 2), graph_p10_us=round(gph[1] * 1e3, 2),
+            graph_p90_us=round(gph[2] * 1e3, 2), **{"graph_TFLOP/s": round(fl / (gph[0] * 1e-3) / 1e12, 1)})
         del ops
         torch.cuda.empty_cache()
 
@@ -553,7 +593,9 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     c0 = torch.empty((A0.shape[0], W0.shape[0]), dtype=torch.bfloat16, device=dev)
     a = _time_kernel(lambda i: bf.gemm_1x128_128x128(qa_0, sa_0, qw_0, sw_0, c=c0, stream=stream), reps,
                      stream, torch)
-    add("gemm_1x128_128x128 2x512x128 (launch floor)", [2, 512, 128], a, 2.0 * 2 * 512 * 128, "TFLOP/s")
+    gph = _time_graph(lambda i: bf.gemm_1x128_128x128_noalloc(qa_0, sa_0, qw_0, sw_0, c0), 16, torch)
+    add("gemm_1x128_128x128 2x512x128 (launch floor)", [2, 512, 128], a, 2.0 * 2 * 512 * 128, "TFLOP/s",
+        graph_avg_us=round(gph[0] * 1e3, 2), graph_p10_us=round(gph[1] * 1e3, 2), graph_p90_us=round(gph[2] * 1e3, 2))
     del A0, W0, qa_0, sa_0, qw_0, sw_0, c0
     return out
 
