@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     quantize_lhs_and_rhs,
     quantize_lhs_and_weight,
     quantize_rhs,
+    quantize_rhs_grouped,
     quantize_weight_128x128,
 )
 from .linear import BlockwiseFp8Linear, blockwise_fp8_linear  # noqa: F401

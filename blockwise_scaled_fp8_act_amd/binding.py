@@ -60,7 +60,9 @@ def lib():
         L.gemm_1x128_128x128_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _vp, _i64, _i64,
                                                  _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]
         L.gemm_1x128_128x1_grouped.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64,
-                                               _i64, _i64, _i64, _i64, _vp]
+                                               _i64, _i64, _i64, _i64, _vp, _vp]
+        L.quantize_rhs_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp]
+        L.quantize_rhs_grouped_fnuz.argtypes = L.quantize_rhs_grouped.argtypes
         L.quantize_lhs_and_weight.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _i64,
                                               _i64, _vp, _i64, _vp, _i64, _vp, _vp]
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
@@ -71,7 +73,7 @@ def lib():
         for f in ("quantize_lhs", "quantize_rhs", "quantize_weight_128x128", "gemm_1x128_128x128",
                   "gemm_1x128_128x1", "encode_e4m3_f32", "quantize_lhs_and_rhs",
                   "gemm_1x128_128x128_grouped", "gemm_1x128_128x1_grouped",
-                  "gemm_1x128_128x128_noalloc",
+                  "gemm_1x128_128x128_noalloc", "quantize_rhs_grouped", "quantize_rhs_grouped_fnuz",
                   "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
                   "gemm_1x128_128x128_fnuz", "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
                   "quantize_lhs_and_rhs_fnuz", "quantize_lhs_and_weight",
@@ -434,10 +436,12 @@ def gemm_1x128_128x128_grouped(a, a_s, b, b_s, offsets, E, b_stride, bs_stride, 
     return c
 
 
-def gemm_1x128_128x1_grouped(a, a_s, b, b_s, offsets, E, c=None, stream=None):
+def gemm_1x128_128x1_grouped(a, a_s, b, b_s, offsets, E, c=None, status=None, stream=None):
     """Per-expert C_e = A_e B_e^T over the token (column) ranges [offsets[e], offsets[e+1]) of
-    A [M, K] and B [N, K] (quantize_rhs codes over all tokens, scales (Kb, M) and (Kb, N)); returns
-    c [E, M, N] bf16."""
+    A [M, K] and B [N, K] (128x1 codes over all tokens, scales (Kb, M) and (Kb, N)); returns
+    c [E, M, N] bf16. Every boundary must be a multiple of 128 (quantize_rhs_grouped's padded
+    offsets are); an expert whose range is not gets NaN outputs and sets ``status`` (an int32 GPU
+    tensor, optional) to 1."""
     M, K = _codes("a", a, "e4m3fn").shape
     N = _codes("b", b, "e4m3fn", (None, K)).shape[0]
     if c is None:
@@ -449,7 +453,35 @@ def gemm_1x128_128x1_grouped(a, a_s, b, b_s, offsets, E, c=None, stream=None):
         raise TypeError("c must be a bfloat16 tensor")
     if c.dim() != 3 or tuple(c.shape) != (E, M, N) or (c.stride(2) != 1 and N > 1):
         raise ValueError(f"expected c [E, M, N] = {(E, M, N)} with contiguous rows, got {tuple(c.shape)}")
-    _gpu(a=a, a_s=a_s, b=b, b_s=b_s, offsets=offsets, c=c)
+    if status is not None and (not isinstance(status, torch.Tensor) or status.dtype != torch.int32
+                               or status.numel() < 1):
+        raise TypeError("status must be an int32 tensor of at least one element")
+    _gpu(a=a, a_s=a_s, b=b, b_s=b_s, offsets=offsets, c=c, status=status)
     _call("gemm_1x128_128x1_grouped", _ptr(a), _ld(a), _ptr(a_s), _ptr(b), _ld(b), _ptr(b_s),
-          _ptr(offsets), E, _ptr(c), c.stride(1), c.stride(0), M, N, K, _stream(stream))
+          _ptr(offsets), E, _ptr(c), c.stride(1), c.stride(0), M, N, K, _ptr(status), _stream(stream))
     return c
+
+
+def quantize_rhs_grouped(x, offsets, E, qT=None, s=None, padded_offsets=None, stream=None, fmt="e4m3fn"):
+    """128x1 quantization of expert-grouped tokens x [T, N] (expert e owns rows
+    [offsets[e], offsets[e+1])) with groups restarting at every expert's first token, in the
+    128-padded token layout. Returns (qT [N, 128 G], s (G, N), padded_offsets [E + 1] int64) with
+    G = ceil(T / 128) + E; columns and scale rows past padded_offsets[E] are not written."""
+    T, N = _matrix("x", x, _BF16).shape
+    _offsets(offsets, E)
+    G = cdiv(T, BLOCK) + E
+    if qT is None:
+        qT = torch.empty((N, G * BLOCK), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((G, N), dtype=torch.float32, device=x.device)
+    if padded_offsets is None:
+        padded_offsets = torch.empty(E + 1, dtype=torch.int64, device=x.device)
+    _codes("qT", qT, fmt, (N, None))
+    if qT.shape[1] < G * BLOCK:
+        raise ValueError(f"qT needs at least 128 (ceil(T/128) + E) = {G * BLOCK} columns, has {qT.shape[1]}")
+    _dense("s", s, torch.float32, (G, N))
+    _offsets(padded_offsets, E)
+    _gpu(x=x, offsets=offsets, qT=qT, s=s, padded_offsets=padded_offsets)
+    _call(_entry("quantize_rhs_grouped", fmt), _ptr(x), T, N, _ld(x), _ptr(offsets), E, _ptr(qT), _ld(qT),
+          _ptr(s), _ptr(padded_offsets), _stream(stream))
+    return qT, s, padded_offsets

@@ -180,6 +180,22 @@ int quantize_rhs_impl(const void* x, int64_t K, int64_t N, int64_t ldx, void* qT
                                              static_cast<hipStream_t>(stream)));
 }
 
+int quantize_rhs_grouped_impl(const void* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets, int64_t E,
+                              void* qT, int64_t ldqT, float* s, int64_t* padded, bool fnuz, void* stream) {
+    if (T < 0 || N < 0 || E < 0) return BSFP8_EINVAL;
+    if (offsets == nullptr || padded == nullptr) return BSFP8_EINVAL;
+    const int64_t groups = cdiv(T, kGroupEdge) + E;  // bound on the padded groups
+    if (groups > kMaxGridY || cdiv(N, 64) > 0x7FFFFFFFLL) return BSFP8_EINVAL;
+    if (T > 0 && N > 0) {
+        if (x == nullptr || qT == nullptr || s == nullptr) return BSFP8_EINVAL;
+        if (ldx < N || ldqT < groups * kGroupEdge) return BSFP8_EINVAL;
+    }
+    if (int rc = check_device()) return rc;
+    return finish(bsfp8::launch_quantize_rhs_grouped(static_cast<const uint16_t*>(x), T, N, ldx, offsets, E,
+                                                     static_cast<uint8_t*>(qT), ldqT, s, padded, fnuz,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 int quantize_weight_impl(const void* w, int64_t N, int64_t K, int64_t ldw, void* q, int64_t ldq,
                          void* qT, int64_t ldqT, float* s, bool fnuz, void* stream) {
     if (N < 0 || K < 0) return BSFP8_EINVAL;
@@ -360,6 +376,17 @@ int quantize_lhs_and_rhs_fnuz(const void* x, int64_t R, int64_t C, int64_t ldx, 
     return quantize_dual_impl(x, R, C, ldx, q, ldq, a_s, qT, ldqT, s, true, stream);
 }
 
+int quantize_rhs_grouped(const void* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets, int64_t E,
+                         void* qT, int64_t ldqT, float* s, int64_t* padded_offsets, void* stream) {
+    return quantize_rhs_grouped_impl(x, T, N, ldx, offsets, E, qT, ldqT, s, padded_offsets, false, stream);
+}
+
+int quantize_rhs_grouped_fnuz(const void* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets,
+                              int64_t E, void* qT, int64_t ldqT, float* s, int64_t* padded_offsets,
+                              void* stream) {
+    return quantize_rhs_grouped_impl(x, T, N, ldx, offsets, E, qT, ldqT, s, padded_offsets, true, stream);
+}
+
 int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s, const void* b,
                                int64_t ldb, int64_t b_stride, const float* b_s, int64_t bs_stride,
                                int64_t bs_stride_nb, int64_t bs_stride_kb, const int64_t* offsets,
@@ -384,7 +411,7 @@ int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s, con
 int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const void* b,
                              int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
                              void* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
-                             int64_t K, void* stream) {
+                             int64_t K, int32_t* status, void* stream) {
     if (E < 0 || K < 0) return BSFP8_EINVAL;
     if (E == 0 || M == 0 || N == 0) return M < 0 || N < 0 ? BSFP8_EINVAL : BSFP8_OK;
     if (K == 0 || K % kGroupEdge != 0 || E > 65535) return BSFP8_EINVAL;
@@ -395,7 +422,7 @@ int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s, const
     if (int rc = check_device()) return rc;
     return finish(bsfp8::launch_gemm_grouped_k(
         static_cast<const uint8_t*>(a), lda, a_s, static_cast<const uint8_t*>(b), ldb, b_s, offsets,
-        E, static_cast<uint16_t*>(c), ldc, c_stride, M, N, K, static_cast<hipStream_t>(stream)));
+        E, static_cast<uint16_t*>(c), ldc, c_stride, M, N, K, status, static_cast<hipStream_t>(stream)));
 }
 
 int quantize_lhs_and_weight(const void* x, int64_t M, int64_t K, int64_t ldx, void* qx, int64_t ldqx,

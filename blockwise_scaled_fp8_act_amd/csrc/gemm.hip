@@ -480,6 +480,7 @@ struct Grouping {
     int64_t b_stride;   // bytes between consecutive experts' B            (kGroupRows)
     int64_t bs_stride;  // floats between consecutive experts' B scales    (kGroupRows)
     int64_t c_stride;   // elements between consecutive experts' C (kGroupK); floats per partial (kSplitK)
+    int32_t* status;    // kGroupK: set to 1 when an expert's token range is not 128-aligned (may be null)
 };
 
 struct Ops {
@@ -609,6 +610,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
     // K-blocks (the last one may be partial: only for the ungrouped GEMMs, whose callers allow it)
     int64_t Kb = (K + kGroup - 1) / kGroup;
+    bool unaligned = false;  // kGroupK: an expert range off the 128 grid (its C becomes NaN)
     if (GROUP == kGroupRows) {
         // tm indexes the concatenated row tiles of the experts; expert e owns rows
         // [offsets[e], offsets[e + 1]) of A and C (clamped to [0, M] and made non-decreasing) and
@@ -636,12 +638,19 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
         b_s += e * grp.bs_stride;
     } else if (GROUP == kGroupK) {
         // expert e = blockIdx.y owns the K-blocks [offsets[e] / 128, offsets[e + 1] / 128) of A and B
-        // (token ranges of the weight gradient, multiples of 128) and writes its own C
+        // (token ranges of the weight gradient, multiples of 128) and writes its own C. A range
+        // whose ends (clamped into [0, K] and to non-decreasing order) are not multiples of 128 has
+        // no K-blocks of its own: its C is filled with NaN and *status set, nothing is rounded.
         const int64_t e = blockIdx.y;
         const int64_t lo = min(max(grp.offsets[e], int64_t{0}), K);
         const int64_t hi = min(max(grp.offsets[e + 1], lo), K);
         const int64_t kb0 = lo / kGroup;
         Kb = hi / kGroup - kb0;
+        if (lo % kGroup != 0 || hi % kGroup != 0) {
+            Kb = 0;
+            unaligned = true;
+            if (grp.status != nullptr && blockIdx.x == 0 && tid == 0) *grp.status = 1;
+        }
         A += kb0 * kGroup;
         B += kb0 * kGroup;
         a_s += kb0 * M;
@@ -690,10 +699,11 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
     }
 
     v4f acc[kMSub][kNSub];
+    const float acc0 = unaligned ? __builtin_nanf("") : 0.0f;
 #pragma unroll
     for (int i = 0; i < kMSub; ++i)
 #pragma unroll
-        for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < kNSub; ++j) acc[i][j] = v4f{acc0, acc0, acc0, acc0};
 
     if (Kb > 0) {
         auto stage_base = [&](int stage) { return op.lds + static_cast<uint32_t>(stage * kStageSize * 16); };
@@ -1065,7 +1075,7 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
     if (plan.S > 1) {
         // K split over plan.S workgroups per tile: fp32 partial tiles, then their sum in bf16
         if (workspace == nullptr) return hipErrorInvalidValue;
-        const fast::Grouping g{nullptr, 0, 0, 0, M * plan.ldp};
+        const fast::Grouping g{nullptr, 0, 0, 0, M * plan.ldp, nullptr};
         const dim3 grid(static_cast<unsigned>(mt * nt), static_cast<unsigned>(plan.S));
         uint16_t* P = reinterpret_cast<uint16_t*>(workspace);
         if (bs.per_column)
@@ -1086,7 +1096,7 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
     }
     const int c_vec16 = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
     const dim3 grid(static_cast<unsigned>(mt * nt));
-    const fast::Grouping none{nullptr, 0, 0, 0, 0};
+    const fast::Grouping none{nullptr, 0, 0, 0, 0, nullptr};
     if (bs.per_column)
         fast::gemm_kernel<true, fast::kGroupNone, BM><<<grid, kThreads, 0, stream>>>(
             a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
@@ -1134,7 +1144,7 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM + E;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const fast::Grouping g{offsets, E, b_stride, bs_stride, 0};
+    const fast::Grouping g{offsets, E, b_stride, bs_stride, 0, nullptr};
     fast::gemm_kernel<false, fast::kGroupRows, fast::kBM><<<dim3(static_cast<unsigned>(mt * nt)), fast::Cfg<fast::kBM>::kThreads, 0, stream>>>(
         a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt, (int)nt,
         c_vec, g);
@@ -1144,13 +1154,13 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
 hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                                  int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
                                  uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
-                                 int64_t K, hipStream_t stream) {
+                                 int64_t K, int32_t* status, hipStream_t stream) {
     if (K % kGroup != 0) return hipErrorInvalidValue;
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0) && (c_stride % 8 == 0);
     const int64_t mt = (M + fast::kBM - 1) / fast::kBM;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL || E > 65535) return hipErrorInvalidValue;
-    const fast::Grouping g{offsets, E, 0, 0, c_stride};
+    const fast::Grouping g{offsets, E, 0, 0, c_stride, status};
     fast::gemm_kernel<true, fast::kGroupK, fast::kBM><<<dim3(static_cast<unsigned>(mt * nt), static_cast<unsigned>(E)), fast::Cfg<fast::kBM>::kThreads, 0, stream>>>(
         a, lda, a_s, b, ldb, b_s, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec, g);
     return hipGetLastError();

@@ -12,6 +12,11 @@ hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t 
 hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
                                 int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
                                 bool fnuz, hipStream_t stream);
+// 128x1 groups that restart at every expert's first token, written in the 128-padded token layout
+// (see quantize_rhs_grouped_kernel); padded: E + 1 padded boundaries (device memory, written).
+hipError_t launch_quantize_rhs_grouped(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets,
+                                      int64_t E, uint8_t* qT, int64_t ldqT, float* s, int64_t* padded, bool fnuz,
+                                      hipStream_t stream);
 hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
                                int64_t ldqT, float* s, bool fnuz, hipStream_t stream);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
@@ -74,6 +79,6 @@ hipError_t launch_gemm_grouped_rows(const uint8_t* a, int64_t lda, const float* 
 hipError_t launch_gemm_grouped_k(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
                                  int64_t ldb, const float* b_s, const int64_t* offsets, int64_t E,
                                  uint16_t* c, int64_t ldc, int64_t c_stride, int64_t M, int64_t N,
-                                 int64_t K, hipStream_t stream);
+                                 int64_t K, int32_t* status, hipStream_t stream);
 
 }  // namespace bsfp8

@@ -225,6 +225,97 @@ __global__ __launch_bounds__(256) void quantize_rhs_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// 128x1 of expert-grouped tokens: x [T, N] holds the tokens of E experts one after the other,
+// expert e owning rows [offsets[e], offsets[e+1]) (clamped into [0, T] and to non-decreasing order).
+// The 128x1 groups restart at every expert's first token, so an expert's last group may hold fewer
+// than 128 tokens. The output puts expert e's tokens at padded position P[e] = the sum of the
+// earlier experts' token counts, each rounded up to a multiple of 128: qT [N, *] holds at column
+// P[e] + t the codes of the expert's token t and zeros in the columns up to the next multiple of
+// 128; s holds the scale of padded group p (columns 128 p .. 128 p + 127) in row p. P (E + 1 values)
+// is written too, for the grouped weight-gradient GEMM. A workgroup owns one padded group x 64
+// columns, as in quantize_rhs_kernel; blockIdx.y runs over an upper bound of the padded groups
+// (ceil(T / 128) + E) and the workgroups past the last group leave at once.
+template <bool FNUZ, bool VEC_X, bool VEC_Q>
+__global__ __launch_bounds__(256) void quantize_rhs_grouped_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t N, int64_t ldx, const int64_t* __restrict__ offsets,
+    int64_t E, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ s, int64_t* __restrict__ padded) {
+    __shared__ uint32_t red[32][kRhsCols + 1];
+    __shared__ float mult[kRhsCols];
+    __shared__ uint4 tileT[kRhsCols * 8];
+
+    const int t = threadIdx.x;
+    const int cg = t & 7;
+    const int rq = t >> 3;
+    const int64_t gp = blockIdx.y;  // padded group
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kRhsCols;
+    const int64_t col = n0 + cg * 8;
+
+    // this group's expert: scan the clamped boundaries (E is small); every workgroup of the first
+    // group row writes P, each thread a part of it
+    int64_t lo = 0, hi = 0, first = 0, prev = 0, groups_before = 0;
+    bool found = false;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t a = min(max(offsets[e], prev), T);
+        const int64_t b = min(max(offsets[e + 1], a), T);
+        prev = b;
+        const int64_t g = (b - a + kGroup - 1) / kGroup;
+        if (!found && gp < groups_before + g) {
+            found = true;
+            lo = a;
+            hi = b;
+            first = groups_before;
+        }
+        if (blockIdx.x == 0 && gp == 0 && t == 0) padded[e] = groups_before * kGroup;
+        groups_before += g;
+    }
+    if (blockIdx.x == 0 && gp == 0 && t == 0) padded[E] = groups_before * kGroup;
+    if (!found) return;  // past the last padded group: the whole workgroup leaves
+
+    const int64_t r0 = lo + (gp - first) * kGroup;  // the group's first token
+    const int64_t rend = min(hi, r0 + kGroup);      // one past its last
+    float f[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load8<VEC_X>(x, ldx, r0 + rq * 4 + i, rend, col, N, f[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t am = max(max(abs_bits(f[0][j]), abs_bits(f[1][j])), max(abs_bits(f[2][j]), abs_bits(f[3][j])));
+        red[rq][cg * 8 + j] = am;
+    }
+    __syncthreads();
+    if (t < kRhsCols) {
+        uint32_t am = 0;
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) am = max(am, red[r][t]);
+        const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
+        mult[t] = g.m;
+        if (n0 + t < N) s[gp * N + n0 + t] = g.s;
+    }
+    __syncthreads();
+    uint32_t* tw = reinterpret_cast<uint32_t*>(tileT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float mj = mult[cg * 8 + j];
+        const uint32_t w = encode4_in_range<FNUZ>(f[0][j] * mj, f[1][j] * mj, f[2][j] * mj, f[3][j] * mj);
+        const int cl = cg * 8 + j;
+        const int chunk = (rq >> 2) ^ (cl >> 3);
+        tw[cl * 32 + chunk * 4 + (rq & 3)] = w;
+    }
+    __syncthreads();
+    // the group's 128 padded columns of each output row (tokens past the expert's end are zeros)
+    const int chunk = t & 7;
+    const int64_t k0 = gp * kGroup;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int cl = p * 32 + (t >> 3);
+        const int64_t n = n0 + cl;
+        if (n < N) {
+            const uint4 v = tileT[cl * 8 + (chunk ^ (cl >> 3))];
+            store16<VEC_Q>(qT + n * ldqT, k0 + chunk * 16, k0 + kGroup, v);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // 128x128 blocks: one workgroup per block; thread t holds rows 8*(t/16) .. +8 x columns
 // 8*(t%16) .. +8 (64 values in registers, read once). The block max is a wave reduction plus a
 // 4-entry LDS combine. The optional transposed copy goes through a swizzled LDS tile.
@@ -646,6 +737,26 @@ hipError_t quantize_rhs_impl(const uint16_t* x, int64_t K, int64_t N, int64_t ld
 }
 
 template <bool FNUZ>
+hipError_t quantize_rhs_grouped_impl(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets,
+                                     int64_t E, uint8_t* qT, int64_t ldqT, float* s, int64_t* padded,
+                                     hipStream_t stream) {
+    // at least the padded groups; one workgroup at least, which writes the padded offsets
+    const int64_t groups = (T + kGroup - 1) / kGroup + E;
+    const int64_t nc = (N + kRhsCols - 1) / kRhsCols;
+    const dim3 grid(static_cast<unsigned>(nc > 0 ? nc : 1), static_cast<unsigned>(groups > 0 ? groups : 1));
+    const bool vx = aligned(x, 16) && (ldx % 8 == 0) && (N % 8 == 0);
+    const bool vq = aligned(qT, 16) && (ldqT % 16 == 0);
+#define BSFP8_QG(A, B) \
+    quantize_rhs_grouped_kernel<FNUZ, A, B><<<grid, 256, 0, stream>>>(x, T, N, ldx, offsets, E, qT, ldqT, s, padded)
+    if (vx && vq) BSFP8_QG(true, true);
+    else if (vx) BSFP8_QG(true, false);
+    else if (vq) BSFP8_QG(false, true);
+    else BSFP8_QG(false, false);
+#undef BSFP8_QG
+    return hipGetLastError();
+}
+
+template <bool FNUZ>
 hipError_t quantize_weight_impl(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, uint8_t* qT, int64_t ldqT, float* s,
                                 hipStream_t stream) {
@@ -722,6 +833,13 @@ hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t 
                                int64_t ldqT, float* s, bool fnuz, hipStream_t stream) {
     return fnuz ? quantize_rhs_impl<true>(x, K, N, ldx, qT, ldqT, s, stream)
                 : quantize_rhs_impl<false>(x, K, N, ldx, qT, ldqT, s, stream);
+}
+
+hipError_t launch_quantize_rhs_grouped(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int64_t* offsets,
+                                      int64_t E, uint8_t* qT, int64_t ldqT, float* s, int64_t* padded, bool fnuz,
+                                      hipStream_t stream) {
+    return fnuz ? quantize_rhs_grouped_impl<true>(x, T, N, ldx, offsets, E, qT, ldqT, s, padded, stream)
+                : quantize_rhs_grouped_impl<false>(x, T, N, ldx, offsets, E, qT, ldqT, s, padded, stream);
 }
 
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,

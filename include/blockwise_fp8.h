@@ -220,23 +220,50 @@ int gemm_1x128_128x128_grouped(const void* a, int64_t lda, const float* a_s,
  * gemm_1x128_128x1_grouped: the weight gradient of an expert-grouped layer in one launch: for every
  * expert e, C_e = A_e B_e^T where A_e and B_e are the columns (tokens) [offsets[e], offsets[e+1])
  * of A and B -- per expert, exactly gemm_1x128_128x1 over its own tokens.
- *   a, lda, a_s   A [M, K] fp8 = quantize_rhs(dY) codes over all K tokens, a_s [ceil(K/128), M].
- *   b, ldb, b_s   B [N, K] fp8 = quantize_rhs(X) codes, b_s [ceil(K/128), N].
- *   offsets       E + 1 int64 token boundaries in DEVICE memory, multiples of 128: each expert's
- *                 128x1 groups then lie inside its own tokens, so one quantize_rhs over all tokens
- *                 is the per-expert quantization. Boundaries are clamped into [0, K] and to
- *                 non-decreasing order and rounded down to a multiple of 128.
+ *   a, lda, a_s   A [M, K] fp8 = the 128x1 codes of dY over all K token columns, a_s [K/128, M].
+ *   b, ldb, b_s   B [N, K] fp8 = the 128x1 codes of X, b_s [K/128, N].
+ *   offsets       E + 1 int64 token boundaries in DEVICE memory, clamped into [0, K] and to
+ *                 non-decreasing order. Each expert's 128x1 groups must lie inside its own tokens:
+ *                 every boundary a multiple of 128. That holds for quantize_rhs_grouped's padded
+ *                 boundaries (any routing), or for quantize_rhs over all tokens when the experts'
+ *                 token counts are multiples of 128.
  *   c, ldc        E outputs [M, N] bf16, expert e's at c + e * c_stride (elements).
+ *   status        NULL or a DEVICE int32: an expert whose clamped boundaries are not multiples of
+ *                 128 is not computed -- its C_e is filled with NaN -- and *status is set to 1
+ *                 (the kernel never clears it). Nothing is rounded to the 128 grid.
  * Requirements (else BSFP8_EINVAL): K a positive multiple of 128, E <= 65535,
  * c_stride >= (M - 1) * ldc + N when E > 1; alignment and size limits as gemm_1x128_128x1.
  * Never split; allocates nothing.
- * E == 0 or an empty M or N: no launch.
  */
 int gemm_1x128_128x1_grouped(const void* a, int64_t lda, const float* a_s,
                              const void* b, int64_t ldb, const float* b_s,
                              const int64_t* offsets, int64_t E,
                              void* c, int64_t ldc, int64_t c_stride,
-                             int64_t M, int64_t N, int64_t K, void* stream);
+                             int64_t M, int64_t N, int64_t K, int32_t* status, void* stream);
+
+/*
+ * quantize_rhs_grouped: 128x1 column-wise quantization (act_quant_rhs) of expert-grouped tokens whose
+ * groups restart at every expert's first token -- the per-expert quantize_rhs the MoE weight
+ * gradient needs when routing gives token counts that are not multiples of 128 (the MoE path the
+ * ROCm page's description refers to; this is the plainest reading: per expert, exactly quantize_rhs
+ * of its own tokens).
+ *   x        [T, N] bf16, row stride ldx >= N; expert e owns rows [offsets[e], offsets[e+1]).
+ *   offsets  E + 1 int64 in DEVICE memory, clamped into [0, T] and to non-decreasing order.
+ *   Output in the 128-padded token layout: P[e] = sum over the experts before e of their token
+ *   counts rounded up to a multiple of 128.
+ *   qT       [N, ldqT] fp8 (transposed codes), ldqT >= 128 G with G = ceil(T/128) + E: column
+ *            P[e] + t holds expert e's token t, the columns up to the next multiple of 128 hold 0;
+ *            columns from P[E] on are not written.
+ *   s        fp32 [G, N] row-major: row p holds the scales of padded group p (columns 128 p ..
+ *            128 p + 127 of qT); rows from P[E] / 128 on are not written. An expert's last group
+ *            takes its amax over the tokens it has.
+ *   padded_offsets  E + 1 int64 in DEVICE memory, written with P (P[0] = 0, P[E] the padded total).
+ * Pass qT, s and padded_offsets to gemm_1x128_128x1_grouped with K = 128 G. Requirements (else
+ * BSFP8_EINVAL): G <= 65535, offsets and padded_offsets not NULL.
+ */
+int quantize_rhs_grouped(const void* x, int64_t T, int64_t N, int64_t ldx,
+                         const int64_t* offsets, int64_t E,
+                         void* qT, int64_t ldqT, float* s, int64_t* padded_offsets, void* stream);
 
 /*
  * encode_e4m3_f32: the quantizers' element conversion applied to n arbitrary fp32 values:
@@ -303,6 +330,9 @@ int gemm_1x128_128x1_fnuz(const void* a, int64_t lda, const float* a_s,
                           const void* b, int64_t ldb, const float* b_s,
                           void* c, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 int encode_e4m3fnuz_f32(const float* x, void* q, int64_t n, void* stream);
+int quantize_rhs_grouped_fnuz(const void* x, int64_t T, int64_t N, int64_t ldx,
+                              const int64_t* offsets, int64_t E,
+                              void* qT, int64_t ldqT, float* s, int64_t* padded_offsets, void* stream);
 
 #ifdef __cplusplus
 }

@@ -196,6 +196,39 @@ def quantize_rhs(x: np.ndarray, fmt: str = "e4m3fn"):
     return qT, s
 
 
+def quantize_rhs_grouped(x: np.ndarray, offsets, fmt: str = "e4m3fn"):
+    """128x1 groups of expert-grouped tokens x [T, N] (bf16 bits) that restart at every expert's
+    first token: expert e owns rows [offsets[e], offsets[e+1]) (clamped into [0, T] and to
+    non-decreasing order) and is quantized on its own by quantize_rhs -- the per-expert act_quant_rhs
+    the MoE weight gradient needs ("Enable blockwise FP8 dense training kernels on ROCm",
+    description: the MoE path; the pages list no kernel for it, so this is the plainest reading).
+    The results go into the 128-padded token layout: P[e] = sum over the experts before e of their
+    token counts rounded up to a multiple of 128. Returns (qT [N, 128 G], s [G, N], P [E + 1]) with
+    G = ceil(T / 128) + E: column P[e] + t of qT holds expert e's token t, row P[e] / 128 + g of s
+    its group g; everything else (padding and the unused tail) is zero."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T, N = x.shape
+    offsets = [int(v) for v in offsets]
+    E = len(offsets) - 1
+    G = cdiv(T, BLOCK) + E
+    qT = np.zeros((N, G * BLOCK), dtype=np.uint8)
+    s = np.zeros((G, N), dtype=np.float32)
+    P = np.zeros(E + 1, dtype=np.int64)
+    prev = pos = 0
+    for e in range(E):
+        a = min(max(offsets[e], prev), T)
+        b = min(max(offsets[e + 1], a), T)
+        prev = b
+        P[e] = pos
+        if b > a:
+            q_e, s_e = quantize_rhs(x[a:b], fmt)
+            qT[:, pos:pos + (b - a)] = q_e
+            s[pos // BLOCK:pos // BLOCK + s_e.shape[0]] = s_e
+        pos += cdiv(b - a, BLOCK) * BLOCK
+    P[E] = pos
+    return qT, s, P
+
+
 def quantize_weight_128x128(w: np.ndarray, want_qT: bool = True, fmt: str = "e4m3fn"):
     """128x128 blocks of w [N, K] (bf16 bits). Returns (q [N, K], qT [K, N] or None, s [Nb, Kb])."""
     w = np.ascontiguousarray(w, dtype=np.uint16)

@@ -35,7 +35,9 @@ def test_every_declared_symbol_is_exported(L):
                           "quantize_lhs_fnuz", "quantize_rhs_fnuz", "quantize_weight_128x128_fnuz",
                           "quantize_lhs_and_rhs_fnuz", "gemm_1x128_128x128_fnuz",
                           "gemm_1x128_128x1_fnuz", "encode_e4m3fnuz_f32",
-                          "quantize_lhs_and_weight", "quantize_lhs_and_weight_fnuz"}
+                          "quantize_lhs_and_weight", "quantize_lhs_and_weight_fnuz",
+                          "quantize_rhs_grouped", "quantize_rhs_grouped_fnuz",
+                          "gemm_1x128_128x128_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -82,11 +84,23 @@ def test_grouped_gemms_reject_bad_arguments(L):
     assert g(P, 128, P, P, 128, 0, P, -1, 1, 1, P, 2, P, 64, 256, 64, 128, None) == 1     # bs_stride < 0
     assert g(None, 0, None, None, 0, 0, None, 0, 0, 0, None, 0, None, 0, 5, 5, 128, None) == 0  # E = 0
     h = L.gemm_1x128_128x1_grouped
-    #      a   lda  a_s b  ldb  b_s off E  c  ldc cstr    M   N   K
-    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 64 * 64, 64, 64, 130, None) == 1          # K % 128
-    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 100, 64, 64, 256, None) == 1              # outputs overlap
-    assert h(P, 256, P, P, 256, P, None, 2, P, 64, 64 * 64, 64, 64, 256, None) == 1       # offsets
-    assert h(None, 0, None, None, 0, None, None, 0, None, 0, 0, 3, 4, 256, None) == 0     # E = 0
+    #      a   lda  a_s b  ldb  b_s off E  c  ldc cstr    M   N   K  status
+    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 64 * 64, 64, 64, 130, None, None) == 1    # K % 128
+    assert h(P, 256, P, P, 256, P, P, 2, P, 64, 100, 64, 64, 256, None, None) == 1        # outputs overlap
+    assert h(P, 256, P, P, 256, P, None, 2, P, 64, 64 * 64, 64, 64, 256, None, None) == 1  # offsets
+    assert h(None, 0, None, None, 0, None, None, 0, None, 0, 0, 3, 4, 256, None, None) == 0  # E = 0
+
+
+def test_grouped_quantizer_rejects_bad_arguments(L):
+    for f in (L.quantize_rhs_grouped, L.quantize_rhs_grouped_fnuz):
+        #        x   T    N   ldx off E  qT  ldqT s  padded
+        assert f(P, 300, 64, 64, P, 2, P, 624, P, P, None) == 1     # ldqT < 128 (ceil(T/128) + E) = 640
+        assert f(P, 300, 64, 63, P, 2, P, 768, P, P, None) == 1     # ldx < N
+        assert f(P, 300, 64, 64, None, 2, P, 768, P, P, None) == 1  # offsets
+        assert f(P, 300, 64, 64, P, 2, P, 768, P, None, None) == 1  # padded offsets
+        assert f(P, -1, 64, 64, P, 2, P, 768, P, P, None) == 1      # negative size
+        assert f(P, 300, 64, 64, P, -1, P, 768, P, P, None) == 1    # negative E
+        assert f(P, 128 * 65535, 64, 64, P, 1, P, 1 << 30, P, P, None) == 1  # more groups than the grid holds
 
 
 def test_empty_problems_are_noops(L):

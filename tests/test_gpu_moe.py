@@ -132,3 +132,88 @@ def test_grouped_weight_gradient(counts):
         co = oracle.gemm_1x128_128x1(np.ascontiguousarray(qdyT[:, kr]), sdy[kbr],
                                      np.ascontiguousarray(qxT[:, kr]), sx[kbr])
         _check(dw_h[e], co, f"wgrad expert {e}")
+
+
+# ------------------------------------------------------------------ ragged expert token counts
+
+RAGGED = [[300, 0, 5, 700, 128, 1], [1], [129, 127], [0, 0, 640]]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e4m3fnuz"])
+@pytest.mark.parametrize("N", [200, 203])
+@pytest.mark.parametrize("counts", RAGGED, ids=lambda c: "-".join(map(str, c)))
+def test_quantize_rhs_grouped_bit_exact(counts, N, fmt):
+    """Groups restarting at each expert's first token, in the 128-padded layout: codes, scales and
+    padded offsets equal the oracle's (quantize_rhs applied expert by expert) bit for bit, in the
+    written region; N = 203 takes the unvectorised loads."""
+    E = len(counts)
+    lead = 7                                             # tokens before the first expert
+    offsets = np.concatenate([[lead], lead + np.cumsum(counts)]).astype(np.int64)
+    T = int(offsets[-1]) + 3                             # and after the last
+    x = inputs.normal_bf16(_g(31 + N), (T, N))
+    xd = torch.from_numpy(x.view(np.int16)).to(DEV)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    qT, s, P = bf.quantize_rhs_grouped(xd, off, E, fmt=fmt)
+    torch.cuda.synchronize()
+    oqT, os_, oP = oracle.quantize_rhs_grouped(x, offsets, fmt=fmt)
+    assert np.array_equal(P.cpu().numpy(), oP)
+    tot = int(oP[-1])
+    assert np.array_equal(qT.cpu().numpy()[:, :tot], oqT[:, :tot])
+    assert np.array_equal(s.cpu().numpy()[:tot // 128].view(np.uint32), os_[:tot // 128].view(np.uint32))
+
+
+@pytest.mark.parametrize("counts", [[300, 0, 5, 700, 128, 1], [129, 127], [1000]],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_grouped_weight_gradient_ragged_counts(counts):
+    """The MoE weight gradient for any routing: both token operands through quantize_rhs_grouped,
+    then gemm_1x128_128x1_grouped over the padded offsets; expert by expert against the oracle's
+    dense gemm_1x128_128x1 of that expert's own tokens (quantize_rhs of its slice of dY and X)."""
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    T = int(offsets[-1])
+    n_out, n_in = 256, 384
+    x = inputs.normal_bf16(_g(41), (T, n_in))
+    dy = inputs.normal_bf16(_g(42), (T, n_out), 0.01)
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    qdyT, sdy, P = bf.quantize_rhs_grouped(torch.from_numpy(dy.view(np.int16)).to(DEV), off, E)
+    qxT, sx, P2 = bf.quantize_rhs_grouped(torch.from_numpy(x.view(np.int16)).to(DEV), off, E)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dw = bf.gemm_1x128_128x1_grouped(qdyT, sdy, qxT, sx, P, E, status=status)
+    torch.cuda.synchronize()
+    assert torch.equal(P, P2) and int(status.item()) == 0
+    dw_h = dw.float().cpu().numpy()
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            assert np.all(dw_h[e] == 0.0)
+            continue
+        a_q, a_s = oracle.quantize_rhs(dy[lo:hi])
+        b_q, b_s = oracle.quantize_rhs(x[lo:hi])
+        _check(dw_h[e], oracle.gemm_1x128_128x1(a_q, a_s, b_q, b_s), f"wgrad expert {e}")
+
+
+def test_grouped_weight_gradient_flags_unaligned_offsets():
+    """Boundaries off the 128 grid are not rounded: the experts they touch get NaN outputs and the
+    status flag is set; an aligned expert in the same launch is computed normally, and a launch
+    with aligned boundaries leaves a fresh flag at 0."""
+    T, n_out, n_in = 256, 128, 256
+    x = inputs.normal_bf16(_g(51), (T, n_in))
+    dy = inputs.normal_bf16(_g(52), (T, n_out), 0.01)
+    qxT, sx = oracle.quantize_rhs(x)
+    qdyT, sdy = oracle.quantize_rhs(dy)
+    args = [to_dev(qdyT), to_dev(sdy), to_dev(qxT), to_dev(sx)]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    off = torch.tensor([0, 128, 200, 256], dtype=torch.int64, device=DEV)
+    dw = bf.gemm_1x128_128x1_grouped(*args, off, 3, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    dw_h = dw.float().cpu().numpy()
+    assert np.all(np.isnan(dw_h[1])) and np.all(np.isnan(dw_h[2]))
+    co = oracle.gemm_1x128_128x1(np.ascontiguousarray(qdyT[:, :128]), sdy[:1],
+                                 np.ascontiguousarray(qxT[:, :128]), sx[:1])
+    _check(dw_h[0], co, "aligned expert next to unaligned ones")
+    fresh = torch.zeros(1, dtype=torch.int32, device=DEV)
+    bf.gemm_1x128_128x1_grouped(*args, torch.tensor([0, 128, 256], dtype=torch.int64, device=DEV), 2,
+                                status=fresh)
+    torch.cuda.synchronize()
+    assert int(fresh.item()) == 0

@@ -240,3 +240,61 @@ def test_pages_quant_shapes_consistent(M, K):
     ql, sl = oracle.quantize_lhs(x)
     qr, sr = oracle.quantize_rhs(np.ascontiguousarray(x.T))
     assert np.array_equal(ql, qr) and np.array_equal(sl, sr)
+
+
+# ------------------------------------------------------------------ expert-grouped 128x1 groups
+
+def test_grouped_rhs_with_aligned_experts_is_plain_rhs():
+    """Experts whose token counts are multiples of 128: the groups never cross a boundary, so the
+    grouped quantization is quantize_rhs over all tokens and P equals the offsets."""
+    g = inputs.rng(21)
+    x = inputs.normal_bf16(g, (640, 72))
+    offs = [0, 256, 256, 640]
+    qT, s, P = oracle.quantize_rhs_grouped(x, offs)
+    q_all, s_all = oracle.quantize_rhs(x)
+    assert list(P) == offs
+    assert np.array_equal(qT[:, :640], q_all) and np.array_equal(s[:5], s_all)
+    assert not qT[:, 640:].any() and not s[5:].any()
+
+
+def test_grouped_rhs_groups_restart_at_each_expert():
+    """Expert 0 has 3 tokens of magnitude 100, expert 1 has 130 tokens of magnitude 1: expert 1's
+    first group covers its own first 128 tokens only (scale 1/448), its second group its last 2
+    (scale 0.5/448), and expert 0's group pads 125 columns with zeros."""
+    N = 8
+    x = np.zeros((133, N))
+    x[:3] = 100.0
+    x[3:] = 1.0
+    x[-2:] = 0.5
+    xb = inputs.bf16_bits_from_f64(x)
+    qT, s, P = oracle.quantize_rhs_grouped(xb, [0, 3, 133])
+    assert list(P) == [0, 128, 384]
+    assert np.all(s[0] == np.float32(100.0) / np.float32(448.0))
+    assert np.all(s[1] == np.float32(1.0) / np.float32(448.0))
+    assert np.all(s[2] == np.float32(0.5) / np.float32(448.0))
+    code448 = oracle.e4m3_encode(np.array([448.0], dtype=np.float32))[0]
+    assert np.all(qT[:, :3] == code448) and not qT[:, 3:128].any()
+    assert np.all(qT[:, 128:256] == code448) and np.all(qT[:, 256:258] == code448)
+    assert not qT[:, 258:].any()
+    # a plain 128x1 quantization over all tokens mixes the experts: its first group takes 100
+    _, s_plain = oracle.quantize_rhs(xb)
+    assert np.all(s_plain[0] == np.float32(100.0) / np.float32(448.0))
+
+
+def test_grouped_rhs_single_expert_and_clamped_offsets():
+    """One expert over all T tokens is quantize_rhs of x padded to the 128 grid; a decreasing
+    boundary clamps to an empty expert, a boundary past T to T, leading tokens before offsets[0]
+    belong to no expert."""
+    g = inputs.rng(22)
+    x = inputs.normal_bf16(g, (300, 16))
+    qT, s, P = oracle.quantize_rhs_grouped(x, [0, 300])
+    q_all, s_all = oracle.quantize_rhs(x)
+    assert list(P) == [0, 384]
+    assert np.array_equal(qT[:, :300], q_all) and not qT[:, 300:].any()
+    assert np.array_equal(s[:3], s_all)
+    qT2, s2, P2 = oracle.quantize_rhs_grouped(x, [10, 200, 150, 999])
+    assert list(P2) == [0, 256, 256, 384]
+    q_a, s_a = oracle.quantize_rhs(x[10:200])
+    q_b, s_b = oracle.quantize_rhs(x[200:300])
+    assert np.array_equal(qT2[:, :190], q_a) and np.array_equal(qT2[:, 256:356], q_b)
+    assert np.array_equal(s2[:2], s_a) and np.array_equal(s2[2:3], s_b)
