@@ -512,6 +512,21 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     a = _time_kernel(lambda i: bf.gemm_1x128_128x1_grouped(qdyTm, sdyTm, qxTm, sxTm, offs, E, c=dwm,
                                                            stream=stream), reps, stream, torch)
     add("gemm_1x128_128x1_grouped wgrad (8 experts)", [Do, Di, Tm], a, 2.0 * Tm * Do * Di, "TFLOP/s")
+    # ragged routing: token counts drawn per token, not in multiples of 128; the expert-grouped
+    # 128x1 quantizer writes the 128-padded layout the grouped weight gradient reads
+    counts_r = gm.multinomial(Tm, np.full(E, 1.0 / E))
+    offs_r = torch.tensor(np.concatenate([[0], np.cumsum(counts_r)]), dtype=torch.int64, device=dev)
+    Gr = _cdiv(Tm, BLOCK) + E
+    qTr = [torch.empty((Di, Gr * BLOCK), dtype=torch.uint8, device=dev) for _ in range(nsm)]
+    sr = [torch.empty((Gr, Di), dtype=torch.float32, device=dev) for _ in range(nsm)]
+    pr = torch.empty(E + 1, dtype=torch.int64, device=dev)
+    a = _time_kernel(lambda i: bf.quantize_rhs_grouped(Am[i % nsm], offs_r, E, qT=qTr[i % nsm], s=sr[i % nsm],
+                                                       padded_offsets=pr, stream=stream), reps, stream, torch)
+    torch.cuda.synchronize()
+    ptot = int(pr[-1].item())
+    add("quantize_rhs_grouped (8 experts, ragged counts)", [Tm, Di], a,
+        2 * Tm * Di + ptot * Di + 4 * (ptot // BLOCK) * Di, "GB/s")
+    del qTr, sr, pr
     del Am, Wm, dYm, qam, qwm, swm, qxTm, sxTm, qdyTm, sdyTm, cm, dwm
     torch.cuda.empty_cache()
 
