@@ -145,8 +145,7 @@ struct Operands {
     __amdgpu_buffer_rsrc_t a[kMSub], b_reg[2], b_dma[2], as, bs;
     uint32_t a_lane, b_lane, bdma_lane;
     uint32_t as_base[kMSub];  // geom::gen_ascale_base
-    uint32_t bs_base[kNSub];  // geom::gen_bscale_base (per-column scales)
-    uint32_t bs_partial;      // bit j: the lane's 4 columns of subtile j straddle column N
+    uint32_t bs_col;          // geom::gen_bscale_tile_base (per-column scales, staged in LDS)
     int64_t M, N;
 };
 
@@ -199,8 +198,11 @@ __device__ __forceinline__ void dma_b(u32x4* __restrict__ sb, const Operands& op
     }
 }
 
+// Scales of K-block kb: the lane's four A-row scales into registers; per column, the thread's one
+// tile-column scale (threads 0..127; the others read nothing useful and store nothing), which the
+// kernel stages in LDS; 128x128, the tile's one column-block scale.
 template <bool PER_COL>
-__device__ __forceinline__ void load_scales(float (&as)[kMSub], u32x4 (&bsv)[kNSub], float& bscal,
+__device__ __forceinline__ void load_scales(float (&as)[kMSub], float& bcol, float& bscal,
                                             const Operands& op, const float* __restrict__ b_s,
                                             int64_t bs_nb, int64_t bs_kb, int64_t kb, int tn) {
     const uint32_t acol = static_cast<uint32_t>(4 * kb * op.M);
@@ -208,20 +210,7 @@ __device__ __forceinline__ void load_scales(float (&as)[kMSub], u32x4 (&bsv)[kNS
     for (int i = 0; i < kMSub; ++i)
         as[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(op.as, op.as_base[i] + acol, 0, 0));
     if (PER_COL) {
-        const uint32_t brow = static_cast<uint32_t>(4 * kb * op.N);
-#pragma unroll
-        for (int j = 0; j < kNSub; ++j) {
-            if (op.bs_partial & (1u << j)) {  // the quad straddles column N: per-element loads
-                const int64_t n = op.bs_base[j] / 4;
-                u32x4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = (n + e < op.N) ? __builtin_amdgcn_raw_buffer_load_b32(op.bs, op.bs_base[j] + 4 * e + brow, 0, 0) : 0u;
-                bsv[j] = v;
-            } else {
-                bsv[j] = __builtin_amdgcn_raw_buffer_load_b128(op.bs, op.bs_base[j] + brow, 0, 0);
-            }
-        }
+        bcol = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(op.bs, op.bs_col + static_cast<uint32_t>(4 * kb * op.N), 0, 0));
     } else {
         // the tile's one 128-column block (tiles exist only for columns below N)
         bscal = b_s[static_cast<int64_t>(tn) * bs_nb + kb * bs_kb];
@@ -235,6 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc,
     int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
     __shared__ u32x4 sB[2][kBN * 8];
+    __shared__ float sBS[2][kBN];  // per-column B scales of the two K-blocks in flight
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -269,13 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
         op.bdma_lane = geom::gen_bdma_lane(wave, lane, ldb);
 #pragma unroll
         for (int i = 0; i < kMSub; ++i) op.as_base[i] = geom::gen_ascale_base(m0, wm, i, lane, M);
-        op.bs_partial = 0u;
-#pragma unroll
-        for (int j = 0; j < kNSub; ++j) {
-            const int64_t n = geom::gen_col(n0, wn, j, lane);
-            op.bs_base[j] = geom::gen_bscale_base(n, N);
-            if (geom::gen_bscale_straddles(n, N)) op.bs_partial |= 1u << j;
-        }
+        op.bs_col = geom::gen_bscale_tile_base(n0, N, tid);
         op.M = M;
         op.N = N;
     }
@@ -289,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     if (Kb > 0) {
         v8i af[2][kMSub];
         float as[2][kMSub];
-        u32x4 bsv[2][kNSub];
+        float bcol[2];
         float bscal[2];
 
         // prologue: B(0) -> LDS[0]; A(0) and scales(0) -> registers
@@ -302,7 +286,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
             store_b(sB[0], bst, tid);
             load_a<false>(af[0], op, 0, K, lane);
         }
-        load_scales<PER_COL>(as[0], bsv[0], bscal[0], op, b_s, bs_nb, bs_kb, 0, tn);
+        load_scales<PER_COL>(as[0], bcol[0], bscal[0], op, b_s, bs_nb, bs_kb, 0, tn);
+        if (PER_COL && tid < kBN) sBS[0][tid] = bcol[0];
         __syncthreads();
 
         // One K-block; the buffer index is a compile-time constant so every register array stays
@@ -321,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                     } else {
                         load_a<false>(af[nxt], op, kb + 1, K, lane);
                     }
-                    load_scales<PER_COL>(as[nxt], bsv[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, tn);
+                    load_scales<PER_COL>(as[nxt], bcol[nxt], bscal[nxt], op, b_s, bs_nb, bs_kb, kb + 1, tn);
                 }
             };
             // the next block's loads are issued once this block's A codes are all widened (half
@@ -366,13 +351,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                     if (j > 0) asm volatile("" ::: "memory");
                     h8v bc[4];
                     fnuz_frag_to_f16(read_bf(j), bc);
+                    // per column: the scales of the lane's four columns of subtile j
+                    const v4f bsj = PER_COL ? *reinterpret_cast<const v4f*>(&sBS[cur][kWN * wn + 16 * j + 4 * lg])
+                                            : v4f{1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
                     for (int i = 0; i < kHalf; ++i) {
                         const v4f p = mfma_f16_kblock(bc, ac[i]);
                         const int ii = h * kHalf + i;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float fe = PER_COL ? f[ii] * __uint_as_float(bsv[cur][j][e]) : f[ii];
+                            const float fe = PER_COL ? f[ii] * bsj[e] : f[ii];
                             acc[ii][j][e] = fmaf(p[e], fe, acc[ii][j][e]);
                         }
                     }
@@ -383,6 +371,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
                 load_b_tail(bst, op, kb + 1, K, tid);
                 store_b(sB[nxt], bst, tid);
             }
+            // the next block's per-column scales (sBS[nxt] was last read in the previous step)
+            if (PER_COL && more && tid < kBN) sBS[nxt][tid] = bcol[nxt];
             __syncthreads();
         };
         for (int64_t kb = 0; kb < Kb; kb += 2) {

@@ -190,12 +190,14 @@ BSFP8_HD uint32_t gen_ascale_base(int64_t m0, int wm, int i, int lane, int64_t M
     const int64_t m = m0 + gen_a_row(wm, i, lane);
     return m < M ? static_cast<uint32_t>(4 * m) : kOob;
 }
-// Per-column B scales of subtile j: columns n .. n + 3 with n = n0 + 64 wn + 16 j + 4 (lane / 16):
-// base 4 n (kOob for n >= N), advance 4 kb N; a quad that straddles N is read element by element,
-// only below N.
+// Output columns n .. n + 3 of subtile j: n = n0 + 64 wn + 16 j + 4 (lane / 16).
 BSFP8_HD int64_t gen_col(int64_t n0, int wn, int j, int lane) { return n0 + 64 * wn + 16 * j + 4 * (lane >> 4); }
-BSFP8_HD uint32_t gen_bscale_base(int64_t n, int64_t N) { return n < N ? static_cast<uint32_t>(4 * n) : kOob; }
-BSFP8_HD bool gen_bscale_straddles(int64_t n, int64_t N) { return n < N && n + 4 > N; }
+// Per-column B scales of a K-block, staged in LDS: thread tid < 128 loads the scale of tile column
+// tid (LDS float tid), base 4 (n0 + tid), kOob for the other threads and for columns >= N; advance
+// 4 kb N.
+BSFP8_HD uint32_t gen_bscale_tile_base(int64_t n0, int64_t N, int tid) {
+    return (tid < kGenBN && n0 + tid < N) ? static_cast<uint32_t>(4 * (n0 + tid)) : kOob;
+}
 
 // ---------------------------------------------------------------------------------------------
 // Quantizer scale stores. Each function gives the scale element a thread writes and whether it

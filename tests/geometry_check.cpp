@@ -248,7 +248,7 @@ static bool check_gen(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
             const int64_t arows = M - m0 < kGenBM ? M - m0 : kGenBM;
             const int64_t brows = N - n0 < kGenBN ? N - n0 : kGenBN;
             for (int64_t kb = 0; kb < Kb; ++kb) {
-                std::vector<uint8_t> ga(2 * 256 * 8, 0), gb(128 * 8, 0), gbd(128 * 8, 0);  // A: once per column half (wave % 2)
+                std::vector<uint8_t> ga(2 * 256 * 8, 0), gb(128 * 8, 0), gbd(128 * 8, 0), gbs(128, 0);  // A: once per column half (wave % 2)
                 for (int wave = 0; wave < 8; ++wave)
                     for (int lane = 0; lane < 64; ++lane) {
                         bool ok;
@@ -281,26 +281,18 @@ static bool check_gen(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
                             CHECK(in == (m < M), "gen a_s row %lld", (long long)m);
                             if (in) CHECK(static_cast<int64_t>(off) == 4 * (kb * M + m), "gen a_s address");
                         }
-                        // per-column B scales
-                        for (int j = 0; j < 4; ++j) {
-                            const int64_t n = gen_col(n0, wave & 1, j, lane);
-                            const uint32_t base = gen_bscale_base(n, N);
-                            if (gen_bscale_straddles(n, N)) {
-                                for (int e = 0; e < 4; ++e) {
-                                    if (n + e >= N) continue;  // not read
-                                    const uint64_t off = static_cast<uint64_t>(base) + 4 * e + 4 * kb * N;
-                                    const bool in = access(off, 4 * N * Kb, 4, ok);
-                                    CHECK(ok && in && static_cast<int64_t>(off) == 4 * (kb * N + n + e), "gen b_s element");
-                                }
+                        // per-column B scales: one per thread of the first 128, staged in LDS
+                        {
+                            const int tid = 64 * wave + lane;
+                            const uint64_t off = static_cast<uint64_t>(gen_bscale_tile_base(n0, N, tid)) + 4 * kb * N;
+                            const bool in = access(off, 4 * N * Kb, 4, ok);
+                            CHECK(ok, "gen b_s offset");
+                            const int64_t n = n0 + tid;
+                            if (tid < kGenBN && n < N) {
+                                CHECK(in && static_cast<int64_t>(off) == 4 * (kb * N + n), "gen b_s[%lld, %lld] address", (long long)kb, (long long)n);
+                                ++gbs[tid];
                             } else {
-                                const uint64_t off = static_cast<uint64_t>(base) + 4 * kb * N;
-                                const bool in = access(off, 4 * N * Kb, 16, ok);
-                                CHECK(off < (1ull << 32) && off % 4 == 0, "gen b_s quad offset");
-                                if (n < N) {
-                                    CHECK(in && static_cast<int64_t>(off) + 16 <= 4 * N * Kb, "gen b_s quad in range");
-                                } else {
-                                    CHECK(static_cast<int64_t>(off) >= 4 * N * Kb, "gen b_s column %lld >= N read", (long long)n);
-                                }
+                                CHECK(!in, "gen b_s thread %d (column %lld) read", tid, (long long)n);
                             }
                         }
                         // B through registers (partial K-block) and straight into LDS
@@ -334,11 +326,13 @@ static bool check_gen(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb)
                 for (int r = 0; r < arows; ++r)
                     for (int c = 0; c < 8; ++c)
                         if (kb * kBlockK + 16 * c < K) CHECK(ga[r * 8 + c] == 1 && ga[2048 + r * 8 + c] == 1, "gen A row %d chunk %d", r, c);
-                for (int r = 0; r < brows; ++r)
+                for (int r = 0; r < brows; ++r) {
                     for (int c = 0; c < 8; ++c) {
                         if (kb * kBlockK + 16 * c < K) CHECK(gb[r * 8 + c] == 1, "gen B row %d chunk %d", r, c);
                         if ((kb + 1) * kBlockK <= K) CHECK(gbd[r * 8 + c] == 1, "gen B DMA row %d chunk %d", r, c);
                     }
+                    CHECK(gbs[r] == 1, "gen b_s column %lld not loaded once", (long long)(n0 + r));
+                }
             }
             for (int wave = 0; wave < 8; ++wave)
                 for (int i = 0; i < 4; ++i)
