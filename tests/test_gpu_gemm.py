@@ -213,16 +213,16 @@ def test_forward_small_workloads_full(idx):
                          ids=lambda r: "x".join(str(int(v)) for v in r[:3]))
 def test_sqnr_at_pages_table_shapes(row):
     """The GPU path at every shape of the ROCm page's GEMM-correctness table (SQNR 28.6-28.8 dB
-    against a BF16 matmul): within the table's band of the printed value (1.2 dB for the tiny M = 2,
-    4 outputs, 0.3 dB otherwise, as for the oracle path) and within 0.05 dB of the oracle path on
-    the same inputs (A ~ N(0,1), W ~ N(0, 0.02^2), seed 0)."""
+    against a BF16 matmul): at least 28 dB, within the table's band of the printed value (1.2 dB
+    for the tiny M = 2, 4 outputs, 0.3 dB otherwise, as for the oracle path) and within 0.05 dB of
+    the oracle path on the same inputs (A ~ N(0,1), W ~ N(0, 0.02^2), seed 0)."""
     M, N, K, db = int(row[0]), int(row[1]), int(row[2]), row[3]
     g = inputs.rng(0)
     a_h = inputs.normal_bf16(g, (M, K))
     w_h = inputs.normal_bf16(g, (N, K), 0.02)
     rows = np.arange(M) if M <= 128 else np.linspace(0, M - 1, 64).astype(np.int64)
     band = 1.2 if M * N < 100000 else 0.3
-    s_gpu, _ = _forward_check(a_h, w_h, rows, sqnr_min=db - band)
+    s_gpu, _ = _forward_check(a_h, w_h, rows, sqnr_min=max(28.0, db - band))  # never below 28 dB
     assert abs(s_gpu - db) <= band, s_gpu
 
 
