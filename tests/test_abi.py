@@ -129,13 +129,26 @@ def test_gemms_reject_bad_arguments(L):
     assert L.encode_e4m3_f32(odd, P, 16, None) == 2
 
 
-def test_gemms_reject_sizes_past_32bit_offsets(L):
+def test_gemm_size_limits_at_2_31(L):
+    """Every operand and scale read goes through a buffer resource of at most 2^31 bytes: the
+    largest admissible sizes pass validation (status 3 or 4 here: no GPU), one step past them is
+    EINVAL before any HIP call."""
     g, h = L.gemm_1x128_128x128, L.gemm_1x128_128x1
-    big_ld = (2**32) // 256 + 16                       # 256 rows of the operand exceed 2^32 bytes
-    assert g(P, big_ld, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1
-    assert g(P, 128, P, P, big_ld, P, 1, 1, P, 64, 4, 64, 128, None) == 1
-    assert g(P, 128, P, P, 128, P, 1, 1, P, 64, 2**30, 64, 128, None) == 1   # 4 M Kb >= 2^32
-    assert h(P, 128, P, P, 128, P, P, 2**30, 4, 2**30, 128, None) == 1     # 4 N Kb >= 2^32
+    passed = lambda rc: rc not in (1, 2)                 # noqa: E731
+    ld = 2 ** 31 // 256                                  # 256 rows of ld bytes: exactly 2^31
+    assert passed(g(P, ld, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None))
+    assert g(P, ld + 16, P, P, 128, P, 1, 1, P, 64, 4, 64, 128, None) == 1
+    assert g(P, 128, P, P, ld + 16, P, 1, 1, P, 64, 4, 64, 128, None) == 1
+    M = 65535 * 128                                      # the most rows the grid takes
+    assert passed(g(P, 8192, P, P, 8192, P, 64, 1, P, 64, M, 64, 8192, None))   # 4 M Kb < 2^31
+    assert g(P, 8320, P, P, 8320, P, 65, 1, P, 64, M, 64, 8320, None) == 1      # 4 M Kb > 2^31
+    assert g(P, 128, P, P, 128, P, 1, 1, P, 64, M + 128, 64, 128, None) == 1    # ceil(M/128) > 65535
+    N = 2 ** 24
+    assert passed(h(P, 4096, P, P, 4096, P, P, N, 4, N, 4096, None))            # 4 N Kb = 2^31
+    assert h(P, 4224, P, P, 4224, P, P, N, 4, N, 4224, None) == 1               # 4 N Kb > 2^31
+    # 128x128 B scales: the floats the strides span, times 4, at most 2^31
+    assert passed(g(P, 128, P, P, 128, P, 2 ** 29 - 1, 1, P, 256, 4, 256, 128, None))
+    assert g(P, 128, P, P, 128, P, 2 ** 29, 1, P, 256, 4, 256, 128, None) == 1
 
 
 def test_fnuz_variants_validate_like_their_e4m3fn_twins(L):

@@ -369,3 +369,28 @@ def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):
     a_h = inputs.normal_bf16(g, (M, K))
     w_h = inputs.normal_bf16(g, (N, K), 0.02)
     _forward_check(a_h, w_h, np.arange(M), sqnr_min=27.5)
+
+
+@pytest.mark.parametrize("bm", [256, 128], ids=["tile256", "tile128"])
+def test_gemm_operand_row_stride_at_the_limit(bm, monkeypatch):
+    """Operand rows 2^23 bytes apart, the largest stride the GEMMs accept (256 rows of a tile then
+    span exactly 2^31 bytes, the size of a buffer resource): ragged M and N against the oracle."""
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", str(bm))
+    monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
+    M, N, K, ld = 200, 300, 256, 2 ** 23
+    g = np.random.Generator(np.random.PCG64(62))
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    ah, bh = g.choice(finite, size=(M, K)), g.choice(finite, size=(N, K))
+    a = torch.zeros((M, ld), dtype=torch.uint8, device=DEV)
+    b = torch.zeros((N, ld), dtype=torch.uint8, device=DEV)
+    a[:, :K] = torch.from_numpy(ah).to(DEV)
+    b[:, :K] = torch.from_numpy(bh).to(DEV)
+    Kb = _cdiv(K, 128)
+    a_s, b_s = _scales((Kb, M), 63), _scales((_cdiv(N, 128), Kb), 64)
+    got = _run_guarded(lambda c: bf.gemm_1x128_128x128(a[:, :K], to_dev(a_s), b[:, :K], to_dev(b_s), Kb, 1, c=c),
+                       M, N, N)
+    co = oracle.gemm_1x128_128x128(ah, a_s, bh, b_s, Kb, 1)
+    c_abs = oracle.gemm_1x128_128x128(_abs_codes(ah), a_s, _abs_codes(bh), b_s, Kb, 1)
+    _assert_dot_bound(got, co, c_abs, "row stride 2^23")
+    del a, b
+    torch.cuda.empty_cache()
