@@ -394,3 +394,29 @@ def test_gemm_operand_row_stride_at_the_limit(bm, monkeypatch):
     _assert_dot_bound(got, co, c_abs, "row stride 2^23")
     del a, b
     torch.cuda.empty_cache()
+
+
+def test_split_gemms_on_two_streams_concurrently(monkeypatch):
+    """The split-K workspace comes from a stream-ordered pool: split GEMMs enqueued on two streams
+    at once get separate workspaces, and every result equals the same call made alone."""
+    monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
+    monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
+    shapes = [(128, 4096, 4096), (64, 2048, 3072)]
+    ops, ref = [], []
+    for i, (M, N, K) in enumerate(shapes):
+        qa, sa, qb, sb, *_ = _quantized_operands(M, N, K, K, 70 + i, False)
+        ops.append((qa, sa, qb, sb))
+        ref.append(bf.gemm_1x128_128x128(qa, sa, qb, sb))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(r) for _ in range(6)] for r in ref]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(6):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                bf.gemm_1x128_128x128(*ops[i], c=outs[i][rep], stream=s)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        for rep in range(6):
+            assert torch.equal(outs[i][rep].view(torch.int16), ref[i].view(torch.int16)), (i, rep)
