@@ -530,9 +530,9 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     del Am, Wm, dYm, qam, qwm, swm, qxTm, sxTm, qdyTm, sdyTm, cm, dwm
     torch.cuda.empty_cache()
 
-    # tail-masking workload (130 x 5120 x 1280): the GEMM has 40 output tiles for 256 CUs and a few
-    # MB of data, so it is occupancy-bound and served from cache; reported for completeness (its
-    # quantizers finish faster than one launch from Python, so timing them here would time the host)
+    # tail-masking workload (130 x 5120 x 1280): a few MB of data in 64 x 32 tiles of the thin kernel
+    # (480 workgroups), served from cache; reported for completeness (its quantizers finish faster
+    # than one launch from Python, so timing them here would time the host)
     d1 = inputs.make_workload(1)
     A1, W1 = dev_bf16(d1["A"]), dev_bf16(d1["W"])
     M1 = d1["A"].shape[0]
@@ -573,7 +573,7 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
     # the forward GEMM at every shape of the ROCm page's performance table (its FP8 Triton GEMM on
     # MI300X, printed there as context: another chip, not a target). Operands from N(0,1) / N(0,
     # 0.02^2) bf16 through the quantizers, copied into enough rotating sets to exceed the 256 MB
-    # last-level cache (at most 32 sets); shapes with few output tiles take the split-K schedule.
+    # last-level cache (at most 32 sets); shapes with few rows take the thin kernel's 64-row tiles.
     g8 = np.random.Generator(np.random.PCG64(8))
     for (Mp, Np, Kp, page_tflops) in PAGES_GEMM_TABLE:
         ap = dev_bf16(inputs.normal_bf16(g8, (Mp, Kp)))
@@ -600,8 +600,8 @@ def kernel_rows(bf, inputs, dev_bf16, dev, stream, torch, reps=32, nsets=4):
         del ops
         torch.cuda.empty_cache()
 
-    # the smallest workload (2 x 512 x 128: one K-block, two output tiles): host-launch-bound, so
-    # it is timed like the others but only shows the launch floor
+    # the smallest workload (2 x 512 x 128: one K-block, 16 thin tiles): host-launch-bound, so it
+    # is timed like the others but only shows the launch floor
     d0 = inputs.make_workload(0)
     A0, W0 = dev_bf16(d0["A"]), dev_bf16(d0["W"])
     qa_0, sa_0, qw_0, _, sw_0 = bf.quantize_lhs_and_weight(A0, W0)

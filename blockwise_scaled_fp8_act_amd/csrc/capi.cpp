@@ -110,8 +110,9 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// BSFP8_GEMM_SPLIT and BSFP8_GEMM_TILE_M (environment, read at each call): a slice count (1 =
-// never split) and a tile height (256 or 128) that replace the automatic choices of
+// BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M and BSFP8_GEMM_TILE_N (environment, read at each call): a
+// slice count (1 = never split), a tile height (256 or 128: the fast kernel; 64: the thin kernel)
+// and the thin kernel's tile width (32, 64 or 128) that replace the automatic choices of
 // gemm_split_plan, so tests and benchmarks can run every schedule on any shape. Unset or empty:
 // automatic.
 int env_int(const char* name) {
@@ -129,9 +130,11 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
              bool use_scratch, hipStream_t stream) {
     const int cus = bsfp8::device_cus();
     const int forced_s = env_int("BSFP8_GEMM_SPLIT"), forced_bm = env_int("BSFP8_GEMM_TILE_M");
+    const int forced_bn = env_int("BSFP8_GEMM_TILE_N");
     const bsfp8::SplitPlan plan =
-        forced_s || forced_bm ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, cus, forced_s, forced_bm, kMaxSplitWorkspace)
-                              : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+        forced_s || forced_bm || forced_bn
+            ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, cus, forced_s, forced_bm, forced_bn, kMaxSplitWorkspace)
+            : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
     if (use_scratch) {
         if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
         float* ws = nullptr;

@@ -958,6 +958,188 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 }  // namespace fast
 
+// ==============================================================================================
+// Thin kernel: 64 x BN tiles (BN = 32, 64 or 128) of 4 waves (2 x 2, each 32 x BN/2), for problems
+// whose 128-row tiles of the fast kernel would leave compute units idle (few rows: the short-and-
+// wide GEMMs). Such a problem is bound by moving operands into the CUs, not by the matrix cores, so
+// it takes more, smaller tiles (several workgroups per CU), every one over the whole K range: no
+// partial tiles to sum. Each K-block's A and B rows go global -> LDS by the fast kernel's direct
+// loads and LDS swizzle, STAGES - 1 blocks ahead of the one being multiplied (one workgroup barrier
+// per K-block); a wave multiplies its 2 x BN/32 subtiles and rescales each partial into its totals
+// exactly as the fast kernel does, so the two kernels give bit-identical results.
+namespace thin {
+
+constexpr int kThreads = 64 * geom::kThinWaves;
+
+template <int BN, bool PER_COL>
+struct TCfg {
+    static constexpr int kMS = 2;        // 16-row subtiles per wave
+    static constexpr int kNS = BN / 32;  // 16-column subtiles per wave
+    static constexpr int kLoads = (geom::kThinBM + BN) / 32;
+    // LDS image of one stage (16-byte units): A rows 0..63, B rows 0..BN-1, the 64 A scales, the B
+    // scales (per column: BN floats; 128x128: one float)
+    static constexpr int kStageA = 0;
+    static constexpr int kStageB = geom::kThinBM * 8;
+    static constexpr int kStageSA = kStageB + BN * 8;
+    static constexpr int kStageSB = kStageSA + geom::kThinBM / 4;
+    static constexpr int kStageSize = kStageSB + (PER_COL ? BN / 4 : 1);
+};
+
+// Wait until this wave's loads of the block being multiplied have landed: `later` (0..2) blocks
+// issued after it are still allowed in flight, L instructions each.
+template <int L>
+__device__ __forceinline__ void wait_block(int64_t later) {
+    if (later >= 2) fast::wait_own_loads<2 * L>();
+    else if (later == 1) fast::wait_own_loads<L>();
+    else fast::wait_own_loads<0>();
+}
+
+template <bool PER_COL, int BN, int STAGES>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
+    int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C,
+    int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
+    static_assert(STAGES >= 2 && STAGES <= 4, "wait_block covers at most two blocks in flight");
+    using T = TCfg<BN, PER_COL>;
+    constexpr int kMS = T::kMS, kNS = T::kNS, kLoads = T::kLoads;
+    __shared__ u32x4 smem[STAGES * T::kStageSize];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;   // rows 32 wm .. of the tile
+    const int wn = wave >> 1;  // columns (BN / 2) wn .. of the tile
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    int tm, tn;
+    geom::tile_of(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * geom::kThinBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
+    const int64_t Kb = (K + kGroup - 1) / kGroup;
+
+    const int64_t arows = (M - m0) < geom::kThinBM ? (M - m0) : geom::kThinBM;
+    const int64_t brows = (N - n0) < BN ? (N - n0) : BN;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + m0 * lda, geom::thin_operand_range(arows, lda));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + n0 * ldb, geom::thin_operand_range(brows, ldb));
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_s, M * Kb * 4);
+    const __amdgpu_buffer_rsrc_t rbs =
+        make_rsrc(b_s, PER_COL ? N * Kb * 4 : 4 * geom::bscale_blk_extent(N, Kb, bs_nb, bs_kb));
+    uint32_t lane_off[kLoads];
+#pragma unroll
+    for (int p = 0; p < kLoads; ++p)
+        lane_off[p] = geom::thin_operand_lane(geom::thin_group(BN, wave, p), lane,
+                                              geom::thin_load_is_a(BN, wave, p) ? lda : ldb);
+    const bool b_scales = geom::thin_has_bscale_load(BN, PER_COL, wave);
+    const uint32_t as_base = geom::thin_ascale_base(m0, M, lane);
+    const uint32_t bs_base = PER_COL ? geom::thin_bscale_col_base(BN, n0, N, wave, lane)
+                                     : geom::thin_bscale_blk_base(n0, bs_nb, lane);
+    const int64_t bs_step = PER_COL ? 4 * N : 4 * bs_kb;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)));
+    const uint64_t bs_lanes = geom::thin_bscale_lanes(BN, PER_COL);
+
+    // K-block kb into stage s: the wave's operand groups, then its scale load (wave 0: A scales;
+    // waves 3 and, per column at BN = 128, 2: B scales)
+    auto issue = [&](int64_t kb, int s) {
+        const uint32_t base = lds0 + static_cast<uint32_t>(s * T::kStageSize * 16);
+        const uint32_t adv = geom::fast_operand_advance(kb);
+#pragma unroll
+        for (int p = 0; p < kLoads; ++p)
+            fast::dma16(base + geom::thin_load_unit(BN, wave, p) * 16, geom::thin_load_is_a(BN, wave, p) ? ra : rb,
+                        lane_off[p] + adv, ~0ull);
+        if (wave == 0)
+            fast::dma4(base + T::kStageSA * 16, ras, as_base + geom::fast_ascale_advance(kb, M), ~0ull);
+        else if (b_scales)
+            fast::dma4(base + T::kStageSB * 16 + (wave == 2 ? 256 : 0), rbs,
+                       bs_base + static_cast<uint32_t>(kb * bs_step), bs_lanes);
+    };
+
+    v4f acc[kMS][kNS];
+#pragma unroll
+    for (int i = 0; i < kMS; ++i)
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Fragment lane (l16, lg) holds 16-byte chunks lg and lg + 4 of its row, as in the fast kernel;
+    // the bytes of a partial last K-block at and past K are zeroed in the fragment registers.
+    const int sw = geom::lds_swizzle(l16);
+    const int pos_lo = lg ^ sw;
+    const int pos_hi = (lg + 4) ^ sw;
+    const int krem = static_cast<int>(K - (Kb - 1) * kGroup);
+    const bool scale_wave = wave == 0 || b_scales;
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < Kb) issue(s, s);
+
+    for (int64_t kb = 0; kb < Kb; ++kb) {
+        // block kb has landed for every wave; no wave reads the stage of block kb - 1 any more
+        const int64_t later = min(static_cast<int64_t>(STAGES - 2), Kb - 1 - kb);
+        if (scale_wave) wait_block<kLoads + 1>(later);
+        else wait_block<kLoads>(later);
+        fast::lds_barrier();
+        if (kb + STAGES - 1 < Kb) issue(kb + STAGES - 1, static_cast<int>((kb + STAGES - 1) % STAGES));
+
+        const u32x4* st = smem + static_cast<int>(kb % STAGES) * T::kStageSize;
+        const bool tail = kb == Kb - 1 && krem != kGroup;
+        auto frag = [&](int unit) {
+            v8i v = to_v8i(st[unit + pos_lo], st[unit + pos_hi]);
+            if (tail) {
+#pragma unroll
+                for (int d = 0; d < 8; ++d) v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & geom::tail_keep_mask(krem, lg, d));
+            }
+            return v;
+        };
+        v8i af[kMS], bf[kNS];
+        float fa[kMS];
+        const float* sa = reinterpret_cast<const float*>(st + T::kStageSA);
+        const float* sb = reinterpret_cast<const float*>(st + T::kStageSB);
+#pragma unroll
+        for (int i = 0; i < kMS; ++i) {
+            const int r = 32 * wm + 16 * i + l16;
+            af[i] = frag(T::kStageA + r * 8);
+            fa[i] = PER_COL ? sa[r] : sa[r] * sb[0];
+        }
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) bf[j] = frag(T::kStageB + ((BN / 2) * wn + 16 * j + l16) * 8);
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) {
+            const v4f bsj = PER_COL ? *reinterpret_cast<const v4f*>(sb + (BN / 2) * wn + 16 * j + 4 * lg)
+                                    : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+#pragma unroll
+            for (int i = 0; i < kMS; ++i) {
+                const v4f p = mfma_fp8_16x16x128(bf[j], af[i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[i][j][e] = fmaf(p[e], PER_COL ? fa[i] * bsj[e] : fa[i], acc[i][j][e]);
+            }
+        }
+    }
+
+    // bf16 outputs straight from the totals: a lane's four consecutive columns of one row
+#pragma unroll
+    for (int i = 0; i < kMS; ++i) {
+        const int64_t m = geom::thin_store_row(m0, wm, i, lane);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) {
+            const int64_t n = geom::thin_store_col(n0, BN, wn, j, lane);
+            uint16_t* dst = C + m * ldc + n;
+            const uint32_t w0 = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            const uint32_t w1 = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            if (c_vec && n + 4 <= N) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            } else {
+                const uint32_t w[2] = {w0, w1};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    }
+}
+
+}  // namespace thin
+
 }  // namespace
 
 // Scratch of the allocation-free GEMM entry point: the split-K partial tiles, in a file-scope device
@@ -990,27 +1172,42 @@ hipError_t gemm_scratch(float** out) {
     return hipSuccess;
 }
 
-// Tile height and K split, from measurements on MI355X (256 CUs; back-to-back launches, settled
-// clock). 256-row tiles (8 waves, two per SIMD) run the K-loop fastest, so they are kept whenever
-// they give every CU a tile; a problem with fewer 256-row tiles than half the CUs takes 128-row
-// tiles (4 waves, one per SIMD; twice the tiles), as does any M <= 128, whose 256-row tile would be
-// at least half empty. A K split then costs its fp32 partial tiles (written, then read by the sum)
-// and a second launch, so it pays only when the tiles still leave most CUs idle and K is long. The
-// slices always fit in one round of workgroups.
-SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
-    SplitPlan plan{1, 0, 0, fast::kBM};
-    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
-    const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
-    const int64_t tiles256 = ((M + fast::kBM - 1) / fast::kBM) * nt;
-    if (M <= fast::kBMSmall || 2 * tiles256 <= cus) plan.bm = fast::kBMSmall;
-    const int64_t tiles = ((M + plan.bm - 1) / plan.bm) * nt;
-    const int64_t Kb = (K + kGroup - 1) / kGroup;
-    if (M > 512 || 4 * tiles > cus) return plan;
+// Schedule, from measurements on MI355X (256 CUs; back-to-back launches, settled clock). 256-row
+// tiles (8 waves, two per SIMD) run the K-loop fastest, so they are kept whenever they give every
+// CU a tile; a problem with fewer 256-row tiles than half the CUs takes 128-row tiles (4 waves, one
+// per SIMD; twice the tiles), as does any M <= 128, whose 256-row tile would be at least half empty.
+// When even the 128-row tiles leave CUs idle, the problem is bound by moving operands into the CUs
+// and takes the thin kernel's 64-row tiles, the widest (128, 64 or 32 columns) that still give two
+// workgroups per CU. Only when those are few and K is long does K get split instead: S workgroups
+// per 128- or 256-row tile, whose fp32 partial tiles (written, then read by the sum) and second
+// launch pay off when the tiles leave most CUs idle. The slices always fit in one round.
+namespace {
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The fast kernel's tile height for M x N.
+int fast_bm(int64_t M, int64_t N, int cus) {
+    const int64_t tiles256 = cdiv64(M, fast::kBM) * cdiv64(N, fast::kBN);
+    return (M <= fast::kBMSmall || 2 * tiles256 <= cus) ? fast::kBMSmall : fast::kBM;
+}
+
+// The thin kernel's tile width for M x N.
+int thin_bn(int64_t M, int64_t N, int cus) {
+    for (const int bn : {128, 64})
+        if (cdiv64(M, geom::kThinBM) * cdiv64(N, bn) >= 2 * static_cast<int64_t>(cus)) return bn;
+    return 32;
+}
+
+// The automatic K split of the fast kernel's tiles of height plan.bm.
+void fast_split(SplitPlan& plan, int64_t M, int64_t N, int64_t K, int cus, int64_t max_bytes) {
+    const int64_t tiles = cdiv64(M, plan.bm) * cdiv64(N, fast::kBN);
+    const int64_t Kb = cdiv64(K, kGroup);
+    if (M > 512 || 4 * tiles > cus) return;
     int64_t S = cus / tiles;  // one round of workgroups
     if (M <= 64) {
         if (S > Kb) S = Kb;
     } else {
-        if (Kb <= 10) return plan;  // short K: the slice overhead outweighs the idle CUs
+        if (Kb <= 10) return;  // short K: the slice overhead outweighs the idle CUs
         if (S > Kb / 2) S = Kb / 2;
         if (S > (M <= 256 ? 12 : 4)) S = M <= 256 ? 12 : 4;
     }
@@ -1018,25 +1215,53 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, i
     const int64_t slice_bytes = M * ldp * 4;
     if (S * slice_bytes > max_bytes) S = max_bytes / slice_bytes;
     if (S > 65535) S = 65535;
-    if (S < 2) return plan;
+    if (S < 2) return;
     plan.S = static_cast<int>(S);
     plan.ldp = ldp;
     plan.bytes = S * slice_bytes;
+}
+
+}  // namespace
+
+SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
+    SplitPlan plan{1, 0, 0, fast::kBM, 0};
+    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    plan.bm = fast_bm(M, N, cus);
+    if (cdiv64(M, fast::kBMSmall) * cdiv64(N, fast::kBN) < cus) {
+        const int bn = thin_bn(M, N, cus);
+        const int64_t wgs = cdiv64(M, geom::kThinBM) * cdiv64(N, bn);
+        if (2 * wgs >= cus || cdiv64(K, kGroup) < 32) {
+            plan.bm = geom::kThinBM;
+            plan.bn = bn;
+            return plan;
+        }
+    }
+    fast_split(plan, M, N, K, cus, max_bytes);
     return plan;
 }
 
-// A slice count and tile height chosen by the caller: S clamped to the K-blocks and to the
-// workspace bound (fewer than two slices: no split); bm 0 keeps the automatic tile height.
-SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm,
+// A schedule chosen by the caller: bm 64 -- the thin kernel, with tile width bn (32, 64 or 128;
+// other values: the automatic width), never split; bm 256 or 128 -- the fast kernel with that tile
+// height and its automatic split; bm 0 -- the automatic schedule, whose thin width bn may be set.
+// S > 0 then sets the slice count (clamped to the K-blocks and to the workspace bound; fewer than
+// two: no split); a split runs on the fast kernel.
+SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm, int bn,
                                  int64_t max_bytes) {
     SplitPlan plan = gemm_split_plan(M, N, K, fnuz, cus, max_bytes);
     if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
-    if (bm == fast::kBM || bm == fast::kBMSmall) plan.bm = bm;
-    if (S <= 0) return plan;  // tile height only
+    const bool bn_ok = bn == 32 || bn == 64 || bn == 128;
+    if (bm == geom::kThinBM) return SplitPlan{1, 0, 0, geom::kThinBM, bn_ok ? bn : thin_bn(M, N, cus)};
+    if (bm == fast::kBM || bm == fast::kBMSmall || (S >= 2 && plan.bm == geom::kThinBM)) {
+        plan = SplitPlan{1, 0, 0, (bm == fast::kBM || bm == fast::kBMSmall) ? bm : fast_bm(M, N, cus), 0};
+        fast_split(plan, M, N, K, cus, max_bytes);
+    } else if (plan.bm == geom::kThinBM && bn_ok) {
+        plan.bn = bn;
+    }
+    if (S <= 0 || plan.bm == geom::kThinBM) return plan;
     plan.S = 1;
     plan.ldp = 0;
     plan.bytes = 0;
-    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    const int64_t Kb = cdiv64(K, kGroup);
     const int64_t ldp = (N + 7) / 8 * 8;
     const int64_t slice_bytes = M * ldp * 4;
     int64_t s = S > Kb ? Kb : S;
@@ -1096,6 +1321,26 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
     return hipGetLastError();
 }
 
+// The thin kernel with tile width BN (no split; every tile over the whole K range).
+template <int BN>
+hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
+                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    // three LDS stages at 128 columns (two workgroups per CU), four below
+    constexpr int kSt = BN == 128 ? 3 : 4;
+    const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
+    const int64_t nt = (N + BN - 1) / BN;
+    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    const dim3 grid(static_cast<unsigned>(mt * nt));
+    if (bs.per_column)
+        thin::gemm_kernel<true, BN, kSt><<<grid, thin::kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
+    else
+        thin::gemm_kernel<false, BN, kSt><<<grid, thin::kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
@@ -1103,6 +1348,11 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        int64_t K, bool fnuz, const SplitPlan& plan, float* workspace, int cus,
                        hipStream_t stream) {
     if (!fnuz) {
+        if (plan.bm == geom::kThinBM) {
+            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
+            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
+            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
+        }
         if (plan.bm == fast::kBMSmall)
             return launch_fast<fast::kBMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
         return launch_fast<fast::kBM>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);

@@ -148,6 +148,63 @@ BSFP8_HD int64_t fast_partial_col(int64_t n0, int wn, int j, int lane) { return 
 BSFP8_HD int64_t split_begin(int64_t Kb, int64_t S, int64_t s) { return Kb * s / S; }
 
 // ---------------------------------------------------------------------------------------------
+// Thin GEMM kernel (problems with few rows): 64 x bn tiles, bn = 32, 64 or 128, 4 waves; wave w owns
+// rows 32 (w % 2).. and columns (bn / 2) (w / 2).. of the tile. A K-block's tile is (64 + bn) rows
+// of 128 bytes (A rows 0..63, then B rows 0..bn-1), loaded in groups of 8 rows, one 16-byte chunk
+// per lane; the 8 + bn / 8 groups are dealt to the waves in order, thin_loads(bn) each. Each operand
+// is read through one resource that starts at the tile's first row and spans its in-range rows, so
+// a row past M or N is past the end of the resource.
+constexpr int kThinBM = 64;
+constexpr int kThinWaves = 4;
+BSFP8_HD int thin_loads(int bn) { return (kThinBM + bn) / 32; }
+// Load p (0 .. thin_loads(bn) - 1) of wave w: row group g = w thin_loads(bn) + p of the tile; A's
+// groups are 0..7, B's follow. thin_group: the group's index within its operand.
+BSFP8_HD bool thin_load_is_a(int bn, int wave, int p) { return wave * thin_loads(bn) + p < kThinBM / 8; }
+BSFP8_HD int thin_group(int bn, int wave, int p) {
+    const int g = wave * thin_loads(bn) + p;
+    return g < kThinBM / 8 ? g : g - kThinBM / 8;
+}
+// Lane l of a load of group gr: operand row 8 gr + l / 8, chunk (l % 8) ^ swz(row) (the LDS swizzle
+// of the fast kernel, lds_swizzle), landing at LDS unit (operand base) + 64 gr + l = row 8 + l % 8.
+BSFP8_HD int thin_operand_row(int gr, int lane) { return 8 * gr + (lane >> 3); }
+BSFP8_HD uint32_t thin_operand_lane(int gr, int lane, int64_t ld) {
+    return static_cast<uint32_t>(thin_operand_row(gr, lane) * ld + 16 * fast_operand_chunk(gr, lane));
+}
+BSFP8_HD int64_t thin_operand_range(int64_t rows_in_range, int64_t ld) { return rows_in_range > 0 ? rows_in_range * ld : 0; }
+// LDS unit (16 bytes) of lane 0 of the load, within a stage: A rows at 0, B rows at 64 * 8.
+BSFP8_HD int thin_load_unit(int bn, int wave, int p) {
+    return (thin_load_is_a(bn, wave, p) ? 0 : kThinBM * 8) + 64 * thin_group(bn, wave, p);
+}
+// Scale loads of a K-block: wave 0 loads the A scales of the tile's 64 rows (lane = tile row, LDS
+// float lane); the B scales come from wave 3 (per column: tile columns 0..63, LDS float = column;
+// 128x128: lane 0 alone, the scale of the tile's 128-column block) and, for the per-column scales
+// of a 128-column tile, from wave 2 (columns 64..127).
+BSFP8_HD uint32_t thin_ascale_base(int64_t m0, int64_t M, int lane) {
+    return m0 + lane < M ? static_cast<uint32_t>(4 * (m0 + lane)) : kOob;
+}
+BSFP8_HD bool thin_has_bscale_load(int bn, bool per_col, int wave) { return wave == 3 || (per_col && bn > 64 && wave == 2); }
+BSFP8_HD int thin_bscale_col(int wave, int lane) { return (wave == 2 ? 64 : 0) + lane; }
+BSFP8_HD uint32_t thin_bscale_col_base(int bn, int64_t n0, int64_t N, int wave, int lane) {
+    const int c = thin_bscale_col(wave, lane);
+    return (lane < bn && c < bn && n0 + c < N) ? static_cast<uint32_t>(4 * (n0 + c)) : kOob;
+}
+// Lanes switched on for a B-scale load (a direct load writes LDS for every active lane, in range or
+// not): per column, lanes 0 .. bn - 1 (at most 64); 128x128, lane 0.
+BSFP8_HD uint64_t thin_bscale_lanes(int bn, bool per_col) {
+    return !per_col ? 1ull : (bn >= 64 ? ~0ull : ((1ull << bn) - 1));
+}
+BSFP8_HD uint32_t thin_bscale_blk_base(int64_t n0, int64_t bs_nb, int lane) {
+    return lane == 0 ? static_cast<uint32_t>(4 * (n0 / kBlockK) * bs_nb) : kOob;
+}
+// Output of subtile (i, j) of wave (wm, wn): row 32 wm + 16 i + lane % 16 and columns
+// (bn / 2) wn + 16 j + 4 (lane / 16) .. + 4 of the tile; element n + e is stored iff the row is
+// below M and n + e < N.
+BSFP8_HD int64_t thin_store_row(int64_t m0, int wm, int i, int lane) { return m0 + 32 * wm + 16 * i + (lane & 15); }
+BSFP8_HD int64_t thin_store_col(int64_t n0, int bn, int wn, int j, int lane) {
+    return n0 + (bn / 2) * wn + 16 * j + 4 * (lane >> 4);
+}
+
+// ---------------------------------------------------------------------------------------------
 // General GEMM kernel (float8_e4m3fnuz operands): 256 x 128 tile, 8 waves (wm = wave / 2 owns rows
 // 64 wm.., wn = wave % 2 columns 64 wn..), operands read through buffer loads into registers.
 constexpr int kGenBM = 256;

@@ -41,21 +41,26 @@ struct BScale {
 // Compute units of the current device (cached per device after the first query).
 int device_cus();
 
-// Schedule of a GEMM: the fast kernel's tile height bm (256 or 128 rows), and the K split of a GEMM
-// whose output tiles cannot fill the chip: S workgroups per tile each multiply a range of K-blocks
-// into an fp32 partial tile (rows of ldp floats, ldp = N rounded up to 8), and a second kernel sums
-// the S partials into C. S == 1: no split. bytes: the fp32 workspace it needs.
+// Schedule of a GEMM: the tile height bm -- 256 or 128 rows (the fast kernel) or 64 (the thin
+// kernel, whose tiles are bn = 32, 64 or 128 columns wide; bn is 0 for the fast kernel's 256) --
+// and the K split of a fast-kernel GEMM whose output tiles cannot fill the chip: S workgroups per
+// tile each multiply a range of K-blocks into an fp32 partial tile (rows of ldp floats, ldp = N
+// rounded up to 8), and a second kernel sums the S partials into C. S == 1: no split. bytes: the
+// fp32 workspace it needs.
 struct SplitPlan {
     int S;
     int64_t ldp;
     int64_t bytes;
     int bm;
+    int bn;
 };
 SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes);
-// The automatic plan with the slice count S (> 0; clamped to the K-block count and to max_bytes of
-// workspace; below two: no split) and / or the tile height bm (256 or 128; other values keep the
-// automatic one) replaced, so tests and sweeps can run any schedule on any shape.
-SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm,
+// A schedule chosen by the caller, so tests and sweeps can run any schedule on any shape: bm 64 --
+// the thin kernel with tile width bn (32, 64 or 128; other values: automatic), never split; bm 256
+// or 128 -- the fast kernel with that tile height and its automatic split; bm 0 -- automatic (its
+// thin width may be set by bn). S > 0 sets the slice count (clamped to the K-block count and to
+// max_bytes of workspace; below two: no split); a split runs on the fast kernel.
+SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm, int bn,
                                  int64_t max_bytes);
 
 // The allocation-free GEMM's scratch: a device array of gemm_scratch_bytes() bytes per device;

@@ -13,7 +13,8 @@
 //   * the partial-K-block masks keep exactly the fragment bytes below K;
 //   * quantize_lhs stores each scale of the column-major [M, Kb] tensor exactly once and never a row
 //     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm").
-// Both tile heights of the fast kernel (256 rows, 8 waves; 128 rows, 4 waves) are enumerated.
+// Both tile heights of the fast kernel (256 rows, 8 waves; 128 rows, 4 waves) and the three tile
+// widths of the thin kernel (64 rows by 32, 64 or 128 columns, 4 waves) are enumerated.
 // Usage: geometry_check M N K [M N K ...]; prints one line per shape, exits 1 on the first failure.
 #include <cstdint>
 #include <cstdio>
@@ -236,6 +237,143 @@ static bool check_tail_masks() {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Thin kernel: 64 x bn tiles (bn = 32, 64, 128), 4 waves; every operand group, scale and output.
+static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bn) {
+    const int mt = static_cast<int>(cdiv(M, kThinBM)), nt = static_cast<int>(cdiv(N, bn));
+    const int64_t Kb = cdiv(K, kBlockK);
+    if (!check_tiles(mt, nt)) return false;
+    const int64_t Nb = cdiv(N, kBlockK);
+    const int64_t strides[2][2] = {{Kb, 1}, {1, Nb}};
+    // the row groups of a tile are dealt to the waves exactly once
+    {
+        std::vector<int> ga(kThinBM / 8, 0), gb(bn / 8, 0);
+        for (int wave = 0; wave < kThinWaves; ++wave)
+            for (int p = 0; p < thin_loads(bn); ++p) {
+                const int gr = thin_group(bn, wave, p);
+                if (thin_load_is_a(bn, wave, p)) {
+                    CHECK(gr >= 0 && gr < kThinBM / 8, "A group %d", gr);
+                    ++ga[gr];
+                } else {
+                    CHECK(gr >= 0 && gr < bn / 8, "B group %d", gr);
+                    ++gb[gr];
+                }
+            }
+        for (int g : ga) CHECK(g == 1, "A group dealt %d times", g);
+        for (int g : gb) CHECK(g == 1, "B group dealt %d times", g);
+    }
+    std::vector<uint8_t> stored(static_cast<size_t>(M) * N, 0);
+    for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < nt; ++tn) {
+            const int64_t m0 = static_cast<int64_t>(tm) * kThinBM, n0 = static_cast<int64_t>(tn) * bn;
+            const int64_t arows = M - m0 < kThinBM ? M - m0 : kThinBM;
+            const int64_t brows = N - n0 < bn ? N - n0 : bn;
+            for (int64_t kb = 0; kb < Kb; ++kb) {
+                std::vector<uint8_t> got_a(kThinBM * 8, 0), got_b(static_cast<size_t>(bn) * 8, 0);
+                for (int wave = 0; wave < kThinWaves; ++wave)
+                    for (int p = 0; p < thin_loads(bn); ++p) {
+                        const bool is_a = thin_load_is_a(bn, wave, p);
+                        const int gr = thin_group(bn, wave, p);
+                        const int64_t rows = is_a ? arows : brows, ld = is_a ? lda : ldb;
+                        const int64_t r0 = is_a ? m0 : n0, total = is_a ? M : N;
+                        const int64_t range = thin_operand_range(rows, ld);
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const uint64_t off = static_cast<uint64_t>(thin_operand_lane(gr, lane, ld)) + fast_operand_advance(kb);
+                            bool ok;
+                            const bool in = access(off, range, 16, ok);
+                            CHECK(ok, "thin operand offset %llu (range %lld)", (unsigned long long)off, (long long)range);
+                            const int r = thin_operand_row(gr, lane);
+                            const int c = fast_operand_chunk(gr, lane);
+                            // LDS slot: row r, position lane % 8, read by the fragments as logical
+                            // chunk (lane % 8) ^ swizzle(r)
+                            CHECK(thin_load_unit(bn, wave, p) + lane == (is_a ? 0 : kThinBM * 8) + r * 8 + (lane & 7), "thin LDS unit");
+                            CHECK(((lane & 7) ^ lds_swizzle(r)) == c, "thin LDS chunk position");
+                            if (r < rows) {
+                                CHECK(static_cast<int64_t>(off) == r * ld + kb * kBlockK + 16 * c, "thin operand address");
+                                if (kb * kBlockK + 16 * c < K) {
+                                    CHECK(in, "thin row %d chunk %d below K not read", r, c);
+                                    std::vector<uint8_t>& got = is_a ? got_a : got_b;
+                                    CHECK(++got[r * 8 + c] == 1, "thin row %d chunk %d loaded twice", r, c);
+                                }
+                            } else {
+                                CHECK(!in, "thin row %d past the tile's %lld rows is read", r, (long long)rows);
+                            }
+                            if (in) CHECK(r0 * ld + static_cast<int64_t>(off) + 16 <= total * ld, "thin read past the operand");
+                        }
+                    }
+                for (int r = 0; r < arows; ++r)
+                    for (int c = 0; c < 8; ++c)
+                        if (kb * kBlockK + 16 * c < K) CHECK(got_a[r * 8 + c] == 1, "thin A row %d chunk %d not loaded", r, c);
+                for (int r = 0; r < brows; ++r)
+                    for (int c = 0; c < 8; ++c)
+                        if (kb * kBlockK + 16 * c < K) CHECK(got_b[r * 8 + c] == 1, "thin B row %d chunk %d not loaded", r, c);
+                // A scales: wave 0, every lane (LDS float lane)
+                std::vector<uint8_t> sa(kThinBM, 0), sbc(bn, 0);
+                for (int lane = 0; lane < 64; ++lane) {
+                    bool ok;
+                    const uint64_t off = static_cast<uint64_t>(thin_ascale_base(m0, M, lane)) + fast_ascale_advance(kb, M);
+                    const bool in = access(off, 4 * M * Kb, 4, ok);
+                    CHECK(ok, "thin a_s offset");
+                    const int64_t m = m0 + lane;
+                    if (m < M) {
+                        CHECK(in && static_cast<int64_t>(off) == 4 * (kb * M + m), "thin a_s[%lld, %lld] address", (long long)m, (long long)kb);
+                        ++sa[lane];
+                    } else {
+                        CHECK(!in, "thin a_s row %lld >= M read", (long long)m);
+                    }
+                }
+                for (int r = 0; r < arows; ++r) CHECK(sa[r] == 1, "thin a_s row %lld not loaded once", (long long)(m0 + r));
+                // per-column B scales: the active lanes of the B-scale waves, each writing one LDS
+                // float of the tile's bn
+                for (int wave = 0; wave < kThinWaves; ++wave) {
+                    if (!thin_has_bscale_load(bn, true, wave)) continue;
+                    for (int lane = 0; lane < 64; ++lane) {
+                        if (!((thin_bscale_lanes(bn, true) >> lane) & 1)) continue;
+                        bool ok;
+                        const uint64_t off = static_cast<uint64_t>(thin_bscale_col_base(bn, n0, N, wave, lane)) + fast_bscale_col_advance(kb, N);
+                        const bool in = access(off, 4 * N * Kb, 4, ok);
+                        CHECK(ok, "thin b_s offset");
+                        const int col = thin_bscale_col(wave, lane);
+                        CHECK(col < bn, "thin b_s LDS float %d outside the tile's %d", col, bn);
+                        const int64_t n = n0 + col;
+                        if (n < N) {
+                            CHECK(in && static_cast<int64_t>(off) == 4 * (kb * N + n), "thin b_s[%lld, %lld] address", (long long)kb, (long long)n);
+                            ++sbc[col];
+                        } else {
+                            CHECK(!in, "thin b_s column %lld >= N read", (long long)n);
+                        }
+                    }
+                }
+                for (int r = 0; r < brows; ++r) CHECK(sbc[r] == 1, "thin b_s column %lld not loaded once", (long long)(n0 + r));
+                // 128x128 B scale: lane 0 of wave 3, the tile's column block
+                for (const auto& st : strides) {
+                    CHECK(thin_has_bscale_load(bn, false, 3) && !thin_has_bscale_load(bn, false, 2), "thin 128x128 scale wave");
+                    CHECK(thin_bscale_lanes(bn, false) == 1, "thin 128x128 scale lanes");
+                    bool ok;
+                    const uint64_t off = static_cast<uint64_t>(thin_bscale_blk_base(n0, st[0], 0)) + fast_bscale_blk_advance(kb, st[1]);
+                    const bool in = access(off, 4 * bscale_blk_extent(N, Kb, st[0], st[1]), 4, ok);
+                    CHECK(ok, "thin 128x128 b_s offset");
+                    const int64_t nb = n0 / kBlockK;
+                    CHECK(in && static_cast<int64_t>(off) == 4 * (nb * st[0] + kb * st[1]), "thin 128x128 b_s address");
+                    CHECK((n0 + brows - 1) / kBlockK == nb, "thin tile spans two column blocks");
+                }
+            }
+            for (int wave = 0; wave < kThinWaves; ++wave)
+                for (int i = 0; i < 2; ++i)
+                    for (int j = 0; j < bn / 32; ++j)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int64_t m = thin_store_row(m0, wave & 1, i, lane);
+                            const int64_t n = thin_store_col(n0, bn, wave >> 1, j, lane);
+                            CHECK(m - m0 < kThinBM && n - n0 < bn, "thin output outside the tile");
+                            if (m >= M) continue;
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < N) CHECK(++stored[m * N + n + e] == 1, "thin C[%lld, %lld] stored twice", (long long)m, (long long)(n + e));
+                        }
+        }
+    for (int64_t i = 0; i < M * N; ++i) CHECK(stored[i] == 1, "thin C element %lld not stored", (long long)i);
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------
 // General (float8_e4m3fnuz) kernel: 256 x 128 tiles, 8 waves of 64 x 64.
 static bool check_gen(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     const int mt = static_cast<int>(cdiv(M, kGenBM)), nt = static_cast<int>(cdiv(N, kGenBN));
@@ -382,6 +520,8 @@ int main(int argc, char** argv) {
         for (int bm : {kFastBM, kFastBMSmall})
             ok = ok && check_fast(M, N, K, ld, ld, bm) && check_fast(M, N, K, ld + 16, ld + 48, bm) &&
                  check_split(M, N, K, bm);
+        for (int bn : {32, 64, 128})
+            ok = ok && check_thin(M, N, K, ld, ld, bn) && check_thin(M, N, K, ld + 16, ld + 48, bn);
         ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);
         std::printf("%s M=%lld N=%lld K=%lld\n", ok ? "ok" : "FAILED", (long long)M, (long long)N, (long long)K);
         if (!ok) return 1;

@@ -93,6 +93,24 @@ def test_planted_operand_row_read_is_caught(tmp_path):
     assert r.returncode != 0, r.stdout
 
 
+def test_planted_thin_scale_read_is_caught(tmp_path):
+    """The masking page's bug in the thin kernel: its A-scale read of rows >= M left unmasked."""
+    exe = _planted(tmp_path,
+                   "return m0 + lane < M ? static_cast<uint32_t>(4 * (m0 + lane)) : kOob;",
+                   "return static_cast<uint32_t>(4 * (m0 + lane));", "planted_thin_read")
+    r = _run(exe, [(130, 256, 256)])
+    assert r.returncode != 0 and "thin a_s row" in r.stdout, r.stdout
+
+
+def test_planted_thin_bscale_lane_is_caught(tmp_path):
+    """A per-column B-scale load of the thin kernel whose lanes run past the tile's columns."""
+    exe = _planted(tmp_path,
+                   "return !per_col ? 1ull : (bn >= 64 ? ~0ull : ((1ull << bn) - 1));",
+                   "return !per_col ? 1ull : ~0ull;", "planted_thin_bs")
+    r = _run(exe, [(130, 256, 256)])
+    assert r.returncode != 0 and "outside the tile" in r.stdout, r.stdout
+
+
 def test_checker_needs_no_hip():
     """The header compiles for the host with the plain C++ compiler (no HIP headers)."""
     assert shutil.which("g++") is not None

@@ -357,21 +357,54 @@ def test_gemm_forced_schedule(M, N, K, ld, S, bm, per_col, monkeypatch):
     _assert_close(got, co, f"split {S}")
 
 
+THIN_SHAPES = SPLIT_SHAPES + [
+    # one row; M at and around the 64-row tile; a column tail inside a 4-column group; K < 128
+    (1, 4100, 640, 640), (64, 96, 256, 256), (65, 130, 384, 400), (127, 33, 100, 112), (2, 512, 128, 128),
+]
+
+
+@pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
+@pytest.mark.parametrize("bn", [32, 64, 128], ids=lambda v: f"bn{v}")
+@pytest.mark.parametrize("M,N,K,ld", THIN_SHAPES, ids=lambda v: str(v))
+def test_gemm_thin_schedule(M, N, K, ld, bn, per_col, monkeypatch):
+    """The thin kernel (BSFP8_GEMM_TILE_M=64, tile width BSFP8_GEMM_TILE_N) on ragged shapes:
+    against the oracle in full, and bit for bit against the fast kernel's 128-row tiles without a
+    split, which apply the same per-K-block arithmetic in the same order."""
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + 3 * N + K + bn, per_col)
+    monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
+    if per_col:
+        fn = lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x1(oqa, osa, oqb, osb)
+    else:
+        fn = lambda c: bf.gemm_1x128_128x128(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x128(oqa, osa, oqb, osb, osb.shape[1], 1)
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "64")
+    monkeypatch.setenv("BSFP8_GEMM_TILE_N", str(bn))
+    got = _run_guarded(fn, M, N, N + 3)
+    _assert_close(got, co, f"thin {bn}")
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "128")
+    monkeypatch.setenv("BSFP8_GEMM_SPLIT", "1")
+    monkeypatch.delenv("BSFP8_GEMM_TILE_N")
+    fast = _run_guarded(fn, M, N, N + 3)
+    assert np.array_equal(got.view(np.uint32), fast.view(np.uint32)), "thin and fast kernels differ"
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2048, 4096, 4096),
                                    (2, 5120, 1280), (4, 3584, 640)], ids=lambda v: str(v))
 def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):
-    """The pages' short-and-wide GEMM shapes, where the automatic plan takes 128-row tiles and / or
-    splits K: every output row against the oracle, and the SQNR against the fp64 matmul of the bf16
-    inputs."""
+    """The pages' short-and-wide GEMM shapes, which the automatic plan gives to the thin kernel
+    (2048 rows: the fast kernel's 128-row tiles): every output row against the oracle, and the SQNR
+    against the fp64 matmul of the bf16 inputs."""
     monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
     monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
+    monkeypatch.delenv("BSFP8_GEMM_TILE_N", raising=False)
     g = inputs.rng(0)
     a_h = inputs.normal_bf16(g, (M, K))
     w_h = inputs.normal_bf16(g, (N, K), 0.02)
     _forward_check(a_h, w_h, np.arange(M), sqnr_min=27.5)
 
 
-@pytest.mark.parametrize("bm", [256, 128], ids=["tile256", "tile128"])
+@pytest.mark.parametrize("bm", [256, 128, 64], ids=["tile256", "tile128", "thin"])
 def test_gemm_operand_row_stride_at_the_limit(bm, monkeypatch):
     """Operand rows 2^23 bytes apart, the largest stride the GEMMs accept (256 rows of a tile then
     span exactly 2^31 bytes, the size of a buffer resource): ragged M and N against the oracle."""
@@ -398,9 +431,11 @@ def test_gemm_operand_row_stride_at_the_limit(bm, monkeypatch):
 
 def test_split_gemms_on_two_streams_concurrently(monkeypatch):
     """The split-K workspace comes from a stream-ordered pool: split GEMMs enqueued on two streams
-    at once get separate workspaces, and every result equals the same call made alone."""
+    at once get separate workspaces, and every result equals the same call made alone. (128-row
+    tiles forced: these shapes would otherwise take the thin kernel, which does not split.)"""
     monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
-    monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "128")
+    monkeypatch.delenv("BSFP8_GEMM_TILE_N", raising=False)
     shapes = [(128, 4096, 4096), (64, 2048, 3072)]
     ops, ref = [], []
     for i, (M, N, K) in enumerate(shapes):

@@ -1,7 +1,8 @@
 """gemm_1x128_128x128_noalloc under HIP graph capture: the allocation-free entry point is for
-callers that record their launches into a graph. Three calls (a K split whose partial tiles live in
-the static scratch, a 128-row-tile shape and a 256-row-tile shape) are captured once and the graph
-is replayed several times, with other eager work on the GPU between the replays; every replay must
+callers that record their launches into a graph. Four calls (a K split whose partial tiles live in
+the static scratch, a thin-kernel shape, a 128-row-tile shape and a 256-row-tile shape; the schedule
+of each set through the environment, which each call reads) are captured once and the graph is
+replayed several times, with other eager work on the GPU between the replays; every replay must
 reproduce the eager results bit for bit."""
 import numpy as np
 import pytest
@@ -21,16 +22,28 @@ def _operands(M, N, K, seed):
     return qa, sa, qw, sw
 
 
-def test_noalloc_gemm_graph_replays_match_eager(monkeypatch):
+def _schedule(monkeypatch, tile_m):
     monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
-    monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
-    shapes = [(128, 4096, 4096), (300, 520, 704), (1024, 2048, 1024)]
+    monkeypatch.delenv("BSFP8_GEMM_TILE_N", raising=False)
+    if tile_m:
+        monkeypatch.setenv("BSFP8_GEMM_TILE_M", str(tile_m))
+    else:
+        monkeypatch.delenv("BSFP8_GEMM_TILE_M", raising=False)
+
+
+def test_noalloc_gemm_graph_replays_match_eager(monkeypatch):
+    # (shape, forced tile height): 128 rows here splits K into 12 slices; automatic: thin kernel
+    calls = [((128, 4096, 4096), 128), ((300, 520, 704), 0), ((1024, 2048, 1024), 128), ((1024, 2048, 1024), 256)]
+    shapes = [sh for sh, _ in calls]
     ops = [_operands(M, N, K, 60 + i) for i, (M, N, K) in enumerate(shapes)]
-    eager = []
-    for (M, N, K), o in zip(shapes, ops):
-        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        bf.gemm_1x128_128x128_noalloc(*o, c)
-        eager.append(c)
+
+    def run_all(outs):
+        for (_, tile_m), o, c in zip(calls, ops, outs):
+            _schedule(monkeypatch, tile_m)
+            bf.gemm_1x128_128x128_noalloc(*o, c)
+
+    eager = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for (M, N, K) in shapes]
+    run_all(eager)
     torch.cuda.synchronize()
     eager = [c.clone() for c in eager]
 
@@ -38,14 +51,12 @@ def test_noalloc_gemm_graph_replays_match_eager(monkeypatch):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):                      # warm-up outside the capture
-        for o, c in zip(ops, outs):
-            bf.gemm_1x128_128x128_noalloc(*o, c)
+        run_all(outs)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for o, c in zip(ops, outs):
-            bf.gemm_1x128_128x128_noalloc(*o, c)
+        run_all(outs)
     torch.cuda.synchronize()
 
     junk = torch.randn(1 << 22, device="cuda")
@@ -55,6 +66,7 @@ def test_noalloc_gemm_graph_replays_match_eager(monkeypatch):
         # eager work between replays, including a library GEMM that uses the same scratch
         junk.mul_(1.0001)
         other = torch.empty((64, 4096), dtype=torch.bfloat16, device="cuda")
+        _schedule(monkeypatch, 128)
         bf.gemm_1x128_128x128_noalloc(*_operands(64, 4096, 4096, 99), other)
         torch.cuda.synchronize()
         graph.replay()

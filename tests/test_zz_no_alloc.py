@@ -42,17 +42,18 @@ def _check_guard(buf, M, N):
     assert np.all(np.isnan(h[0])) and np.all(np.isnan(h[M + 1])) and np.all(np.isnan(h[1:M + 1, N:]))
 
 
-# first call large (split into 12 slices: ~25 MiB of partials), second smaller (16 slices of a
-# 64 x 1024 output), then a shape that does not split
+# with 128-row tiles: first call large (split into 12 slices: ~25 MiB of partials), second smaller
+# (16 slices of a 64 x 1000 output), then a shape that does not split; automatic: the thin kernel
 CALLS = [(128, 4096, 4096), (64, 1000, 2000), (300, 520, 704)]
+ENVS = {"auto": {}, "tile128": {"BSFP8_GEMM_TILE_M": "128"}, "forced3": {"BSFP8_GEMM_SPLIT": "3"}}
 
 
-@pytest.mark.parametrize("env", [None, "3"], ids=["auto", "forced3"])
+@pytest.mark.parametrize("env", list(ENVS), ids=list(ENVS))
 def test_noalloc_matches_allocating_entry(env, monkeypatch):
-    if env is None:
-        monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
-    else:
-        monkeypatch.setenv("BSFP8_GEMM_SPLIT", env)
+    for k in ("BSFP8_GEMM_SPLIT", "BSFP8_GEMM_TILE_M", "BSFP8_GEMM_TILE_N"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in ENVS[env].items():
+        monkeypatch.setenv(k, v)
     for i, (M, N, K) in enumerate(CALLS):
         print(f"noalloc call {i}: M={M} N={N} K={K} split={env}", flush=True)
         qa, sa, qw, sw, oqa, osa, oqw, osw = _operands(M, N, K, 40 + i)
