@@ -988,7 +988,7 @@ struct TCfg {
 // Wait until this wave's loads of the block being multiplied have landed: `later` (0..2) blocks
 // issued after it are still allowed in flight, L instructions each.
 template <int L>
-__device__ __forceinline__ void wait_block(int64_t later) {
+__device__ __forceinline__ void wait_block(int later) {
     if (later >= 2) fast::wait_own_loads<2 * L>();
     else if (later == 1) fast::wait_own_loads<L>();
     else fast::wait_own_loads<0>();
@@ -1015,7 +1015,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     geom::tile_of(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * geom::kThinBM;
     const int64_t n0 = static_cast<int64_t>(tn) * BN;
-    const int64_t Kb = (K + kGroup - 1) / kGroup;
+    // K-blocks as int: K <= ld <= 2^23 (the C ABI's operand bound)
+    const int Kb = static_cast<int>((K + kGroup - 1) / kGroup);
 
     const int64_t arows = (M - m0) < geom::kThinBM ? (M - m0) : geom::kThinBM;
     const int64_t brows = (N - n0) < BN ? (N - n0) : BN;
@@ -1024,11 +1025,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_s, M * Kb * 4);
     const __amdgpu_buffer_rsrc_t rbs =
         make_rsrc(b_s, PER_COL ? N * Kb * 4 : 4 * geom::bscale_blk_extent(N, Kb, bs_nb, bs_kb));
-    uint32_t lane_off[kLoads];
+    uint32_t lane_off[kLoads], unit[kLoads];
+    bool is_a[kLoads];
 #pragma unroll
-    for (int p = 0; p < kLoads; ++p)
-        lane_off[p] = geom::thin_operand_lane(geom::thin_group(BN, wave, p), lane,
-                                              geom::thin_load_is_a(BN, wave, p) ? lda : ldb);
+    for (int p = 0; p < kLoads; ++p) {
+        is_a[p] = geom::thin_load_is_a(BN, wave, p);
+        lane_off[p] = geom::thin_operand_lane(geom::thin_group(BN, wave, p), lane, is_a[p] ? lda : ldb);
+        unit[p] = static_cast<uint32_t>(geom::thin_load_unit(BN, wave, p));
+    }
     const bool b_scales = geom::thin_has_bscale_load(BN, PER_COL, wave);
     const uint32_t as_base = geom::thin_ascale_base(m0, M, lane);
     const uint32_t bs_base = PER_COL ? geom::thin_bscale_col_base(BN, n0, N, wave, lane)
@@ -1039,13 +1043,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
     // K-block kb into stage s: the wave's operand groups, then its scale load (wave 0: A scales;
     // waves 3 and, per column at BN = 128, 2: B scales)
-    auto issue = [&](int64_t kb, int s) {
+    auto issue = [&](int kb, int s) {
         const uint32_t base = lds0 + static_cast<uint32_t>(s * T::kStageSize * 16);
         const uint32_t adv = geom::fast_operand_advance(kb);
 #pragma unroll
-        for (int p = 0; p < kLoads; ++p)
-            fast::dma16(base + geom::thin_load_unit(BN, wave, p) * 16, geom::thin_load_is_a(BN, wave, p) ? ra : rb,
-                        lane_off[p] + adv, ~0ull);
+        for (int p = 0; p < kLoads; ++p) fast::dma16(base + unit[p] * 16, is_a[p] ? ra : rb, lane_off[p] + adv, ~0ull);
         if (wave == 0)
             fast::dma4(base + T::kStageSA * 16, ras, as_base + geom::fast_ascale_advance(kb, M), ~0ull);
         else if (b_scales)
@@ -1064,26 +1066,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int sw = geom::lds_swizzle(l16);
     const int pos_lo = lg ^ sw;
     const int pos_hi = (lg + 4) ^ sw;
-    const int krem = static_cast<int>(K - (Kb - 1) * kGroup);
+    const int krem = static_cast<int>(K - static_cast<int64_t>(Kb - 1) * kGroup);
     const bool scale_wave = wave == 0 || b_scales;
 
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < Kb) issue(s, s);
 
-    for (int64_t kb = 0; kb < Kb; ++kb) {
+    // One K-block. TAIL: the partial last block, whose fragment bytes at and past K are zeroed (a
+    // second instance of the body, so the full blocks carry no per-fragment branch).
+    // cur: the stage of block kb; nxt: the stage block kb + STAGES - 1 goes into (that of kb - 1)
+    int cur = 0, nxt = STAGES - 1;
+    auto body = [&](int kb, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         // block kb has landed for every wave; no wave reads the stage of block kb - 1 any more
-        const int64_t later = min(static_cast<int64_t>(STAGES - 2), Kb - 1 - kb);
+        const int later = min(STAGES - 2, Kb - 1 - kb);
         if (scale_wave) wait_block<kLoads + 1>(later);
         else wait_block<kLoads>(later);
         fast::lds_barrier();
-        if (kb + STAGES - 1 < Kb) issue(kb + STAGES - 1, static_cast<int>((kb + STAGES - 1) % STAGES));
+        if (kb + STAGES - 1 < Kb) issue(kb + STAGES - 1, nxt);
 
-        const u32x4* st = smem + static_cast<int>(kb % STAGES) * T::kStageSize;
-        const bool tail = kb == Kb - 1 && krem != kGroup;
+        const u32x4* st = smem + cur * T::kStageSize;
+        cur = cur + 1 == STAGES ? 0 : cur + 1;
+        nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
         auto frag = [&](int unit) {
             v8i v = to_v8i(st[unit + pos_lo], st[unit + pos_hi]);
-            if (tail) {
+            if (TAIL) {
 #pragma unroll
                 for (int d = 0; d < 8; ++d) v[d] = static_cast<int>(static_cast<uint32_t>(v[d]) & geom::tail_keep_mask(krem, lg, d));
             }
@@ -1113,7 +1121,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                     acc[i][j][e] = fmaf(p[e], PER_COL ? fa[i] * bsj[e] : fa[i], acc[i][j][e]);
             }
         }
-    }
+    };
+    const int Kb_full = krem != kGroup ? Kb - 1 : Kb;
+    for (int kb = 0; kb < Kb_full; ++kb) body(kb, std::false_type{});
+    if (Kb_full < Kb) body(Kb - 1, std::true_type{});
 
     // bf16 outputs straight from the totals: a lane's four consecutive columns of one row
 #pragma unroll
@@ -1178,9 +1189,11 @@ hipError_t gemm_scratch(float** out) {
 // per SIMD; twice the tiles), as does any M <= 128, whose 256-row tile would be at least half empty.
 // When even the 128-row tiles leave CUs idle, the problem is bound by moving operands into the CUs
 // and takes the thin kernel's 64-row tiles, the widest (128, 64 or 32 columns) that still give two
-// workgroups per CU. Only when those are few and K is long does K get split instead: S workgroups
-// per 128- or 256-row tile, whose fp32 partial tiles (written, then read by the sum) and second
-// launch pay off when the tiles leave most CUs idle. The slices always fit in one round.
+// workgroups per CU. Only when those are fewer than half the CUs and K is longer than 64 blocks
+// does K get split instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64
+// slices, 27 against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles
+// (written, then read by the sum) and second launch pay off when the tiles leave most CUs idle.
+// The slices always fit in one round.
 namespace {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1230,7 +1243,7 @@ SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, i
     if (cdiv64(M, fast::kBMSmall) * cdiv64(N, fast::kBN) < cus) {
         const int bn = thin_bn(M, N, cus);
         const int64_t wgs = cdiv64(M, geom::kThinBM) * cdiv64(N, bn);
-        if (2 * wgs >= cus || cdiv64(K, kGroup) < 32) {
+        if (2 * wgs >= cus || cdiv64(K, kGroup) <= 64) {
             plan.bm = geom::kThinBM;
             plan.bn = bn;
             return plan;
@@ -1321,24 +1334,41 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
     return hipGetLastError();
 }
 
-// The thin kernel with tile width BN (no split; every tile over the whole K range).
+// The thin kernel with tile width BN (no split; every tile over the whole K range) and STAGES LDS
+// stages (STAGES - 1 K-blocks in flight per workgroup).
+template <int BN, int STAGES>
+hipError_t launch_thin_stages(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
+                              BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt,
+                              hipStream_t stream) {
+    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+    const dim3 grid(static_cast<unsigned>(mt) * static_cast<unsigned>(nt));
+    if (bs.per_column)
+        thin::gemm_kernel<true, BN, STAGES><<<grid, thin::kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, mt, nt, c_vec);
+    else
+        thin::gemm_kernel<false, BN, STAGES><<<grid, thin::kThreads, 0, stream>>>(
+            a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, mt, nt, c_vec);
+    return hipGetLastError();
+}
+
+// The deepest pipeline (4, 3 or 2 stages) whose LDS still lets every workgroup of the grid be
+// resident at once (160 KB per CU): the thin kernel waits on memory, and with operands coming from
+// HBM rather than the last-level cache (measured: 128 x 4096 x 4096, 256 workgroups, 22.8 us with
+// two stages, 14.7 with four) the blocks in flight matter more than extra workgroups per CU.
 template <int BN>
 hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
-                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    // three LDS stages at 128 columns (two workgroups per CU), four below
-    constexpr int kSt = BN == 128 ? 3 : 4;
+                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int cus,
+                       hipStream_t stream) {
     const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
     const int64_t nt = (N + BN - 1) / BN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
-    const dim3 grid(static_cast<unsigned>(mt * nt));
-    if (bs.per_column)
-        thin::gemm_kernel<true, BN, kSt><<<grid, thin::kThreads, 0, stream>>>(
-            a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
-    else
-        thin::gemm_kernel<false, BN, kSt><<<grid, thin::kThreads, 0, stream>>>(
-            a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, (int)mt, (int)nt, c_vec);
-    return hipGetLastError();
+    const int64_t stage_bytes = 16 * (bs.per_column ? thin::TCfg<BN, true>::kStageSize : thin::TCfg<BN, false>::kStageSize);
+    auto resident = [&](int stages) { return mt * nt <= static_cast<int64_t>(cus) * ((160 << 10) / (stages * stage_bytes)); };
+    if (resident(4))
+        return launch_thin_stages<BN, 4>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
+    if (resident(3))
+        return launch_thin_stages<BN, 3>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
+    return launch_thin_stages<BN, 2>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
 }
 
 }  // namespace
@@ -1349,9 +1379,9 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        hipStream_t stream) {
     if (!fnuz) {
         if (plan.bm == geom::kThinBM) {
-            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
-            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
-            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, stream);
+            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
+            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
+            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
         }
         if (plan.bm == fast::kBMSmall)
             return launch_fast<fast::kBMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
