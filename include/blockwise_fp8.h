@@ -147,13 +147,16 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  *   2^31; ceil(M/128) at most 65535.
  * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
  * Schedule: one workgroup per 256 x 256 output tile, or per 128 x 256 tile when M <= 128 or the
- * 256-row tiles number at most half the compute units. When the tiles still leave most compute
- * units idle (M <= 512 and at most a quarter as many tiles as compute units, on a long enough K)
- * the K-blocks are split over S workgroups per tile, which write fp32 partial tiles to the pooled
+ * 256-row tiles number at most half the compute units. When even the 128 x 256 tiles are fewer
+ * than the compute units, one workgroup per 64 x 128, 64 x 64 or 64 x 32 tile (the widest giving
+ * two workgroups per compute unit) over the whole K range, with bit-identical results. Only when
+ * those tiles are fewer than half the compute units and K exceeds 64 blocks are the K-blocks split
+ * over S workgroups per 128- or 256-row tile, which write fp32 partial tiles to the pooled
  * workspace, and a second kernel sums the S partials in a fixed order into C (same result on every
- * call). The environment variables BSFP8_GEMM_SPLIT and BSFP8_GEMM_TILE_M, read at each call,
- * force S (1 = never split; S is clamped to ceil(K/128) and to the workspace bound) and the tile
- * height (256 or 128).
+ * call). The environment variables BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M and BSFP8_GEMM_TILE_N,
+ * read at each call, force S (1 = never split; S is clamped to ceil(K/128) and to the workspace
+ * bound; a split uses the 128- or 256-row tiles), the tile height (256, 128 or 64) and the width
+ * of the 64-row tiles (32, 64 or 128).
  */
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
                        const void* b, int64_t ldb, const float* b_s,
