@@ -37,6 +37,11 @@ STEP_SHAPES = [
     (2100, 4000, 4008, 2192, 4000, 4008, True),    # several tiles per workgroup, every edge ragged
     (5, 7, 8, 3, 9, 16, False),                    # sub-group sizes
     (129, 256, 263, 256, 129, 131, True),          # odd strides: the two single-purpose kernels
+    # without the transposed copy (reads and writes in separate phases): ragged edges, several
+    # tiles per workgroup, and two runs of tiles per workgroup
+    (300, 200, 208, 144, 296, 304, False),
+    (2100, 4000, 4008, 2192, 4000, 4008, False),
+    (8192, 4096, 4096, 4096, 4096, 4096, False),
 ]
 
 
