@@ -218,7 +218,7 @@ def test_gemm_128x128_fnuz(M, N, K, ld, ldc):
     co = oracle.gemm_1x128_128x128(oqa, osa, oqw, osw, osw.shape[1], 1, fmt=FMT)
     _check(got, co, "gemm_1x128_128x128_fnuz")
     ref = oracle.matmul_bf16_f64(ah, wh)
-    assert oracle.sqnr_db(ref, got) >= 27.5
+    assert oracle.sqnr_db(ref, got) >= 28.0  # the oracle's fnuz path: 28.66-30.39 dB on these shapes
 
 
 @pytest.mark.parametrize("M,N,K,ld,ldc", GEMM_SHAPES, ids=lambda v: str(v))

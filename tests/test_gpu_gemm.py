@@ -401,7 +401,7 @@ def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):
     g = inputs.rng(0)
     a_h = inputs.normal_bf16(g, (M, K))
     w_h = inputs.normal_bf16(g, (N, K), 0.02)
-    _forward_check(a_h, w_h, np.arange(M), sqnr_min=27.5)
+    _forward_check(a_h, w_h, np.arange(M), sqnr_min=28.0)  # the oracle path: 28.66-28.74 dB here
 
 
 @pytest.mark.parametrize("bm", [256, 128, 64], ids=["tile256", "tile128", "thin"])
