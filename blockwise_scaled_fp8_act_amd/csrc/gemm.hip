@@ -983,6 +983,7 @@ struct TCfg {
     static constexpr int kStageSA = kStageB + BN * 8;
     static constexpr int kStageSB = kStageSA + geom::kThinBM / 4;
     static constexpr int kStageSize = kStageSB + (PER_COL ? BN / 4 : 1);
+    static_assert(kStageSize == geom::thin_stage_units(BN, PER_COL), "stage size as the schedule counts it");
 };
 
 // Wait until this wave's loads of the block being multiplied have landed: `later` (0..2) blocks
@@ -1183,109 +1184,7 @@ hipError_t gemm_scratch(float** out) {
     return hipSuccess;
 }
 
-// Schedule, from measurements on MI355X (256 CUs; back-to-back launches, settled clock). 256-row
-// tiles (8 waves, two per SIMD) run the K-loop fastest, so they are kept whenever they give every
-// CU a tile; a problem with fewer 256-row tiles than half the CUs takes 128-row tiles (4 waves, one
-// per SIMD; twice the tiles), as does any M <= 128, whose 256-row tile would be at least half empty.
-// When even the 128-row tiles leave CUs idle, the problem is bound by moving operands into the CUs
-// and takes the thin kernel's 64-row tiles, the widest (128, 64 or 32 columns) that still give two
-// workgroups per CU. Only when those are fewer than half the CUs and K is longer than 64 blocks
-// does K get split instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64
-// slices, 27 against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles
-// (written, then read by the sum) and second launch pay off when the tiles leave most CUs idle.
-// The slices always fit in one round.
-namespace {
-
-int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// The fast kernel's tile height for M x N.
-int fast_bm(int64_t M, int64_t N, int cus) {
-    const int64_t tiles256 = cdiv64(M, fast::kBM) * cdiv64(N, fast::kBN);
-    return (M <= fast::kBMSmall || 2 * tiles256 <= cus) ? fast::kBMSmall : fast::kBM;
-}
-
-// The thin kernel's tile width for M x N.
-int thin_bn(int64_t M, int64_t N, int cus) {
-    for (const int bn : {128, 64})
-        if (cdiv64(M, geom::kThinBM) * cdiv64(N, bn) >= 2 * static_cast<int64_t>(cus)) return bn;
-    return 32;
-}
-
-// The automatic K split of the fast kernel's tiles of height plan.bm.
-void fast_split(SplitPlan& plan, int64_t M, int64_t N, int64_t K, int cus, int64_t max_bytes) {
-    const int64_t tiles = cdiv64(M, plan.bm) * cdiv64(N, fast::kBN);
-    const int64_t Kb = cdiv64(K, kGroup);
-    if (M > 512 || 4 * tiles > cus) return;
-    int64_t S = cus / tiles;  // one round of workgroups
-    if (M <= 64) {
-        if (S > Kb) S = Kb;
-    } else {
-        if (Kb <= 10) return;  // short K: the slice overhead outweighs the idle CUs
-        if (S > Kb / 2) S = Kb / 2;
-        if (S > (M <= 256 ? 12 : 4)) S = M <= 256 ? 12 : 4;
-    }
-    const int64_t ldp = (N + 7) / 8 * 8;
-    const int64_t slice_bytes = M * ldp * 4;
-    if (S * slice_bytes > max_bytes) S = max_bytes / slice_bytes;
-    if (S > 65535) S = 65535;
-    if (S < 2) return;
-    plan.S = static_cast<int>(S);
-    plan.ldp = ldp;
-    plan.bytes = S * slice_bytes;
-}
-
-}  // namespace
-
-SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
-    SplitPlan plan{1, 0, 0, fast::kBM, 0};
-    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
-    plan.bm = fast_bm(M, N, cus);
-    if (cdiv64(M, fast::kBMSmall) * cdiv64(N, fast::kBN) < cus) {
-        const int bn = thin_bn(M, N, cus);
-        const int64_t wgs = cdiv64(M, geom::kThinBM) * cdiv64(N, bn);
-        if (2 * wgs >= cus || cdiv64(K, kGroup) <= 64) {
-            plan.bm = geom::kThinBM;
-            plan.bn = bn;
-            return plan;
-        }
-    }
-    fast_split(plan, M, N, K, cus, max_bytes);
-    return plan;
-}
-
-// A schedule chosen by the caller: bm 64 -- the thin kernel, with tile width bn (32, 64 or 128;
-// other values: the automatic width), never split; bm 256 or 128 -- the fast kernel with that tile
-// height and its automatic split; bm 0 -- the automatic schedule, whose thin width bn may be set.
-// S > 0 then sets the slice count (clamped to the K-blocks and to the workspace bound; fewer than
-// two: no split); a split runs on the fast kernel.
-SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm, int bn,
-                                 int64_t max_bytes) {
-    SplitPlan plan = gemm_split_plan(M, N, K, fnuz, cus, max_bytes);
-    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
-    const bool bn_ok = bn == 32 || bn == 64 || bn == 128;
-    if (bm == geom::kThinBM) return SplitPlan{1, 0, 0, geom::kThinBM, bn_ok ? bn : thin_bn(M, N, cus)};
-    if (bm == fast::kBM || bm == fast::kBMSmall || (S >= 2 && plan.bm == geom::kThinBM)) {
-        plan = SplitPlan{1, 0, 0, (bm == fast::kBM || bm == fast::kBMSmall) ? bm : fast_bm(M, N, cus), 0};
-        fast_split(plan, M, N, K, cus, max_bytes);
-    } else if (plan.bm == geom::kThinBM && bn_ok) {
-        plan.bn = bn;
-    }
-    if (S <= 0 || plan.bm == geom::kThinBM) return plan;
-    plan.S = 1;
-    plan.ldp = 0;
-    plan.bytes = 0;
-    const int64_t Kb = cdiv64(K, kGroup);
-    const int64_t ldp = (N + 7) / 8 * 8;
-    const int64_t slice_bytes = M * ldp * 4;
-    int64_t s = S > Kb ? Kb : S;
-    if (s * slice_bytes > max_bytes) s = max_bytes / slice_bytes;
-    if (s > 65535) s = 65535;
-    if (s < 2) return plan;
-    plan.S = static_cast<int>(s);
-    plan.ldp = ldp;
-    plan.bytes = s * slice_bytes;
-    return plan;
-}
+// The schedule (tile shape, K split, thin pipeline depth) is in schedule.hpp.
 
 namespace {
 
@@ -1351,10 +1250,7 @@ hipError_t launch_thin_stages(const uint8_t* a, int64_t lda, const float* a_s, c
     return hipGetLastError();
 }
 
-// The deepest pipeline (4, 3 or 2 stages) whose LDS still lets every workgroup of the grid be
-// resident at once (160 KB per CU): the thin kernel waits on memory, and with operands coming from
-// HBM rather than the last-level cache (measured: 128 x 4096 x 4096, 256 workgroups, 22.8 us with
-// two stages, 14.7 with four) the blocks in flight matter more than extra workgroups per CU.
+// The pipeline depth: sched::thin_stages.
 template <int BN>
 hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
                        BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int cus,
@@ -1362,11 +1258,10 @@ hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const ui
     const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
     const int64_t nt = (N + BN - 1) / BN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const int64_t stage_bytes = 16 * (bs.per_column ? thin::TCfg<BN, true>::kStageSize : thin::TCfg<BN, false>::kStageSize);
-    auto resident = [&](int stages) { return mt * nt <= static_cast<int64_t>(cus) * ((160 << 10) / (stages * stage_bytes)); };
-    if (resident(4))
+    const int stages = sched::thin_stages(BN, bs.per_column != 0, mt * nt, cus);
+    if (stages == 4)
         return launch_thin_stages<BN, 4>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
-    if (resident(3))
+    if (stages == 3)
         return launch_thin_stages<BN, 3>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
     return launch_thin_stages<BN, 2>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
 }

@@ -157,6 +157,9 @@ BSFP8_HD int64_t split_begin(int64_t Kb, int64_t S, int64_t s) { return Kb * s /
 constexpr int kThinBM = 64;
 constexpr int kThinWaves = 4;
 BSFP8_HD int thin_loads(int bn) { return (kThinBM + bn) / 32; }
+// LDS image of one pipeline stage, in 16-byte units: A rows 0..63 and B rows 0..bn-1 (8 units of
+// 128 bytes each), the 64 A scales, then the B scales (per column: bn floats; 128x128: one float).
+constexpr int thin_stage_units(int bn, bool per_col) { return (kThinBM + bn) * 8 + kThinBM / 4 + (per_col ? bn / 4 : 1); }
 // Load p (0 .. thin_loads(bn) - 1) of wave w: row group g = w thin_loads(bn) + p of the tile; A's
 // groups are 0..7, B's follow. thin_group: the group's index within its operand.
 BSFP8_HD bool thin_load_is_a(int bn, int wave, int p) { return wave * thin_loads(bn) + p < kThinBM / 8; }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "schedule.hpp"
+
 namespace bsfp8 {
 
 // fnuz: float8_e4m3fnuz codes (FP8_MAX 240) instead of float8_e4m3fn (FP8_MAX 448).
@@ -41,27 +43,7 @@ struct BScale {
 // Compute units of the current device (cached per device after the first query).
 int device_cus();
 
-// Schedule of a GEMM: the tile height bm -- 256 or 128 rows (the fast kernel) or 64 (the thin
-// kernel, whose tiles are bn = 32, 64 or 128 columns wide; bn is 0 for the fast kernel's 256) --
-// and the K split of a fast-kernel GEMM whose output tiles cannot fill the chip: S workgroups per
-// tile each multiply a range of K-blocks into an fp32 partial tile (rows of ldp floats, ldp = N
-// rounded up to 8), and a second kernel sums the S partials into C. S == 1: no split. bytes: the
-// fp32 workspace it needs.
-struct SplitPlan {
-    int S;
-    int64_t ldp;
-    int64_t bytes;
-    int bm;
-    int bn;
-};
-SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes);
-// A schedule chosen by the caller, so tests and sweeps can run any schedule on any shape: bm 64 --
-// the thin kernel with tile width bn (32, 64 or 128; other values: automatic), never split; bm 256
-// or 128 -- the fast kernel with that tile height and its automatic split; bm 0 -- automatic (its
-// thin width may be set by bn). S > 0 sets the slice count (clamped to the K-block count and to
-// max_bytes of workspace; below two: no split); a split runs on the fast kernel.
-SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm, int bn,
-                                 int64_t max_bytes);
+// SplitPlan, gemm_split_plan and gemm_split_plan_forced: schedule.hpp.
 
 // The allocation-free GEMM's scratch: a device array of gemm_scratch_bytes() bytes per device;
 // gemm_scratch gives its address on the current device (looked up once per device).

@@ -1,0 +1,151 @@
+// GEMM schedule: which kernel and tiles a problem takes, whether K is split, and the thin kernel's
+// pipeline depth. Plain C++ (no HIP): the library calls it on the host before every GEMM launch,
+// and tests/schedule_check.cpp compiles the same header with the host compiler to check the rules
+// shape by shape.
+//
+// The rules, from measurements on MI355X (256 CUs; settled clock):
+//   * 256 x 256 tiles (8 waves, two per SIMD) run the K-loop fastest and are kept whenever they
+//     give every CU a tile; a problem with fewer 256-row tiles than half the CUs, or with
+//     M <= 128 (a 256-row tile would be at least half empty), takes 128 x 256 tiles (4 waves, one
+//     per SIMD; twice the tiles);
+//   * when even the 128-row tiles number fewer than the CUs, the problem is bound by moving
+//     operands into the CUs, not by the matrix cores, and takes the thin kernel's 64-row tiles,
+//     the widest (128, 64 or 32 columns) that still give two workgroups per CU;
+//   * only when those are fewer than half the CUs and K is longer than 64 blocks does K get split
+//     instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64 slices, 27
+//     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
+//     then read by the sum) and second launch pay off when the tiles leave most CUs idle; the
+//     slices always fit in one round;
+//   * the thin kernel runs the deepest pipeline (4, 3 or 2 LDS stages) whose LDS still lets every
+//     workgroup of the grid be resident at once: with operands coming from HBM the K-blocks in
+//     flight per workgroup matter more than extra workgroups per CU (128 x 4096 x 4096, 256
+//     workgroups: 22.8 us with two stages, 14.7 with four).
+#pragma once
+
+#include <stdint.h>
+
+#include "geometry.hpp"
+
+namespace bsfp8 {
+
+// Schedule of a GEMM: the tile height bm -- 256 or 128 rows (the fast kernel) or 64 (the thin
+// kernel, whose tiles are bn = 32, 64 or 128 columns wide; bn is 0 for the fast kernel's 256) --
+// and the K split of a fast-kernel GEMM whose output tiles cannot fill the chip: S workgroups per
+// tile each multiply a range of K-blocks into an fp32 partial tile (rows of ldp floats, ldp = N
+// rounded up to 8), and a second kernel sums the S partials into C. S == 1: no split. bytes: the
+// fp32 workspace it needs.
+struct SplitPlan {
+    int S;
+    int64_t ldp;
+    int64_t bytes;
+    int bm;
+    int bn;
+};
+
+namespace sched {
+
+constexpr int64_t kLdsPerCu = 160 * 1024;  // LDS bytes of a gfx950 compute unit
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The fast kernel's tile height for M x N.
+inline int fast_bm(int64_t M, int64_t N, int cus) {
+    const int64_t tiles256 = cdiv(M, geom::kFastBM) * cdiv(N, geom::kFastBN);
+    return (M <= geom::kFastBMSmall || 2 * tiles256 <= cus) ? geom::kFastBMSmall : geom::kFastBM;
+}
+
+// The thin kernel's tile width for M x N.
+inline int thin_bn(int64_t M, int64_t N, int cus) {
+    for (const int bn : {128, 64})
+        if (cdiv(M, geom::kThinBM) * cdiv(N, bn) >= 2 * static_cast<int64_t>(cus)) return bn;
+    return 32;
+}
+
+// The automatic K split of the fast kernel's tiles of height plan.bm.
+inline void fast_split(SplitPlan& plan, int64_t M, int64_t N, int64_t K, int cus, int64_t max_bytes) {
+    const int64_t tiles = cdiv(M, plan.bm) * cdiv(N, geom::kFastBN);
+    const int64_t Kb = cdiv(K, geom::kBlockK);
+    if (M > 512 || 4 * tiles > cus) return;
+    int64_t S = cus / tiles;  // one round of workgroups
+    if (M <= 64) {
+        if (S > Kb) S = Kb;
+    } else {
+        if (Kb <= 10) return;  // short K: the slice overhead outweighs the idle CUs
+        if (S > Kb / 2) S = Kb / 2;
+        if (S > (M <= 256 ? 12 : 4)) S = M <= 256 ? 12 : 4;
+    }
+    const int64_t ldp = (N + 7) / 8 * 8;
+    const int64_t slice_bytes = M * ldp * 4;
+    if (S * slice_bytes > max_bytes) S = max_bytes / slice_bytes;
+    if (S > 65535) S = 65535;
+    if (S < 2) return;
+    plan.S = static_cast<int>(S);
+    plan.ldp = ldp;
+    plan.bytes = S * slice_bytes;
+}
+
+// LDS stages of the thin kernel for a grid of wgs workgroups of tile width bn: the deepest of 4, 3
+// and 2 that keeps the whole grid resident (2 when none does).
+inline int thin_stages(int bn, bool per_col, int64_t wgs, int cus) {
+    const int64_t stage_bytes = 16 * static_cast<int64_t>(geom::thin_stage_units(bn, per_col));
+    for (const int st : {4, 3})
+        if (wgs <= static_cast<int64_t>(cus) * (kLdsPerCu / (st * stage_bytes))) return st;
+    return 2;
+}
+
+}  // namespace sched
+
+// The automatic schedule. fnuz (the general kernel): one 256 x 128 tile per workgroup, never split.
+inline SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int64_t max_bytes) {
+    SplitPlan plan{1, 0, 0, geom::kFastBM, 0};
+    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    plan.bm = sched::fast_bm(M, N, cus);
+    if (sched::cdiv(M, geom::kFastBMSmall) * sched::cdiv(N, geom::kFastBN) < cus) {
+        const int bn = sched::thin_bn(M, N, cus);
+        const int64_t wgs = sched::cdiv(M, geom::kThinBM) * sched::cdiv(N, bn);
+        if (2 * wgs >= cus || sched::cdiv(K, geom::kBlockK) <= 64) {
+            plan.bm = geom::kThinBM;
+            plan.bn = bn;
+            return plan;
+        }
+    }
+    sched::fast_split(plan, M, N, K, cus, max_bytes);
+    return plan;
+}
+
+// A schedule chosen by the caller, so tests and sweeps can run any schedule on any shape: bm 64 --
+// the thin kernel with tile width bn (32, 64 or 128; other values: automatic), never split; bm 256
+// or 128 -- the fast kernel with that tile height and its automatic split; bm 0 -- automatic (its
+// thin width may be set by bn). S > 0 sets the slice count (clamped to the K-block count and to
+// max_bytes of workspace; below two: no split); a split runs on the fast kernel.
+inline SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fnuz, int cus, int S, int bm, int bn,
+                                        int64_t max_bytes) {
+    SplitPlan plan = gemm_split_plan(M, N, K, fnuz, cus, max_bytes);
+    if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
+    const bool bn_ok = bn == 32 || bn == 64 || bn == 128;
+    if (bm == geom::kThinBM) return SplitPlan{1, 0, 0, geom::kThinBM, bn_ok ? bn : sched::thin_bn(M, N, cus)};
+    const bool fast_forced = bm == geom::kFastBM || bm == geom::kFastBMSmall;
+    if (fast_forced || (S >= 2 && plan.bm == geom::kThinBM)) {
+        plan = SplitPlan{1, 0, 0, fast_forced ? bm : sched::fast_bm(M, N, cus), 0};
+        sched::fast_split(plan, M, N, K, cus, max_bytes);
+    } else if (plan.bm == geom::kThinBM && bn_ok) {
+        plan.bn = bn;
+    }
+    if (S <= 0 || plan.bm == geom::kThinBM) return plan;
+    plan.S = 1;
+    plan.ldp = 0;
+    plan.bytes = 0;
+    const int64_t Kb = sched::cdiv(K, geom::kBlockK);
+    const int64_t ldp = (N + 7) / 8 * 8;
+    const int64_t slice_bytes = M * ldp * 4;
+    int64_t s = S > Kb ? Kb : S;
+    if (s * slice_bytes > max_bytes) s = max_bytes / slice_bytes;
+    if (s > 65535) s = 65535;
+    if (s < 2) return plan;
+    plan.S = static_cast<int>(s);
+    plan.ldp = ldp;
+    plan.bytes = s * slice_bytes;
+    return plan;
+}
+
+}  // namespace bsfp8

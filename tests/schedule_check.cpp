@@ -1,0 +1,45 @@
+// Host driver for the GEMM schedule rules (blockwise_scaled_fp8_act_amd/csrc/schedule.hpp, the
+// header the library calls before each GEMM launch). Reads one query per line from stdin and
+// prints one answer per line:
+//   plan M N K fnuz cus max_bytes            -> S bm bn bytes
+//   forced M N K cus S bm bn max_bytes       -> S bm bn bytes
+//   stages bn per_col wgs cus                -> stages
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <iostream>
+#include <sstream>
+#include <string>
+
+#include "schedule.hpp"
+
+int main() {
+    std::string line;
+    while (std::getline(std::cin, line)) {
+        std::istringstream in(line);
+        std::string kind;
+        in >> kind;
+        if (kind == "plan") {
+            int64_t M, N, K, maxb;
+            int fnuz, cus;
+            in >> M >> N >> K >> fnuz >> cus >> maxb;
+            const bsfp8::SplitPlan p = bsfp8::gemm_split_plan(M, N, K, fnuz != 0, cus, maxb);
+            std::printf("%d %d %d %lld\n", p.S, p.bm, p.bn, (long long)p.bytes);
+        } else if (kind == "forced") {
+            int64_t M, N, K, maxb;
+            int cus, S, bm, bn;
+            in >> M >> N >> K >> cus >> S >> bm >> bn >> maxb;
+            const bsfp8::SplitPlan p = bsfp8::gemm_split_plan_forced(M, N, K, false, cus, S, bm, bn, maxb);
+            std::printf("%d %d %d %lld\n", p.S, p.bm, p.bn, (long long)p.bytes);
+        } else if (kind == "stages") {
+            int bn, per_col, cus;
+            int64_t wgs;
+            in >> bn >> per_col >> wgs >> cus;
+            std::printf("%d\n", bsfp8::sched::thin_stages(bn, per_col != 0, wgs, cus));
+        } else {
+            std::printf("?\n");
+        }
+        std::fflush(stdout);
+    }
+    return 0;
+}

@@ -1,0 +1,145 @@
+"""CPU check of the GEMM schedule rules (csrc/schedule.hpp, compiled with the host compiler): which
+kernel and tiles each shape takes, when K is split, and the thin kernel's pipeline depth -- for the
+workloads, the ROCm page's GEMM table shapes, the rule boundaries and the forced schedules the
+tests and sweeps use. 256 compute units (MI355X) unless stated."""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "blockwise_scaled_fp8_act_amd", "csrc")
+SRC = os.path.join(ROOT, "tests", "schedule_check.cpp")
+CUS = 256
+MAXB = 256 << 20  # the library's workspace bound for a split
+
+
+@pytest.fixture(scope="module")
+def sched(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("sched") / "schedule_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-Wall", "-I", CSRC, SRC, "-o", exe], check=True)
+
+    def ask(queries):
+        r = subprocess.run([exe], input="\n".join(queries) + "\n", capture_output=True, text=True, check=True)
+        return [tuple(int(v) for v in ln.split()) for ln in r.stdout.strip().split("\n")]
+    return ask
+
+
+def _plans(sched, shapes, fnuz=0, cus=CUS):
+    return sched([f"plan {M} {N} {K} {fnuz} {cus} {MAXB}" for (M, N, K) in shapes])
+
+
+# (M, N, K) -> (S, bm, bn): bm 256 / 128 the fast kernel, 64 the thin kernel (tile width bn)
+EXPECTED = {
+    (4096, 4096, 4096): (1, 256, 0),     # the bench step: one 256 x 256 tile per CU
+    (8192, 4096, 4096): (1, 256, 0),     # training-step forward / dgrad: two rounds
+    (4096, 4096, 8192): (1, 256, 0),     # weight gradient over 8192 tokens
+    (16384, 5120, 5120): (1, 256, 0),    # outlier workload
+    (4096, 5120, 5120): (1, 256, 0),     # 320 tiles: more than the CUs
+    (2048, 4096, 4096): (1, 128, 0),     # 128 tiles of 256 rows -> 256 of 128 rows
+    (2048, 8192, 4096): (1, 256, 0),
+    (1024, 4096, 4096): (1, 64, 128),    # 128-row tiles leave CUs idle: thin, 512 tiles of 64 x 128
+    (512, 4096, 4096): (1, 64, 64),      # 64 x 128 would give 256 tiles (one per CU): 64 x 64
+    (128, 4096, 4096): (1, 64, 32),      # no width gives two per CU: the narrowest
+    (130, 5120, 1280): (1, 64, 32),      # tail-masking workload
+    (2, 512, 128): (1, 64, 32),          # smallest workload
+    (64, 1024, 8192): (1, 64, 32),       # 32 thin tiles, K = 64 blocks: still thin
+    (64, 1024, 8320): (64, 128, 0),      # K = 65 blocks: split, 4 tiles x 64 slices = one round
+    (300, 520, 704): (1, 64, 32),
+}
+
+
+def test_automatic_schedule(sched):
+    shapes = list(EXPECTED)
+    got = _plans(sched, shapes)
+    for sh, g in zip(shapes, got):
+        assert g[:3] == EXPECTED[sh], (sh, g)
+
+
+def test_split_workspace_is_slices_of_padded_rows(sched):
+    (S, bm, bn, nbytes), = _plans(sched, [(64, 1000, 16384)])
+    assert bm == 128 and bn == 0 and S == 64
+    assert nbytes == S * 64 * 1000 * 4  # rows padded to 8 floats: 1000 already is
+    (S2, _, _, nbytes2), = _plans(sched, [(50, 1001, 16384)])
+    assert nbytes2 == S2 * 50 * 1008 * 4
+
+
+def test_fnuz_and_empty_problems_never_split(sched):
+    for g in _plans(sched, [(128, 4096, 4096), (2, 512, 128)], fnuz=1) + _plans(sched, [(0, 5, 5), (5, 0, 5), (5, 5, 0)]):
+        assert g[:3] == (1, 256, 0)
+
+
+def test_thin_kernel_boundary(sched):
+    """The thin kernel exactly when the 128-row tiles number fewer than the CUs (N = 4096: 16
+    column tiles, so at most cus / 16 - 1 row tiles), here and on a chip with 128 CUs."""
+    for cus in (256, 128):
+        last = (cus // 16 - 1) * 128  # the most rows whose 128-row tiles leave a CU idle
+        below, at = _plans(sched, [(last, 4096, 4096), (last + 1, 4096, 4096)], cus=cus)
+        assert below[1] == 64 and at[1] != 64, (cus, below, at)
+
+
+def test_thin_width_gives_two_workgroups_per_cu(sched):
+    for M in (64, 100, 128, 200, 256, 512, 700, 1024, 1536):
+        (_, bm, bn, _), = _plans(sched, [(M, 4096, 4096)])
+        assert bm == 64
+        wgs = lambda w: -(-M // 64) * -(-4096 // w)  # noqa: E731
+        wider = [w for w in (128, 64, 32) if w > bn]
+        assert bn == 32 or wgs(bn) >= 2 * CUS, (M, bn)
+        assert all(wgs(w) < 2 * CUS for w in wider), (M, bn)
+
+
+def test_split_slices_fit_one_round_and_the_workspace(sched):
+    for (M, N, K) in [(64, 256, 65536), (100, 512, 65536), (200, 512, 32768), (512, 256, 65536)]:
+        (S, bm, bn, nbytes), = _plans(sched, [(M, N, K)])
+        assert bn == 0 and S >= 2, (M, N, K)
+        tiles = -(-M // bm) * -(-N // 256)
+        assert S * tiles <= CUS and nbytes <= MAXB and S <= -(-K // 128)
+
+
+FORCED = [
+    # M, N, K, S, bm, bn -> S, bm, bn
+    ((512, 4096, 4096, 0, 64, 128), (1, 64, 128)),   # thin with a chosen width
+    ((512, 4096, 4096, 0, 64, 0), (1, 64, 64)),      # thin, automatic width
+    ((512, 4096, 4096, 3, 64, 0), (1, 64, 64)),      # the thin kernel never splits
+    ((512, 4096, 4096, 3, 0, 0), (3, 128, 0)),       # a forced split takes the fast kernel
+    ((128, 4096, 4096, 0, 128, 0), (12, 128, 0)),    # 128-row tiles with their automatic split
+    ((128, 4096, 4096, 1, 128, 0), (1, 128, 0)),     # ... and without a split
+    ((1024, 4096, 4096, 0, 256, 0), (1, 256, 0)),    # 256-row tiles: M > 512, never split
+    ((4096, 4096, 4096, 2, 0, 0), (2, 256, 0)),      # a split of the 256-row tiles
+    ((512, 4096, 4096, 0, 0, 32), (1, 64, 32)),      # the automatic thin plan with a chosen width
+    ((300, 520, 704, 100, 0, 0), (6, 128, 0)),       # S clamped to the 6 K-blocks
+]
+
+
+def test_forced_schedules(sched):
+    got = sched([f"forced {M} {N} {K} {CUS} {S} {bm} {bn} {MAXB}" for (M, N, K, S, bm, bn), _ in FORCED])
+    for (q, want), g in zip(FORCED, got):
+        assert g[:3] == want, (q, g)
+
+
+def test_forced_split_respects_the_workspace_bound(sched):
+    (S, bm, bn, nbytes), = sched([f"forced 512 1024 8192 {CUS} 64 0 0 {MAXB}"])
+    assert (S, bm, bn) == (64, 128, 0) and nbytes == 64 * 512 * 1024 * 4  # 128 MiB: over the 64 MiB scratch
+    (S, _, _, nbytes), = sched([f"forced 512 1024 8192 {CUS} 64 0 0 {64 << 20}"])
+    assert S == 32 and nbytes == 64 << 20
+
+
+STAGES = [
+    # bn, per_col, workgroups -> stages (160 KB of LDS per CU, 256 CUs)
+    ((32, 0, 256), 4),      # 12.6 KB stages: four fit three times per CU
+    ((32, 0, 768), 4),
+    ((32, 0, 769), 3),
+    ((64, 0, 512), 4),      # 16.7 KB stages: 66.6 KB, two per CU
+    ((64, 0, 513), 3),
+    ((128, 0, 256), 4),     # 24.8 KB stages: 99.4 KB, one per CU
+    ((128, 0, 512), 3),     # 74.5 KB, two per CU
+    ((128, 0, 768), 2),     # 49.7 KB, three per CU
+    ((128, 0, 5000), 2),    # more than one round at any depth: two
+    ((128, 1, 512), 3),
+]
+
+
+def test_thin_pipeline_depth(sched):
+    got = sched([f"stages {bn} {pc} {w} {CUS}" for (bn, pc, w), _ in STAGES])
+    for (q, want), g in zip(STAGES, got):
+        assert g[0] == want, (q, g)
