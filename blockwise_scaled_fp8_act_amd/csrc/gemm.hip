@@ -422,20 +422,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 namespace fast {
 
 constexpr int kBN = geom::kFastBN;
-constexpr int kWM = 64;
+constexpr int kWM = 64;                   // wave block rows of the 256-row tile
+constexpr int kWMSmall = 32;              // ... of the 128-row tile (8 waves, two per SIMD)
 constexpr int kWN = 128;
-constexpr int kMSub = kWM / 16;           // 4
 constexpr int kNSub = kWN / 16;           // 8
 constexpr int kStages = 2;
 
-// Tile geometry for tile height BM: 256 rows (8 waves, 4 (M) x 2 (N), two per SIMD) or 128 rows
-// (4 waves, 2 x 2, one per SIMD, for problems whose 256-row tiles would leave compute units idle).
-// Every wave computes a 64 x 128 block either way.
-template <int BM>
+// Tile geometry for tile height BM and wave block height WM (each wave computes a WM x 128 block):
+// BM 256, WM 64 -- 8 waves, 4 (M) x 2 (N), two per SIMD; BM 128, WM 32 -- 8 waves, 4 x 2, two per
+// SIMD, for problems whose 256-row tiles would leave compute units idle (10-17% faster than 4 waves
+// of 64 x 128, one per SIMD, which the template also describes: 2048 x 4096 x 4096 37.3 against
+// 43.0 us).
+template <int BM, int WM = kWM>
 struct Cfg {
-    static constexpr int kWaves = BM / 32;
-    static constexpr int kWavesM = BM / 64;
+    static constexpr int kWaveM = WM;
+    static constexpr int kMSub = WM / 16;       // 16-row subtiles per wave
+    static constexpr int kWavesM = BM / WM;
+    static constexpr int kWaves = 2 * kWavesM;
     static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kARows = BM / kWaves;  // A rows (and A scales) a wave loads: 32 or 16
+    static constexpr int kALoads = kARows / 8;
     static constexpr int kBRows = kBN / kWaves;  // B rows (and per-column B scales) a wave loads: 32 or 64
     static constexpr int kBLoads = kBRows / 8;
     // LDS image of one stage (16-byte units): A tile rows 0..BM-1, B tile rows 0..255, then the A
@@ -446,10 +452,10 @@ struct Cfg {
     static constexpr int kStageSA = kStageB + kBN * 8;
     static constexpr int kStageSB = kStageSA + BM / 4;
     static constexpr int kStageSize = kStageSB + kBN / 4;
-    // vector-memory instructions each wave issues per stage: 4 A loads and kBLoads B loads (8 rows
-    // of 128 bytes each), the A scales of 32 rows, the B scales (kBRows columns, or the two
+    // vector-memory instructions each wave issues per stage: kALoads A loads and kBLoads B loads (8
+    // rows of 128 bytes each), the A scales of kARows rows, the B scales (kBRows columns, or the two
     // column-block scales)
-    static constexpr int kLoads = 4 + kBLoads + 2;
+    static constexpr int kLoads = kALoads + kBLoads + 2;
     // a block's loads past the first four are issued two per subtile column over this many columns
     static constexpr int kPendCols = (kLoads - 3) / 2;
 };
@@ -532,27 +538,30 @@ __device__ __forceinline__ void dma4(uint32_t lds, __amdgpu_buffer_rsrc_t r, uin
         : "memory");
 }
 
-// Load number q of a stage, q = 0 .. kLoads - 1: 0..3 A rows 32 wave + 8 q .., then kBLoads B loads
-// of rows kBRows wave + 8 (q - 4) .., then the A scales of rows 32 wave .. + 32, then the B scales
+// Load number q of a stage, q = 0 .. kLoads - 1: kALoads A loads of rows kARows wave + 8 q .., then
+// kBLoads B loads of rows kBRows wave + 8 (q - kALoads) .., then the A scales of rows kARows wave ..
+// + kARows, then the B scales
 // (per column: of columns kBRows wave .. + kBRows; 128x128: the two column-block scales, by wave
 // 0). `on` (wave-uniform) false: the load is issued with no lane enabled, so nothing is read or
 // written. Every offset is the lane's offset in the load's resource (a position in the tensor, or
 // kOob for a scale outside it) plus this K-block's advance.
-template <bool PER_COL, int BM>
+template <bool PER_COL, int BM, int WM>
 __device__ __forceinline__ void issue_load(int q, const Ops& op, uint32_t stage_base, int64_t kb, int wave,
                                            bool on = true) {
-    using C = Cfg<BM>;
+    using C = Cfg<BM, WM>;
     const uint32_t k = geom::fast_operand_advance(kb);
     const uint64_t all = on ? ~0ull : 0ull;
     const uint64_t half = on ? 0xFFFFFFFFull : 0ull;
-    if (q < 4) {
-        dma16(stage_base + (C::kStageA + (32 * wave + 8 * q) * 8) * 16, op.a[q], op.a_lane[q & 1] + k, all);
-    } else if (q < 4 + C::kBLoads) {
-        const int qb = q - 4;
+    const uint64_t a_rows = on ? (C::kARows == 32 ? 0xFFFFFFFFull : 0xFFFFull) : 0ull;
+    if (q < C::kALoads) {
+        dma16(stage_base + (C::kStageA + (C::kARows * wave + 8 * q) * 8) * 16, op.a[q], op.a_lane[q & 1] + k, all);
+    } else if (q < C::kALoads + C::kBLoads) {
+        const int qb = q - C::kALoads;
         dma16(stage_base + (C::kStageB + (C::kBRows * wave + 8 * qb) * 8) * 16, op.b[qb & 3],
               op.b_lane[(qb & 1) + 2 * (qb >> 2)] + k, all);
-    } else if (q == 4 + C::kBLoads) {
-        dma4(stage_base + C::kStageSA * 16 + 128 * wave, op.as, op.as_base + static_cast<uint32_t>(kb * op.as_step), half);
+    } else if (q == C::kALoads + C::kBLoads) {
+        dma4(stage_base + C::kStageSA * 16 + 4 * C::kARows * wave, op.as,
+             op.as_base + static_cast<uint32_t>(kb * op.as_step), a_rows);
     } else if (PER_COL) {
         dma4(stage_base + C::kStageSB * 16 + 4 * C::kBRows * wave, op.bs,
              op.bs_base + static_cast<uint32_t>(kb * op.bs_step), C::kBRows == 64 ? all : half);
@@ -575,21 +584,22 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool PER_COL, int GROUP, int BM>
-__global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
+template <bool PER_COL, int GROUP, int BM, int WM = kWM>
+__global__ __launch_bounds__((Cfg<BM, WM>::kThreads), 1) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb,
     int64_t bs_kb, uint16_t* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt,
     int nt, int c_vec, Grouping grp) {
-    using Cf = Cfg<BM>;
+    using Cf = Cfg<BM, WM>;
     constexpr int kStageA = Cf::kStageA, kStageB = Cf::kStageB, kStageSA = Cf::kStageSA, kStageSB = Cf::kStageSB;
     constexpr int kStageSize = Cf::kStageSize, kLoads = Cf::kLoads;
+    constexpr int kMSub = Cf::kMSub;
     __shared__ u32x4 smem[kStages * kStageSize];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % Cf::kWavesM;  // rows 64 wm .. of the tile
+    const int wm = wave % Cf::kWavesM;  // rows WM wm .. of the tile
     const int wn = wave / Cf::kWavesM;  // columns 128 wn .. of the tile
     const int l16 = lane & 15;
     const int lg = lane >> 4;
@@ -672,11 +682,11 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
         op.as = make_rsrc(a_s, M * Kb * 4);
         op.bs = make_rsrc(b_s, PER_COL ? N * Kb * 4 : 4 * geom::bscale_blk_extent(N, Kb, bs_nb, bs_kb));
 #pragma unroll
-        for (int par = 0; par < 2; ++par) op.a_lane[par] = geom::fast_operand_lane(32, wave, par, lane, lda);
+        for (int par = 0; par < 2; ++par) op.a_lane[par] = geom::fast_operand_lane(Cf::kARows, wave, par, lane, lda);
 #pragma unroll
         for (int v = 0; v < (Cf::kBLoads > 4 ? 4 : 2); ++v)
             op.b_lane[v] = geom::fast_operand_lane(Cf::kBRows, wave, (v & 1) + 4 * (v >> 1), lane, ldb);
-        op.as_base = geom::fast_ascale_base(m0, m_end, wave, lane);
+        op.as_base = geom::fast_ascale_base(Cf::kARows, m0, m_end, wave, lane);
         op.as_step = 4 * M;
         if (PER_COL) {
             op.bs_base = geom::fast_bscale_col_base(Cf::kBRows, n0, N, wave, lane);
@@ -708,7 +718,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
 
         // prologue: block 0 into stage 0
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM>(q, op, stage_base(0), 0, wave);
+        for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM, WM>(q, op, stage_base(0), 0, wave);
         wait_own_loads<0>();
 
         // Bytes of the last K-block that lie below K (128 when K % 128 == 0). Its loads read whole
@@ -726,11 +736,11 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
         lds_barrier();
         if (Kb > 1) {
 #pragma unroll
-            for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM>(q, op, stage_base(1), 1, wave);
+            for (int q = 0; q < kLoads; ++q) issue_load<PER_COL, BM, WM>(q, op, stage_base(1), 1, wave);
         }
 
         auto read_a = [&](const u32x4* st, int i, bool tail) {
-            const int r = 64 * wm + 16 * i + l16;
+            const int r = WM * wm + 16 * i + l16;
             const v8i v = to_v8i(st[kStageA + r * 8 + pos_lo], st[kStageA + r * 8 + pos_hi]);
             return tail ? tail_mask(v) : v;
         };
@@ -747,7 +757,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
         // the factor a_s[m, kb] (times the 128x128 B scale of the wave's column block) of each of
         // the lane's four rows
         auto read_factors = [&](const u32x4* st, float (&fo)[kMSub]) {
-            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + 64 * wm;
+            const float* sa = reinterpret_cast<const float*>(st + kStageSA) + WM * wm;
             const float bsc = PER_COL ? 1.0f : reinterpret_cast<const float*>(st + kStageSB)[wn];
 #pragma unroll
             for (int i = 0; i < kMSub; ++i) fo[i] = PER_COL ? sa[16 * i + l16] : sa[16 * i + l16] * bsc;
@@ -811,7 +821,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
                     const bool more = kb + 2 < Kb;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        issue_load<PER_COL, BM>(q, op, stage_base(cur), more ? kb + 2 : kb, wave, more);
+                        issue_load<PER_COL, BM, WM>(q, op, stage_base(cur), more ? kb + 2 : kb, wave, more);
                     // slots 0 and 1 were last used by subtiles 4 and 5
                     bf[0] = read_b(stn, 0, false);
                     bf[1] = read_b(stn, 1, false);
@@ -822,8 +832,8 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
                     // block after its barrier; block 0 issues none, the prologue loaded block 1)
                     const bool pend = kb >= 1 && kb + 1 < Kb;
                     const int64_t pkb = pend ? kb + 1 : kb;
-                    if (4 + 2 * j < kLoads) issue_load<PER_COL, BM>(4 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
-                    if (5 + 2 * j < kLoads) issue_load<PER_COL, BM>(5 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
+                    if (4 + 2 * j < kLoads) issue_load<PER_COL, BM, WM>(4 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
+                    if (5 + 2 * j < kLoads) issue_load<PER_COL, BM, WM>(5 + 2 * j, op, stage_base(cur ^ 1), pkb, wave, pend);
                 }
                 if (j + 2 < kNSub) bf[(j + 2) % 4] = read_b(st, j + 2, TAIL);
                 v4f bsj;
@@ -873,7 +883,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
         float* P = reinterpret_cast<float*>(C) + static_cast<int64_t>(blockIdx.y) * grp.c_stride;
 #pragma unroll
         for (int i = 0; i < kMSub; ++i) {
-            const int64_t m = geom::fast_partial_row(m0, wm, i, lane);
+            const int64_t m = geom::fast_partial_row(WM, m0, wm, i, lane);
             if (m >= m_end) continue;
 #pragma unroll
             for (int j = 0; j < kNSub; ++j) {
@@ -889,7 +899,7 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
     // lines (a lane's own outputs are 4 columns of one row). Row r of a block holds 16 chunks of 16
     // bytes, chunk c at position c ^ (r % 16), which keeps both LDS passes free of bank conflicts.
     __syncthreads();
-    uint8_t* cblk = reinterpret_cast<uint8_t*>(smem) + wave * (kWM * kWN * 2);
+    uint8_t* cblk = reinterpret_cast<uint8_t*>(smem) + wave * (WM * kWN * 2);
 #pragma unroll
     for (int i = 0; i < kMSub; ++i) {
         const int r = 16 * i + l16;
@@ -904,10 +914,10 @@ __global__ __launch_bounds__(Cfg<BM>::kThreads, 1) void gemm_kernel(
     }
     const int cc = lane & 15;  // 16-byte chunk (8 columns) of a row
 #pragma unroll
-    for (int p = 0; p < kWM / 4; ++p) {
+    for (int p = 0; p < WM / 4; ++p) {
         const int r = 4 * p + (lane >> 4);
         const u32x4 v = *reinterpret_cast<const u32x4*>(cblk + r * 256 + ((cc ^ (r & 15)) * 16));
-        const int64_t m = geom::fast_store_row(m0, wm, p, lane);
+        const int64_t m = geom::fast_store_row(WM, m0, wm, p, lane);
         if (m >= m_end) continue;
         const int64_t n = geom::fast_store_col(n0, wn, lane);
         uint16_t* dst = C + m * ldc + n;
@@ -1189,11 +1199,11 @@ hipError_t gemm_scratch(float** out) {
 namespace {
 
 // The fast kernel with tile height BM, unsplit or split over plan.S slices.
-template <int BM>
+template <int BM, int WM>
 hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
                        BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K,
                        const SplitPlan& plan, float* workspace, int cus, hipStream_t stream) {
-    constexpr int kThreads = fast::Cfg<BM>::kThreads;
+    constexpr int kThreads = fast::Cfg<BM, WM>::kThreads;
     const int64_t mt = (M + BM - 1) / BM;
     const int64_t nt = (N + fast::kBN - 1) / fast::kBN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
@@ -1206,10 +1216,10 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
         const dim3 grid(static_cast<unsigned>(mt * nt), static_cast<unsigned>(plan.S));
         uint16_t* P = reinterpret_cast<uint16_t*>(workspace);
         if (bs.per_column)
-            fast::gemm_kernel<true, fast::kSplitK, BM><<<grid, kThreads, 0, stream>>>(
+            fast::gemm_kernel<true, fast::kSplitK, BM, WM><<<grid, kThreads, 0, stream>>>(
                 a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
         else
-            fast::gemm_kernel<false, fast::kSplitK, BM><<<grid, kThreads, 0, stream>>>(
+            fast::gemm_kernel<false, fast::kSplitK, BM, WM><<<grid, kThreads, 0, stream>>>(
                 a, lda, a_s, b, ldb, bs.ptr, nb, kbs, P, plan.ldp, M, N, K, (int)mt, (int)nt, 0, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1225,10 +1235,10 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
     const dim3 grid(static_cast<unsigned>(mt * nt));
     const fast::Grouping none{nullptr, 0, 0, 0, 0, nullptr};
     if (bs.per_column)
-        fast::gemm_kernel<true, fast::kGroupNone, BM><<<grid, kThreads, 0, stream>>>(
+        fast::gemm_kernel<true, fast::kGroupNone, BM, WM><<<grid, kThreads, 0, stream>>>(
             a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
     else
-        fast::gemm_kernel<false, fast::kGroupNone, BM><<<grid, kThreads, 0, stream>>>(
+        fast::gemm_kernel<false, fast::kGroupNone, BM, WM><<<grid, kThreads, 0, stream>>>(
             a, lda, a_s, b, ldb, bs.ptr, nb, kbs, c, ldc, M, N, K, (int)mt, (int)nt, c_vec16, none);
     return hipGetLastError();
 }
@@ -1279,8 +1289,8 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
             return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
         }
         if (plan.bm == fast::kBMSmall)
-            return launch_fast<fast::kBMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
-        return launch_fast<fast::kBM>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
+            return launch_fast<fast::kBMSmall, fast::kWMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
+        return launch_fast<fast::kBM, fast::kWM>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);
     }
     // float8_e4m3fnuz: general kernel
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);

@@ -54,17 +54,14 @@ BSFP8_HD void tile_of(int bid, int mt, int nt, int& tm, int& tn) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fast GEMM kernel: BM x 256 tiles, BM = 256 (8 waves) or 128 (4 waves); wave w owns rows
-// 64 wm.. (wm = w % (BM / 64)) and columns 128 wn.. (wn = w / (BM / 64)) of the tile. Each
-// K-block's operand tiles are loaded by the waves together, 16 bytes per lane, straight into LDS:
-// every wave loads 32 rows of the A tile and 256 / waves rows (32 or 64) of the B tile.
+// Fast GEMM kernel: BM x 256 tiles of 2 BM / WM waves, BM = 256 with WM = 64 (8 waves) or BM = 128
+// with WM = 64 (4 waves) or 32 (8 waves); wave w owns rows WM wm.. (wm = w % (BM / WM)) and columns
+// 128 wn.. (wn = w / (BM / WM)) of the tile. Each K-block's operand tiles are loaded by the waves
+// together, 16 bytes per lane, straight into LDS: every wave loads BM / waves rows of the A tile
+// (32 or 16) and 256 / waves rows of the B tile (32 or 64).
 constexpr int kFastBM = 256;
 constexpr int kFastBN = 256;
-constexpr int kFastWaves = 8;
 constexpr int kFastBMSmall = 128;
-constexpr int kFastWavesSmall = 4;
-BSFP8_HD int fast_waves(int bm) { return bm == kFastBMSmall ? kFastWavesSmall : kFastWaves; }
-BSFP8_HD int fast_b_rows_per_wave(int bm) { return kFastBN / fast_waves(bm); }
 
 // Operand load q (0 .. rows_per_wave / 8 - 1) of a wave whose share of the tile is rows_per_wave
 // rows (32 for A; 32 or 64 for B): tile row rows_per_wave * wave + 8 q + lane / 8, 16-byte chunk
@@ -93,11 +90,12 @@ BSFP8_HD int64_t fast_operand_range(int q, int64_t rows_in_range, int64_t ld) {
 }
 BSFP8_HD uint32_t fast_operand_advance(int64_t kb) { return static_cast<uint32_t>(kb * kBlockK); }
 
-// A scales of a K-block: lanes 0..31 of each wave load one fp32 each, tile row 32 wave + lane
-// (LDS float 32 wave + lane). a_s is column-major [M, Kb] with ld M: element (m, kb) at kb * M + m.
-BSFP8_HD uint32_t fast_ascale_base(int64_t m0, int64_t m_end, int wave, int lane) {
-    const int64_t m = m0 + 32 * wave + lane;
-    return (lane < 32 && m < m_end) ? static_cast<uint32_t>(4 * m) : kOob;
+// A scales of a K-block: lanes 0 .. rows_per_wave - 1 of each wave (rows_per_wave = the A rows a
+// wave loads, 32 or 16) load one fp32 each, tile row rows_per_wave wave + lane (LDS float of the
+// same index). a_s is column-major [M, Kb] with ld M: element (m, kb) at kb * M + m.
+BSFP8_HD uint32_t fast_ascale_base(int rows_per_wave, int64_t m0, int64_t m_end, int wave, int lane) {
+    const int64_t m = m0 + rows_per_wave * wave + lane;
+    return (lane < rows_per_wave && m < m_end) ? static_cast<uint32_t>(4 * m) : kOob;
 }
 BSFP8_HD uint32_t fast_ascale_advance(int64_t kb, int64_t M) { return static_cast<uint32_t>(4 * kb * M); }
 
@@ -132,16 +130,20 @@ BSFP8_HD uint32_t tail_keep_mask(int krem, int lg, int d) {
     return keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
 }
 
-// bf16 epilogue: pass p (0..15) of a wave stores 16 bytes per lane: row 64 wm + 4 p + lane / 16,
-// columns 128 wn + 8 (lane % 16) .. + 8 of the tile; element n + e is stored iff row < m_end and
-// n + e < N.
-BSFP8_HD int64_t fast_store_row(int64_t m0, int wm, int p, int lane) { return m0 + 64 * wm + 4 * p + (lane >> 4); }
+// bf16 epilogue: pass p (0 .. WM / 4 - 1) of a wave (a block of WM = 64 or 32 rows) stores 16 bytes
+// per lane: row WM wm + 4 p + lane / 16, columns 128 wn + 8 (lane % 16) .. + 8 of the tile; element
+// n + e is stored iff row < m_end and n + e < N.
+BSFP8_HD int64_t fast_store_row(int wave_rows, int64_t m0, int wm, int p, int lane) {
+    return m0 + wave_rows * wm + 4 * p + (lane >> 4);
+}
 BSFP8_HD int64_t fast_store_col(int64_t n0, int wn, int lane) { return n0 + 128 * wn + 8 * (lane & 15); }
 
 // fp32 partial epilogue (split K): subtile (i, j) of a wave stores a lane's four totals at row
-// 64 wm + 16 i + lane % 16, columns 128 wn + 16 j + 4 (lane / 16) .. + 4 of the tile, iff the row is
+// WM wm + 16 i + lane % 16, columns 128 wn + 16 j + 4 (lane / 16) .. + 4 of the tile, iff the row is
 // below m_end and the first column below N (the partial rows are padded to a multiple of 4 floats).
-BSFP8_HD int64_t fast_partial_row(int64_t m0, int wm, int i, int lane) { return m0 + 64 * wm + 16 * i + (lane & 15); }
+BSFP8_HD int64_t fast_partial_row(int wave_rows, int64_t m0, int wm, int i, int lane) {
+    return m0 + wave_rows * wm + 16 * i + (lane & 15);
+}
 BSFP8_HD int64_t fast_partial_col(int64_t n0, int wn, int j, int lane) { return n0 + 128 * wn + 16 * j + 4 * (lane >> 4); }
 
 // Split K: slice s of S owns K-blocks [split_begin(Kb, S, s), split_begin(Kb, S, s + 1)).

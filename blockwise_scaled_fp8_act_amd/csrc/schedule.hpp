@@ -4,13 +4,14 @@
 // shape by shape.
 //
 // The rules, from measurements on MI355X (256 CUs; settled clock):
-//   * 256 x 256 tiles (8 waves, two per SIMD) run the K-loop fastest and are kept whenever they
-//     give every CU a tile; a problem with fewer 256-row tiles than half the CUs, or with
-//     M <= 128 (a 256-row tile would be at least half empty), takes 128 x 256 tiles (4 waves, one
-//     per SIMD; twice the tiles);
-//   * when even the 128-row tiles number fewer than the CUs, the problem is bound by moving
+//   * 256 x 256 tiles (8 waves of 64 x 128, two per SIMD) run the K-loop fastest and are kept
+//     whenever they give every CU a tile; a problem with at most half as many 256-row tiles as CUs,
+//     or with M <= 128 (a 256-row tile would be at least half empty), takes 128 x 256 tiles (8
+//     waves of 32 x 128; twice the tiles);
+//   * when the 128-row tiles would fill at most half the CUs, the problem is bound by moving
 //     operands into the CUs, not by the matrix cores, and takes the thin kernel's 64-row tiles,
-//     the widest (128, 64 or 32 columns) that still give two workgroups per CU;
+//     the widest (128, 64 or 32 columns) that still give two workgroups per CU (1024 x 4096 x
+//     4096: 27.3 us in 64 x 128 thin tiles, 32.9 in 128 x 256 tiles; 1536 rows: 38.0 against 33.3);
 //   * only when those are fewer than half the CUs and K is longer than 64 blocks does K get split
 //     instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64 slices, 27
 //     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
@@ -100,7 +101,7 @@ inline SplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K, bool fnuz, int
     SplitPlan plan{1, 0, 0, geom::kFastBM, 0};
     if (fnuz || M <= 0 || N <= 0 || K <= 0) return plan;
     plan.bm = sched::fast_bm(M, N, cus);
-    if (sched::cdiv(M, geom::kFastBMSmall) * sched::cdiv(N, geom::kFastBN) < cus) {
+    if (2 * sched::cdiv(M, geom::kFastBMSmall) * sched::cdiv(N, geom::kFastBN) <= cus) {
         const int bn = sched::thin_bn(M, N, cus);
         const int64_t wgs = sched::cdiv(M, geom::kThinBM) * sched::cdiv(N, bn);
         if (2 * wgs >= cus || sched::cdiv(K, geom::kBlockK) <= 64) {

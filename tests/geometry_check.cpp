@@ -13,12 +13,14 @@
 //   * the partial-K-block masks keep exactly the fragment bytes below K;
 //   * quantize_lhs stores each scale of the column-major [M, Kb] tensor exactly once and never a row
 //     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm").
-// Both tile heights of the fast kernel (256 rows, 8 waves; 128 rows, 4 waves) and the three tile
-// widths of the thin kernel (64 rows by 32, 64 or 128 columns, 4 waves) are enumerated.
+// The fast kernel's three tile shapes (256 rows, 8 waves of 64 rows; 128 rows, 4 waves of 64 rows or
+// 8 waves of 32 rows) and the three tile widths of the thin kernel (64 rows by 32, 64 or 128
+// columns, 4 waves) are enumerated.
 // Usage: geometry_check M N K [M N K ...]; prints one line per shape, exits 1 on the first failure.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <utility>
 #include <vector>
 
 #include "geometry.hpp"
@@ -100,9 +102,10 @@ static bool check_fast_operand(int64_t r0, int64_t rows, int64_t total_rows, int
     return true;
 }
 
-// bm: the tile height (256: 8 waves; 128: 4 waves).
-static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bm) {
-    const int waves = fast_waves(bm), wms = bm / 64, cpw = fast_b_rows_per_wave(bm);
+// bm: the tile height; wr: the rows of a wave's block (256 / 64: 8 waves; 128 / 64: 4 waves; 128 /
+// 32: 8 waves). Each wave loads bm / waves rows of A and 256 / waves rows of B.
+static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bm, int wr) {
+    const int wms = bm / wr, waves = 2 * wms, cpw = kFastBN / waves, apw = bm / waves;
     const int mt = static_cast<int>(cdiv(M, bm)), nt = static_cast<int>(cdiv(N, kFastBN));
     const int64_t Kb = cdiv(K, kBlockK);
     if (!check_tiles(mt, nt)) return false;
@@ -116,22 +119,23 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
             const int64_t arows = M - m0 < bm ? M - m0 : bm;
             const int64_t brows = N - n0 < kFastBN ? N - n0 : kFastBN;
             for (int64_t kb = 0; kb < Kb; ++kb) {
-                if (!check_fast_operand(m0, arows, M, lda, K, kb, 32, waves)) return false;
+                if (!check_fast_operand(m0, arows, M, lda, K, kb, apw, waves)) return false;
                 if (!check_fast_operand(n0, brows, N, ldb, K, kb, cpw, waves)) return false;
-                // A scales: lanes 0..31 of each wave (the others are switched off); per-column B
-                // scales: lanes 0 .. cpw - 1
+                // A scales: lanes 0 .. apw - 1 of each wave (the others are switched off); per-column
+                // B scales: lanes 0 .. cpw - 1
                 std::vector<uint8_t> sa(256, 0), sbc(256, 0);
                 for (int wave = 0; wave < waves; ++wave)
                     for (int lane = 0; lane < 64; ++lane) {
                         bool ok;
-                        if (lane < 32) {
-                            const uint64_t off = static_cast<uint64_t>(fast_ascale_base(m0, M, wave, lane)) + fast_ascale_advance(kb, M);
+                        if (lane < apw) {
+                            const uint64_t off = static_cast<uint64_t>(fast_ascale_base(apw, m0, M, wave, lane)) + fast_ascale_advance(kb, M);
                             const bool in = access(off, 4 * M * Kb, 4, ok);
                             CHECK(ok, "a_s offset");
-                            const int64_t m = m0 + 32 * wave + lane;
+                            const int64_t m = m0 + apw * wave + lane;
+                            CHECK(apw * wave + lane < bm, "a_s LDS float past the tile");
                             if (m < M) {
                                 CHECK(in && static_cast<int64_t>(off) == 4 * (kb * M + m), "a_s[%lld, %lld] address", (long long)m, (long long)kb);
-                                ++sa[32 * wave + lane];
+                                ++sa[apw * wave + lane];
                             } else {
                                 CHECK(!in, "a_s row %lld >= M read", (long long)m);
                             }
@@ -169,9 +173,10 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
             }
             // bf16 epilogue
             for (int wave = 0; wave < waves; ++wave)
-                for (int p = 0; p < 16; ++p)
+                for (int p = 0; p < wr / 4; ++p)
                     for (int lane = 0; lane < 64; ++lane) {
-                        const int64_t m = fast_store_row(m0, wave % wms, p, lane);
+                        const int64_t m = fast_store_row(wr, m0, wave % wms, p, lane);
+                        CHECK(m - m0 < bm, "output row outside the tile");
                         const int64_t n = fast_store_col(n0, wave / wms, lane);
                         if (m >= M) continue;
                         for (int e = 0; e < 8; ++e)
@@ -183,8 +188,8 @@ static bool check_fast(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
 }
 
 // Split K: slices partition the K-blocks; each slice's fp32 partial tile covers every output once.
-static bool check_split(int64_t M, int64_t N, int64_t K, int bm) {
-    const int waves = fast_waves(bm), wms = bm / 64;
+static bool check_split(int64_t M, int64_t N, int64_t K, int bm, int wr) {
+    const int wms = bm / wr, waves = 2 * wms;
     const int64_t Kb = cdiv(K, kBlockK);
     for (int64_t S = 1; S <= Kb && S <= 40; ++S) {
         int64_t next = 0;
@@ -201,10 +206,10 @@ static bool check_split(int64_t M, int64_t N, int64_t K, int bm) {
     for (int tm = 0; tm < mt; ++tm)
         for (int tn = 0; tn < nt; ++tn)
             for (int wave = 0; wave < waves; ++wave)
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < wr / 16; ++i)
                     for (int j = 0; j < 8; ++j)
                         for (int lane = 0; lane < 64; ++lane) {
-                            const int64_t m = fast_partial_row(static_cast<int64_t>(tm) * bm, wave % wms, i, lane);
+                            const int64_t m = fast_partial_row(wr, static_cast<int64_t>(tm) * bm, wave % wms, i, lane);
                             const int64_t n = fast_partial_col(static_cast<int64_t>(tn) * kFastBN, wave / wms, j, lane);
                             if (m >= M || n >= N) continue;
                             CHECK(n % 4 == 0 && n + 4 <= ldp, "partial store past the padded row");
@@ -517,9 +522,9 @@ int main(int argc, char** argv) {
         const int64_t M = std::atoll(argv[a]), N = std::atoll(argv[a + 1]), K = std::atoll(argv[a + 2]);
         const int64_t ld = (K + 15) / 16 * 16;  // the GEMMs' 16-byte row rule
         bool ok = true;
-        for (int bm : {kFastBM, kFastBMSmall})
-            ok = ok && check_fast(M, N, K, ld, ld, bm) && check_fast(M, N, K, ld + 16, ld + 48, bm) &&
-                 check_split(M, N, K, bm);
+        for (const auto& t : {std::pair<int, int>{kFastBM, 64}, {kFastBMSmall, 64}, {kFastBMSmall, 32}})
+            ok = ok && check_fast(M, N, K, ld, ld, t.first, t.second) &&
+                 check_fast(M, N, K, ld + 16, ld + 48, t.first, t.second) && check_split(M, N, K, t.first, t.second);
         for (int bn : {32, 64, 128})
             ok = ok && check_thin(M, N, K, ld, ld, bn) && check_thin(M, N, K, ld + 16, ld + 48, bn);
         ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);

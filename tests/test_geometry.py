@@ -70,8 +70,8 @@ def _planted(tmp_path, old, new, name):
 def test_unmasked_scale_read_is_caught(tmp_path):
     """The bug of the masking page: the A-scale read of rows >= M left unmasked."""
     exe = _planted(tmp_path,
-                   "return (lane < 32 && m < m_end) ? static_cast<uint32_t>(4 * m) : kOob;",
-                   "return lane < 32 ? static_cast<uint32_t>(4 * m) : kOob;", "planted_read")
+                   "return (lane < rows_per_wave && m < m_end) ? static_cast<uint32_t>(4 * m) : kOob;",
+                   "return lane < rows_per_wave ? static_cast<uint32_t>(4 * m) : kOob;", "planted_read")
     r = _run(exe, [(130, 256, 256)])
     assert r.returncode != 0 and "a_s row" in r.stdout, r.stdout
 

@@ -368,8 +368,9 @@ THIN_SHAPES = SPLIT_SHAPES + [
 @pytest.mark.parametrize("M,N,K,ld", THIN_SHAPES, ids=lambda v: str(v))
 def test_gemm_thin_schedule(M, N, K, ld, bn, per_col, monkeypatch):
     """The thin kernel (BSFP8_GEMM_TILE_M=64, tile width BSFP8_GEMM_TILE_N) on ragged shapes:
-    against the oracle in full, and bit for bit against the fast kernel's 128-row tiles without a
-    split, which apply the same per-K-block arithmetic in the same order."""
+    against the oracle in full, and bit for bit against the fast kernel's 128-row tiles (8 waves of
+    32 rows) and 256-row tiles (8 waves of 64 rows) without a split: the three apply the same
+    per-K-block arithmetic to every output in the same order."""
     qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + 3 * N + K + bn, per_col)
     monkeypatch.delenv("BSFP8_GEMM_SPLIT", raising=False)
     if per_col:
@@ -382,11 +383,12 @@ def test_gemm_thin_schedule(M, N, K, ld, bn, per_col, monkeypatch):
     monkeypatch.setenv("BSFP8_GEMM_TILE_N", str(bn))
     got = _run_guarded(fn, M, N, N + 3)
     _assert_close(got, co, f"thin {bn}")
-    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "128")
     monkeypatch.setenv("BSFP8_GEMM_SPLIT", "1")
     monkeypatch.delenv("BSFP8_GEMM_TILE_N")
-    fast = _run_guarded(fn, M, N, N + 3)
-    assert np.array_equal(got.view(np.uint32), fast.view(np.uint32)), "thin and fast kernels differ"
+    for bm in (128, 256):
+        monkeypatch.setenv("BSFP8_GEMM_TILE_M", str(bm))
+        fast = _run_guarded(fn, M, N, N + 3)
+        assert np.array_equal(got.view(np.uint32), fast.view(np.uint32)), f"thin and {bm}-row tiles differ"
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2048, 4096, 4096),

@@ -37,8 +37,9 @@ EXPECTED = {
     (16384, 5120, 5120): (1, 256, 0),    # outlier workload
     (4096, 5120, 5120): (1, 256, 0),     # 320 tiles: more than the CUs
     (2048, 4096, 4096): (1, 128, 0),     # 128 tiles of 256 rows -> 256 of 128 rows
+    (1536, 4096, 4096): (1, 128, 0),     # 192 tiles of 128 rows: more than half the CUs
     (2048, 8192, 4096): (1, 256, 0),
-    (1024, 4096, 4096): (1, 64, 128),    # 128-row tiles leave CUs idle: thin, 512 tiles of 64 x 128
+    (1024, 4096, 4096): (1, 64, 128),    # 128 tiles of 128 rows, half the CUs: thin, 512 of 64 x 128
     (512, 4096, 4096): (1, 64, 64),      # 64 x 128 would give 256 tiles (one per CU): 64 x 64
     (128, 4096, 4096): (1, 64, 32),      # no width gives two per CU: the narrowest
     (130, 5120, 1280): (1, 64, 32),      # tail-masking workload
@@ -70,16 +71,16 @@ def test_fnuz_and_empty_problems_never_split(sched):
 
 
 def test_thin_kernel_boundary(sched):
-    """The thin kernel exactly when the 128-row tiles number fewer than the CUs (N = 4096: 16
-    column tiles, so at most cus / 16 - 1 row tiles), here and on a chip with 128 CUs."""
+    """The thin kernel exactly when the 128-row tiles would fill at most half the CUs (N = 4096:
+    16 column tiles, so at most cus / 32 row tiles), here and on a chip with 128 CUs."""
     for cus in (256, 128):
-        last = (cus // 16 - 1) * 128  # the most rows whose 128-row tiles leave a CU idle
+        last = cus // 32 * 128  # the most rows whose 128-row tiles fill at most half the CUs
         below, at = _plans(sched, [(last, 4096, 4096), (last + 1, 4096, 4096)], cus=cus)
         assert below[1] == 64 and at[1] != 64, (cus, below, at)
 
 
 def test_thin_width_gives_two_workgroups_per_cu(sched):
-    for M in (64, 100, 128, 200, 256, 512, 700, 1024, 1536):
+    for M in (64, 100, 128, 200, 256, 512, 700, 1000, 1024):
         (_, bm, bn, _), = _plans(sched, [(M, 4096, 4096)])
         assert bm == 64
         wgs = lambda w: -(-M // 64) * -(-4096 // w)  # noqa: E731
