@@ -970,7 +970,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 
 // ==============================================================================================
 // Thin kernel: 64 x BN tiles (BN = 32, 64 or 128) of 4 waves (2 x 2, each 32 x BN/2), for problems
-// whose 128-row tiles of the fast kernel would leave compute units idle (few rows: the short-and-
+// whose 128-row tiles of the fast kernel would fill at most half the CUs (few rows: the short-and-
 // wide GEMMs). Such a problem is bound by moving operands into the CUs, not by the matrix cores, so
 // it takes more, smaller tiles (several workgroups per CU), every one over the whole K range: no
 // partial tiles to sum. Each K-block's A and B rows go global -> LDS by the fast kernel's direct
