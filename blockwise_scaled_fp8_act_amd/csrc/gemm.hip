@@ -16,12 +16,13 @@
 //     per-lane register, and a lane whose row, column or scale lies outside the tensor gets an
 //     out-of-range offset (geometry.hpp, whose arithmetic the CPU tests enumerate lane by lane);
 //     outputs of rows >= M or columns >= N are never stored.
-// The fast kernel (namespace fast) serves every float8_e4m3fn GEMM, a partial last K-block
+// The fast kernel (namespace fast) serves the float8_e4m3fn GEMMs, a partial last K-block
 // included, in 256 x 256 tiles, or in 128 x 256 tiles when the larger ones would leave CUs idle;
-// for short-and-wide shapes whose tiles still leave most CUs idle it splits K over several
-// workgroups per tile (fp32 partial tiles, summed by a second kernel; gemm_split_plan). The general
-// kernel (namespace gen) serves the float8_e4m3fnuz operands. Both zero the bytes of a partial last
-// K-block that lie at or past K.
+// the thin kernel (namespace thin) serves short-and-wide shapes whose 128-row tiles would fill at
+// most half the CUs, in 64-row tiles over the whole K range; when even those are few and K is long,
+// the fast kernel splits K over several workgroups per tile (fp32 partial tiles, summed by a second
+// kernel). The rules are in schedule.hpp. The general kernel (namespace gen) serves the
+// float8_e4m3fnuz operands. All zero the bytes of a partial last K-block that lie at or past K.
 //
 // float8_e4m3fnuz operands (the format of the ROCm page's MI300X runs, FP8_MAX 240): gfx950's FP8
 // matrix instructions read e4m3fn, and no power-of-two rescaling maps every fnuz value onto an
@@ -409,7 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
 // ==============================================================================================
 // Fast kernel: a 256 x 256 workgroup tile of 8 waves, two per SIMD, each wave owning a 64 x 128
-// block of the tile (128 fp32 totals in VGPRs).
+// block of the tile (128 fp32 totals in VGPRs); the 128 x 256 tile has 8 waves of 32 x 128. The
+// figures below are those of the 256-row tile.
 //   * Every K-block's A tile (256 x 128 bytes), B tile (256 x 128 bytes) and scale slices go
 //     global -> LDS by direct buffer loads (no registers) into one of two LDS stages. Each wave
 //     loads 1/8 of every tile; a workgroup barrier that follows each wave's wait for its own loads
