@@ -158,6 +158,16 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
     return finish(e != hipSuccess ? e : f);
 }
 
+// BSFP8_QUANT_LHS_STRIP (environment, read at each call): 1, 2, 4, 8 or 16 runs quantize_lhs in
+// row strips of that many 16-byte pieces per thread wherever the alignment allows, 0 always in
+// tiles, so tests and benchmarks can compare the variants. Unset or empty: automatic.
+int env_lhs_strip() {
+    const char* v = std::getenv("BSFP8_QUANT_LHS_STRIP");
+    if (v == nullptr || *v == 0) return 0;
+    const long n = std::strtol(v, nullptr, 10);
+    return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 ? static_cast<int>(n) : -1;
+}
+
 int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
                       float* a_s, bool fnuz, void* stream) {
     if (M < 0 || K < 0) return BSFP8_EINVAL;
@@ -166,7 +176,7 @@ int quantize_lhs_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
     if (ldx < K || ldq < K) return BSFP8_EINVAL;
     if (int rc = check_device()) return rc;
     return finish(bsfp8::launch_quantize_lhs(static_cast<const uint16_t*>(x), M, K, ldx,
-                                             static_cast<uint8_t*>(q), ldq, a_s, fnuz,
+                                             static_cast<uint8_t*>(q), ldq, a_s, fnuz, env_lhs_strip(),
                                              static_cast<hipStream_t>(stream)));
 }
 

@@ -279,5 +279,62 @@ BSFP8_HD int64_t colmajor_index(int64_t kb, int64_t M, int64_t m) { return kb * 
 // a row's codes and scale are stored only when the row is inside the tensor
 BSFP8_HD bool row_stored(int64_t m, int64_t M) { return m < M; }
 
+// quantize_lhs, row strips (the path for K % 16 == 0 with 16-byte aligned rows). A 512-thread
+// workgroup owns a strip: `rows` consecutive rows times a chunk of g K-blocks. Its bf16 input is
+// cut into 16-byte pieces numbered row-major, p = r * 16 g + cp (cp: the 8-column piece of the
+// chunk row); thread t loads pieces t + 512 j. A 1x128 group is 16 aligned consecutive pieces, so
+// its 16 lanes are one aligned 16-lane row of a wave. The codes go to LDS row-major and leave as
+// 16-byte pieces numbered the same way, s = r * 8 g + cs; the chunk's scales leave K-block by
+// K-block, `rows` consecutive floats of a column-major scale column each.
+constexpr int kStripThreads = 512;
+struct StripShape {
+    int rows;        // rows per strip
+    int g;           // K-blocks per chunk
+    int loads;       // 16-byte input pieces per thread (the last may be partial across the workgroup)
+    int64_t chunks;  // chunks per row
+    int64_t units;   // workgroups: strips x chunks, chunk fastest
+};
+// Strip of `loads_max` pieces per thread: chunks of at most 32 K-blocks split K evenly, and as many
+// rows as fill 512 x loads_max pieces.
+BSFP8_HD StripShape strip_shape(int64_t M, int64_t Kb, int loads_max) {
+    StripShape s;
+    s.chunks = (Kb + 31) / 32;
+    s.g = static_cast<int>((Kb + s.chunks - 1) / s.chunks);
+    s.rows = kStripThreads * loads_max / (16 * s.g);
+    s.loads = (s.rows * 16 * s.g + kStripThreads - 1) / kStripThreads;
+    s.units = (M + s.rows - 1) / s.rows * s.chunks;
+    return s;
+}
+BSFP8_HD void strip_unit(int64_t u, int64_t chunks, int64_t& strip, int64_t& chunk) {
+    strip = u / chunks;
+    chunk = u - strip * chunks;
+}
+// input piece p of the strip: row m0 + p / (16 g), columns c0 + 8 (p % (16 g)) .. + 7; it holds
+// data when p < rows * 16 g, the row is < M and the column < K (K % 8 == 0: all 8 or none)
+BSFP8_HD bool strip_piece(int p, const StripShape& s, int64_t m0, int64_t c0, int64_t M, int64_t K,
+                          int64_t& m, int64_t& c) {
+    const int per_row = 16 * s.g;
+    m = m0 + p / per_row;
+    c = c0 + 8 * (p % per_row);
+    return p < s.rows * per_row && m < M && c < K;
+}
+// output piece q of the strip (16 code bytes): row m0 + q / (8 g), byte column c0 + 16 (q % (8 g));
+// stored when q < rows * 8 g, the row is < M and the column < K (K % 16 == 0: all 16 or none)
+BSFP8_HD bool strip_out_piece(int q, const StripShape& s, int64_t m0, int64_t c0, int64_t M, int64_t K,
+                              int64_t& m, int64_t& c) {
+    const int per_row = 8 * s.g;
+    m = m0 + q / per_row;
+    c = c0 + 16 * (q % per_row);
+    return q < s.rows * per_row && m < M && c < K;
+}
+// scale i of the strip (i < rows * g): K-block kb0 + i / rows of row m0 + i % rows, stored at
+// a_s[kb * M + m] when the row is < M and the K-block < Kb
+BSFP8_HD bool strip_scale(int i, const StripShape& s, int64_t m0, int64_t kb0, int64_t M, int64_t Kb,
+                          int64_t& kb, int64_t& m) {
+    kb = kb0 + i / s.rows;
+    m = m0 + i % s.rows;
+    return i < s.rows * s.g && m < M && kb < Kb;
+}
+
 }  // namespace geom
 }  // namespace bsfp8

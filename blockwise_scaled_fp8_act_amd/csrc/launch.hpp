@@ -9,8 +9,11 @@
 namespace bsfp8 {
 
 // fnuz: float8_e4m3fnuz codes (FP8_MAX 240) instead of float8_e4m3fn (FP8_MAX 448).
+// strip_loads: 0 = automatic (row strips of sched::lhs_strip_loads pieces per thread where the
+// alignment allows, else tiles); 1, 2, 4, 8 or 16 = row strips of that many where the alignment
+// allows; -1 = always the tile kernel.
 hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                               int64_t ldq, float* a_s, bool fnuz, hipStream_t stream);
+                               int64_t ldq, float* a_s, bool fnuz, int strip_loads, hipStream_t stream);
 hipError_t launch_quantize_dual(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint8_t* q,
                                 int64_t ldq, float* a_s, uint8_t* qT, int64_t ldqT, float* s,
                                 bool fnuz, hipStream_t stream);

@@ -153,6 +153,67 @@ __global__ __launch_bounds__(256) void quantize_lhs_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// 1x128 in row strips (16-byte aligned rows, K % 16 == 0): a 512-thread workgroup reads a strip of
+// whole rows (or a chunk of at most 32 K-blocks of them) -- NL 16-byte pieces per thread, all in
+// flight together -- encodes it into LDS, and only then writes it: codes as 16-byte pieces of
+// contiguous rows, scales as runs of consecutive rows of each column-major scale column. Each
+// workgroup's reads and writes are long contiguous streams and its read and write phases do not
+// interleave, which the HBM serves faster than the tile kernel's 256-byte pieces of many rows with
+// loads and stores mixed (8192 x 4096: 17.4 against 19.5 us; 4096 x 4096: 8.7 against 10.7 us).
+template <bool FNUZ, int NL>
+__global__ __launch_bounds__(geom::kStripThreads) void quantize_lhs_strip_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ a_s, int64_t Kb, geom::StripShape sh) {
+    constexpr int T = geom::kStripThreads;
+    __shared__ uint2 codes[T * NL];      // the strip's codes, row-major [rows][128 g] bytes
+    __shared__ float scl[T * NL / 16];   // its scales, row-major [rows][g]
+
+    const int t = threadIdx.x;
+    int64_t strip, chunk;
+    geom::strip_unit(blockIdx.x, sh.chunks, strip, chunk);
+    const int64_t m0 = strip * sh.rows, kb0 = chunk * sh.g, c0 = kb0 * kGroup;
+
+    uint32_t w[NL][4];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        int64_t m, c;
+        const bool in = geom::strip_piece(t + T * j, sh, m0, c0, M, K, m, c);
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (in ? m * ldx + c : 0)));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[j][d] = in ? v[d] : 0u;
+    }
+    // pieces past the strip hold zeros; their codes and scales land in LDS slots nothing reads
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) am = max(am, max((w[j][d] << 16) & 0x7FFFFFFFu, w[j][d] & 0x7FFF0000u));
+        am = umax_row16(am);
+        const GroupScale g = group_scale<FNUZ>(__uint_as_float(am));
+        const int p = t + T * j;
+        codes[p] = make_uint2(encode4_in_range<FNUZ>(bf16_lo(w[j][0]) * g.m, bf16_hi(w[j][0]) * g.m,
+                                                     bf16_lo(w[j][1]) * g.m, bf16_hi(w[j][1]) * g.m),
+                              encode4_in_range<FNUZ>(bf16_lo(w[j][2]) * g.m, bf16_hi(w[j][2]) * g.m,
+                                                     bf16_lo(w[j][3]) * g.m, bf16_hi(w[j][3]) * g.m));
+        if ((t & 15) == 0) scl[p >> 4] = g.s;
+    }
+    __syncthreads();
+    const u32x4* cs = reinterpret_cast<const u32x4*>(codes);
+#pragma unroll
+    for (int i = 0; i < (NL + 1) / 2; ++i) {
+        int64_t m, c;
+        const int qi = t + T * i;
+        if (geom::strip_out_piece(qi, sh, m0, c0, M, K, m, c))
+            __builtin_nontemporal_store(cs[qi], reinterpret_cast<u32x4*>(q + m * ldq + c));
+    }
+    for (int i = t; i < sh.rows * sh.g; i += T) {
+        int64_t kb, m;
+        if (geom::strip_scale(i, sh, m0, kb0, M, Kb, kb, m))
+            a_s[geom::colmajor_index(kb, M, m)] = scl[(i % sh.rows) * sh.g + i / sh.rows];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // 128x1 with transposed output: a workgroup owns one K-block (128 rows) x 64 columns.
 // Thread t loads 4 consecutive rows (4*(t/8) ..) x 8 columns (8*(t%8) ..); column maxima go
 // through LDS; the 4 codes of a column form one dword of the transposed tile, which is then
@@ -699,8 +760,25 @@ bool aligned(const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a)
 
 template <bool FNUZ>
 hipError_t quantize_lhs_impl(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                             int64_t ldq, float* a_s, hipStream_t stream) {
+                             int64_t ldq, float* a_s, int strip_loads, hipStream_t stream) {
     const int64_t Kb = (K + kGroup - 1) / kGroup;
+    if (strip_loads >= 0 && aligned(x, 16) && ldx % 8 == 0 && aligned(q, 16) && ldq % 16 == 0 && K % 16 == 0) {
+        const int nl = strip_loads > 0 ? strip_loads : sched::lhs_strip_loads(M, Kb, device_cus());
+        const geom::StripShape sh = geom::strip_shape(M, Kb, nl);
+        const dim3 grid(static_cast<unsigned>(sh.units));
+#define BSFP8_QS(N) \
+    quantize_lhs_strip_kernel<FNUZ, N><<<grid, geom::kStripThreads, 0, stream>>>(x, M, K, ldx, q, ldq, a_s, Kb, sh)
+        switch (nl) {
+            case 16: BSFP8_QS(16); break;
+            case 8: BSFP8_QS(8); break;
+            case 4: BSFP8_QS(4); break;
+            case 2: BSFP8_QS(2); break;
+            case 1: BSFP8_QS(1); break;
+            default: return hipErrorInvalidValue;
+        }
+#undef BSFP8_QS
+        return hipGetLastError();
+    }
     const int64_t units = (M + kLhsRows - 1) / kLhsRows * Kb;
     const int64_t most = static_cast<int64_t>(device_cus()) * kLhsWgPerCu;
     const dim3 grid(static_cast<unsigned>(units < most ? units : most));
@@ -824,9 +902,9 @@ hipError_t quantize_step_impl(const uint16_t* x, int64_t M, int64_t K, int64_t l
 }  // namespace
 
 hipError_t launch_quantize_lhs(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
-                               int64_t ldq, float* a_s, bool fnuz, hipStream_t stream) {
-    return fnuz ? quantize_lhs_impl<true>(x, M, K, ldx, q, ldq, a_s, stream)
-                : quantize_lhs_impl<false>(x, M, K, ldx, q, ldq, a_s, stream);
+                               int64_t ldq, float* a_s, bool fnuz, int strip_loads, hipStream_t stream) {
+    return fnuz ? quantize_lhs_impl<true>(x, M, K, ldx, q, ldq, a_s, strip_loads, stream)
+                : quantize_lhs_impl<false>(x, M, K, ldx, q, ldq, a_s, strip_loads, stream);
 }
 
 hipError_t launch_quantize_rhs(const uint16_t* x, int64_t K, int64_t N, int64_t ldx, uint8_t* qT,
@@ -868,7 +946,7 @@ hipError_t launch_quantize_step(const uint16_t* x, int64_t M, int64_t K, int64_t
                      ldqx % 8 == 0 && aligned(qw, 8) && ldqw % 8 == 0 &&
                      (qwT == nullptr || (aligned(qwT, 16) && ldqwT % 16 == 0 && N % 16 == 0));
     if (!vec) {
-        const hipError_t e = launch_quantize_lhs(x, M, K, ldx, qx, ldqx, sx, fnuz, stream);
+        const hipError_t e = launch_quantize_lhs(x, M, K, ldx, qx, ldqx, sx, fnuz, 0, stream);
         if (e != hipSuccess) return e;
         return launch_quantize_weight(w, N, Kw, ldw, qw, ldqw, qwT, ldqwT, sw, fnuz, stream);
     }

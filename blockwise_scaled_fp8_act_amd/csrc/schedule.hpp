@@ -49,6 +49,32 @@ constexpr int64_t kLdsPerCu = 160 * 1024;  // LDS bytes of a gfx950 compute unit
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// quantize_lhs in row strips: 16-byte input pieces per thread (1, 2, 4, 8 or 16; the strip height
+// follows) for an M x (128 Kb) activation. A workgroup of 16 pieces per thread holds 66 KB of LDS
+// (two per CU), one of 8 or fewer at most four per CU (32 waves of 8-wave workgroups). The rules,
+// from a sweep on MI355X:
+//   * when some strip size gives every CU at least two workgroups and still lets the whole grid be
+//     resident at once, the largest such size (4096 x 4096: 8 pieces, 9.8 us, against 11.0 us with
+//     4 and 10.8 us in tiles; 8192 x 4096: 16 pieces, 18.7 us, against 19.4 with 4);
+//   * when every size needs more rounds of workgroups than one, 4 pieces: small workgroups that
+//     come and go keep the HBM busier than big ones that wait for whole strips (16384 x 4096:
+//     35.0 us, against 36.2 with 16 and 39.7 in tiles; 32768 x 4096: 66.5 against 69.9);
+//   * when even one piece per thread leaves CUs with fewer than two workgroups, one piece (the
+//     most workgroups; these shapes take a few microseconds whatever the choice).
+inline int strip_resident(int nl) {
+    // LDS of the strip kernel: 8 code bytes per piece, one fp32 scale per 16 pieces
+    const int64_t lds = static_cast<int64_t>(geom::kStripThreads) * nl * 8 + geom::kStripThreads * nl / 16 * 4;
+    const int64_t by_lds = kLdsPerCu / lds;
+    return static_cast<int>(by_lds < 4 ? by_lds : 4);
+}
+inline int lhs_strip_loads(int64_t M, int64_t Kb, int cus) {
+    for (const int nl : {16, 8, 4, 2, 1}) {
+        const int64_t u = geom::strip_shape(M, Kb, nl).units;
+        if (u >= 2 * static_cast<int64_t>(cus) && u <= static_cast<int64_t>(strip_resident(nl)) * cus) return nl;
+    }
+    return geom::strip_shape(M, Kb, 1).units < 2 * static_cast<int64_t>(cus) ? 1 : 4;
+}
+
 // The fast kernel's tile height for M x N.
 inline int fast_bm(int64_t M, int64_t N, int cus) {
     const int64_t tiles256 = cdiv(M, geom::kFastBM) * cdiv(N, geom::kFastBN);

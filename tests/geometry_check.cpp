@@ -12,7 +12,8 @@
 //     epilogue, split-K partial tiles), and the split slices partition the K-blocks;
 //   * the partial-K-block masks keep exactly the fragment bytes below K;
 //   * quantize_lhs stores each scale of the column-major [M, Kb] tensor exactly once and never a row
-//     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm").
+//     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm"), in its
+//     tile kernel and in its row-strip kernel (whose code reads and stores are checked too).
 // The fast kernel's three tile shapes (256 rows, 8 waves of 64 rows; 128 rows, 4 waves of 64 rows or
 // 8 waves of 32 rows) and the three tile widths of the thin kernel (64 rows by 32, 64 or 128
 // columns, 4 waves) are enumerated.
@@ -516,6 +517,70 @@ static bool check_lhs_scales(int64_t M, int64_t K) {
     return true;
 }
 
+// ---------------------------------------------------------------------------------------------
+// quantize_lhs in row strips (K % 16 == 0), every pieces-per-thread count the library launches:
+// each input piece of 8 columns is read once and lands in the LDS slot of its (row, K-block) group,
+// a group's 16 pieces sit in one aligned 16-lane row of a wave, each 16-byte output piece is written
+// once from the LDS bytes its two input pieces encoded, each scale once from its group's LDS slot,
+// and no row >= M and no column >= K is read or written.
+static bool check_lhs_strips(int64_t M, int64_t K) {
+    if (K % 16 != 0) return true;  // such shapes run the tile kernel
+    const int64_t Kb = cdiv(K, kBlockK);
+    for (int nl : {1, 2, 4, 8, 16}) {
+        const StripShape sh = strip_shape(M, Kb, nl);
+        CHECK(sh.g >= 1 && sh.g <= 32 && sh.rows >= 1, "strip shape nl=%d: rows %d g %d", nl, sh.rows, sh.g);
+        CHECK(sh.rows * 16 * sh.g <= kStripThreads * nl && sh.loads <= nl, "strip of nl=%d overflows", nl);
+        CHECK(sh.chunks * sh.g >= Kb && (sh.chunks - 1) * sh.g < Kb, "strip chunks nl=%d", nl);
+        std::vector<uint8_t> rd(static_cast<size_t>(M) * (K / 8), 0), wr(static_cast<size_t>(M) * (K / 16), 0);
+        std::vector<uint8_t> sc(static_cast<size_t>(M) * Kb, 0);
+        for (int64_t u = 0; u < sh.units; ++u) {
+            int64_t strip, chunk;
+            strip_unit(u, sh.chunks, strip, chunk);
+            const int64_t m0 = strip * sh.rows, kb0 = chunk * sh.g, c0 = kb0 * kBlockK;
+            CHECK(kb0 < Kb && m0 < M, "strip unit %lld outside the tensor", (long long)u);
+            for (int t = 0; t < kStripThreads; ++t) {
+                for (int j = 0; j < nl; ++j) {
+                    const int p = t + kStripThreads * j;
+                    int64_t m, c;
+                    if (!strip_piece(p, sh, m0, c0, M, K, m, c)) continue;
+                    CHECK(m >= 0 && m < M && c >= 0 && c + 8 <= K && c % 8 == 0, "strip read row %lld col %lld", (long long)m, (long long)c);
+                    CHECK(++rd[static_cast<size_t>(m * (K / 8) + c / 8)] == 1, "strip piece read twice");
+                    // the group of 16 aligned lanes: one row, one K-block, lane t % 16 at piece t % 16
+                    CHECK(c / kBlockK == kb0 + (p % (16 * sh.g)) / 16 && (c % kBlockK) / 8 == (t & 15) &&
+                              m == m0 + (p >> 4) / sh.g,
+                          "strip group of lane %d", t);
+                    CHECK(p < kStripThreads * nl && (p >> 4) < kStripThreads * nl / 16, "strip LDS slot");
+                }
+                for (int i = 0; i < (nl + 1) / 2; ++i) {
+                    const int q = t + kStripThreads * i;
+                    int64_t m, c;
+                    if (!strip_out_piece(q, sh, m0, c0, M, K, m, c)) continue;
+                    CHECK(m >= 0 && m < M && c >= 0 && c + 16 <= K && c % 16 == 0, "strip store row %lld col %lld", (long long)m, (long long)c);
+                    CHECK(++wr[static_cast<size_t>(m * (K / 16) + c / 16)] == 1, "strip piece stored twice");
+                    CHECK(16 * (q + 1) <= 8 * kStripThreads * nl, "strip LDS read past the codes");
+                    // LDS bytes 16 q .. 16 q + 15 hold the codes of input pieces 2 q and 2 q + 1
+                    int64_t ma, ca, mb, cb;
+                    const bool ia = strip_piece(2 * q, sh, m0, c0, M, K, ma, ca);
+                    const bool ib = strip_piece(2 * q + 1, sh, m0, c0, M, K, mb, cb);
+                    CHECK(ia && ib && ma == m && mb == m && ca == c && cb == c + 8, "strip store of piece %d", q);
+                }
+            }
+            for (int i = 0; i < sh.rows * sh.g; ++i) {
+                int64_t kb, m;
+                if (!strip_scale(i, sh, m0, kb0, M, Kb, kb, m)) continue;
+                const int64_t idx = colmajor_index(kb, M, m);
+                CHECK(m < M && kb < Kb && idx >= 0 && idx < M * Kb, "strip a_s store of row %lld (index %lld)", (long long)m, (long long)idx);
+                CHECK(++sc[static_cast<size_t>(idx)] == 1, "strip a_s[%lld] stored twice", (long long)idx);
+                CHECK((i % sh.rows) * sh.g + i / sh.rows == (m - m0) * sh.g + (kb - kb0), "strip scale slot");
+            }
+        }
+        for (size_t i = 0; i < rd.size(); ++i) CHECK(rd[i] == 1, "strip piece %zu not read (nl=%d)", i, nl);
+        for (size_t i = 0; i < wr.size(); ++i) CHECK(wr[i] == 1, "strip piece %zu not stored (nl=%d)", i, nl);
+        for (size_t i = 0; i < sc.size(); ++i) CHECK(sc[i] == 1, "strip a_s[%zu] not stored (nl=%d)", i, nl);
+    }
+    return true;
+}
+
 int main(int argc, char** argv) {
     if (!check_tail_masks()) return 1;
     for (int a = 1; a + 2 < argc; a += 3) {
@@ -527,7 +592,7 @@ int main(int argc, char** argv) {
                  check_fast(M, N, K, ld + 16, ld + 48, t.first, t.second) && check_split(M, N, K, t.first, t.second);
         for (int bn : {32, 64, 128})
             ok = ok && check_thin(M, N, K, ld, ld, bn) && check_thin(M, N, K, ld + 16, ld + 48, bn);
-        ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K);
+        ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K) && check_lhs_strips(M, K);
         std::printf("%s M=%lld N=%lld K=%lld\n", ok ? "ok" : "FAILED", (long long)M, (long long)N, (long long)K);
         if (!ok) return 1;
     }

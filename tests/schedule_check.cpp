@@ -4,6 +4,7 @@
 //   plan M N K fnuz cus max_bytes            -> S bm bn bytes
 //   forced M N K cus S bm bn max_bytes       -> S bm bn bytes
 //   stages bn per_col wgs cus                -> stages
+//   lhs M Kb cus                             -> pieces per thread of quantize_lhs's row strips
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -36,6 +37,11 @@ int main() {
             int64_t wgs;
             in >> bn >> per_col >> wgs >> cus;
             std::printf("%d\n", bsfp8::sched::thin_stages(bn, per_col != 0, wgs, cus));
+        } else if (kind == "lhs") {
+            int64_t M, Kb;
+            int cus;
+            in >> M >> Kb >> cus;
+            std::printf("%d\n", bsfp8::sched::lhs_strip_loads(M, Kb, cus));
         } else {
             std::printf("?\n");
         }

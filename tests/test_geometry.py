@@ -6,8 +6,9 @@ row and column), extended to every operand and scale read, every output store an
 quantizer's column-major scale stores (root-cause comment of "Enable blockwise FP8 dense training
 kernels on ROCm").
 
-Two planted mistakes -- the pages' two bugs, an A-scale read without the row mask and a scale store
-without the row mask -- are compiled into scratch copies of the header and must make the check fail.
+Planted mistakes -- the pages' two bugs, an A-scale read without the row mask and a scale store
+without the row mask (in the tile and in the row-strip LHS quantizer), and lane masks of the GEMM
+kernels -- are compiled into scratch copies of the header and must make the check fail.
 """
 import itertools
 import os
@@ -58,6 +59,15 @@ def test_workload_shapes(checker):
     assert r.returncode == 0, r.stdout[-2000:]
 
 
+def test_lhs_strip_shapes(checker):
+    """quantize_lhs's row strips: K with a partial last group (144, 4112), K split into chunks of
+    K-blocks (5248 = 41 blocks in chunks of 21 and 20, 8192, 12304), ragged strips of rows."""
+    shapes = [(130, 1, 144), (1, 1, 16), (257, 1, 4112), (4097, 1, 5248), (8192, 1, 8192),
+              (4096, 1, 4096), (2, 1, 1280), (3, 1, 640), (1000, 1, 12304)]
+    r = _run(checker, shapes)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
 def _planted(tmp_path, old, new, name):
     d = tmp_path / name
     d.mkdir()
@@ -82,6 +92,14 @@ def test_unmasked_scale_store_is_caught(tmp_path):
                    "BSFP8_HD bool row_stored(int64_t m, int64_t M) { return m < M + 64; }", "planted_store")
     r = _run(exe, [(130, 256, 256)])
     assert r.returncode != 0 and "a_s store" in r.stdout, r.stdout
+
+
+def test_unmasked_strip_scale_store_is_caught(tmp_path):
+    """The root-cause comment's bug in the row-strip kernel: scale stores of rows >= M."""
+    exe = _planted(tmp_path, "return i < s.rows * s.g && m < M && kb < Kb;",
+                   "return i < s.rows * s.g && kb < Kb;", "planted_strip")
+    r = _run(exe, [(130, 1, 256)])
+    assert r.returncode != 0 and "strip a_s store" in r.stdout, r.stdout
 
 
 def test_planted_operand_row_read_is_caught(tmp_path):

@@ -66,7 +66,8 @@ def test_encode_fnuz_exhaustive_vs_oracle(chunk):
 # ------------------------------------------------------------------ quantizers
 
 LHS_SHAPES = [(2, 128, 128, 128), (130, 1280, 1280, 1280), (3, 127, 128, 127),
-              (65, 384, 392, 400), (129, 4100, 4104, 4112)]
+              (65, 384, 392, 400), (129, 4100, 4104, 4112),
+              (300, 5248, 5256, 5264), (4096, 4096, 4096, 4096)]  # row strips: chunked K, one round
 
 
 @pytest.mark.parametrize("M,K,ldx,ldq", LHS_SHAPES, ids=lambda v: str(v))

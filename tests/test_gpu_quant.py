@@ -80,6 +80,35 @@ def test_quantize_lhs_parity(M, K, ldx, ldq):
     assert np.array_equal(a_s.host().view(np.uint32), os_.view(np.uint32))
 
 
+# row strips (K % 16 == 0, aligned rows): partial last groups, K cut into chunks of K-blocks
+# (5248: 41 blocks in chunks of 21 and 20; 12304: 97 in 4), ragged strips; the last two shapes
+# are not eligible (ldq % 16 != 0, K % 16 != 0) and run the tile kernel under every setting
+STRIP_SHAPES = [
+    (130, 144, 144, 144), (257, 4112, 4112, 4112), (300, 5248, 5256, 5264), (33, 12304, 12304, 12304),
+    (2, 640, 640, 640), (1000, 1280, 1288, 1296), (4096, 4096, 4096, 4096),
+    (77, 1280, 1280, 1288), (50, 1160, 1160, 1168),
+]
+
+
+@pytest.mark.parametrize("M,K,ldx,ldq", STRIP_SHAPES, ids=lambda v: str(v))
+def test_quantize_lhs_every_strip_size(M, K, ldx, ldq, monkeypatch):
+    """Every strip size and the tile kernel (BSFP8_QUANT_LHS_STRIP = 0) give the oracle's codes and
+    scales bit for bit, with nothing written outside the tensors."""
+    xh = _rand_bf16((M, K), seed=M * 11 + K)
+    oq, os_ = oracle.quantize_lhs(xh)
+    x = bf16_view(M, K, ldx, xh)
+    for setting in ("", "0", "1", "2", "4", "8", "16"):
+        monkeypatch.setenv("BSFP8_QUANT_LHS_STRIP", setting)
+        q = GuardedU8(M, K, ldq)
+        a_s = GuardedF32((_cdiv(K, 128), M))
+        bf.quantize_lhs(x, q.view, a_s.view)
+        torch.cuda.synchronize()
+        q.check_untouched()
+        a_s.check_untouched()
+        assert np.array_equal(q.host(), oq), setting
+        assert np.array_equal(a_s.host().view(np.uint32), os_.view(np.uint32)), setting
+
+
 def test_quantize_lhs_edge_values():
     """Zero and negative-zero groups (eps path), +-448 boundaries, subnormal-range products,
     huge and tiny magnitudes."""

@@ -144,3 +144,36 @@ def test_thin_pipeline_depth(sched):
     got = sched([f"stages {bn} {pc} {w} {CUS}" for (bn, pc, w), _ in STAGES])
     for (q, want), g in zip(STAGES, got):
         assert g[0] == want, (q, g)
+
+
+# quantize_lhs row strips: (M, K) -> 16-byte pieces per thread
+LHS_EXPECTED = {
+    (4096, 4096): 8,      # 512 strips of 8 rows: two per CU, all resident
+    (8192, 4096): 16,     # 512 strips of 16 rows
+    (16384, 4096): 4,     # no size fits one round: 4
+    (32768, 4096): 4,
+    (2048, 4096): 4,      # 512 strips of 4 rows
+    (1024, 4096): 2,
+    (512, 4096): 1,       # 512 single rows
+    (256, 4096): 1,       # fewer than two per CU even with one row each
+    (2, 128): 1,
+    (4096, 1280): 2,      # 10 K-blocks: 6-row strips of 2 pieces per thread, 683 of them
+    (8192, 1280): 4,
+    (4096, 7168): 8,      # two chunks of 28 K-blocks
+    (4096, 14336): 4,     # four chunks of 28: more than one round at every size
+}
+
+
+def test_lhs_strip_sizes(sched):
+    shapes = list(LHS_EXPECTED)
+    got = sched([f"lhs {M} {(K + 127) // 128} {CUS}" for (M, K) in shapes])
+    for sh, g in zip(shapes, got):
+        assert g[0] == LHS_EXPECTED[sh], (sh, g)
+
+
+def test_lhs_strip_size_is_always_launchable(sched):
+    """Every answer is one of the instantiated sizes, for M from 1 to 65536 and K up to 32768."""
+    qs = [f"lhs {M} {kb} {cus}" for M in (1, 7, 100, 513, 3000, 12345, 65536)
+          for kb in (1, 2, 9, 32, 33, 100, 256) for cus in (256, 128, 80)]
+    for g in sched(qs):
+        assert g[0] in (1, 2, 4, 8, 16)
