@@ -86,8 +86,13 @@ const char* bsfp8_status_string(int status);
  *   a_s column-major [M, ceil(K/128)] fp32 with leading dimension exactly M: the scale of row m,
  *       K-block kb is a_s[kb * M + m] (the layout of the ROCm page's root-cause comment; nothing
  *       past M * ceil(K/128) floats is written).
- * Any alignment and row length are accepted; 16-byte-aligned rows whose length is a multiple of 8
- * take the vector path (the others load and store element by element).
+ * Any alignment and row length are accepted. With x and q 16-byte aligned, ldx % 8 == 0,
+ * ldq % 16 == 0 and K % 16 == 0 each workgroup reads a strip of whole rows (or of up to 32
+ * K-blocks of them) and then writes it; other 16-byte-aligned rows whose length is a multiple of 8
+ * take the vector tile path, the rest load and store element by element. The result is the same
+ * on every path. The environment variable BSFP8_QUANT_LHS_STRIP (1, 2, 4, 8, 16: strips of that
+ * many 16-byte pieces per thread; 0: tiles), read at each call, overrides the choice for tests
+ * and sweeps.
  */
 int quantize_lhs(const void* x, int64_t M, int64_t K, int64_t ldx,
                  void* q, int64_t ldq, float* a_s, void* stream);
