@@ -25,6 +25,8 @@
 
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "geometry.hpp"
 
 namespace bsfp8 {

@@ -177,3 +177,12 @@ def test_lhs_strip_size_is_always_launchable(sched):
           for kb in (1, 2, 9, 32, 33, 100, 256) for cus in (256, 128, 80)]
     for g in sched(qs):
         assert g[0] in (1, 2, 4, 8, 16)
+
+
+def test_header_is_self_contained(tmp_path):
+    """schedule.hpp compiles on its own (nothing it needs comes from an earlier include)."""
+    src = tmp_path / "only.cpp"
+    src.write_text('#include "schedule.hpp"\nint main() { return bsfp8::sched::lhs_strip_loads(8192, 32, 256) == 16 ? 0 : 1; }\n')
+    exe = str(tmp_path / "only")
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I", CSRC, str(src), "-o", exe], check=True)
+    assert subprocess.run([exe]).returncode == 0
