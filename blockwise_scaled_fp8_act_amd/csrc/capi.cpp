@@ -110,11 +110,12 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M and BSFP8_GEMM_TILE_N (environment, read at each call): a
-// slice count (1 = never split), a tile height (256 or 128: the fast kernel; 64: the thin kernel)
-// and the thin kernel's tile width (32, 64 or 128) that replace the automatic choices of
-// gemm_split_plan, so tests and benchmarks can run every schedule on any shape. Unset or empty:
-// automatic.
+// BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N and BSFP8_GEMM_THIN_STAGES (environment,
+// read at each call): a slice count (1 = never split), a tile height (256 or 128: the fast kernel;
+// 64: the thin kernel), the thin kernel's tile width (32, 64 or 128) and its LDS stages (2, 3, 4, 6,
+// 8 or 12, as far as the tile's stages fit the LDS; others fail with BSFP8_EHIP) that replace the
+// automatic choices of gemm_split_plan, so tests and benchmarks can run every schedule on any
+// shape. Unset or empty: automatic.
 int env_int(const char* name) {
     const char* v = std::getenv(name);
     if (v == nullptr || *v == 0) return 0;
@@ -131,10 +132,11 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
     const int cus = bsfp8::device_cus();
     const int forced_s = env_int("BSFP8_GEMM_SPLIT"), forced_bm = env_int("BSFP8_GEMM_TILE_M");
     const int forced_bn = env_int("BSFP8_GEMM_TILE_N");
-    const bsfp8::SplitPlan plan =
+    bsfp8::SplitPlan plan =
         forced_s || forced_bm || forced_bn
             ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, cus, forced_s, forced_bm, forced_bn, kMaxSplitWorkspace)
             : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
+    if (plan.bm == bsfp8::geom::kThinBM) plan.stages = env_int("BSFP8_GEMM_THIN_STAGES");
     if (use_scratch) {
         if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
         float* ws = nullptr;

@@ -998,13 +998,17 @@ struct TCfg {
     static_assert(kStageSize == geom::thin_stage_units(BN, PER_COL), "stage size as the schedule counts it");
 };
 
-// Wait until this wave's loads of the block being multiplied have landed: `later` (0..2) blocks
-// issued after it are still allowed in flight, L instructions each.
-template <int L>
+// Wait until this wave's loads of the block being multiplied have landed: `later` (0..MAXL)
+// blocks issued after it are still allowed in flight, L instructions each (vmcnt is 6 bits wide).
+template <int L, int MAXL>
 __device__ __forceinline__ void wait_block(int later) {
-    if (later >= 2) fast::wait_own_loads<2 * L>();
-    else if (later == 1) fast::wait_own_loads<L>();
-    else fast::wait_own_loads<0>();
+    static_assert(L * MAXL <= 63, "outstanding loads beyond the vmcnt range");
+    if constexpr (MAXL == 0) {
+        fast::wait_own_loads<0>();
+    } else {
+        if (later >= MAXL) fast::wait_own_loads<L * MAXL>();
+        else wait_block<L, MAXL - 1>(later);
+    }
 }
 
 template <bool PER_COL, int BN, int STAGES>
@@ -1012,8 +1016,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C,
     int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
-    static_assert(STAGES >= 2 && STAGES <= 4, "wait_block covers at most two blocks in flight");
     using T = TCfg<BN, PER_COL>;
+    static_assert(STAGES >= 2 && STAGES * T::kStageSize * 16 <= sched::kLdsPerCu, "stages beyond the LDS");
     constexpr int kMS = T::kMS, kNS = T::kNS, kLoads = T::kLoads;
     __shared__ u32x4 smem[STAGES * T::kStageSize];
 
@@ -1082,26 +1086,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int krem = static_cast<int>(K - static_cast<int64_t>(Kb - 1) * kGroup);
     const bool scale_wave = wave == 0 || b_scales;
 
+    // K-block kb lives in stage kb % STAGES. An iteration multiplies NB consecutive blocks (two when
+    // there are at least four stages, else one) behind one barrier: it waits for its blocks, passes
+    // the barrier (after which no wave reads the stages of the previous iteration's blocks), issues
+    // the NB blocks AHEAD = STAGES - NB after its first into those stages, and multiplies. At the
+    // start of the iteration for block kb, blocks through kb + AHEAD - 1 have been issued.
+    constexpr int NB = STAGES >= 4 ? 2 : 1;
+    constexpr int AHEAD = STAGES - NB;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
+    for (int s = 0; s < AHEAD; ++s)
         if (s < Kb) issue(s, s);
 
-    // One K-block. TAIL: the partial last block, whose fragment bytes at and past K are zeroed (a
-    // second instance of the body, so the full blocks carry no per-fragment branch).
-    // cur: the stage of block kb; nxt: the stage block kb + STAGES - 1 goes into (that of kb - 1)
-    int cur = 0, nxt = STAGES - 1;
-    auto body = [&](int kb, auto tail_tag) {
+    // One K-block's products. TAIL: the partial last block, whose fragment bytes at and past K are
+    // zeroed (a second instance, so the full blocks carry no per-fragment branch).
+    auto compute = [&](int kb, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        // block kb has landed for every wave; no wave reads the stage of block kb - 1 any more
-        const int later = min(STAGES - 2, Kb - 1 - kb);
-        if (scale_wave) wait_block<kLoads + 1>(later);
-        else wait_block<kLoads>(later);
-        fast::lds_barrier();
-        if (kb + STAGES - 1 < Kb) issue(kb + STAGES - 1, nxt);
-
-        const u32x4* st = smem + cur * T::kStageSize;
-        cur = cur + 1 == STAGES ? 0 : cur + 1;
-        nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
+        const u32x4* st = smem + (kb % STAGES) * T::kStageSize;
         auto frag = [&](int unit) {
             v8i v = to_v8i(st[unit + pos_lo], st[unit + pos_hi]);
             if (TAIL) {
@@ -1135,9 +1135,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             }
         }
     };
+    // Blocks kb .. kb + n - 1 (n <= NB) have landed for every wave, then the next n are issued;
+    // the blocks kb + n .. kb + AHEAD - 1 may stay in flight.
+    auto step = [&](int kb, int n) {
+        const int later = min(AHEAD - n, Kb - kb - n);
+        if (scale_wave) wait_block<kLoads + 1, AHEAD - 1>(later);
+        else wait_block<kLoads, AHEAD - 1>(later);
+        fast::lds_barrier();
+        for (int q = 0; q < n; ++q)
+            if (kb + AHEAD + q < Kb) issue(kb + AHEAD + q, (kb + AHEAD + q) % STAGES);
+    };
     const int Kb_full = krem != kGroup ? Kb - 1 : Kb;
-    for (int kb = 0; kb < Kb_full; ++kb) body(kb, std::false_type{});
-    if (Kb_full < Kb) body(Kb - 1, std::true_type{});
+    int kb = 0;
+    for (; kb + NB <= Kb_full; kb += NB) {
+        step(kb, NB);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) compute(kb + q, std::false_type{});
+    }
+    if (NB == 2 && kb < Kb_full) {
+        step(kb, 1);
+        compute(kb, std::false_type{});
+    }
+    if (Kb_full < Kb) {
+        step(Kb - 1, 1);
+        compute(Kb - 1, std::true_type{});
+    }
 
     // bf16 outputs straight from the totals: a lane's four consecutive columns of one row
 #pragma unroll
@@ -1262,20 +1284,30 @@ hipError_t launch_thin_stages(const uint8_t* a, int64_t lda, const float* a_s, c
     return hipGetLastError();
 }
 
-// The pipeline depth: sched::thin_stages.
+// The pipeline depth: `stages` when the plan forces one (it must be instantiated for BN and fit the
+// LDS), else sched::thin_stages.
 template <int BN>
 hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
                        BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int cus,
-                       hipStream_t stream) {
+                       int stages, hipStream_t stream) {
     const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
     const int64_t nt = (N + BN - 1) / BN;
     if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    const int stages = sched::thin_stages(BN, bs.per_column != 0, mt * nt, cus);
-    if (stages == 4)
-        return launch_thin_stages<BN, 4>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
-    if (stages == 3)
-        return launch_thin_stages<BN, 3>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
-    return launch_thin_stages<BN, 2>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream);
+    if (stages == 0) stages = sched::thin_stages(BN, bs.per_column != 0, mt * nt, cus);
+    if (stages > sched::thin_max_stages(BN, bs.per_column != 0)) return hipErrorInvalidValue;
+#define BSFP8_THIN(S) \
+    return launch_thin_stages<BN, (S)>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream)
+    switch (stages) {
+        case 2: BSFP8_THIN(2);
+        case 3: BSFP8_THIN(3);
+        case 4: BSFP8_THIN(4);
+        case 6: BSFP8_THIN(6);
+        case 8: if constexpr (BN <= 64) { BSFP8_THIN(8); } break;
+        case 12: if constexpr (BN <= 32) { BSFP8_THIN(12); } break;
+        default: break;
+    }
+#undef BSFP8_THIN
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1286,9 +1318,9 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        hipStream_t stream) {
     if (!fnuz) {
         if (plan.bm == geom::kThinBM) {
-            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
-            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
-            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, stream);
+            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
+            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
+            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
         }
         if (plan.bm == fast::kBMSmall)
             return launch_fast<fast::kBMSmall, fast::kWMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);

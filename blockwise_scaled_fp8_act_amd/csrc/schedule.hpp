@@ -17,10 +17,14 @@
 //     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
 //     then read by the sum) and second launch pay off when the tiles leave most CUs idle; the
 //     slices always fit in one round;
-//   * the thin kernel runs the deepest pipeline (4, 3 or 2 LDS stages) whose LDS still lets every
-//     workgroup of the grid be resident at once: with operands coming from HBM the K-blocks in
-//     flight per workgroup matter more than extra workgroups per CU (128 x 4096 x 4096, 256
-//     workgroups: 22.8 us with two stages, 14.7 with four).
+//   * the thin kernel runs the deepest pipeline (8, 6, 4, 3 or 2 LDS stages) whose LDS still lets
+//     every workgroup of the grid be resident at once; from four stages on it multiplies two
+//     K-blocks per barrier. Its loop is latency-bound (one or two 4-wave workgroups per CU: at
+//     128 x 4096 x 4096 it takes as long with its operand loads pointed at an empty buffer), so
+//     blocks in flight and work per barrier matter more than extra workgroups per CU (128 x 4096 x
+//     4096, 256 workgroups, settled clock: 15.8 us with three stages, 15.9 with four, 12.4 with
+//     eight; 12 stages were slower again). The deepest pipeline that fits a workgroup's LDS
+//     (thin_max_stages) bounds what a forced schedule may ask for.
 #pragma once
 
 #include <stdint.h>
@@ -43,6 +47,7 @@ struct SplitPlan {
     int64_t bytes;
     int bm;
     int bn;
+    int stages = 0;  // the thin kernel's LDS stages; 0: sched::thin_stages at launch
 };
 
 namespace sched {
@@ -115,9 +120,17 @@ inline void fast_split(SplitPlan& plan, int64_t M, int64_t N, int64_t K, int cus
 
 // LDS stages of the thin kernel for a grid of wgs workgroups of tile width bn: the deepest of 4, 3
 // and 2 that keeps the whole grid resident (2 when none does).
+// The deepest instantiated pipeline (2, 3, 4, 6, 8 or 12 stages) whose LDS fits one workgroup.
+inline int thin_max_stages(int bn, bool per_col) {
+    const int64_t stage_bytes = 16 * static_cast<int64_t>(geom::thin_stage_units(bn, per_col));
+    for (const int st : {12, 8, 6, 4, 3})
+        if (st * stage_bytes <= kLdsPerCu) return st;
+    return 2;
+}
+
 inline int thin_stages(int bn, bool per_col, int64_t wgs, int cus) {
     const int64_t stage_bytes = 16 * static_cast<int64_t>(geom::thin_stage_units(bn, per_col));
-    for (const int st : {4, 3})
+    for (const int st : {8, 6, 4, 3})
         if (wgs <= static_cast<int64_t>(cus) * (kLdsPerCu / (st * stage_bytes))) return st;
     return 2;
 }

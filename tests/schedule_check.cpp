@@ -5,6 +5,7 @@
 //   forced M N K cus S bm bn max_bytes       -> S bm bn bytes
 //   stages bn per_col wgs cus                -> stages
 //   lhs M Kb cus                             -> pieces per thread of quantize_lhs's row strips
+//   maxstages bn per_col                     -> the thin kernel's deepest pipeline that fits the LDS
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -37,6 +38,10 @@ int main() {
             int64_t wgs;
             in >> bn >> per_col >> wgs >> cus;
             std::printf("%d\n", bsfp8::sched::thin_stages(bn, per_col != 0, wgs, cus));
+        } else if (kind == "maxstages") {
+            int bn, per_col;
+            in >> bn >> per_col;
+            std::printf("%d\n", bsfp8::sched::thin_max_stages(bn, per_col != 0));
         } else if (kind == "lhs") {
             int64_t M, Kb;
             int cus;

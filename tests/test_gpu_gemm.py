@@ -391,6 +391,42 @@ def test_gemm_thin_schedule(M, N, K, ld, bn, per_col, monkeypatch):
         assert np.array_equal(got.view(np.uint32), fast.view(np.uint32)), f"thin and {bm}-row tiles differ"
 
 
+# K-block counts 1, 2, 3 (one pair and a single), 5 and 16; partial last blocks (K = 200, 650,
+# 4000); the depths each tile width instantiates (2 and 3: one block per barrier; 4 and more: two)
+STAGE_SHAPES = [(70, 200, 128, 128), (65, 136, 200, 208), (130, 100, 384, 384), (70, 260, 650, 656),
+                (129, 520, 2048, 2048), (70, 4096, 4000, 4000)]
+STAGES_OF = {32: (2, 3, 4, 6, 8, 12), 64: (2, 3, 4, 6, 8), 128: (2, 3, 4, 6)}
+
+
+@pytest.mark.parametrize("per_col", [False, True], ids=["128x128", "128x1"])
+@pytest.mark.parametrize("bn", [32, 64, 128], ids=lambda v: f"bn{v}")
+@pytest.mark.parametrize("M,N,K,ld", STAGE_SHAPES, ids=lambda v: str(v))
+def test_gemm_thin_every_pipeline_depth(M, N, K, ld, bn, per_col, monkeypatch):
+    """Every LDS pipeline depth of the thin kernel (BSFP8_GEMM_THIN_STAGES) gives the same bits as
+    the fast kernel's 128-row tiles without a split, and the oracle's values; a depth the tile's
+    LDS cannot hold is refused."""
+    qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + 5 * N + K + bn, per_col)
+    if per_col:
+        fn = lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x1(oqa, osa, oqb, osb)
+    else:
+        fn = lambda c: bf.gemm_1x128_128x128(qa, sa, qb, sb, c=c)
+        co = oracle.gemm_1x128_128x128(oqa, osa, oqb, osb, osb.shape[1], 1)
+    monkeypatch.setenv("BSFP8_GEMM_SPLIT", "1")
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "128")
+    ref = _run_guarded(fn, M, N, N + 3)
+    _assert_close(ref, co, "128-row tiles")
+    monkeypatch.setenv("BSFP8_GEMM_TILE_M", "64")
+    monkeypatch.setenv("BSFP8_GEMM_TILE_N", str(bn))
+    for st in STAGES_OF[bn]:
+        monkeypatch.setenv("BSFP8_GEMM_THIN_STAGES", str(st))
+        got = _run_guarded(fn, M, N, N + 3)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{st} stages"
+    monkeypatch.setenv("BSFP8_GEMM_THIN_STAGES", str(max(STAGES_OF[bn]) * 2))
+    with pytest.raises(bf.Bsfp8Error):
+        fn(torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2048, 4096, 4096),
                                    (2, 5120, 1280), (4, 3584, 640)], ids=lambda v: str(v))
 def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):

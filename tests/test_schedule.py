@@ -127,12 +127,14 @@ def test_forced_split_respects_the_workspace_bound(sched):
 
 STAGES = [
     # bn, per_col, workgroups -> stages (160 KB of LDS per CU, 256 CUs)
-    ((32, 0, 256), 4),      # 12.6 KB stages: four fit three times per CU
-    ((32, 0, 768), 4),
+    ((32, 0, 256), 8),      # 12.6 KB stages: eight (100 KB) once per CU
+    ((32, 0, 512), 6),      # six (75 KB) twice per CU
+    ((32, 0, 768), 4),      # four (50 KB) three times per CU
     ((32, 0, 769), 3),
-    ((64, 0, 512), 4),      # 16.7 KB stages: 66.6 KB, two per CU
+    ((64, 0, 256), 8),      # 16.7 KB stages: 133 KB, one per CU
+    ((64, 0, 512), 4),      # 66.6 KB, two per CU
     ((64, 0, 513), 3),
-    ((128, 0, 256), 4),     # 24.8 KB stages: 99.4 KB, one per CU
+    ((128, 0, 256), 6),     # 24.8 KB stages: 149 KB, one per CU
     ((128, 0, 512), 3),     # 74.5 KB, two per CU
     ((128, 0, 768), 2),     # 49.7 KB, three per CU
     ((128, 0, 5000), 2),    # more than one round at any depth: two
@@ -186,3 +188,10 @@ def test_header_is_self_contained(tmp_path):
     exe = str(tmp_path / "only")
     subprocess.run(["g++", "-std=c++17", "-Wall", "-Werror", "-I", CSRC, str(src), "-o", exe], check=True)
     assert subprocess.run([exe]).returncode == 0
+
+
+def test_thin_deepest_pipeline_fits_the_lds(sched):
+    """The deepest instantiated thin pipeline per tile width: 12 stages of 64 x 32 tiles (12.3 KB
+    each), 8 of 64 x 64 (16.3 KB), 6 of 64 x 128 (24.3 KB) within 160 KB, per-column scales too."""
+    got = sched([f"maxstages {bn} {pc}" for bn in (32, 64, 128) for pc in (0, 1)])
+    assert [g[0] for g in got] == [12, 12, 8, 8, 6, 6]
