@@ -1086,12 +1086,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int krem = static_cast<int>(K - static_cast<int64_t>(Kb - 1) * kGroup);
     const bool scale_wave = wave == 0 || b_scales;
 
-    // K-block kb lives in stage kb % STAGES. An iteration multiplies NB consecutive blocks (two when
-    // there are at least four stages, else one) behind one barrier: it waits for its blocks, passes
-    // the barrier (after which no wave reads the stages of the previous iteration's blocks), issues
-    // the NB blocks AHEAD = STAGES - NB after its first into those stages, and multiplies. At the
-    // start of the iteration for block kb, blocks through kb + AHEAD - 1 have been issued.
-    constexpr int NB = STAGES >= 4 ? 2 : 1;
+    // K-block kb lives in stage kb % STAGES. An iteration multiplies NB consecutive blocks (four
+    // from twelve stages on, two from four, else one) behind one barrier: it waits for its blocks
+    // (AHEAD - NB later ones may stay in flight), passes the barrier (after which no wave reads the
+    // stages of the previous iteration's blocks), issues the NB blocks AHEAD = STAGES - NB after its
+    // first into those stages, and multiplies. At the start of the iteration for block kb, blocks
+    // through kb + AHEAD - 1 have been issued.
+    constexpr int NB = STAGES >= 12 ? 4 : STAGES >= 4 ? 2 : 1;
     constexpr int AHEAD = STAGES - NB;
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s)
@@ -1152,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int q = 0; q < NB; ++q) compute(kb + q, std::false_type{});
     }
-    if (NB == 2 && kb < Kb_full) {
+    for (; kb < Kb_full; ++kb) {
         step(kb, 1);
         compute(kb, std::false_type{});
     }

@@ -17,14 +17,15 @@
 //     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
 //     then read by the sum) and second launch pay off when the tiles leave most CUs idle; the
 //     slices always fit in one round;
-//   * the thin kernel runs the deepest pipeline (8, 6, 4, 3 or 2 LDS stages) whose LDS still lets
-//     every workgroup of the grid be resident at once; from four stages on it multiplies two
-//     K-blocks per barrier. Its loop is latency-bound (one or two 4-wave workgroups per CU: at
-//     128 x 4096 x 4096 it takes as long with its operand loads pointed at an empty buffer), so
-//     blocks in flight and work per barrier matter more than extra workgroups per CU (128 x 4096 x
-//     4096, 256 workgroups, settled clock: 15.8 us with three stages, 15.9 with four, 12.4 with
-//     eight; 12 stages were slower again). The deepest pipeline that fits a workgroup's LDS
-//     (thin_max_stages) bounds what a forced schedule may ask for.
+//   * the thin kernel runs the deepest pipeline (12, 8, 6, 4, 3 or 2 LDS stages) whose LDS still
+//     lets every workgroup of the grid be resident at once; from four stages on it multiplies two
+//     K-blocks per barrier, from twelve four. Its loop is latency-bound (one or two 4-wave
+//     workgroups per CU: at 128 x 4096 x 4096 it takes as long with its operand loads pointed at
+//     an empty buffer), so blocks in flight and work per barrier matter more than extra workgroups
+//     per CU (128 x 4096 x 4096, 256 workgroups, settled clock: 15.8 us with three stages, 15.9
+//     with four, 12.4 with eight, 11.7 with twelve; 64 x 1024 x 8192: 21.1 with eight, 19.3 with
+//     twelve). The deepest pipeline that fits a workgroup's LDS (thin_max_stages) bounds what a
+//     forced schedule may ask for.
 #pragma once
 
 #include <stdint.h>
@@ -130,7 +131,7 @@ inline int thin_max_stages(int bn, bool per_col) {
 
 inline int thin_stages(int bn, bool per_col, int64_t wgs, int cus) {
     const int64_t stage_bytes = 16 * static_cast<int64_t>(geom::thin_stage_units(bn, per_col));
-    for (const int st : {8, 6, 4, 3})
+    for (const int st : {12, 8, 6, 4, 3})
         if (wgs <= static_cast<int64_t>(cus) * (kLdsPerCu / (st * stage_bytes))) return st;
     return 2;
 }

@@ -127,7 +127,7 @@ def test_forced_split_respects_the_workspace_bound(sched):
 
 STAGES = [
     # bn, per_col, workgroups -> stages (160 KB of LDS per CU, 256 CUs)
-    ((32, 0, 256), 8),      # 12.6 KB stages: eight (100 KB) once per CU
+    ((32, 0, 256), 12),     # 12.6 KB stages: twelve (151 KB) once per CU
     ((32, 0, 512), 6),      # six (75 KB) twice per CU
     ((32, 0, 768), 4),      # four (50 KB) three times per CU
     ((32, 0, 769), 3),
