@@ -8,10 +8,13 @@
 //     whenever they give every CU a tile; a problem with at most half as many 256-row tiles as CUs,
 //     or with M <= 128 (a 256-row tile would be at least half empty), takes 128 x 256 tiles (8
 //     waves of 32 x 128; twice the tiles);
-//   * when the 128-row tiles would fill at most half the CUs, the problem is bound by moving
-//     operands into the CUs, not by the matrix cores, and takes the thin kernel's 64-row tiles,
-//     the widest (128, 64 or 32 columns) that still give two workgroups per CU (1024 x 4096 x
-//     4096: 27.3 us in 64 x 128 thin tiles, 32.9 in 128 x 256 tiles; 1536 rows: 38.0 against 33.3);
+//   * when the 128-row tiles would fill at most half the CUs, the problem takes the thin kernel's
+//     64-row tiles, the widest (128, 64 or 32 columns) that still give every CU a workgroup: its
+//     loop is latency-bound, so a wider tile's extra work per barrier beats a second workgroup per
+//     CU (settled clock: 256 x 4096 x 4096 15.0 us in 64 x 64 tiles against 17.0 in twice as many
+//     64 x 32; 768 rows 26.9 in 64 x 128 against 29.7; 512 rows: 20.7 and 20.4, a tie; 1024 x 4096
+//     x 4096: 27.3 us in 64 x 128 thin tiles, 32.9 in 128 x 256 tiles; 1536 rows: 38.0 against
+//     33.3);
 //   * only when those are fewer than half the CUs and K is longer than 64 blocks does K get split
 //     instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64 slices, 27
 //     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
@@ -92,7 +95,7 @@ inline int fast_bm(int64_t M, int64_t N, int cus) {
 // The thin kernel's tile width for M x N.
 inline int thin_bn(int64_t M, int64_t N, int cus) {
     for (const int bn : {128, 64})
-        if (cdiv(M, geom::kThinBM) * cdiv(N, bn) >= 2 * static_cast<int64_t>(cus)) return bn;
+        if (cdiv(M, geom::kThinBM) * cdiv(N, bn) >= static_cast<int64_t>(cus)) return bn;
     return 32;
 }
 

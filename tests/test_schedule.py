@@ -40,7 +40,9 @@ EXPECTED = {
     (1536, 4096, 4096): (1, 128, 0),     # 192 tiles of 128 rows: more than half the CUs
     (2048, 8192, 4096): (1, 256, 0),
     (1024, 4096, 4096): (1, 64, 128),    # 128 tiles of 128 rows, half the CUs: thin, 512 of 64 x 128
-    (512, 4096, 4096): (1, 64, 64),      # 64 x 128 would give 256 tiles (one per CU): 64 x 64
+    (512, 4096, 4096): (1, 64, 128),     # 64 x 128: 256 tiles, one per CU
+    (256, 4096, 4096): (1, 64, 64),      # 64 x 128 would leave CUs idle: 64 x 64, 256 tiles
+    (384, 4096, 4096): (1, 64, 64),      # 384 tiles of 64 x 64
     (128, 4096, 4096): (1, 64, 32),      # no width gives two per CU: the narrowest
     (130, 5120, 1280): (1, 64, 32),      # tail-masking workload
     (2, 512, 128): (1, 64, 32),          # smallest workload
@@ -79,14 +81,15 @@ def test_thin_kernel_boundary(sched):
         assert below[1] == 64 and at[1] != 64, (cus, below, at)
 
 
-def test_thin_width_gives_two_workgroups_per_cu(sched):
+def test_thin_width_gives_every_cu_a_workgroup(sched):
+    """The widest thin tile whose workgroups still cover the CUs (32 columns when none does)."""
     for M in (64, 100, 128, 200, 256, 512, 700, 1000, 1024):
         (_, bm, bn, _), = _plans(sched, [(M, 4096, 4096)])
         assert bm == 64
         wgs = lambda w: -(-M // 64) * -(-4096 // w)  # noqa: E731
         wider = [w for w in (128, 64, 32) if w > bn]
-        assert bn == 32 or wgs(bn) >= 2 * CUS, (M, bn)
-        assert all(wgs(w) < 2 * CUS for w in wider), (M, bn)
+        assert bn == 32 or wgs(bn) >= CUS, (M, bn)
+        assert all(wgs(w) < CUS for w in wider), (M, bn)
 
 
 def test_split_slices_fit_one_round_and_the_workspace(sched):
@@ -100,8 +103,8 @@ def test_split_slices_fit_one_round_and_the_workspace(sched):
 FORCED = [
     # M, N, K, S, bm, bn -> S, bm, bn
     ((512, 4096, 4096, 0, 64, 128), (1, 64, 128)),   # thin with a chosen width
-    ((512, 4096, 4096, 0, 64, 0), (1, 64, 64)),      # thin, automatic width
-    ((512, 4096, 4096, 3, 64, 0), (1, 64, 64)),      # the thin kernel never splits
+    ((512, 4096, 4096, 0, 64, 0), (1, 64, 128)),     # thin, automatic width
+    ((512, 4096, 4096, 3, 64, 0), (1, 64, 128)),     # the thin kernel never splits
     ((512, 4096, 4096, 3, 0, 0), (3, 128, 0)),       # a forced split takes the fast kernel
     ((128, 4096, 4096, 0, 128, 0), (12, 128, 0)),    # 128-row tiles with their automatic split
     ((128, 4096, 4096, 1, 128, 0), (1, 128, 0)),     # ... and without a split
