@@ -1092,17 +1092,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // stages of the previous iteration's blocks), issues the NB blocks AHEAD = STAGES - NB after its
     // first into those stages, and multiplies. At the start of the iteration for block kb, blocks
     // through kb + AHEAD - 1 have been issued.
-    constexpr int NB = STAGES >= 12 ? 4 : STAGES >= 4 ? 2 : 1;
-    constexpr int AHEAD = STAGES - NB;
+    constexpr int NB = geom::thin_blocks_per_step(STAGES);
+    constexpr int AHEAD = geom::thin_ahead(STAGES);
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s)
-        if (s < Kb) issue(s, s);
+        if (s < Kb) issue(s, geom::thin_stage_of(STAGES, s));
 
     // One K-block's products. TAIL: the partial last block, whose fragment bytes at and past K are
     // zeroed (a second instance, so the full blocks carry no per-fragment branch).
     auto compute = [&](int kb, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const u32x4* st = smem + (kb % STAGES) * T::kStageSize;
+        const u32x4* st = smem + geom::thin_stage_of(STAGES, kb) * T::kStageSize;
         auto frag = [&](int unit) {
             v8i v = to_v8i(st[unit + pos_lo], st[unit + pos_hi]);
             if (TAIL) {
@@ -1139,12 +1139,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // Blocks kb .. kb + n - 1 (n <= NB) have landed for every wave, then the next n are issued;
     // the blocks kb + n .. kb + AHEAD - 1 may stay in flight.
     auto step = [&](int kb, int n) {
-        const int later = min(AHEAD - n, Kb - kb - n);
+        const int later = geom::thin_wait_later(STAGES, kb, n, Kb);
         if (scale_wave) wait_block<kLoads + 1, AHEAD - 1>(later);
         else wait_block<kLoads, AHEAD - 1>(later);
         fast::lds_barrier();
         for (int q = 0; q < n; ++q)
-            if (kb + AHEAD + q < Kb) issue(kb + AHEAD + q, (kb + AHEAD + q) % STAGES);
+            if (kb + AHEAD + q < Kb) issue(kb + AHEAD + q, geom::thin_stage_of(STAGES, kb + AHEAD + q));
     };
     const int Kb_full = krem != kGroup ? Kb - 1 : Kb;
     int kb = 0;

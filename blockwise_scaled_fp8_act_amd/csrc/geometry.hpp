@@ -162,6 +162,18 @@ BSFP8_HD int thin_loads(int bn) { return (kThinBM + bn) / 32; }
 // LDS image of one pipeline stage, in 16-byte units: A rows 0..63 and B rows 0..bn-1 (8 units of
 // 128 bytes each), the 64 A scales, then the B scales (per column: bn floats; 128x128: one float).
 constexpr int thin_stage_units(int bn, bool per_col) { return (kThinBM + bn) * 8 + kThinBM / 4 + (per_col ? bn / 4 : 1); }
+// The thin kernel's LDS pipeline of `stages` stages: K-block b lives in stage b % stages; one
+// iteration waits for its n blocks (n = thin_blocks_per_step, or 1 for the last few), passes one
+// barrier, issues the n blocks thin_ahead blocks after its first, and multiplies its blocks; the
+// prologue issues blocks 0 .. thin_ahead - 1.
+BSFP8_HD constexpr int thin_blocks_per_step(int stages) { return stages >= 12 ? 4 : stages >= 4 ? 2 : 1; }
+BSFP8_HD constexpr int thin_ahead(int stages) { return stages - thin_blocks_per_step(stages); }
+BSFP8_HD constexpr int thin_stage_of(int stages, int kb) { return kb % stages; }
+// Blocks that may still be in flight when the iteration for blocks kb .. kb + n - 1 (of Kb) waits.
+BSFP8_HD int thin_wait_later(int stages, int kb, int n, int Kb) {
+    const int a = thin_ahead(stages) - n, b = Kb - kb - n;
+    return a < b ? a : b;
+}
 // Load p (0 .. thin_loads(bn) - 1) of wave w: row group g = w thin_loads(bn) + p of the tile; A's
 // groups are 0..7, B's follow. thin_group: the group's index within its operand.
 BSFP8_HD bool thin_load_is_a(int bn, int wave, int p) { return wave * thin_loads(bn) + p < kThinBM / 8; }

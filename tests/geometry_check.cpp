@@ -518,6 +518,84 @@ static bool check_lhs_scales(int64_t M, int64_t K) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// The thin kernel's LDS pipeline, simulated wave by wave for every depth it instantiates and every
+// K-block count up to 40 (with and without a partial last block, which runs as a step of its own),
+// with L loads per wave per block (the kernel's 3..7 operand and scale loads). The iterations
+// mirror the kernel's three loops: blocks_per_step blocks while that many full blocks remain, then
+// single full blocks, then the partial one. Loads complete in issue order (what vmcnt counts); the
+// wait of an iteration lets at most thin_wait_later * L of them stay outstanding. Checked: the
+// blocks an iteration multiplies have all landed; a block is issued into a stage only when that
+// stage's previous block was multiplied before the iteration's barrier; the vmcnt immediate fits
+// its 6 bits; every block is issued once and multiplied once, in order.
+static bool check_thin_pipeline() {
+    for (int stages : {2, 3, 4, 6, 8, 12})
+        for (int L = 3; L <= 8; ++L) {
+            const int nb = thin_blocks_per_step(stages), ahead = thin_ahead(stages);
+            CHECK(nb >= 1 && ahead >= nb && L * (ahead - 1) <= 63, "stages %d: nb %d ahead %d", stages, nb, ahead);
+            for (int Kb = 1; Kb <= 40; ++Kb)
+                for (int partial = 0; partial < 2; ++partial) {
+                    const int Kb_full = partial ? Kb - 1 : Kb;
+                    std::vector<int> owner(stages, -1);      // block resident in each stage
+                    std::vector<int> done_mult(Kb, 0), issued(Kb, 0);
+                    std::vector<int> fifo;                   // outstanding loads (block of each), oldest first
+                    std::vector<int> landed(Kb, 0);          // loads of the block completed
+                    std::vector<int> freed_at_barrier;       // blocks multiplied since the last barrier
+                    auto issue = [&](int b) -> bool {
+                        const int st = thin_stage_of(stages, b);
+                        CHECK(st >= 0 && st < stages, "stage of block %d", b);
+                        CHECK(owner[st] == -1 || done_mult[owner[st]] == 2,
+                              "stages %d Kb %d: block %d issued into stage %d, still holding block %d", stages, Kb, b, st, owner[st]);
+                        CHECK(!issued[b], "block %d issued twice", b);
+                        owner[st] = b;
+                        issued[b] = 1;
+                        for (int l = 0; l < L; ++l) fifo.push_back(b);
+                        return true;
+                    };
+                    for (int b = 0; b < ahead; ++b)
+                        if (b < Kb && !issue(b)) return false;
+                    int next = 0;  // next block to multiply
+                    auto step = [&](int kb, int n) -> bool {
+                        const int later = thin_wait_later(stages, kb, n, Kb);
+                        const int allowed = later > 0 ? later * L : 0;
+                        CHECK(allowed <= 63, "vmcnt %d", allowed);
+                        while (static_cast<int>(fifo.size()) > allowed) {
+                            const int b = fifo.front();
+                            fifo.erase(fifo.begin());
+                            int left = 0;
+                            for (int x : fifo) left += x == b;
+                            if (left == 0) landed[b] = 1;
+                        }
+                        // barrier: blocks multiplied before it no longer hold their stages
+                        for (int b : freed_at_barrier) done_mult[b] = 2;
+                        freed_at_barrier.clear();
+                        for (int q = 0; q < n; ++q)
+                            if (kb + ahead + q < Kb && !issue(kb + ahead + q)) return false;
+                        for (int q = 0; q < n; ++q) {
+                            const int b = kb + q;
+                            CHECK(b == next, "block %d multiplied out of order (expected %d)", b, next);
+                            CHECK(issued[b] && landed[b], "stages %d Kb %d L %d: block %d multiplied before its loads landed",
+                                  stages, Kb, L, b);
+                            CHECK(owner[thin_stage_of(stages, b)] == b, "block %d not in its stage", b);
+                            done_mult[b] = 1;
+                            freed_at_barrier.push_back(b);
+                            ++next;
+                        }
+                        return true;
+                    };
+                    int kb = 0;
+                    for (; kb + nb <= Kb_full; kb += nb)
+                        if (!step(kb, nb)) return false;
+                    for (; kb < Kb_full; ++kb)
+                        if (!step(kb, 1)) return false;
+                    if (Kb_full < Kb && !step(Kb - 1, 1)) return false;
+                    CHECK(next == Kb, "stages %d Kb %d: %d of %d blocks multiplied", stages, Kb, next, Kb);
+                    CHECK(fifo.empty(), "loads left in flight at the end");
+                }
+        }
+    return true;
+}
+
+// ---------------------------------------------------------------------------------------------
 // quantize_lhs in row strips (K % 16 == 0), every pieces-per-thread count the library launches:
 // each input piece of 8 columns is read once and lands in the LDS slot of its (row, K-block) group,
 // a group's 16 pieces sit in one aligned 16-lane row of a wave, each 16-byte output piece is written
@@ -583,6 +661,7 @@ static bool check_lhs_strips(int64_t M, int64_t K) {
 
 int main(int argc, char** argv) {
     if (!check_tail_masks()) return 1;
+    if (!check_thin_pipeline()) return 1;
     for (int a = 1; a + 2 < argc; a += 3) {
         const int64_t M = std::atoll(argv[a]), N = std::atoll(argv[a + 1]), K = std::atoll(argv[a + 2]);
         const int64_t ld = (K + 15) / 16 * 16;  // the GEMMs' 16-byte row rule

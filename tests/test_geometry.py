@@ -102,6 +102,24 @@ def test_unmasked_strip_scale_store_is_caught(tmp_path):
     assert r.returncode != 0 and "strip a_s store" in r.stdout, r.stdout
 
 
+def test_planted_thin_pipeline_short_wait_is_caught(tmp_path):
+    """The thin kernel's wait letting one block too many stay in flight: a block is multiplied
+    before its loads have landed."""
+    exe = _planted(tmp_path, "const int a = thin_ahead(stages) - n, b = Kb - kb - n;",
+                   "const int a = thin_ahead(stages) - n + 1, b = Kb - kb - n + 1;", "planted_wait")
+    r = _run(exe, [(130, 256, 256)])
+    assert r.returncode != 0 and "before its loads landed" in r.stdout, r.stdout
+
+
+def test_planted_thin_pipeline_stage_overrun_is_caught(tmp_path):
+    """Issuing one block further ahead than the stages allow overwrites a stage still in use."""
+    exe = _planted(tmp_path, "BSFP8_HD constexpr int thin_ahead(int stages) { return stages - thin_blocks_per_step(stages); }",
+                   "BSFP8_HD constexpr int thin_ahead(int stages) { return stages - thin_blocks_per_step(stages) + 1; }",
+                   "planted_ahead")
+    r = _run(exe, [(130, 256, 256)])
+    assert r.returncode != 0 and "still holding" in r.stdout, r.stdout
+
+
 def test_planted_operand_row_read_is_caught(tmp_path):
     """An operand resource that runs past the tile's in-range rows."""
     exe = _planted(tmp_path,
