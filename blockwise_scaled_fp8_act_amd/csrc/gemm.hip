@@ -973,12 +973,14 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // ==============================================================================================
 // Thin kernel: 64 x BN tiles (BN = 32, 64 or 128) of 4 waves (2 x 2, each 32 x BN/2), for problems
 // whose 128-row tiles of the fast kernel would fill at most half the CUs (few rows: the short-and-
-// wide GEMMs). Such a problem is bound by moving operands into the CUs, not by the matrix cores, so
-// it takes more, smaller tiles (several workgroups per CU), every one over the whole K range: no
-// partial tiles to sum. Each K-block's A and B rows go global -> LDS by the fast kernel's direct
-// loads and LDS swizzle, STAGES - 1 blocks ahead of the one being multiplied (one workgroup barrier
-// per K-block); a wave multiplies its 2 x BN/32 subtiles and rescales each partial into its totals
-// exactly as the fast kernel does, so the two kernels give bit-identical results.
+// wide GEMMs), every tile over the whole K range: no partial tiles to sum. With one or two such
+// workgroups per CU the K-loop is bound by latency (waits, barriers, LDS reads, the MFMA -> FMA
+// chains), not by the matrix cores or memory, so the pipeline is deep (STAGES = 2 .. 12 LDS
+// stages) and an iteration multiplies one, two or four K-blocks behind one workgroup barrier
+// (geometry.hpp: thin_blocks_per_step, thin_ahead, thin_wait_later; the CPU check simulates it).
+// Each K-block's A and B rows go global -> LDS by the fast kernel's direct loads and LDS swizzle; a
+// wave multiplies its 2 x BN/32 subtiles and rescales each partial into its totals exactly as the
+// fast kernel does, so the two kernels give bit-identical results.
 namespace thin {
 
 constexpr int kThreads = 64 * geom::kThinWaves;

@@ -16,7 +16,10 @@
 // All are HBM-bound: every input byte is read once with 16-byte loads, all of a tile's loads are in
 // flight before the first wait, every output byte is written once, 16-lane (1x128) or LDS (128x1,
 // 128x128) max reductions run on data already in registers, and the transposing variants turn the
-// tile around in LDS so global stores stay contiguous along the output rows.
+// tile around in LDS so global stores stay contiguous along the output rows. quantize_lhs on
+// aligned rows (K % 16 == 0) works in row strips instead of tiles: a workgroup reads whole rows,
+// encodes them into LDS and only then writes them, so its reads and its writes are each one long
+// contiguous stream.
 #include "device_common.hpp"
 #include "geometry.hpp"
 #include "launch.hpp"
