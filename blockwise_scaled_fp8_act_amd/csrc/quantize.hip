@@ -768,6 +768,7 @@ hipError_t quantize_lhs_impl(const uint16_t* x, int64_t M, int64_t K, int64_t ld
     if (strip_loads >= 0 && aligned(x, 16) && ldx % 8 == 0 && aligned(q, 16) && ldq % 16 == 0 && K % 16 == 0) {
         const int nl = strip_loads > 0 ? strip_loads : sched::lhs_strip_loads(M, Kb, device_cus());
         const geom::StripShape sh = geom::strip_shape(M, Kb, nl);
+        if (sh.units > 0x7FFFFFFFLL) return quantize_lhs_impl<FNUZ>(x, M, K, ldx, q, ldq, a_s, -1, stream);
         const dim3 grid(static_cast<unsigned>(sh.units));
 #define BSFP8_QS(N) \
     quantize_lhs_strip_kernel<FNUZ, N><<<grid, geom::kStripThreads, 0, stream>>>(x, M, K, ldx, q, ldq, a_s, Kb, sh)
