@@ -110,12 +110,13 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
-// BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N and BSFP8_GEMM_THIN_STAGES (environment,
-// read at each call): a slice count (1 = never split), a tile height (256 or 128: the fast kernel;
-// 64: the thin kernel), the thin kernel's tile width (32, 64 or 128) and its LDS stages (2, 3, 4, 6,
-// 8 or 12, as far as the tile's stages fit the LDS; others fail with BSFP8_EHIP) that replace the
-// automatic choices of gemm_split_plan, so tests and benchmarks can run every schedule on any
-// shape. Unset or empty: automatic.
+// BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N, BSFP8_GEMM_THIN_STAGES and
+// BSFP8_GEMM_THIN_WAVES (environment, read at each call): a slice count (1 = never split), a tile
+// height (256 or 128: the fast kernel; 64: the thin kernel), the thin kernel's tile width (32, 64 or
+// 128), its LDS stages (2, 3, 4, 6, 8 or 12, as far as the tile's stages fit the LDS) and its waves
+// per workgroup (4, or 8 for tiles of 64 or 128 columns; other values fail with BSFP8_EHIP) that
+// replace the automatic choices of gemm_split_plan, so tests and benchmarks can run every schedule
+// on any shape. Unset or empty: automatic.
 int env_int(const char* name) {
     const char* v = std::getenv(name);
     if (v == nullptr || *v == 0) return 0;
@@ -136,7 +137,10 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
         forced_s || forced_bm || forced_bn
             ? bsfp8::gemm_split_plan_forced(M, N, K, fnuz, cus, forced_s, forced_bm, forced_bn, kMaxSplitWorkspace)
             : bsfp8::gemm_split_plan(M, N, K, fnuz, cus, kMaxSplitWorkspace);
-    if (plan.bm == bsfp8::geom::kThinBM) plan.stages = env_int("BSFP8_GEMM_THIN_STAGES");
+    if (plan.bm == bsfp8::geom::kThinBM) {
+        plan.stages = env_int("BSFP8_GEMM_THIN_STAGES");
+        plan.waves = env_int("BSFP8_GEMM_THIN_WAVES");
+    }
     if (use_scratch) {
         if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
         float* ws = nullptr;

@@ -971,7 +971,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 }  // namespace fast
 
 // ==============================================================================================
-// Thin kernel: 64 x BN tiles (BN = 32, 64 or 128) of 4 waves (2 x 2, each 32 x BN/2), for problems
+// Thin kernel: 64 x BN tiles (BN = 32, 64 or 128) of 4 waves (2 x 2, each 32 x BN/2) or, for BN >= 64
+// when the grid is at most one workgroup per CU, 8 waves (4 x 2, each 16 x BN/2), for problems
 // whose 128-row tiles of the fast kernel would fill at most half the CUs (few rows: the short-and-
 // wide GEMMs), every tile over the whole K range: no partial tiles to sum. With one or two such
 // workgroups per CU the K-loop is bound by latency (waits, barriers, LDS reads, the MFMA -> FMA
@@ -983,13 +984,13 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // fast kernel does, so the two kernels give bit-identical results.
 namespace thin {
 
-constexpr int kThreads = 64 * geom::kThinWaves;
-
-template <int BN, bool PER_COL>
+// W waves per workgroup: 4 (2 x 2, each 32 x BN/2) or, for BN >= 64, 8 (4 x 2, each 16 x BN/2).
+template <int BN, bool PER_COL, int W>
 struct TCfg {
-    static constexpr int kMS = 2;        // 16-row subtiles per wave
+    static_assert(W == 4 || (W == 8 && BN >= 64), "8-wave thin tiles are 64 or 128 columns wide");
+    static constexpr int kMS = 8 / W;    // 16-row subtiles per wave
     static constexpr int kNS = BN / 32;  // 16-column subtiles per wave
-    static constexpr int kLoads = (geom::kThinBM + BN) / 32;
+    static constexpr int kLoads = (geom::kThinBM + BN) / (8 * W);
     // LDS image of one stage (16-byte units): A rows 0..63, B rows 0..BN-1, the 64 A scales, the B
     // scales (per column: BN floats; 128x128: one float)
     static constexpr int kStageA = 0;
@@ -1013,12 +1014,12 @@ __device__ __forceinline__ void wait_block(int later) {
     }
 }
 
-template <bool PER_COL, int BN, int STAGES>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(
+template <bool PER_COL, int BN, int STAGES, int W>
+__global__ __launch_bounds__(64 * W) void gemm_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ a_s, const uint8_t* __restrict__ B,
     int64_t ldb, const float* __restrict__ b_s, int64_t bs_nb, int64_t bs_kb, uint16_t* __restrict__ C,
     int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt, int c_vec) {
-    using T = TCfg<BN, PER_COL>;
+    using T = TCfg<BN, PER_COL, W>;
     static_assert(STAGES >= 2 && STAGES * T::kStageSize * 16 <= sched::kLdsPerCu, "stages beyond the LDS");
     constexpr int kMS = T::kMS, kNS = T::kNS, kLoads = T::kLoads;
     __shared__ u32x4 smem[STAGES * T::kStageSize];
@@ -1026,8 +1027,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1;   // rows 32 wm .. of the tile
-    const int wn = wave >> 1;  // columns (BN / 2) wn .. of the tile
+    const int wm = wave % (W / 2);  // rows thin_rows_per_wave(W) wm .. of the tile
+    const int wn = wave / (W / 2);  // columns (BN / 2) wn .. of the tile
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     int tm, tn;
@@ -1048,9 +1049,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     bool is_a[kLoads];
 #pragma unroll
     for (int p = 0; p < kLoads; ++p) {
-        is_a[p] = geom::thin_load_is_a(BN, wave, p);
-        lane_off[p] = geom::thin_operand_lane(geom::thin_group(BN, wave, p), lane, is_a[p] ? lda : ldb);
-        unit[p] = static_cast<uint32_t>(geom::thin_load_unit(BN, wave, p));
+        is_a[p] = geom::thin_load_is_a(BN, W, wave, p);
+        lane_off[p] = geom::thin_operand_lane(geom::thin_group(BN, W, wave, p), lane, is_a[p] ? lda : ldb);
+        unit[p] = static_cast<uint32_t>(geom::thin_load_unit(BN, W, wave, p));
     }
     const bool b_scales = geom::thin_has_bscale_load(BN, PER_COL, wave);
     const uint32_t as_base = geom::thin_ascale_base(m0, M, lane);
@@ -1119,7 +1120,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         const float* sb = reinterpret_cast<const float*>(st + T::kStageSB);
 #pragma unroll
         for (int i = 0; i < kMS; ++i) {
-            const int r = 32 * wm + 16 * i + l16;
+            const int r = geom::thin_rows_per_wave(W) * wm + 16 * i + l16;
             af[i] = frag(T::kStageA + r * 8);
             fa[i] = PER_COL ? sa[r] : sa[r] * sb[0];
         }
@@ -1167,7 +1168,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // bf16 outputs straight from the totals: a lane's four consecutive columns of one row
 #pragma unroll
     for (int i = 0; i < kMS; ++i) {
-        const int64_t m = geom::thin_store_row(m0, wm, i, lane);
+        const int64_t m = geom::thin_store_row(m0, W, wm, i, lane);
         if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < kNS; ++j) {
@@ -1272,34 +1273,26 @@ hipError_t launch_fast(const uint8_t* a, int64_t lda, const float* a_s, const ui
 
 // The thin kernel with tile width BN (no split; every tile over the whole K range) and STAGES LDS
 // stages (STAGES - 1 K-blocks in flight per workgroup).
-template <int BN, int STAGES>
+template <int BN, int STAGES, int W>
 hipError_t launch_thin_stages(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
                               BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt,
                               hipStream_t stream) {
     const int c_vec = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
     const dim3 grid(static_cast<unsigned>(mt) * static_cast<unsigned>(nt));
     if (bs.per_column)
-        thin::gemm_kernel<true, BN, STAGES><<<grid, thin::kThreads, 0, stream>>>(
+        thin::gemm_kernel<true, BN, STAGES, W><<<grid, 64 * W, 0, stream>>>(
             a, lda, a_s, b, ldb, bs.ptr, 0, 0, c, ldc, M, N, K, mt, nt, c_vec);
     else
-        thin::gemm_kernel<false, BN, STAGES><<<grid, thin::kThreads, 0, stream>>>(
+        thin::gemm_kernel<false, BN, STAGES, W><<<grid, 64 * W, 0, stream>>>(
             a, lda, a_s, b, ldb, bs.ptr, bs.stride_nb, bs.stride_kb, c, ldc, M, N, K, mt, nt, c_vec);
     return hipGetLastError();
 }
 
-// The pipeline depth: `stages` when the plan forces one (it must be instantiated for BN and fit the
-// LDS), else sched::thin_stages.
-template <int BN>
-hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
-                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int cus,
-                       int stages, hipStream_t stream) {
-    const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
-    const int64_t nt = (N + BN - 1) / BN;
-    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    if (stages == 0) stages = sched::thin_stages(BN, bs.per_column != 0, mt * nt, cus);
-    if (stages > sched::thin_max_stages(BN, bs.per_column != 0)) return hipErrorInvalidValue;
-#define BSFP8_THIN(S) \
-    return launch_thin_stages<BN, (S)>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stream)
+template <int BN, int W>
+hipError_t launch_thin_waves(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
+                             BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int mt, int nt,
+                             int stages, hipStream_t stream) {
+#define BSFP8_THIN(S) return launch_thin_stages<BN, (S), W>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, mt, nt, stream)
     switch (stages) {
         case 2: BSFP8_THIN(2);
         case 3: BSFP8_THIN(3);
@@ -1313,6 +1306,28 @@ hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const ui
     return hipErrorInvalidValue;
 }
 
+// The pipeline depth and the waves per workgroup: `stages` / `waves` when the plan forces them (a
+// depth must be instantiated for BN and fit the LDS; 8 waves need BN >= 64), else
+// sched::thin_stages / sched::thin_waves.
+template <int BN>
+hipError_t launch_thin(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b, int64_t ldb,
+                       BScale bs, uint16_t* c, int64_t ldc, int64_t M, int64_t N, int64_t K, int cus,
+                       int stages, int waves, hipStream_t stream) {
+    const int64_t mt = (M + geom::kThinBM - 1) / geom::kThinBM;
+    const int64_t nt = (N + BN - 1) / BN;
+    if (mt * nt > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    if (stages == 0) stages = sched::thin_stages(BN, bs.per_column != 0, mt * nt, cus);
+    if (waves == 0) waves = sched::thin_waves(BN, mt * nt, cus);
+    if (stages > sched::thin_max_stages(BN, bs.per_column != 0)) return hipErrorInvalidValue;
+    if (waves == 8) {
+        if constexpr (BN >= 64)
+            return launch_thin_waves<BN, 8>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stages, stream);
+        return hipErrorInvalidValue;
+    }
+    if (waves != 4) return hipErrorInvalidValue;
+    return launch_thin_waves<BN, 4>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, (int)mt, (int)nt, stages, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const uint8_t* b,
@@ -1321,9 +1336,11 @@ hipError_t launch_gemm(const uint8_t* a, int64_t lda, const float* a_s, const ui
                        hipStream_t stream) {
     if (!fnuz) {
         if (plan.bm == geom::kThinBM) {
-            if (plan.bn == 128) return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
-            if (plan.bn == 64) return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
-            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, stream);
+            if (plan.bn == 128)
+                return launch_thin<128>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, plan.waves, stream);
+            if (plan.bn == 64)
+                return launch_thin<64>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, plan.waves, stream);
+            return launch_thin<32>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, cus, plan.stages, plan.waves, stream);
         }
         if (plan.bm == fast::kBMSmall)
             return launch_fast<fast::kBMSmall, fast::kWMSmall>(a, lda, a_s, b, ldb, bs, c, ldc, M, N, K, plan, workspace, cus, stream);

@@ -157,8 +157,9 @@ BSFP8_HD int64_t split_begin(int64_t Kb, int64_t S, int64_t s) { return Kb * s /
 // is read through one resource that starts at the tile's first row and spans its in-range rows, so
 // a row past M or N is past the end of the resource.
 constexpr int kThinBM = 64;
-constexpr int kThinWaves = 4;
-BSFP8_HD int thin_loads(int bn) { return (kThinBM + bn) / 32; }
+// A thin workgroup has 4 waves (2 x 2, each 32 x bn/2) or, for bn >= 64, 8 (4 x 2, each 16 x bn/2).
+BSFP8_HD int thin_rows_per_wave(int waves) { return 2 * kThinBM / waves; }
+BSFP8_HD int thin_loads(int bn, int waves) { return (kThinBM + bn) / (8 * waves); }
 // LDS image of one pipeline stage, in 16-byte units: A rows 0..63 and B rows 0..bn-1 (8 units of
 // 128 bytes each), the 64 A scales, then the B scales (per column: bn floats; 128x128: one float).
 constexpr int thin_stage_units(int bn, bool per_col) { return (kThinBM + bn) * 8 + kThinBM / 4 + (per_col ? bn / 4 : 1); }
@@ -174,11 +175,11 @@ BSFP8_HD int thin_wait_later(int stages, int kb, int n, int Kb) {
     const int a = thin_ahead(stages) - n, b = Kb - kb - n;
     return a < b ? a : b;
 }
-// Load p (0 .. thin_loads(bn) - 1) of wave w: row group g = w thin_loads(bn) + p of the tile; A's
+// Load p (0 .. thin_loads(bn, waves) - 1) of wave w: row group g = w thin_loads + p of the tile; A's
 // groups are 0..7, B's follow. thin_group: the group's index within its operand.
-BSFP8_HD bool thin_load_is_a(int bn, int wave, int p) { return wave * thin_loads(bn) + p < kThinBM / 8; }
-BSFP8_HD int thin_group(int bn, int wave, int p) {
-    const int g = wave * thin_loads(bn) + p;
+BSFP8_HD bool thin_load_is_a(int bn, int waves, int wave, int p) { return wave * thin_loads(bn, waves) + p < kThinBM / 8; }
+BSFP8_HD int thin_group(int bn, int waves, int wave, int p) {
+    const int g = wave * thin_loads(bn, waves) + p;
     return g < kThinBM / 8 ? g : g - kThinBM / 8;
 }
 // Lane l of a load of group gr: operand row 8 gr + l / 8, chunk (l % 8) ^ swz(row) (the LDS swizzle
@@ -189,8 +190,8 @@ BSFP8_HD uint32_t thin_operand_lane(int gr, int lane, int64_t ld) {
 }
 BSFP8_HD int64_t thin_operand_range(int64_t rows_in_range, int64_t ld) { return rows_in_range > 0 ? rows_in_range * ld : 0; }
 // LDS unit (16 bytes) of lane 0 of the load, within a stage: A rows at 0, B rows at 64 * 8.
-BSFP8_HD int thin_load_unit(int bn, int wave, int p) {
-    return (thin_load_is_a(bn, wave, p) ? 0 : kThinBM * 8) + 64 * thin_group(bn, wave, p);
+BSFP8_HD int thin_load_unit(int bn, int waves, int wave, int p) {
+    return (thin_load_is_a(bn, waves, wave, p) ? 0 : kThinBM * 8) + 64 * thin_group(bn, waves, wave, p);
 }
 // Scale loads of a K-block: wave 0 loads the A scales of the tile's 64 rows (lane = tile row, LDS
 // float lane); the B scales come from wave 3 (per column: tile columns 0..63, LDS float = column;
@@ -213,10 +214,12 @@ BSFP8_HD uint64_t thin_bscale_lanes(int bn, bool per_col) {
 BSFP8_HD uint32_t thin_bscale_blk_base(int64_t n0, int64_t bs_nb, int lane) {
     return lane == 0 ? static_cast<uint32_t>(4 * (n0 / kBlockK) * bs_nb) : kOob;
 }
-// Output of subtile (i, j) of wave (wm, wn): row 32 wm + 16 i + lane % 16 and columns
-// (bn / 2) wn + 16 j + 4 (lane / 16) .. + 4 of the tile; element n + e is stored iff the row is
-// below M and n + e < N.
-BSFP8_HD int64_t thin_store_row(int64_t m0, int wm, int i, int lane) { return m0 + 32 * wm + 16 * i + (lane & 15); }
+// Output of subtile (i, j) of wave (wm, wn) (wm = wave % (waves / 2), wn = wave / (waves / 2)): row
+// thin_rows_per_wave wm + 16 i + lane % 16 and columns (bn / 2) wn + 16 j + 4 (lane / 16) .. + 4
+// of the tile; element n + e is stored iff the row is below M and n + e < N.
+BSFP8_HD int64_t thin_store_row(int64_t m0, int waves, int wm, int i, int lane) {
+    return m0 + thin_rows_per_wave(waves) * wm + 16 * i + (lane & 15);
+}
 BSFP8_HD int64_t thin_store_col(int64_t n0, int bn, int wn, int j, int lane) {
     return n0 + (bn / 2) * wn + 16 * j + 4 * (lane >> 4);
 }

@@ -52,6 +52,7 @@ struct SplitPlan {
     int bm;
     int bn;
     int stages = 0;  // the thin kernel's LDS stages; 0: sched::thin_stages at launch
+    int waves = 0;   // the thin kernel's waves per workgroup (4 or 8); 0: sched::thin_waves at launch
 };
 
 namespace sched {
@@ -131,6 +132,10 @@ inline int thin_max_stages(int bn, bool per_col) {
         if (st * stage_bytes <= kLdsPerCu) return st;
     return 2;
 }
+
+// The thin kernel's waves per workgroup: 8 (16-row waves, two per SIMD) for 64- and 128-column
+// tiles when the grid is at most one workgroup per CU, else 4.
+inline int thin_waves(int bn, int64_t wgs, int cus) { return bn >= 64 && wgs <= static_cast<int64_t>(cus) ? 8 : 4; }
 
 inline int thin_stages(int bn, bool per_col, int64_t wgs, int cus) {
     const int64_t stage_bytes = 16 * static_cast<int64_t>(geom::thin_stage_units(bn, per_col));

@@ -159,12 +159,12 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  * those tiles are fewer than half the compute units and K exceeds 64 blocks are the K-blocks split
  * over S workgroups per 128- or 256-row tile, which write fp32 partial tiles to the pooled
  * workspace, and a second kernel sums the S partials in a fixed order into C (same result on every
- * call). The environment variables BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N and
- * BSFP8_GEMM_THIN_STAGES, read at each call, force S (1 = never split; S is clamped to ceil(K/128)
- * and to the workspace bound; a split uses the 128- or 256-row tiles), the tile height (256, 128 or
- * 64), the width of the 64-row tiles (32, 64 or 128) and their LDS pipeline depth (2, 3, 4, 6, 8 or
- * 12 where the tile's stages fit; a depth that does not fit, or is not one of these, is
- * BSFP8_EHIP before any launch).
+ * call). The environment variables BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N,
+ * BSFP8_GEMM_THIN_STAGES and BSFP8_GEMM_THIN_WAVES, read at each call, force S (1 = never split; S
+ * is clamped to ceil(K/128) and to the workspace bound; a split uses the 128- or 256-row tiles), the
+ * tile height (256, 128 or 64), the width of the 64-row tiles (32, 64 or 128), their LDS pipeline
+ * depth (2, 3, 4, 6, 8 or 12 where the tile's stages fit) and their waves per workgroup (4, or 8 for
+ * 64- and 128-column tiles); a depth or wave count outside these is BSFP8_EHIP before any launch.
  */
 int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
                        const void* b, int64_t ldb, const float* b_s,

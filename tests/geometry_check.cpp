@@ -15,8 +15,8 @@
 //     >= M (the root-cause comment of "Enable blockwise FP8 dense training kernels on ROCm"), in its
 //     tile kernel and in its row-strip kernel (whose code reads and stores are checked too).
 // The fast kernel's three tile shapes (256 rows, 8 waves of 64 rows; 128 rows, 4 waves of 64 rows or
-// 8 waves of 32 rows) and the three tile widths of the thin kernel (64 rows by 32, 64 or 128
-// columns, 4 waves) are enumerated.
+// 8 waves of 32 rows) and the thin kernel's tiles (64 rows by 32, 64 or 128 columns in 4 waves;
+// 64 or 128 columns in 8 waves) are enumerated.
 // Usage: geometry_check M N K [M N K ...]; prints one line per shape, exits 1 on the first failure.
 #include <cstdint>
 #include <cstdio>
@@ -244,7 +244,7 @@ static bool check_tail_masks() {
 
 // ---------------------------------------------------------------------------------------------
 // Thin kernel: 64 x bn tiles (bn = 32, 64, 128), 4 waves; every operand group, scale and output.
-static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bn) {
+static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int bn, int waves) {
     const int mt = static_cast<int>(cdiv(M, kThinBM)), nt = static_cast<int>(cdiv(N, bn));
     const int64_t Kb = cdiv(K, kBlockK);
     if (!check_tiles(mt, nt)) return false;
@@ -253,10 +253,10 @@ static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
     // the row groups of a tile are dealt to the waves exactly once
     {
         std::vector<int> ga(kThinBM / 8, 0), gb(bn / 8, 0);
-        for (int wave = 0; wave < kThinWaves; ++wave)
-            for (int p = 0; p < thin_loads(bn); ++p) {
-                const int gr = thin_group(bn, wave, p);
-                if (thin_load_is_a(bn, wave, p)) {
+        for (int wave = 0; wave < waves; ++wave)
+            for (int p = 0; p < thin_loads(bn, waves); ++p) {
+                const int gr = thin_group(bn, waves, wave, p);
+                if (thin_load_is_a(bn, waves, wave, p)) {
                     CHECK(gr >= 0 && gr < kThinBM / 8, "A group %d", gr);
                     ++ga[gr];
                 } else {
@@ -275,10 +275,10 @@ static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
             const int64_t brows = N - n0 < bn ? N - n0 : bn;
             for (int64_t kb = 0; kb < Kb; ++kb) {
                 std::vector<uint8_t> got_a(kThinBM * 8, 0), got_b(static_cast<size_t>(bn) * 8, 0);
-                for (int wave = 0; wave < kThinWaves; ++wave)
-                    for (int p = 0; p < thin_loads(bn); ++p) {
-                        const bool is_a = thin_load_is_a(bn, wave, p);
-                        const int gr = thin_group(bn, wave, p);
+                for (int wave = 0; wave < waves; ++wave)
+                    for (int p = 0; p < thin_loads(bn, waves); ++p) {
+                        const bool is_a = thin_load_is_a(bn, waves, wave, p);
+                        const int gr = thin_group(bn, waves, wave, p);
                         const int64_t rows = is_a ? arows : brows, ld = is_a ? lda : ldb;
                         const int64_t r0 = is_a ? m0 : n0, total = is_a ? M : N;
                         const int64_t range = thin_operand_range(rows, ld);
@@ -291,7 +291,7 @@ static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
                             const int c = fast_operand_chunk(gr, lane);
                             // LDS slot: row r, position lane % 8, read by the fragments as logical
                             // chunk (lane % 8) ^ swizzle(r)
-                            CHECK(thin_load_unit(bn, wave, p) + lane == (is_a ? 0 : kThinBM * 8) + r * 8 + (lane & 7), "thin LDS unit");
+                            CHECK(thin_load_unit(bn, waves, wave, p) + lane == (is_a ? 0 : kThinBM * 8) + r * 8 + (lane & 7), "thin LDS unit");
                             CHECK(((lane & 7) ^ lds_swizzle(r)) == c, "thin LDS chunk position");
                             if (r < rows) {
                                 CHECK(static_cast<int64_t>(off) == r * ld + kb * kBlockK + 16 * c, "thin operand address");
@@ -330,7 +330,7 @@ static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
                 for (int r = 0; r < arows; ++r) CHECK(sa[r] == 1, "thin a_s row %lld not loaded once", (long long)(m0 + r));
                 // per-column B scales: the active lanes of the B-scale waves, each writing one LDS
                 // float of the tile's bn
-                for (int wave = 0; wave < kThinWaves; ++wave) {
+                for (int wave = 0; wave < waves; ++wave) {
                     if (!thin_has_bscale_load(bn, true, wave)) continue;
                     for (int lane = 0; lane < 64; ++lane) {
                         if (!((thin_bscale_lanes(bn, true) >> lane) & 1)) continue;
@@ -363,12 +363,12 @@ static bool check_thin(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
                     CHECK((n0 + brows - 1) / kBlockK == nb, "thin tile spans two column blocks");
                 }
             }
-            for (int wave = 0; wave < kThinWaves; ++wave)
-                for (int i = 0; i < 2; ++i)
+            for (int wave = 0; wave < waves; ++wave)
+                for (int i = 0; i < 8 / waves; ++i)
                     for (int j = 0; j < bn / 32; ++j)
                         for (int lane = 0; lane < 64; ++lane) {
-                            const int64_t m = thin_store_row(m0, wave & 1, i, lane);
-                            const int64_t n = thin_store_col(n0, bn, wave >> 1, j, lane);
+                            const int64_t m = thin_store_row(m0, waves, wave % (waves / 2), i, lane);
+                            const int64_t n = thin_store_col(n0, bn, wave / (waves / 2), j, lane);
                             CHECK(m - m0 < kThinBM && n - n0 < bn, "thin output outside the tile");
                             if (m >= M) continue;
                             for (int e = 0; e < 4; ++e)
@@ -670,7 +670,10 @@ int main(int argc, char** argv) {
             ok = ok && check_fast(M, N, K, ld, ld, t.first, t.second) &&
                  check_fast(M, N, K, ld + 16, ld + 48, t.first, t.second) && check_split(M, N, K, t.first, t.second);
         for (int bn : {32, 64, 128})
-            ok = ok && check_thin(M, N, K, ld, ld, bn) && check_thin(M, N, K, ld + 16, ld + 48, bn);
+            for (int waves : {4, 8}) {
+                if (waves == 8 && bn < 64) continue;  // 8-wave tiles are 64 or 128 columns wide
+                ok = ok && check_thin(M, N, K, ld, ld, bn, waves) && check_thin(M, N, K, ld + 16, ld + 48, bn, waves);
+            }
         ok = ok && check_gen(M, N, K, ld, ld) && check_lhs_scales(M, K) && check_lhs_strips(M, K);
         std::printf("%s M=%lld N=%lld K=%lld\n", ok ? "ok" : "FAILED", (long long)M, (long long)N, (long long)K);
         if (!ok) return 1;

@@ -6,6 +6,7 @@
 //   stages bn per_col wgs cus                -> stages
 //   lhs M Kb cus                             -> pieces per thread of quantize_lhs's row strips
 //   maxstages bn per_col                     -> the thin kernel's deepest pipeline that fits the LDS
+//   waves bn wgs cus                         -> the thin kernel's waves per workgroup
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -38,6 +39,11 @@ int main() {
             int64_t wgs;
             in >> bn >> per_col >> wgs >> cus;
             std::printf("%d\n", bsfp8::sched::thin_stages(bn, per_col != 0, wgs, cus));
+        } else if (kind == "waves") {
+            int bn, cus;
+            int64_t wgs;
+            in >> bn >> wgs >> cus;
+            std::printf("%d\n", bsfp8::sched::thin_waves(bn, wgs, cus));
         } else if (kind == "maxstages") {
             int bn, per_col;
             in >> bn >> per_col;

@@ -402,9 +402,10 @@ STAGES_OF = {32: (2, 3, 4, 6, 8, 12), 64: (2, 3, 4, 6, 8), 128: (2, 3, 4, 6)}
 @pytest.mark.parametrize("bn", [32, 64, 128], ids=lambda v: f"bn{v}")
 @pytest.mark.parametrize("M,N,K,ld", STAGE_SHAPES, ids=lambda v: str(v))
 def test_gemm_thin_every_pipeline_depth(M, N, K, ld, bn, per_col, monkeypatch):
-    """Every LDS pipeline depth of the thin kernel (BSFP8_GEMM_THIN_STAGES) gives the same bits as
-    the fast kernel's 128-row tiles without a split, and the oracle's values; a depth the tile's
-    LDS cannot hold is refused."""
+    """Every LDS pipeline depth of the thin kernel (BSFP8_GEMM_THIN_STAGES), with 4 and (64- and
+    128-column tiles) 8 waves per workgroup (BSFP8_GEMM_THIN_WAVES), gives the same bits as the fast
+    kernel's 128-row tiles without a split, and the oracle's values; a depth the tile's LDS cannot
+    hold, or a wave count the width has no layout for, is refused."""
     qa, sa, qb, sb, oqa, osa, oqb, osb = _quantized_operands(M, N, K, ld, M + 5 * N + K + bn, per_col)
     if per_col:
         fn = lambda c: bf.gemm_1x128_128x1(qa, sa, qb, sb, c=c)
@@ -418,11 +419,17 @@ def test_gemm_thin_every_pipeline_depth(M, N, K, ld, bn, per_col, monkeypatch):
     _assert_close(ref, co, "128-row tiles")
     monkeypatch.setenv("BSFP8_GEMM_TILE_M", "64")
     monkeypatch.setenv("BSFP8_GEMM_TILE_N", str(bn))
-    for st in STAGES_OF[bn]:
-        monkeypatch.setenv("BSFP8_GEMM_THIN_STAGES", str(st))
-        got = _run_guarded(fn, M, N, N + 3)
-        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{st} stages"
+    for waves in ((4, 8) if bn >= 64 else (4,)):
+        monkeypatch.setenv("BSFP8_GEMM_THIN_WAVES", str(waves))
+        for st in STAGES_OF[bn]:
+            monkeypatch.setenv("BSFP8_GEMM_THIN_STAGES", str(st))
+            got = _run_guarded(fn, M, N, N + 3)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{waves} waves, {st} stages"
     monkeypatch.setenv("BSFP8_GEMM_THIN_STAGES", str(max(STAGES_OF[bn]) * 2))
+    with pytest.raises(bf.Bsfp8Error):
+        fn(torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
+    monkeypatch.delenv("BSFP8_GEMM_THIN_STAGES")
+    monkeypatch.setenv("BSFP8_GEMM_THIN_WAVES", "8" if bn == 32 else "6")  # not a layout of this width
     with pytest.raises(bf.Bsfp8Error):
         fn(torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
 

@@ -198,3 +198,13 @@ def test_thin_deepest_pipeline_fits_the_lds(sched):
     each), 8 of 64 x 64 (16.3 KB), 6 of 64 x 128 (24.3 KB) within 160 KB, per-column scales too."""
     got = sched([f"maxstages {bn} {pc}" for bn in (32, 64, 128) for pc in (0, 1)])
     assert [g[0] for g in got] == [12, 12, 8, 8, 6, 6]
+
+
+def test_thin_waves(sched):
+    """8 waves (16-row waves) for 64- and 128-column thin tiles when the grid is at most one
+    workgroup per CU (256 x 4096 x 4096 in 64 x 64 tiles: 13.9 us against 15.0 with 4 waves; 512
+    rows in 64 x 128: 19.3 against 20.6-20.9), 4 otherwise (768 rows, 384 workgroups: 8 waves were
+    slower) and always for 32-column tiles."""
+    q = [(64, 256, 8), (128, 256, 8), (128, 200, 8), (64, 257, 4), (128, 384, 4), (32, 256, 4), (32, 100, 4)]
+    got = sched([f"waves {bn} {w} {CUS}" for bn, w, _ in q])
+    assert [g[0] for g in got] == [want for _, _, want in q]
