@@ -9,12 +9,15 @@
 //     or with M <= 128 (a 256-row tile would be at least half empty), takes 128 x 256 tiles (8
 //     waves of 32 x 128; twice the tiles);
 //   * when the 128-row tiles would fill at most half the CUs, the problem takes the thin kernel's
-//     64-row tiles, the widest (128, 64 or 32 columns) that still give every CU a workgroup: its
-//     loop is latency-bound, so a wider tile's extra work per barrier beats a second workgroup per
-//     CU (settled clock: 256 x 4096 x 4096 15.0 us in 64 x 64 tiles against 17.0 in twice as many
-//     64 x 32; 768 rows 26.9 in 64 x 128 against 29.7; 512 rows: 20.7 and 20.4, a tie; 1024 x 4096
-//     x 4096: 27.3 us in 64 x 128 thin tiles, 32.9 in 128 x 256 tiles; 1536 rows: 38.0 against
-//     33.3);
+//     64-row tiles, the widest (128, 64 or 32 columns) that still occupy three quarters of the CUs,
+//     in 8 waves of 16-row blocks when the grid is at most one workgroup per CU: the loop is
+//     latency-bound, so a wider tile's extra work per barrier and a second wave per SIMD beat more
+//     workgroups (settled clock: 256 x 4096 x 4096 13.9 us in 64 x 64 tiles of 8 waves against
+//     17.0 in twice as many 64 x 32; 192 rows 13.8 in 192 such tiles against 16.9 in 384 of 64 x 32;
+//     160 x 4096 x 8192 24.0 against 28.1; 384 rows 19.1 in 192 tiles of 64 x 128 against 19.5 in
+//     384 of 64 x 64; 768 rows 26.9 in 64 x 128 tiles (4 waves) against 29.7; M = 128, where 64 x 64
+//     tiles would leave half the CUs idle: 11.7 in 64 x 32 against 13.6; 1024 x 4096 x 4096: 27.3
+//     us in 64 x 128 thin tiles, 32.9 in 128 x 256 tiles; 1536 rows: 38.0 against 33.3);
 //   * only when those are fewer than half the CUs and K is longer than 64 blocks does K get split
 //     instead (at 64 x 1024 x 8192 the thin kernel's 32 workgroups still beat 64 slices, 27
 //     against 32 us): S workgroups per 128- or 256-row tile, whose fp32 partial tiles (written,
@@ -96,7 +99,7 @@ inline int fast_bm(int64_t M, int64_t N, int cus) {
 // The thin kernel's tile width for M x N.
 inline int thin_bn(int64_t M, int64_t N, int cus) {
     for (const int bn : {128, 64})
-        if (cdiv(M, geom::kThinBM) * cdiv(N, bn) >= static_cast<int64_t>(cus)) return bn;
+        if (4 * cdiv(M, geom::kThinBM) * cdiv(N, bn) >= 3 * static_cast<int64_t>(cus)) return bn;
     return 32;
 }
 
@@ -134,7 +137,8 @@ inline int thin_max_stages(int bn, bool per_col) {
 }
 
 // The thin kernel's waves per workgroup: 8 (16-row waves, two per SIMD) for 64- and 128-column
-// tiles when the grid is at most one workgroup per CU, else 4.
+// tiles when the grid is at most one workgroup per CU, else 4 (768 x 4096 x 4096, 384 workgroups of
+// 64 x 128: 29.7 us in 8 waves, 26.8 in 4).
 inline int thin_waves(int bn, int64_t wgs, int cus) { return bn >= 64 && wgs <= static_cast<int64_t>(cus) ? 8 : 4; }
 
 inline int thin_stages(int bn, bool per_col, int64_t wgs, int cus) {

@@ -153,8 +153,8 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  * Scale reads are limited to rows < M, columns < N and K-blocks < ceil(K/128).
  * Schedule: one workgroup per 256 x 256 output tile, or per 128 x 256 tile when M <= 128 or the
  * 256-row tiles number at most half the compute units. When the 128 x 256 tiles would fill at most
- * half the compute units, one workgroup per 64 x 128, 64 x 64 or 64 x 32 tile (the widest giving
- * every compute unit a workgroup) over the whole K range; all three tile shapes give
+ * half the compute units, one workgroup per 64 x 128, 64 x 64 or 64 x 32 tile (the widest whose
+ * workgroups occupy three quarters of the compute units) over the whole K range; all tile shapes give
  * bit-identical results. Only when
  * those tiles are fewer than half the compute units and K exceeds 64 blocks are the K-blocks split
  * over S workgroups per 128- or 256-row tile, which write fp32 partial tiles to the pooled

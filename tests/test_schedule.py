@@ -42,9 +42,11 @@ EXPECTED = {
     (1024, 4096, 4096): (1, 64, 128),    # 128 tiles of 128 rows, half the CUs: thin, 512 of 64 x 128
     (512, 4096, 4096): (1, 64, 128),     # 64 x 128: 256 tiles, one per CU
     (256, 4096, 4096): (1, 64, 64),      # 64 x 128 would leave CUs idle: 64 x 64, 256 tiles
-    (384, 4096, 4096): (1, 64, 64),      # 384 tiles of 64 x 64
+    (384, 4096, 4096): (1, 64, 128),     # 192 tiles of 64 x 128: three quarters of the CUs
+    (192, 4096, 4096): (1, 64, 64),      # 192 tiles of 64 x 64
+    (160, 4096, 8192): (1, 64, 64),
     (128, 4096, 4096): (1, 64, 32),      # no width gives two per CU: the narrowest
-    (130, 5120, 1280): (1, 64, 32),      # tail-masking workload
+    (130, 5120, 1280): (1, 64, 64),      # tail-masking workload: 240 tiles of 64 x 64
     (2, 512, 128): (1, 64, 32),          # smallest workload
     (64, 1024, 8192): (1, 64, 32),       # 32 thin tiles, K = 64 blocks: still thin
     (64, 1024, 8320): (64, 128, 0),      # K = 65 blocks: split, 4 tiles x 64 slices = one round
@@ -81,15 +83,16 @@ def test_thin_kernel_boundary(sched):
         assert below[1] == 64 and at[1] != 64, (cus, below, at)
 
 
-def test_thin_width_gives_every_cu_a_workgroup(sched):
-    """The widest thin tile whose workgroups still cover the CUs (32 columns when none does)."""
-    for M in (64, 100, 128, 200, 256, 512, 700, 1000, 1024):
+def test_thin_width_occupies_three_quarters_of_the_cus(sched):
+    """The widest thin tile whose workgroups still occupy three quarters of the CUs (32 columns
+    when none does)."""
+    for M in (64, 100, 128, 192, 200, 256, 384, 512, 700, 1000, 1024):
         (_, bm, bn, _), = _plans(sched, [(M, 4096, 4096)])
         assert bm == 64
         wgs = lambda w: -(-M // 64) * -(-4096 // w)  # noqa: E731
         wider = [w for w in (128, 64, 32) if w > bn]
-        assert bn == 32 or wgs(bn) >= CUS, (M, bn)
-        assert all(wgs(w) < CUS for w in wider), (M, bn)
+        assert bn == 32 or 4 * wgs(bn) >= 3 * CUS, (M, bn)
+        assert all(4 * wgs(w) < 3 * CUS for w in wider), (M, bn)
 
 
 def test_split_slices_fit_one_round_and_the_workspace(sched):
