@@ -1,4 +1,4 @@
-// Host driver for the GEMM schedule rules (blockwise_scaled_fp8_act_amd/csrc/schedule.hpp, the
+// Host program for the GEMM schedule rules (blockwise_scaled_fp8_act_amd/csrc/schedule.hpp, the
 // header the library calls before each GEMM launch). Reads one query per line from stdin and
 // prints one answer per line:
 //   plan M N K fnuz cus max_bytes            -> S bm bn bytes
