@@ -141,6 +141,39 @@ int run_gemm(const void* a, int64_t lda, const float* a_s, const void* b, int64_
         plan.stages = env_int("BSFP8_GEMM_THIN_STAGES");
         plan.waves = env_int("BSFP8_GEMM_THIN_WAVES");
     }
+    // A partial last round of 256 x 256 tiles: the leading columns as one GEMM, the tail columns
+    // with K split (schedule.hpp, gemm_column_split). Automatic schedules with 128 x 128 B scales
+    // only; BSFP8_GEMM_COLUMN_SPLIT=0 turns it off.
+    const char* col_env = std::getenv("BSFP8_GEMM_COLUMN_SPLIT");
+    const bool col_off = col_env != nullptr && col_env[0] == '0';
+    if (!fnuz && !bs.per_column && !forced_s && !forced_bm && !forced_bn && !col_off) {
+        const bsfp8::ColumnSplit cs = bsfp8::gemm_column_split(M, N, K, cus, kMaxSplitWorkspace);
+        if (cs.n1 > 0 && (!use_scratch || cs.tail.bytes <= bsfp8::gemm_scratch_bytes())) {
+            float* ws = nullptr;
+            hipMemPool_t pool = nullptr;
+            if (use_scratch) {
+                if (bsfp8::gemm_scratch(&ws) != hipSuccess) return BSFP8_EHIP;
+            } else {
+                if (device_pool(&pool) != hipSuccess) return BSFP8_EHIP;
+                if (hipMallocFromPoolAsync(reinterpret_cast<void**>(&ws), static_cast<size_t>(cs.tail.bytes), pool,
+                                           stream) != hipSuccess)
+                    return BSFP8_EHIP;
+            }
+            const uint8_t* a8 = static_cast<const uint8_t*>(a);
+            const uint8_t* b8 = static_cast<const uint8_t*>(b);
+            uint16_t* c16 = static_cast<uint16_t*>(c);
+            hipError_t e = bsfp8::launch_gemm(a8, lda, a_s, b8, ldb, bs, c16, ldc, M, cs.n1, K, false, plan, nullptr,
+                                              cus, stream);
+            if (e == hipSuccess) {
+                bsfp8::BScale bs_tail = bs;
+                bs_tail.ptr = bs.ptr + (cs.n1 / bsfp8::geom::kBlockK) * bs.stride_nb;
+                e = bsfp8::launch_gemm(a8, lda, a_s, b8 + cs.n1 * ldb, ldb, bs_tail, c16 + cs.n1, ldc, M, N - cs.n1, K,
+                                       false, cs.tail, ws, cus, stream);
+            }
+            const hipError_t f = (!use_scratch && ws != nullptr) ? hipFreeAsync(ws, stream) : hipSuccess;
+            return finish(e != hipSuccess ? e : f);
+        }
+    }
     if (use_scratch) {
         if (plan.bytes > bsfp8::gemm_scratch_bytes()) return BSFP8_ESCRATCH;
         float* ws = nullptr;

@@ -203,4 +203,43 @@ inline SplitPlan gemm_split_plan_forced(int64_t M, int64_t N, int64_t K, bool fn
     return plan;
 }
 
+// Column split of a GEMM whose 256 x 256 tiles end in a partial round (4096 x 5120 x 5120: 320 tiles,
+// a second round of 64 on a quarter of the CUs): the first n1 columns (whole tile columns whose
+// tiles fill whole rounds) run as one GEMM; the last N - n1, whose tiles would fill at most a
+// quarter of the CUs, run as a second with K split in at least 4 so its slices fill the chip
+// (`tail`). A tile of a sparse last round runs faster than one of a full round (less contention, a
+// higher clock), which the split gives back: measured at the settled clock, 4096 x 5120 x 5120
+// 125 -> 118 us and 4096 x 5120 x 4096 103 -> 100 us with 4 slices, but 8192 x 5120 x 5120 (a
+// tail of 128 tiles in 2 slices) 195 -> 207 us, hence the quarter. Only where the B scales are
+// 128 x 128 blocks (an offset of n1 / 128 blocks addresses the tail's) and the automatic plan is
+// unsplit 256-row tiles. n1 == 0: no column split.
+struct ColumnSplit {
+    int64_t n1;
+    SplitPlan tail;
+};
+inline ColumnSplit gemm_column_split(int64_t M, int64_t N, int64_t K, int cus, int64_t max_bytes) {
+    const ColumnSplit none{0, SplitPlan{1, 0, 0, geom::kFastBM, 0}};
+    const SplitPlan plan = gemm_split_plan(M, N, K, false, cus, max_bytes);
+    if (plan.bm != geom::kFastBM || plan.S != 1) return none;
+    const int64_t mt = sched::cdiv(M, geom::kFastBM), nt = sched::cdiv(N, geom::kFastBN);
+    const int64_t tiles = mt * nt;
+    if (tiles <= cus || tiles % cus == 0) return none;
+    int64_t nt1 = nt - 1;
+    while (nt1 >= 1 && (mt * nt1) % cus != 0) --nt1;
+    if (nt1 < 1) return none;
+    const int64_t tail_tiles = mt * (nt - nt1);
+    if (4 * tail_tiles > cus) return none;
+    const int64_t n1 = nt1 * geom::kFastBN;
+    const int S = static_cast<int>(cus / tail_tiles);
+    const SplitPlan tail = gemm_split_plan_forced(M, N - n1, K, false, cus, S, geom::kFastBM, 0, max_bytes);
+    if (tail.S < 4 || tail.bm != geom::kFastBM) return none;
+    // Worth it only when the K-blocks the split takes off the tail's critical path (~1.9 us each
+    // for a 256 x 256 tile at the settled clock) outweigh the partial tiles' traffic (S fp32 slices
+    // written and read, bf16 C written; ~5 TB/s).
+    const double saved_us = static_cast<double>(sched::cdiv(K, geom::kBlockK)) * (tail.S - 1) / tail.S * 1.9;
+    const double sum_us = static_cast<double>(M) * static_cast<double>(N - n1) * (8.0 * tail.S + 2.0) / 5e6;
+    if (saved_us < sum_us) return none;
+    return ColumnSplit{n1, tail};
+}
+
 }  // namespace bsfp8

@@ -159,7 +159,11 @@ int quantize_lhs_and_rhs(const void* x, int64_t R, int64_t C, int64_t ldx,
  * those tiles are fewer than half the compute units and K exceeds 64 blocks are the K-blocks split
  * over S workgroups per 128- or 256-row tile, which write fp32 partial tiles to the pooled
  * workspace, and a second kernel sums the S partials in a fixed order into C (same result on every
- * call). The environment variables BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N,
+ * call). When the 256 x 256 tiles end in a last round that would fill at most a quarter of the
+ * compute units and K is long enough, the leading columns that fill whole rounds run as one GEMM and
+ * the remaining columns as a second with K split in at least four (128 x 128 B scales only; the
+ * leading columns' results are those of the unsplit schedule bit for bit; BSFP8_GEMM_COLUMN_SPLIT=0
+ * turns it off). The environment variables BSFP8_GEMM_SPLIT, BSFP8_GEMM_TILE_M, BSFP8_GEMM_TILE_N,
  * BSFP8_GEMM_THIN_STAGES and BSFP8_GEMM_THIN_WAVES, read at each call, force S (1 = never split; S
  * is clamped to ceil(K/128) and to the workspace bound; a split uses the 128- or 256-row tiles), the
  * tile height (256, 128 or 64), the width of the 64-row tiles (32, 64 or 128), their LDS pipeline

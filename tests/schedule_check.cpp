@@ -7,6 +7,7 @@
 //   lhs M Kb cus                             -> pieces per thread of quantize_lhs's row strips
 //   maxstages bn per_col                     -> the thin kernel's deepest pipeline that fits the LDS
 //   waves bn wgs cus                         -> the thin kernel's waves per workgroup
+//   colsplit M N K cus max_bytes             -> n1 S bytes of the column split (n1 0: none)
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -39,6 +40,12 @@ int main() {
             int64_t wgs;
             in >> bn >> per_col >> wgs >> cus;
             std::printf("%d\n", bsfp8::sched::thin_stages(bn, per_col != 0, wgs, cus));
+        } else if (kind == "colsplit") {
+            int64_t M, N, K, maxb;
+            int cus;
+            in >> M >> N >> K >> cus >> maxb;
+            const bsfp8::ColumnSplit c = bsfp8::gemm_column_split(M, N, K, cus, maxb);
+            std::printf("%lld %d %lld\n", (long long)c.n1, c.tail.S, (long long)c.tail.bytes);
         } else if (kind == "waves") {
             int bn, cus;
             int64_t wgs;

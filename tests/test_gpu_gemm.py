@@ -434,6 +434,33 @@ def test_gemm_thin_every_pipeline_depth(M, N, K, ld, bn, per_col, monkeypatch):
         fn(torch.empty((M, N), dtype=torch.bfloat16, device=DEV))
 
 
+def test_gemm_column_split(monkeypatch):
+    """4096 x 5120 x 4096 (320 tiles of 256 x 256: one round and a quarter) runs its first 4096
+    columns as one GEMM and the last 1024 with K split in 4: the leading columns equal the unsplit
+    schedule bit for bit (same tiles, same order), every column is within the oracle's tolerance on
+    sampled rows, and the allocation-free entry point (its tail slices in the static scratch) gives
+    the same bits."""
+    M, N, K = 4096, 5120, 4096
+    g = inputs.rng(11)
+    a_h = inputs.normal_bf16(g, (M, K))
+    w_h = inputs.normal_bf16(g, (N, K), 0.02)
+    oqa, osa = oracle.quantize_lhs(a_h)
+    oqw, _, osw = oracle.quantize_weight_128x128(w_h, want_qT=False)
+    qa, sa, qw, sw = to_dev(oqa), to_dev(osa), to_dev(oqw), to_dev(osw)
+    for k in ("BSFP8_GEMM_SPLIT", "BSFP8_GEMM_TILE_M", "BSFP8_GEMM_TILE_N", "BSFP8_GEMM_COLUMN_SPLIT"):
+        monkeypatch.delenv(k, raising=False)
+    split = bf.gemm_1x128_128x128(qa, sa, qw, sw).cpu().float().numpy()
+    c_na = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    bf.gemm_1x128_128x128_noalloc(qa, sa, qw, sw, c_na)
+    assert np.array_equal(c_na.cpu().float().numpy().view(np.uint32), split.view(np.uint32))
+    monkeypatch.setenv("BSFP8_GEMM_COLUMN_SPLIT", "0")
+    whole = bf.gemm_1x128_128x128(qa, sa, qw, sw).cpu().float().numpy()
+    assert np.array_equal(split[:, :4096].view(np.uint32), whole[:, :4096].view(np.uint32))
+    rows = _sample_rows(M, 256, seed=5)
+    co = oracle.gemm_1x128_128x128(oqa, osa, oqw, osw, osw.shape[1], 1, rows=rows)
+    _assert_close(split[rows], co, "column split")
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (512, 4096, 4096), (2048, 4096, 4096),
                                    (2, 5120, 1280), (4, 3584, 640)], ids=lambda v: str(v))
 def test_forward_short_wide_shapes_full(M, N, K, monkeypatch):

@@ -211,3 +211,28 @@ def test_thin_waves(sched):
     q = [(64, 256, 8), (128, 256, 8), (128, 200, 8), (64, 257, 4), (128, 384, 4), (32, 256, 4), (32, 100, 4)]
     got = sched([f"waves {bn} {w} {CUS}" for bn, w, _ in q])
     assert [g[0] for g in got] == [want for _, _, want in q]
+
+
+# (M, N, K) -> (n1, S of the tail): a partial last round of 256 x 256 tiles runs its leading whole
+# rounds of tile columns as one GEMM and the tail columns with K split
+COLSPLIT = {
+    (4096, 5120, 5120): (4096, 4),   # 320 tiles: 256 + 64 in 4 slices
+    (4096, 5120, 4096): (4096, 4),
+    (8192, 5120, 5120): (0, 1),      # 640 tiles: a tail of 128 would split only in 2 (measured slower)
+    (4096, 5120, 2048): (0, 1),      # 16 K-blocks: the partial sums would cost more than they save
+    (4096, 4096, 4096): (0, 1),      # whole rounds
+    (16384, 5120, 5120): (0, 1),     # 1280 tiles: five whole rounds
+    (6144, 4096, 4096): (0, 1),      # no whole-round prefix of tile columns (24 x nt1 never 256 k)
+    (1024, 4096, 4096): (0, 1),      # the thin kernel's shape
+}
+
+
+def test_column_split(sched):
+    shapes = list(COLSPLIT)
+    got = sched([f"colsplit {M} {N} {K} {CUS} {MAXB}" for (M, N, K) in shapes])
+    for sh, g in zip(shapes, got):
+        assert (g[0], g[1] if g[0] else 1) == COLSPLIT[sh], (sh, g)
+        if g[0]:
+            M, N, K = sh
+            assert g[0] % 256 == 0 and (-(-M // 256) * (g[0] // 256)) % CUS == 0
+            assert g[2] == g[1] * M * ((N - g[0] + 7) // 8 * 8) * 4 <= MAXB
