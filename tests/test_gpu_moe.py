@@ -91,6 +91,31 @@ def test_grouped_forward_and_dgrad(offsets):
     assert np.all(_bf16_of(dx)[~covered] == SENTINEL), "dgrad wrote a row outside every expert"
 
 
+def test_grouped_forward_at_the_workload():
+    """The expert-grouped forward workload (8 experts, 16384 tokens in multiples of 128, 4096 ->
+    2048; six experts end in a half-filled 256-row tile): sampled rows of every expert, its first and
+    last rows and the rows around the last whole tile included, match the oracle."""
+    E, T, Di, Do = 8, 16384, 4096, 2048
+    counts = np.array([2432, 2432, 1920, 1664, 1280, 2048, 2176, 2432])
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    g = _g(11)
+    a = inputs.normal_bf16(g, (T, Di))
+    qa, sa = bf.quantize_lhs(to_dev(a))
+    w, q, qT, s = _stacked_weights(E, Do, Di, seed=12)
+    Kb, Nb = Di // 128, Do // 128
+    off = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    c = bf.gemm_1x128_128x128_grouped(qa, sa, to_dev(q), to_dev(s), off, E, b_stride=Do * Di,
+                                      bs_stride=Nb * Kb, bs_stride_nb=Kb, bs_stride_kb=1, N=Do)
+    torch.cuda.synchronize()
+    qa_h, sa_h = qa.cpu().numpy(), sa.cpu().numpy()
+    c_h = c.float().cpu().numpy()
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        r = np.unique(np.concatenate([[lo, hi - 1, hi - 128, hi - 129], g.integers(lo, hi, 28)]))
+        co = oracle.gemm_1x128_128x128(qa_h[r], sa_h[:, r], q[e * Do:(e + 1) * Do], s[e * Nb:(e + 1) * Nb], Kb, 1)
+        _check(c_h[r], co, f"expert {e}")
+
+
 def test_grouped_single_expert_equals_dense():
     """E = 1 over all rows is the dense kernel, bit for bit (a shape with enough output tiles that
     the dense GEMM does not split K)."""
