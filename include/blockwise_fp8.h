@@ -181,7 +181,9 @@ int gemm_1x128_128x128(const void* a, int64_t lda, const float* a_s,
  * arguments, result, limits and split schedule; the K-split partial tiles live in a static scratch
  * array of 64 MiB that each GPU holds for the life of the process, so the call allocates nothing
  * (no hipMalloc, no pool). 64 MiB covers every automatic split plan; a plan forced larger through
- * BSFP8_GEMM_SPLIT returns BSFP8_ESCRATCH before any launch. Every call on one GPU shares that
+ * BSFP8_GEMM_SPLIT returns BSFP8_ESCRATCH before any launch. The column split of a partial last
+ * round runs here only when its tail's partial tiles fit the scratch; otherwise this entry runs the
+ * unsplit schedule, whose tail columns can then differ from gemm_1x128_128x128's in the last bits. Every call on one GPU shares that
  * GPU's scratch: calls on one stream are ordered, but calls that overlap in time on one GPU (other
  * streams, other threads) race on it. No part of the scratch needs clearing (each slice writes its
  * whole partial tile before the sum reads it).
