@@ -643,7 +643,27 @@ __global__ __launch_bounds__((Cfg<BM, WM>::kThreads), 1) void gemm_kernel(
         // (token ranges of the weight gradient, multiples of 128) and writes its own C. A range
         // whose ends (clamped into [0, K] and to non-decreasing order) are not multiples of 128 has
         // no K-blocks of its own: its C is filled with NaN and *status set, nothing is rounded.
-        const int64_t e = blockIdx.y;
+        // Up to 64 experts, blockIdx.y = r runs the expert of rank r in decreasing order of K-blocks
+        // (ties by index): workgroups are dispatched in order of blockIdx.y, so the longest tiles
+        // start first and the shortest fill the last round.
+        int64_t e = blockIdx.y;
+        if (grp.E <= 64) {
+            const auto kblocks = [&](int64_t j) -> int64_t {
+                const int64_t a = min(max(grp.offsets[j], int64_t{0}), K);
+                const int64_t b = min(max(grp.offsets[j + 1], a), K);
+                return a % kGroup != 0 || b % kGroup != 0 ? 0 : b / kGroup - a / kGroup;
+            };
+            const int64_t mine = lane < grp.E ? kblocks(lane) : -1;  // lane j: expert j's K-blocks
+            int rank = 0;
+            for (int j = 0; j < static_cast<int>(grp.E); ++j) {
+                const uint32_t lo32 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine), j));
+                const uint32_t hi32 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine >> 32), j));
+                const int64_t kj = static_cast<int64_t>((static_cast<uint64_t>(hi32) << 32) | lo32);
+                rank += kj > mine || (kj == mine && j < lane) ? 1 : 0;
+            }
+            const uint64_t hit = __ballot(lane < grp.E && rank == static_cast<int>(blockIdx.y));
+            if (hit != 0) e = __ffsll(static_cast<unsigned long long>(hit)) - 1;  // ranks are a permutation: one lane
+        }
         const int64_t lo = min(max(grp.offsets[e], int64_t{0}), K);
         const int64_t hi = min(max(grp.offsets[e + 1], lo), K);
         const int64_t kb0 = lo / kGroup;
